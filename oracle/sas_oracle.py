@@ -1,0 +1,470 @@
+"""CPU oracle for SAS gated block-sparse attention (test infrastructure).
+
+THIS IS TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT PATH.  Only ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import or call it.  It shares no code with the HIP library and imports nothing
+from it.  Everything is plain numpy in float64; inputs are whatever float arrays
+the caller passes (bf16 workloads pass the bf16-rounded values as float32).
+
+Sources (the only technical description of the method is the Chinese review
+page "论文综述：SAS——通过端到端优化上下文排序实现简单的注意力稀疏化" on
+paper.oopus.info, cited below as [Review]; the project README on gitee is
+cited as [README]):
+
+* [Review §2.1]  contiguous blocks of b = 64 tokens; the current block is
+  always kept.
+* [Review §2.2, selector equation]  scores s for every history block; keep the
+  Top-K history blocks plus the current block; skip the rest.
+* [Review §2.3, equation for o_SAS]  o = softmax(q K_S^T + log g_S) V_S.
+* [Review §2.4, equation for log g_m]  log g_m = s_m - LSE(s) over the history
+  blocks H; the current block has g_0 = 1 (no bias).
+* [Review §2.6]  the fused kernel adds each selected block's log-gate to its
+  logits, masks unselected blocks, leaves the current block unbiased; its
+  backward sums the logit gradients inside each selected block to get that
+  block's gate gradient.
+* [README, figure caption (b)]  Top-K stays a discrete choice; gradients
+  reach the selector only through the continuous gates.
+
+Readings taken where the pages are silent (each is also listed in the design
+notes):
+
+* scale: logits are tau * (q . k) + log g with tau = 1/sqrt(d) by default; the
+  gate bias is not scaled.
+* selection granularity: one selection per (batch, kv-head, 64-query block),
+  shared by the G = Hq/Hkv query heads of the group; query head h uses kv-head
+  h // G.
+* block numbering is absolute, 0 .. n/64-1; q-block i has history {0..i-1}
+  and current block i.
+* the LSE runs over all history blocks, selected or not; with fewer than K
+  history blocks all of them are selected (still gated).
+* ties in s go to the lower block index; -0.0 and +0.0 are equal.
+* idx lists the selected blocks in ascending order, padded with -1; padded
+  log_gate entries are -inf; s_lse of a row with no history is -inf.
+* causal rule inside the current block: key j is visible to query t iff j <= t.
+* decode: the query is token T = seq_len-1; its current block is T // 64 and
+  holds the tokens [64*(T//64), seq_len); its history is the blocks before it.
+* pooling stand-in selector: s[i, m] = mean_{G heads, 64 rows}(q) .
+  mean_{64 rows}(k_m) / sqrt(d), for every (i, m) pair.
+
+Every function here is pinned by the CPU tests in ``tests/test_oracle_*.py``
+(brute force, closed forms, invariants, library special cases, finite
+differences); see each function's docstring for its pins.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+BLOCK = 64
+NEG_INF = -np.inf
+
+
+def _f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+# ============================================================== pooling
+def pool_scores(q, k, Hkv: int):
+    """Mean-pooled block scores (the stand-in selector of the 32K workload).
+
+    s[b, kv, i, m] = qbar[b, kv, i] . kbar[b, kv, m] / sqrt(d), where qbar is
+    the mean of the 64 rows x G query heads of q-block i in kv-group kv, and
+    kbar the mean of the 64 rows of key block m.  Computed for every (i, m).
+
+    Follows [Review §2.2] (a score per history block from q and K_{B_m}) with
+    the mean-pool reading of the selector.  Pinned by: constant-block closed
+    form and a pure-Python brute force on a tiny case.
+    """
+    q, k = _f64(q), _f64(k)
+    B, Hq, n, d = q.shape
+    G = Hq // Hkv
+    nb = n // BLOCK
+    qbar = q.reshape(B, Hkv, G, nb, BLOCK, d).mean(axis=(2, 4))
+    kbar = k.reshape(B, Hkv, nb, BLOCK, d).mean(axis=3)
+    return np.einsum("bkid,bkmd->bkim", qbar, kbar) / math.sqrt(d)
+
+
+# ============================================================== selection
+def select_row(srow, i: int, topk: int):
+    """Select for one query block i from its score row (length >= i).
+
+    Returns (chosen ascending list, log_gate list aligned with it, s_lse).
+
+    [Review §2.2]: keep the Top-K history blocks by score.  [Review §2.4]:
+    log g_m = s_m - LSE over all history blocks.  Ranking key (-s_m, m) makes
+    ties go to the lower index; adding +0.0 turns -0.0 into +0.0 first.
+    Pinned by: a sort-free rank-count brute force, integer and signed-zero tie
+    fixtures, shift invariance, permutation covariance, K = 0 and K >= i.
+    """
+    if i == 0:
+        return [], [], NEG_INF
+    h = _f64(srow[:i]) + 0.0
+    mx = float(h.max())
+    s_lse = mx + math.log(float(np.sum(np.exp(h - mx))))
+    order = sorted(range(i), key=lambda m: (-h[m], m))
+    chosen = sorted(order[:min(topk, i)])
+    return chosen, [float(h[m]) - s_lse for m in chosen], s_lse
+
+
+def select(s, topk: int):
+    """idx [B,Hkv,NQB,K] int32 (ascending, -1 padded), cnt [B,Hkv,NQB] int32,
+    log_gate [B,Hkv,NQB,K] float64 (-inf padded), s_lse [B,Hkv,NQB] float64.
+
+    Row i of s is the score row of q-block i; only entries m < i are read.
+    """
+    s = np.asarray(s)
+    B, Hkv, NQB, _ = s.shape
+    K = int(topk)
+    idx = np.full((B, Hkv, NQB, K), -1, dtype=np.int32)
+    cnt = np.zeros((B, Hkv, NQB), dtype=np.int32)
+    lg = np.full((B, Hkv, NQB, K), NEG_INF)
+    lse = np.full((B, Hkv, NQB), NEG_INF)
+    for b in range(B):
+        for kv in range(Hkv):
+            for i in range(NQB):
+                ch, g, l = select_row(s[b, kv, i], i, K)
+                c = len(ch)
+                cnt[b, kv, i] = c
+                idx[b, kv, i, :c] = ch
+                lg[b, kv, i, :c] = g
+                lse[b, kv, i] = l
+    return idx, cnt, lg, lse
+
+
+# ============================================================== forward
+def bias_matrix(n: int, idx_row, cnt_row, lg_row):
+    """Dense n x n additive bias of one (batch, kv-head) [Review §2.3, §2.6].
+
+    A[t, j] = 0 if j is in t's own block and j <= t (current block, g_0 = 1);
+    A[t, j] = log_gate of block(j) if block(j) is selected by block(t);
+    A[t, j] = -inf otherwise (skipped).
+    """
+    nb = n // BLOCK
+    A = np.full((n, n), NEG_INF)
+    for i in range(nb):
+        r = slice(i * BLOCK, (i + 1) * BLOCK)
+        for slot in range(int(cnt_row[i])):
+            m = int(idx_row[i, slot])
+            A[r, m * BLOCK:(m + 1) * BLOCK] = lg_row[i, slot]
+        tri = np.tril(np.ones((BLOCK, BLOCK), dtype=bool))
+        blk = A[r, r]
+        blk[tri] = 0.0
+        A[r, r] = blk
+    return A
+
+
+def _softmax_rows(Z):
+    L = Z.max(axis=-1, keepdims=True)
+    L = L + np.log(np.sum(np.exp(Z - L), axis=-1, keepdims=True))
+    return np.exp(Z - L), L[..., 0]
+
+
+def fwd_dense(q, k, v, idx, cnt, log_gate, scale=None):
+    """Dense definition: for each query head h (kv-head h // G),
+    Z = tau Q_h K^T + A, L = rowwise logsumexp(Z), O_h = exp(Z - L) V.
+
+    [Review §2.3] equation for o_SAS with the bias A of ``bias_matrix``.
+    Returns (o [B,Hq,n,d], lse [B,Hq,n]) in float64.  Pinned by: K = 0 equals
+    block-diagonal causal SDPA; constant scores with K >= n/64 equal causal
+    SDPA with a -log(i) history bias; q-block 0 equals causal SDPA; output
+    permutation and shift invariance; GQA equals MHA with repeated K/V.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Hq, n, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    tau = (1.0 / math.sqrt(d)) if not scale else float(scale)
+    o = np.zeros_like(q)
+    lse = np.zeros((B, Hq, n))
+    for b in range(B):
+        for kv in range(Hkv):
+            A = bias_matrix(n, idx[b, kv], cnt[b, kv], log_gate[b, kv])
+            for g in range(G):
+                h = kv * G + g
+                P, L = _softmax_rows(tau * q[b, h] @ k[b, kv].T + A)
+                o[b, h] = P @ v[b, kv]
+                lse[b, h] = L
+    return o, lse
+
+
+def _gather_cols(i: int, idx_row, cnt_row, lg_row):
+    """Key columns of q-block i (selected blocks in slot order, then the
+    current block) with their per-column bias and block slot (-1 = current)."""
+    cols, bias, slot = [], [], []
+    for sl in range(int(cnt_row[i])):
+        m = int(idx_row[i, sl])
+        cols.append(np.arange(m * BLOCK, (m + 1) * BLOCK))
+        bias.append(np.full(BLOCK, float(lg_row[i, sl])))
+        slot.append(np.full(BLOCK, sl))
+    cols.append(np.arange(i * BLOCK, (i + 1) * BLOCK))
+    bias.append(np.zeros(BLOCK))
+    slot.append(np.full(BLOCK, -1))
+    return np.concatenate(cols), np.concatenate(bias), np.concatenate(slot)
+
+
+def _block_logits(qi, kc, bias, slot, tau):
+    """Z for the 64 rows of one q-block over its gathered columns, with the
+    causal mask (j <= t) on the current block's columns."""
+    Z = tau * qi @ kc.T + bias[None, :]
+    cur = slot == -1
+    tri = np.tril(np.ones((BLOCK, BLOCK), dtype=bool))
+    Zc = Z[:, cur]
+    Zc[~tri] = NEG_INF
+    Z[:, cur] = Zc
+    return Z
+
+
+def fwd_gather_block(q, k, v, idx, cnt, log_gate, b: int, kv: int, i: int, scale=None):
+    """Gather-mode forward of one (batch, kv-group, q-block): the formula of
+    ``fwd_dense`` evaluated only on columns whose bias is finite, which is
+    exact because exp(-inf) = 0.  Returns (o [G,64,d], lse [G,64])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    Hq, d = q.shape[1], q.shape[3]
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    tau = (1.0 / math.sqrt(d)) if not scale else float(scale)
+    cols, bias, slot = _gather_cols(i, idx[b, kv], cnt[b, kv], log_gate[b, kv])
+    kc, vc = k[b, kv, cols], v[b, kv, cols]
+    r = slice(i * BLOCK, (i + 1) * BLOCK)
+    o = np.zeros((G, BLOCK, d))
+    lse = np.zeros((G, BLOCK))
+    for g in range(G):
+        P, L = _softmax_rows(_block_logits(q[b, kv * G + g, r], kc, bias, slot, tau))
+        o[g] = P @ vc
+        lse[g] = L
+    return o, lse
+
+
+def fwd_gather(q, k, v, idx, cnt, log_gate, scale=None, blocks=None):
+    """Gather-mode forward over all q-blocks (or the (b, kv, i) list given)."""
+    B, Hq, n, d = np.shape(q)
+    Hkv = np.shape(k)[1]
+    G = Hq // Hkv
+    o = np.zeros((B, Hq, n, d))
+    lse = np.zeros((B, Hq, n))
+    todo = blocks if blocks is not None else [
+        (b, kv, i) for b in range(B) for kv in range(Hkv) for i in range(n // BLOCK)]
+    for (b, kv, i) in todo:
+        ob, lb = fwd_gather_block(q, k, v, idx, cnt, log_gate, b, kv, i, scale)
+        r = slice(i * BLOCK, (i + 1) * BLOCK)
+        o[b, kv * G:(kv + 1) * G, r] = ob
+        lse[b, kv * G:(kv + 1) * G, r] = lb
+    return o, lse
+
+
+# ============================================================== backward
+def gate_jacobian(s, s_lse, idx, cnt, dlg):
+    """ds from the per-slot gate gradient dlg (chain rule through [Review §2.4]).
+
+    log g_m = s_m - LSE(s_H) for m in H_i, so for every history block m:
+    ds[i, m] = [m selected] dlg[i, m] - pi_i[m] * sum_{m' selected} dlg[i, m'],
+    pi_i = softmax(s[i, H_i]) = exp(s - s_lse).  Entries m >= i are 0.
+    Pinned by finite differences through select + forward, and by
+    sum_m ds[i, m] = 0.
+    """
+    s = _f64(s)
+    B, Hkv, NQB, NKB = s.shape
+    ds = np.zeros((B, Hkv, NQB, NKB))
+    for b in range(B):
+        for kv in range(Hkv):
+            for i in range(1, NQB):
+                c = int(cnt[b, kv, i])
+                pi = np.exp(s[b, kv, i, :i] - s_lse[b, kv, i])
+                tot = float(np.sum(dlg[b, kv, i, :c]))
+                ds[b, kv, i, :i] = -pi * tot
+                for sl in range(c):
+                    ds[b, kv, i, int(idx[b, kv, i, sl])] += dlg[b, kv, i, sl]
+    return ds
+
+
+def bwd_dense(q, k, v, do, idx, cnt, log_gate, scale=None):
+    """Analytic backward of the dense definition (no autograd).
+
+    With P = softmax(Z), O = P V and upstream dO:
+      D = rowsum(dO o O), dP = dO V^T, dZ = P o (dP - D),
+      dQ_h = tau dZ K, dK = tau sum_h dZ^T Q_h, dV = sum_h P^T dO_h,
+      dlg[i, slot] = sum over the group's heads, rows t of block i and columns
+      j of the slot's block m of dZ[t, j]  ([Review §2.6] block-sum rule).
+    Returns (dq, dk, dv, dlg [B,Hkv,NQB,K]) in float64.  Pinned by central
+    finite differences in float64 and by the row identity sum_j dZ[t, j] = 0.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, Hq, n, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    K = idx.shape[-1]
+    tau = (1.0 / math.sqrt(d)) if not scale else float(scale)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    dlg = np.zeros((B, Hkv, n // BLOCK, K))
+    for b in range(B):
+        for kv in range(Hkv):
+            A = bias_matrix(n, idx[b, kv], cnt[b, kv], log_gate[b, kv])
+            for g in range(G):
+                h = kv * G + g
+                P, _ = _softmax_rows(tau * q[b, h] @ k[b, kv].T + A)
+                O = P @ v[b, kv]
+                D = np.sum(do[b, h] * O, axis=1, keepdims=True)
+                dZ = P * (do[b, h] @ v[b, kv].T - D)
+                dq[b, h] = tau * dZ @ k[b, kv]
+                dk[b, kv] += tau * dZ.T @ q[b, h]
+                dv[b, kv] += P.T @ do[b, h]
+                for i in range(n // BLOCK):
+                    r = slice(i * BLOCK, (i + 1) * BLOCK)
+                    for sl in range(int(cnt[b, kv, i])):
+                        m = int(idx[b, kv, i, sl])
+                        dlg[b, kv, i, sl] += dZ[r, m * BLOCK:(m + 1) * BLOCK].sum()
+    return dq, dk, dv, dlg
+
+
+def bwd_gather_block(q, k, v, do, idx, cnt, log_gate, b: int, kv: int, i: int, scale=None):
+    """Backward contributions of one (batch, kv-group, q-block) in gather mode.
+
+    Returns (dq [G,64,d], cols, dk_cols [len(cols),d], dv_cols, dlg_row [K]):
+    dq of the block's rows is complete; dk_cols/dv_cols are this q-block's
+    additive contributions to the gathered key rows ``cols``.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    Hq, d = q.shape[1], q.shape[3]
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    K = idx.shape[-1]
+    tau = (1.0 / math.sqrt(d)) if not scale else float(scale)
+    cols, bias, slot = _gather_cols(i, idx[b, kv], cnt[b, kv], log_gate[b, kv])
+    kc, vc = k[b, kv, cols], v[b, kv, cols]
+    r = slice(i * BLOCK, (i + 1) * BLOCK)
+    dq = np.zeros((G, BLOCK, d))
+    dkc = np.zeros((len(cols), d))
+    dvc = np.zeros((len(cols), d))
+    dlg = np.zeros(K)
+    for g in range(G):
+        h = kv * G + g
+        P, _ = _softmax_rows(_block_logits(q[b, h, r], kc, bias, slot, tau))
+        O = P @ vc
+        D = np.sum(do[b, h, r] * O, axis=1, keepdims=True)
+        dZ = P * (do[b, h, r] @ vc.T - D)
+        dq[g] = tau * dZ @ kc
+        dkc += tau * dZ.T @ q[b, h, r]
+        dvc += P.T @ do[b, h, r]
+        colsum = dZ.sum(axis=0)
+        for sl in range(int(cnt[b, kv, i])):
+            dlg[sl] += colsum[slot == sl].sum()
+    return dq, cols, dkc, dvc, dlg
+
+
+def bwd_gather(q, k, v, do, idx, cnt, log_gate, scale=None, blocks=None):
+    """Gather-mode backward over all q-blocks (or the listed (b, kv, i)).
+
+    With ``blocks`` given, dq is exact on those q-blocks' rows only and dk/dv
+    hold just their contributions."""
+    B, Hq, n, d = np.shape(q)
+    Hkv = np.shape(k)[1]
+    G = Hq // Hkv
+    K = idx.shape[-1]
+    dq = np.zeros((B, Hq, n, d))
+    dk = np.zeros((B, Hkv, n, d))
+    dv = np.zeros((B, Hkv, n, d))
+    dlg = np.zeros((B, Hkv, n // BLOCK, K))
+    todo = blocks if blocks is not None else [
+        (b, kv, i) for b in range(B) for kv in range(Hkv) for i in range(n // BLOCK)]
+    for (b, kv, i) in todo:
+        dqb, cols, dkc, dvc, dl = bwd_gather_block(q, k, v, do, idx, cnt, log_gate, b, kv, i, scale)
+        dq[b, kv * G:(kv + 1) * G, i * BLOCK:(i + 1) * BLOCK] = dqb
+        np.add.at(dk[b, kv], cols, dkc)
+        np.add.at(dv[b, kv], cols, dvc)
+        dlg[b, kv, i] = dl
+    return dq, dk, dv, dlg
+
+
+def reverse_lists(idx, cnt, b: int, kv: int, m: int):
+    """q-blocks whose key set contains block m: those that selected it, plus
+    block m itself (its current block)."""
+    NQB = idx.shape[2]
+    out = [i for i in range(m + 1, NQB)
+           if m in set(int(x) for x in idx[b, kv, i, :int(cnt[b, kv, i])])]
+    return [m] + out
+
+
+def bwd_kv_block(q, k, v, do, idx, cnt, log_gate, b: int, kv: int, m: int, scale=None):
+    """dk, dv [64, d] of key block m of (b, kv), summed over every q-block
+    that reads it (sampled full-size checks)."""
+    d = np.shape(q)[3]
+    dk = np.zeros((BLOCK, d))
+    dv = np.zeros((BLOCK, d))
+    rows = np.arange(m * BLOCK, (m + 1) * BLOCK)
+    for i in reverse_lists(idx, cnt, b, kv, m):
+        _, cols, dkc, dvc, _ = bwd_gather_block(q, k, v, do, idx, cnt, log_gate, b, kv, i, scale)
+        sel = np.isin(cols, rows)
+        pos = cols[sel] - m * BLOCK
+        np.add.at(dk, pos, dkc[sel])
+        np.add.at(dv, pos, dvc[sel])
+    return dk, dv
+
+
+# ============================================================== full pipeline
+def sas_forward_backward(q, k, v, do, s, topk: int, scale=None, mode: str = "gather"):
+    """select -> forward -> backward -> ds, everything float64.
+    Returns a dict with idx, cnt, log_gate, s_lse, o, lse, dq, dk, dv, dlg, ds."""
+    idx, cnt, lg, s_lse = select(s, topk)
+    if mode == "dense":
+        o, lse = fwd_dense(q, k, v, idx, cnt, lg, scale)
+        dq, dk, dv, dlg = bwd_dense(q, k, v, do, idx, cnt, lg, scale)
+    else:
+        o, lse = fwd_gather(q, k, v, idx, cnt, lg, scale)
+        dq, dk, dv, dlg = bwd_gather(q, k, v, do, idx, cnt, lg, scale)
+    ds = gate_jacobian(s, s_lse, idx, cnt, dlg)
+    return dict(idx=idx, cnt=cnt, log_gate=lg, s_lse=s_lse, o=o, lse=lse,
+                dq=dq, dk=dk, dv=dv, dlg=dlg, ds=ds)
+
+
+# ============================================================== decode
+def decode(q, k_cache, v_cache, seq_lens, s, topk: int, scale=None, rows=None):
+    """Single-token decode.  For batch entry b the query is token
+    T = seq_len - 1 in block i = T // 64; kv-group kv selects from s[b, kv, :i]
+    exactly as ``select_row``; each query head h of the group attends to the
+    selected blocks (bias log_gate) and to keys [64 i, seq_len) (bias 0).
+
+    ``rows`` limits the work to a list of (b, kv); k_cache/v_cache may then be
+    dicts {(b, kv): (k [cap,d] or block-indexable array)} - any object with
+    [b, kv] indexing that returns the [cap, d] cache of that pair works.
+    Returns (o [B,Hq,d] float64, idx [B,Hkv,K] int32); unlisted rows are 0/-1.
+    """
+    q = _f64(q)
+    B, Hq, d = q.shape
+    Hkv = s.shape[1]
+    G = Hq // Hkv
+    K = int(topk)
+    tau = (1.0 / math.sqrt(d)) if not scale else float(scale)
+    o = np.zeros((B, Hq, d))
+    idx = np.full((B, Hkv, K), -1, dtype=np.int32)
+    todo = rows if rows is not None else [(b, kv) for b in range(B) for kv in range(Hkv)]
+    for (b, kv) in todo:
+        L = int(seq_lens[b])
+        T = L - 1
+        i = T // BLOCK
+        chosen, lg, _ = select_row(s[b, kv], i, K)
+        idx[b, kv, :len(chosen)] = chosen
+        kc_all, vc_all = k_cache[b, kv], v_cache[b, kv]
+        cols = [np.arange(m * BLOCK, (m + 1) * BLOCK) for m in chosen]
+        bias = [np.full(BLOCK, g) for g in lg]
+        cols.append(np.arange(i * BLOCK, L))
+        bias.append(np.zeros(L - i * BLOCK))
+        cols = np.concatenate(cols)
+        bias = np.concatenate(bias)
+        kc = _f64(kc_all[cols])
+        vc = _f64(vc_all[cols])
+        for g in range(G):
+            h = kv * G + g
+            z = tau * kc @ q[b, h] + bias
+            z = z - z.max()
+            p = np.exp(z)
+            o[b, h] = (p / p.sum()) @ vc
+    return o, idx
+
+
+# ============================================================== work counts
+def selected_pairs(cnt):
+    """Valid (query, key) pairs per query head, summed over (b, kv, i):
+    64*64 per selected block plus 64*65/2 for the causal current block."""
+    cnt = np.asarray(cnt, dtype=np.int64)
+    return int(cnt.sum()) * BLOCK * BLOCK + cnt.size * (BLOCK * (BLOCK + 1) // 2)
