@@ -1,0 +1,191 @@
+"""Python binding of libsas: same names as the C ABI, torch tensors in.
+
+Argument marshalling only: every function checks that tensors are contiguous
+device tensors of the expected dtype, builds the shape struct and passes raw
+pointers plus the current HIP stream to the library.  All arithmetic happens
+in the library's kernels.  Outputs are written into caller-provided tensors;
+the ``alloc_*`` helpers only allocate (torch) tensors of the right shapes.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from ._lib import (BLOCK, SAS_BF16, SAS_F32, SasDecodeShape, SasError, SasShape, lib,
+                   status_string)
+
+_DT = {torch.float32: SAS_F32, torch.bfloat16: SAS_BF16}
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(t, name, dtype=None, numel=None, device=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+
+
+def _ok(st, where):
+    if st != 0:
+        raise SasError(st, where)
+
+
+def make_shape(B, Hq, Hkv, n, d, topk, dtype=torch.bfloat16, scale=0.0) -> SasShape:
+    return SasShape(B, Hq, Hkv, n, d, topk, float(scale), _DT[dtype])
+
+
+def make_decode_shape(B, Hq, Hkv, cap, d, topk, dtype=torch.bfloat16, scale=0.0) -> SasDecodeShape:
+    return SasDecodeShape(B, Hq, Hkv, cap, d, topk, float(scale), _DT[dtype])
+
+
+def shape_of(q: torch.Tensor, k: torch.Tensor, topk: int, scale: float = 0.0) -> SasShape:
+    B, Hq, n, d = q.shape
+    return make_shape(B, Hq, k.shape[1], n, d, topk, q.dtype, scale)
+
+
+def _dt(shape):
+    return torch.float32 if shape.dtype == SAS_F32 else torch.bfloat16
+
+
+# ------------------------------------------------------------------ entry points
+def sas_pool_workspace_bytes(shape: SasShape) -> int:
+    return int(lib().sas_pool_workspace_bytes(ctypes.byref(shape)))
+
+
+def sas_pool_scores(shape: SasShape, q, k, s, ws, stream=None):
+    dt = _dt(shape)
+    nb = shape.n // BLOCK
+    _check(q, "q", dt, shape.B * shape.Hq * shape.n * shape.d)
+    _check(k, "k", dt, shape.B * shape.Hkv * shape.n * shape.d)
+    _check(s, "s", torch.float32, shape.B * shape.Hkv * nb * nb)
+    _check(ws, "ws", torch.uint8)
+    _ok(lib().sas_pool_scores(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(s), _ptr(ws),
+                              ws.numel(), _stream(stream)), "sas_pool_scores")
+
+
+def sas_select(shape: SasShape, s, idx, cnt, log_gate, s_lse, stream=None):
+    nb = shape.n // BLOCK
+    rows = shape.B * shape.Hkv * nb
+    _check(s, "s", torch.float32, rows * nb)
+    _check(idx, "idx", torch.int32, rows * shape.topk)
+    _check(cnt, "cnt", torch.int32, rows)
+    _check(log_gate, "log_gate", torch.float32, rows * shape.topk)
+    _check(s_lse, "s_lse", torch.float32, rows)
+    _ok(lib().sas_select(ctypes.byref(shape), _ptr(s), _ptr(idx), _ptr(cnt), _ptr(log_gate),
+                         _ptr(s_lse), _stream(stream)), "sas_select")
+
+
+def sas_fwd(shape: SasShape, q, k, v, idx, cnt, log_gate, o, lse, stream=None):
+    dt = _dt(shape)
+    nb = shape.n // BLOCK
+    rows = shape.B * shape.Hkv * nb
+    _check(q, "q", dt, shape.B * shape.Hq * shape.n * shape.d)
+    _check(k, "k", dt, shape.B * shape.Hkv * shape.n * shape.d)
+    _check(v, "v", dt, shape.B * shape.Hkv * shape.n * shape.d)
+    _check(idx, "idx", torch.int32, rows * shape.topk)
+    _check(cnt, "cnt", torch.int32, rows)
+    _check(log_gate, "log_gate", torch.float32, rows * shape.topk)
+    _check(o, "o", dt, shape.B * shape.Hq * shape.n * shape.d)
+    _check(lse, "lse", torch.float32, shape.B * shape.Hq * shape.n)
+    _ok(lib().sas_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(cnt),
+                      _ptr(log_gate), _ptr(o), _ptr(lse), _stream(stream)), "sas_fwd")
+
+
+def sas_bwd_workspace_bytes(shape: SasShape) -> int:
+    return int(lib().sas_bwd_workspace_bytes(ctypes.byref(shape)))
+
+
+def sas_bwd(shape: SasShape, q, k, v, o, dO, lse, idx, cnt, log_gate, s, s_lse, dq, dk, dv, ds,
+            ws, stream=None):
+    dt = _dt(shape)
+    nb = shape.n // BLOCK
+    rows = shape.B * shape.Hkv * nb
+    nq = shape.B * shape.Hq * shape.n * shape.d
+    nk = shape.B * shape.Hkv * shape.n * shape.d
+    for t, nm, n_ in ((q, "q", nq), (o, "o", nq), (dO, "dO", nq), (dq, "dq", nq),
+                      (k, "k", nk), (v, "v", nk), (dk, "dk", nk), (dv, "dv", nk)):
+        _check(t, nm, dt, n_)
+    _check(lse, "lse", torch.float32, shape.B * shape.Hq * shape.n)
+    _check(idx, "idx", torch.int32, rows * shape.topk)
+    _check(cnt, "cnt", torch.int32, rows)
+    _check(log_gate, "log_gate", torch.float32, rows * shape.topk)
+    _check(s, "s", torch.float32, rows * nb)
+    _check(s_lse, "s_lse", torch.float32, rows)
+    _check(ds, "ds", torch.float32, rows * nb)
+    _check(ws, "ws", torch.uint8)
+    _ok(lib().sas_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO),
+                      _ptr(lse), _ptr(idx), _ptr(cnt), _ptr(log_gate), _ptr(s), _ptr(s_lse),
+                      _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ds), _ptr(ws), ws.numel(),
+                      _stream(stream)), "sas_bwd")
+
+
+def sas_decode_workspace_bytes(shape: SasDecodeShape) -> int:
+    return int(lib().sas_decode_workspace_bytes(ctypes.byref(shape)))
+
+
+def sas_decode(shape: SasDecodeShape, q, k_cache, v_cache, seq_lens, s, o, idx_out, ws,
+               stream=None):
+    dt = _dt(shape)
+    _check(q, "q", dt, shape.B * shape.Hq * shape.d)
+    _check(k_cache, "k_cache", dt, shape.B * shape.Hkv * shape.cap * shape.d)
+    _check(v_cache, "v_cache", dt, shape.B * shape.Hkv * shape.cap * shape.d)
+    _check(seq_lens, "seq_lens", torch.int32, shape.B)
+    _check(s, "s", torch.float32, shape.B * shape.Hkv * (shape.cap // BLOCK))
+    _check(o, "o", dt, shape.B * shape.Hq * shape.d)
+    _check(idx_out, "idx_out", torch.int32, shape.B * shape.Hkv * shape.topk)
+    _check(ws, "ws", torch.uint8)
+    _ok(lib().sas_decode(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                         _ptr(seq_lens), _ptr(s), _ptr(o), _ptr(idx_out), _ptr(ws), ws.numel(),
+                         _stream(stream)), "sas_decode")
+
+
+def sas_prof_enable(on: bool):
+    _ok(lib().sas_prof_enable(1 if on else 0), "sas_prof_enable")
+
+
+def sas_prof_collect(max_entries: int = 64):
+    """{kernel name: (total ms, launches)} since the last collect."""
+    names = (ctypes.c_char_p * max_entries)()
+    ms = (ctypes.c_double * max_entries)()
+    nl = (ctypes.c_int32 * max_entries)()
+    n = lib().sas_prof_collect(names, ms, nl, max_entries)
+    return {names[j].decode(): (ms[j], nl[j]) for j in range(min(n, max_entries))}
+
+
+# ------------------------------------------------------------------ allocation helpers
+def alloc_select(shape: SasShape, device="cuda"):
+    nb = shape.n // BLOCK
+    lead = (shape.B, shape.Hkv, nb)
+    return dict(idx=torch.empty(lead + (shape.topk,), dtype=torch.int32, device=device),
+                cnt=torch.empty(lead, dtype=torch.int32, device=device),
+                log_gate=torch.empty(lead + (shape.topk,), dtype=torch.float32, device=device),
+                s_lse=torch.empty(lead, dtype=torch.float32, device=device))
+
+
+def alloc_workspace(nbytes: int, device="cuda"):
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+__all__ = [
+    "make_shape", "make_decode_shape", "shape_of", "sas_pool_workspace_bytes", "sas_pool_scores",
+    "sas_select", "sas_fwd", "sas_bwd_workspace_bytes", "sas_bwd", "sas_decode_workspace_bytes",
+    "sas_decode", "sas_prof_enable", "sas_prof_collect", "alloc_select", "alloc_workspace",
+    "status_string", "SasError", "SasShape", "SasDecodeShape",
+]

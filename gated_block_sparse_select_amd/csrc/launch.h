@@ -1,0 +1,60 @@
+// Internal launcher declarations (host side).  Each launcher enqueues on the
+// given stream and returns hipGetLastError() of its launch(es); argument
+// checking happens in sas_api.cpp before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sas {
+
+// Profiling hooks used around every launch (no-ops unless enabled).
+void prof_before(const char* name, hipStream_t st);
+void prof_after(const char* name, hipStream_t st);
+
+struct ProfScope {
+  const char* name;
+  hipStream_t st;
+  ProfScope(const char* n, hipStream_t s) : name(n), st(s) { prof_before(name, st); }
+  ~ProfScope() { prof_after(name, st); }
+};
+
+// ---- selection (select.hip)
+// Training rows: rows = B*Hkv*nqb, q-block i = row % nqb, row stride nkb.
+// Decode rows (seq_lens != nullptr): rows = B*Hkv, i = (clamp(len,1,cap)-1)/64.
+hipError_t launch_select(const float* s, int32_t* idx, int32_t* cnt, float* log_gate,
+                         float* s_lse, int rows, int nqb, int nkb, int topk,
+                         const int32_t* seq_lens, int hkv, int cap, hipStream_t st);
+
+// ---- pooling (pool.hip); ws holds qbar and kbar (float32 [B*Hkv*nb*d] each)
+hipError_t launch_pool(int dtype, const void* q, const void* k, float* s, float* ws, int B,
+                       int Hq, int Hkv, int n, int d, hipStream_t st);
+
+// ---- reverse (per key block) lists (revidx.hip)
+// rev_off [B*Hkv][nkb+1] (offsets into that pair's rev_list segment of
+// nkb*(topk+1) entries); entries pack (i | slot<<16), slot 0xFFFF = own block.
+hipError_t launch_revidx(const int32_t* idx, const int32_t* cnt, int32_t* rev_off,
+                         int32_t* rev_list, int BH, int nb, int topk, hipStream_t st);
+
+// ---- SIMT (float32) forward / backward (simt.hip)
+hipError_t launch_fwd_simt(int dtype, const void* q, const void* k, const void* v,
+                           const int32_t* idx, const int32_t* cnt, const float* lg, void* o,
+                           float* lse, int B, int Hq, int Hkv, int n, int d, int topk,
+                           float tau, hipStream_t st);
+hipError_t launch_bwd_simt(int dtype, const void* q, const void* k, const void* v,
+                           const void* o, const void* dO, const float* lse, const int32_t* idx,
+                           const int32_t* cnt, const float* lg, const float* s,
+                           const float* s_lse, void* dq, void* dk, void* dv, float* ds,
+                           float* Dws, const int32_t* rev_off, const int32_t* rev_list, int B,
+                           int Hq, int Hkv, int n, int d, int topk, float tau, hipStream_t st);
+
+// ---- decode (decode.hip)
+int decode_nsplit(int B, int Hkv, int topk);
+hipError_t launch_decode(int dtype, const void* q, const void* kc, const void* vc,
+                         const int32_t* seq_lens, const int32_t* idx, const int32_t* cnt,
+                         const float* lg, float* part_acc, float* part_ml, void* o, int B, int Hq,
+                         int Hkv, int cap, int d, int topk, int nsplit, float tau,
+                         hipStream_t st);
+
+}  // namespace sas

@@ -1,0 +1,516 @@
+// bf16 matrix-core backward of SAS gated block-sparse attention (gfx950).
+//
+// With P = softmax(Z), Z = tau q K^T + bias (log-gate on kept blocks, 0 with
+// the causal mask on the current block), O = P V and upstream dO:
+//   D = rowsum(dO o O),  dP = dO V^T,  dZ = P o (dP - D),
+//   dQ = tau dZ K,  dK = tau sum_h dZ^T Q_h,  dV = sum_h P^T dO_h,
+//   dlg[i, m] = sum over the group's heads, rows of q-block i and keys of
+//               block m of dZ  (the block gate gradient of the SAS review
+//               page, paper.oopus.info, §2.6),
+//   ds[i, m] = [m kept] dlg[i, m] - pi_i[m] sum_{kept m'} dlg[i, m'],
+//               pi_i = softmax(s[i, 0..i-1])  (chain rule through §2.4).
+//
+// Three kernels:
+//  * dq kernel, q-block outer (same workgroup shape and tile pipeline as the
+//    forward): recomputes S^T and dP^T per kept tile, accumulates dQ^T =
+//    K^T dZ^T, writes D for the key-outer kernel and the per-tile dZ sums
+//    (per head chunk) for the gate Jacobian.
+//  * ds kernel: sums the head-chunk partials in a fixed order and applies the
+//    gate Jacobian to one score row per workgroup.
+//  * dk/dv kernel, key-block outer: one workgroup per (batch, kv-head, key
+//    block) walks the reverse list of q-blocks that read the block (its own
+//    current block first) for every head of the group, with dK and dV held in
+//    registers - no atomics, so the result is deterministic.
+// The split recomputes S and dP in both passes (7 tile products instead of 5)
+// in exchange for no atomics and no per-pair partial buffers.
+#include "launch.h"
+#include "mfma_common.h"
+
+namespace sas {
+
+// ------------------------------------------------------------------ dq kernel
+template <int D, int GC>
+__global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ o,
+    const uint16_t* __restrict__ dO, const float* __restrict__ lse,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
+    const float* __restrict__ lg, uint16_t* __restrict__ dq, float* __restrict__ Dws,
+    float* __restrict__ dlgp, int Hq, int Hkv, int n, int topk, float tau, float tau2, int BH,
+    int h_off, int hchunks, int nch) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int ROWB = D * 2;
+  constexpr int TB = 64 * ROWB;
+  constexpr int CPR = D / 8;
+  constexpr int HALF = 64 * CPR;
+  constexpr int TOTAL = 2 * HALF;
+  constexpr int NT = 128 * GC;
+  constexpr int CPT = (TOTAL + NT - 1) / NT;
+  float* part = reinterpret_cast<float*>(smem + 4 * TB);  // [2][8] per-wave dZ sums
+
+  const int nqb = n / SAS_BLK;
+  const int G = Hq / Hkv;
+  int bid = blockIdx.x;
+  const int hc = bid % hchunks;
+  bid /= hchunks;
+  const int bk = bid % BH;
+  const int i = nqb - 1 - bid / BH;
+  const int b = bk / Hkv, kv = bk % Hkv;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int lr = lane & 31, hh = lane >> 5;
+  const int h = kv * G + h_off + hc * GC + (wave >> 1);
+  const int rt = wave & 1;
+  const int chunk = h_off / 4 + hc;
+  const size_t rowsel = size_t(bk) * nqb + i;
+  const int c_sel = cnt[rowsel];
+  const int ntiles = c_sel + 1;
+  const int32_t* irow = idx + rowsel * topk;
+  const float* grow = lg + rowsel * topk;
+
+  const size_t qrow = (size_t(b) * Hq + h) * n + size_t(i) * SAS_BLK + rt * 32 + lr;
+  bf16x8 qop[D / 16], dop[D / 16];
+  float dpart = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    const size_t off = qrow * D + c * 16 + hh * 8;
+    qop[c] = *reinterpret_cast<const bf16x8*>(q + off);
+    dop[c] = *reinterpret_cast<const bf16x8*>(dO + off);
+    const bf16x8 oo = *reinterpret_cast<const bf16x8*>(o + off);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dpart += float(dop[c][e]) * float(oo[e]);
+  }
+  const float Drow = dpart + __shfl_xor(dpart, 32);
+  if (hh == 0) Dws[qrow] = Drow;
+  const float lse2 = lse[qrow] * kLog2e;
+
+  const size_t kv0 = (size_t(b) * Hkv + kv) * size_t(n);
+  uint4 stg[CPT];
+  auto load_tile = [&](int t) {
+    const int blk = t < c_sel ? irow[t] : i;
+    const uint16_t* kb = k + (kv0 + size_t(blk) * SAS_BLK) * D;
+    const uint16_t* vb = v + (kv0 + size_t(blk) * SAS_BLK) * D;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int c = tid + NT * u;
+      if (c < TOTAL) {
+        const uint16_t* src = c < HALF ? kb + c * 8 : vb + (c - HALF) * 8;
+        stg[u] = *reinterpret_cast<const uint4*>(src);
+      }
+    }
+  };
+  auto store_tile = [&](int stage) {
+    char* base = smem + stage * 2 * TB;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int c = tid + NT * u;
+      if (c < TOTAL) {
+        const bool isv = c >= HALF;
+        const int cc = isv ? c - HALF : c;
+        *reinterpret_cast<uint4*>(base + (isv ? TB : 0) + tile_off<D>(cc / CPR, cc % CPR)) = stg[u];
+      }
+    }
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  f32x16 dQ[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) dQ[dt][j] = 0.f;
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int stage = t & 1;
+    if (t + 1 < ntiles) load_tile(t + 1);
+    const char* Kt = smem + stage * 2 * TB;
+    const char* Vt = Kt + TB;
+    const bool cur = t == c_sel;
+    const float zoff = (cur ? 0.f : grow[t] * kLog2e) - lse2;
+
+    f32x16 S[2], P2[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        S[kt][j] = 0.f;
+        P2[kt][j] = 0.f;
+      }
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+        S[kt] = mfma32(lds_read16(Kt, tile_off<D>(kt * 32 + lr, 2 * c + hh)), qop[c], S[kt]);
+        P2[kt] = mfma32(lds_read16(Vt, tile_off<D>(kt * 32 + lr, 2 * c + hh)), dop[c], P2[kt]);
+      }
+    }
+    float zs = 0.f;
+    bf16x8 dZp[4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int jc = 0; jc < 2; ++jc) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = 8 * jc + e;
+          float p = exp2f(S[kt][j] * tau2 + zoff);
+          if (cur) {
+            const int key = kt * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
+            if (key > rt * 32 + lr) p = 0.f;
+          }
+          x[e] = p * (P2[kt][j] - Drow);
+          zs += x[e];
+        }
+        dZp[kt * 2 + jc] = pack_bf16x8(x);
+      }
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch)
+        dQ[dt] = mfma32(tr_operand<D>(Kt, ch * 16, dt * 32, lane), dZp[ch], dQ[dt]);
+
+    if (!cur) {
+      zs = wave_sum(zs);
+      if (lane == 0) part[(t & 1) * 8 + wave] = zs;
+    }
+    if (t + 1 < ntiles) store_tile(stage ^ 1);
+    __syncthreads();
+    if (!cur && tid == 0) {
+      float a = 0.f;
+      for (int w = 0; w < 2 * GC; ++w) a += part[(t & 1) * 8 + w];
+      dlgp[(rowsel * nch + chunk) * topk + t] = a;
+    }
+  }
+
+  uint16_t* drow = dq + qrow * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int jg = 0; jg < 4; ++jg) {
+      bf16x4 r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = (__bf16)(dQ[dt][4 * jg + e] * tau);
+      *reinterpret_cast<bf16x4*>(drow + dt * 32 + 8 * jg + 4 * hh) = r;
+    }
+}
+
+// ------------------------------------------------------------------ ds kernel
+// grid: one workgroup (256 threads) per score row (b, kv, i).
+__global__ void __launch_bounds__(256) bwd_ds_kernel(const float* __restrict__ dlgp,
+                                                     const int32_t* __restrict__ idx,
+                                                     const int32_t* __restrict__ cnt,
+                                                     const float* __restrict__ s,
+                                                     const float* __restrict__ s_lse,
+                                                     float* __restrict__ ds, int nqb, int topk,
+                                                     int nch) {
+  __shared__ float dl[2048];      // topk <= 2048
+  __shared__ int slot_of[2048];   // blocks per sequence <= 2048
+  __shared__ float tot_s;
+  const size_t row = blockIdx.x;
+  const int i = int(row % nqb);
+  const int c = cnt[row];
+  for (int sl = threadIdx.x; sl < c; sl += 256) {
+    float a = 0.f;
+    for (int ch = 0; ch < nch; ++ch) a += dlgp[(row * nch + ch) * topk + sl];
+    dl[sl] = a;
+  }
+  for (int m = threadIdx.x; m < nqb; m += 256) slot_of[m] = -1;
+  __syncthreads();
+  for (int sl = threadIdx.x; sl < c; sl += 256) slot_of[idx[row * topk + sl]] = sl;
+  if (threadIdx.x == 0) {
+    float a = 0.f;
+    for (int sl = 0; sl < c; ++sl) a += dl[sl];
+    tot_s = a;
+  }
+  __syncthreads();
+  const float tot = tot_s;
+  const float sl_ = s_lse[row];
+  for (int m = threadIdx.x; m < nqb; m += 256) {
+    float val = 0.f;
+    if (m < i) {
+      const int sm = slot_of[m];
+      val = (sm >= 0 ? dl[sm] : 0.f) - expf(s[row * nqb + m] - sl_) * tot;
+    }
+    ds[row * nqb + m] = val;
+  }
+}
+
+// ------------------------------------------------------------------ dk/dv kernel
+// grid: B*Hkv*nkb workgroups of 4 waves; wave = (key half kh, row half rh).
+template <int D>
+__global__ void __launch_bounds__(256) bwd_dkdv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
+    const float* __restrict__ lse, const float* __restrict__ Dws, const float* __restrict__ lg,
+    const int32_t* __restrict__ rev_off, const int32_t* __restrict__ rev_list,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int Hq, int Hkv, int n, int topk,
+    float tau, float tau2) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int ROWB = D * 2;
+  constexpr int TB = 64 * ROWB;
+  constexpr int CPR = D / 8;
+  constexpr int HALF = 64 * CPR;
+  constexpr int TOTAL = 2 * HALF;       // Q + dO chunks per step
+  constexpr int CPT = TOTAL / 256;
+  constexpr int STAGE = 2 * TB + 512;   // Q tile, dO tile, lse[64], D[64]
+
+  const int nkb = n / SAS_BLK;
+  const int G = Hq / Hkv;
+  const int bk = blockIdx.x / nkb;
+  const int m = blockIdx.x % nkb;
+  const int b = bk / Hkv, kv = bk % Hkv;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int lr = lane & 31, hh = lane >> 5;
+  const int kh = wave & 1, rh = wave >> 1;
+
+  const size_t krow = (size_t(b) * Hkv + kv) * n + size_t(m) * SAS_BLK + kh * 32 + lr;
+  bf16x8 kop[D / 16], vop[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    kop[c] = *reinterpret_cast<const bf16x8*>(k + krow * D + c * 16 + hh * 8);
+    vop[c] = *reinterpret_cast<const bf16x8*>(v + krow * D + c * 16 + hh * 8);
+  }
+  f32x16 dK[D / 32], dV[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      dK[dt][j] = 0.f;
+      dV[dt][j] = 0.f;
+    }
+
+  const int32_t* lst = rev_list + size_t(bk) * nkb * (topk + 1);
+  const int32_t e0 = rev_off[size_t(bk) * (nkb + 1) + m];
+  const int32_t e1 = rev_off[size_t(bk) * (nkb + 1) + m + 1];
+  const int nsteps = (e1 - e0) * G;
+
+  uint4 stg[CPT];
+  float st_val = 0.f;
+  auto load_step = [&](int s) {
+    const int32_t ent = lst[e0 + s / G];
+    const int iq = ent & 0xFFFF;
+    const int hq = kv * G + s % G;
+    const size_t row0 = (size_t(b) * Hq + hq) * n + size_t(iq) * SAS_BLK;
+    const uint16_t* qb = q + row0 * D;
+    const uint16_t* ob = dO + row0 * D;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int c = tid + 256 * u;
+      const uint16_t* src = c < HALF ? qb + c * 8 : ob + (c - HALF) * 8;
+      stg[u] = *reinterpret_cast<const uint4*>(src);
+    }
+    if (tid < 64) st_val = lse[row0 + tid] * kLog2e;
+    else if (tid < 128) st_val = Dws[row0 + tid - 64];
+  };
+  auto store_step = [&](int stage) {
+    char* base = smem + stage * STAGE;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int c = tid + 256 * u;
+      const bool iso = c >= HALF;
+      const int cc = iso ? c - HALF : c;
+      *reinterpret_cast<uint4*>(base + (iso ? TB : 0) + tile_off<D>(cc / CPR, cc % CPR)) = stg[u];
+    }
+    if (tid < 128) reinterpret_cast<float*>(base + 2 * TB)[tid] = st_val;
+  };
+
+  load_step(0);
+  store_step(0);
+  __syncthreads();
+  const int keyw = kh * 32 + lr;  // this lane's key inside block m
+  for (int s = 0; s < nsteps; ++s) {
+    const int stage = s & 1;
+    if (s + 1 < nsteps) load_step(s + 1);
+    const char* Qt = smem + stage * STAGE;
+    const char* Ot = Qt + TB;
+    const float* stl = reinterpret_cast<const float*>(Qt + 2 * TB);
+    const int32_t ent = lst[e0 + s / G];
+    const int iq = ent & 0xFFFF;
+    const int slot = (ent >> 16) & 0xFFFF;
+    const bool own = slot == 0xFFFF;
+    const float bias2 = own ? 0.f : lg[(size_t(bk) * nkb + iq) * topk + slot] * kLog2e;
+    // own block, rows of this half all above the keys of this half: nothing visible
+    const bool skip = own && kh == 1 && rh == 0;
+    if (!skip) {
+      f32x16 S, P2;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        S[j] = 0.f;
+        P2[j] = 0.f;
+      }
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+        const int off = tile_off<D>(rh * 32 + lr, 2 * c + hh);
+        S = mfma32(lds_read16(Qt, off), kop[c], S);
+        P2 = mfma32(lds_read16(Ot, off), vop[c], P2);
+      }
+      // S[row][key]: lane l, reg j: row = rh*32 + 8(j/4) + 4hh + j%4, key = keyw
+      bf16x8 Pp[2], Zp[2];
+#pragma unroll
+      for (int jc = 0; jc < 2; ++jc) {
+        float pv[8], zv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = 8 * jc + e;
+          const int row = rh * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
+          float p = exp2f(S[j] * tau2 + bias2 - stl[row]);
+          if (own && keyw > row) p = 0.f;
+          pv[e] = p;
+          zv[e] = p * (P2[j] - stl[64 + row]);
+        }
+        Pp[jc] = pack_bf16x8(pv);
+        Zp[jc] = pack_bf16x8(zv);
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int jc = 0; jc < 2; ++jc) {
+          dV[dt] = mfma32(Pp[jc], tr_operand<D>(Ot, rh * 32 + 16 * jc, dt * 32, lane), dV[dt]);
+          dK[dt] = mfma32(Zp[jc], tr_operand<D>(Qt, rh * 32 + 16 * jc, dt * 32, lane), dK[dt]);
+        }
+    }
+    if (s + 1 < nsteps) store_step(stage ^ 1);
+    __syncthreads();
+  }
+
+  // Reduce the two row halves through LDS ([64 keys][D] float32), then write
+  // coalesced bf16 rows: first dV, then dK (scaled by tau).
+  float* red = reinterpret_cast<float*>(smem);
+  const size_t out0 = ((size_t(b) * Hkv + kv) * n + size_t(m) * SAS_BLK) * D;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const f32x16* acc = pass == 0 ? dV : dK;
+    if (rh == 1) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          red[(kh * 32 + 8 * (j >> 2) + 4 * hh + (j & 3)) * D + dt * 32 + lr] = acc[dt][j];
+    }
+    __syncthreads();
+    if (rh == 0) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          red[(kh * 32 + 8 * (j >> 2) + 4 * hh + (j & 3)) * D + dt * 32 + lr] += acc[dt][j];
+    }
+    __syncthreads();
+    uint16_t* dst = (pass == 0 ? dv : dk) + out0;
+    const float sc = pass == 0 ? 1.f : tau;
+    for (int c = tid; c < 64 * CPR; c += 256) {
+      const float* src = red + c * 8;
+      bf16x8 r;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r[e] = (__bf16)(src[e] * sc);
+      *reinterpret_cast<bf16x8*>(dst + c * 8) = r;
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ host side
+template <class K>
+static void allow_lds(K kernel, size_t bytes) {
+  if (bytes > 65536)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
+}
+
+template <int D, int GC>
+static void dq_launch(int nblocks, const void* q, const void* k, const void* v, const void* o,
+                      const void* dO, const float* lse, const int32_t* idx, const int32_t* cnt,
+                      const float* lg, void* dq, float* Dws, float* dlgp, int Hq, int Hkv, int n,
+                      int topk, float tau, float tau2, int BH, int h_off, int hchunks, int nch,
+                      hipStream_t st) {
+  const size_t shm = size_t(4) * 64 * D * 2 + 64;
+  auto kern = bwd_dq_kernel<D, GC>;
+  allow_lds(kern, shm);
+  hipLaunchKernelGGL(kern, dim3(nblocks), dim3(128 * GC), shm, st, (const uint16_t*)q,
+                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o,
+                     (const uint16_t*)dO, lse, idx, cnt, lg, (uint16_t*)dq, Dws, dlgp, Hq, Hkv, n,
+                     topk, tau, tau2, BH, h_off, hchunks, nch);
+}
+
+template <int D>
+static void dq_dispatch(int gc, int nblocks, const void* q, const void* k, const void* v,
+                        const void* o, const void* dO, const float* lse, const int32_t* idx,
+                        const int32_t* cnt, const float* lg, void* dq, float* Dws, float* dlgp,
+                        int Hq, int Hkv, int n, int topk, float tau, float tau2, int BH, int h_off,
+                        int hchunks, int nch, hipStream_t st) {
+#define SAS_DQ_ARGS nblocks, q, k, v, o, dO, lse, idx, cnt, lg, dq, Dws, dlgp, Hq, Hkv, n, topk, \
+                    tau, tau2, BH, h_off, hchunks, nch, st
+  switch (gc) {
+    case 1: dq_launch<D, 1>(SAS_DQ_ARGS); break;
+    case 2: dq_launch<D, 2>(SAS_DQ_ARGS); break;
+    case 3: dq_launch<D, 3>(SAS_DQ_ARGS); break;
+    default: dq_launch<D, 4>(SAS_DQ_ARGS); break;
+  }
+#undef SAS_DQ_ARGS
+}
+
+size_t bwd_mfma_extra_ws(int B, int Hq, int Hkv, int n, int topk) {
+  const int G = Hq / Hkv;
+  const int nch = (G + 3) / 4;
+  return sizeof(float) * size_t(B) * Hkv * (n / SAS_BLK) * nch * size_t(topk > 0 ? topk : 1);
+}
+
+hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const void* o,
+                           const void* dO, const float* lse, const int32_t* idx,
+                           const int32_t* cnt, const float* lg, const float* s,
+                           const float* s_lse, void* dq, void* dk, void* dv, float* ds,
+                           float* Dws, const int32_t* rev_off, const int32_t* rev_list,
+                           float* dlgp, int B, int Hq, int Hkv, int n, int d, int topk, float tau,
+                           hipStream_t st) {
+  const int G = Hq / Hkv;
+  const int nqb = n / SAS_BLK;
+  const int BH = B * Hkv;
+  const float tau2 = tau * kLog2e;
+  const int full = G / 4, rem = G % 4;
+  const int nch = full + (rem > 0 ? 1 : 0);
+  const int K = topk > 0 ? topk : 1;
+  {
+    ProfScope ps("sas_bwd_dq_kernel", st);
+    if (full > 0) {
+      if (d == 128) dq_dispatch<128>(4, BH * nqb * full, q, k, v, o, dO, lse, idx, cnt, lg, dq, Dws, dlgp, Hq, Hkv, n, K, tau, tau2, BH, 0, full, nch, st);
+      else dq_dispatch<64>(4, BH * nqb * full, q, k, v, o, dO, lse, idx, cnt, lg, dq, Dws, dlgp, Hq, Hkv, n, K, tau, tau2, BH, 0, full, nch, st);
+    }
+    if (rem > 0) {
+      if (d == 128) dq_dispatch<128>(rem, BH * nqb, q, k, v, o, dO, lse, idx, cnt, lg, dq, Dws, dlgp, Hq, Hkv, n, K, tau, tau2, BH, 4 * full, 1, nch, st);
+      else dq_dispatch<64>(rem, BH * nqb, q, k, v, o, dO, lse, idx, cnt, lg, dq, Dws, dlgp, Hq, Hkv, n, K, tau, tau2, BH, 4 * full, 1, nch, st);
+    }
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  {
+    ProfScope ps("sas_bwd_ds_kernel", st);
+    hipLaunchKernelGGL(bwd_ds_kernel, dim3(BH * nqb), dim3(256), 0, st, dlgp, idx, cnt, s, s_lse,
+                       ds, nqb, K, nch);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  {
+    ProfScope ps("sas_bwd_dkdv_kernel", st);
+    const size_t shm = size_t(2) * (2 * 64 * d * 2 + 512);
+    if (d == 128) {
+      auto kern = bwd_dkdv_kernel<128>;
+      allow_lds(kern, shm);
+      hipLaunchKernelGGL(kern, dim3(BH * nqb), dim3(256), shm, st, (const uint16_t*)q,
+                         (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO, lse, Dws, lg,
+                         rev_off, rev_list, (uint16_t*)dk, (uint16_t*)dv, Hq, Hkv, n, topk, tau,
+                         tau2);
+    } else {
+      auto kern = bwd_dkdv_kernel<64>;
+      allow_lds(kern, shm);
+      hipLaunchKernelGGL(kern, dim3(BH * nqb), dim3(256), shm, st, (const uint16_t*)q,
+                         (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO, lse, Dws, lg,
+                         rev_off, rev_list, (uint16_t*)dk, (uint16_t*)dv, Hq, Hkv, n, topk, tau,
+                         tau2);
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sas

@@ -1,0 +1,331 @@
+// C ABI of libsas: host-side argument checks, workspace carving and dispatch
+// to the gfx950 kernels.  No entry point allocates device memory or
+// synchronises; every launch goes to the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/sas.h"
+#include "launch.h"
+
+namespace sas {
+// bf16 tensor-core kernels (mfma_fwd.hip / mfma_bwd.hip)
+hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, const int32_t* idx,
+                           const int32_t* cnt, const float* lg, void* o, float* lse, int B,
+                           int Hq, int Hkv, int n, int d, int topk, float tau, hipStream_t st);
+hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const void* o,
+                           const void* dO, const float* lse, const int32_t* idx,
+                           const int32_t* cnt, const float* lg, const float* s,
+                           const float* s_lse, void* dq, void* dk, void* dv, float* ds,
+                           float* Dws, const int32_t* rev_off, const int32_t* rev_list,
+                           float* dlgp, int B, int Hq, int Hkv, int n, int d, int topk, float tau,
+                           hipStream_t st);
+size_t bwd_mfma_extra_ws(int B, int Hq, int Hkv, int n, int topk);
+bool mfma_supported(int d, int G);
+}  // namespace sas
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool shape_ok_common(int B, int Hq, int Hkv, int len, int d, int topk, float scale) {
+  if (B < 1 || Hq < 1 || Hkv < 1) return false;
+  if (Hq % Hkv != 0) return false;
+  const int G = Hq / Hkv;
+  if (G > 16) return false;
+  if (len < SAS_BLOCK || len % SAS_BLOCK != 0) return false;
+  if (len / SAS_BLOCK > SAS_MAX_BLOCKS) return false;
+  if (d != 64 && d != 128) return false;
+  if (topk < 0 || topk > SAS_MAX_BLOCKS) return false;
+  if (!(scale >= 0.f) || !std::isfinite(scale)) return false;
+  // element counts must fit the 32-bit grid arithmetic used for block ids
+  if (int64_t(B) * Hq * (len / SAS_BLOCK) > (int64_t(1) << 30)) return false;
+  return true;
+}
+
+sas_status check_shape(const sas_shape* s) {
+  if (!s) return SAS_ERR_ARG;
+  if (s->dtype != SAS_F32 && s->dtype != SAS_BF16) return SAS_ERR_DTYPE;
+  if (!shape_ok_common(s->B, s->Hq, s->Hkv, s->n, s->d, s->topk, s->scale)) return SAS_ERR_ARG;
+  return SAS_OK;
+}
+
+sas_status check_dshape(const sas_decode_shape* s) {
+  if (!s) return SAS_ERR_ARG;
+  if (s->dtype != SAS_F32 && s->dtype != SAS_BF16) return SAS_ERR_DTYPE;
+  if (!shape_ok_common(s->B, s->Hq, s->Hkv, s->cap, s->d, s->topk, s->scale)) return SAS_ERR_ARG;
+  return SAS_OK;
+}
+
+float tau_of(float scale, int d) { return scale > 0.f ? scale : 1.0f / std::sqrt(float(d)); }
+
+thread_local hipError_t g_last_hip = hipSuccess;
+
+sas_status from_hip(hipError_t e) {
+  if (e == hipSuccess) return SAS_OK;
+  g_last_hip = e;
+  return SAS_ERR_HIP;
+}
+
+// hipGetLastError() reports the last error of ANY runtime call on this thread;
+// drop whatever an unrelated earlier call left there before our launches.
+void clear_stale_error() { (void)hipGetLastError(); }
+
+// ----------------------------------------------------------- bwd workspace
+struct BwdWs {
+  size_t D_off, off_off, list_off, dlg_off, total;
+};
+BwdWs bwd_layout(const sas_shape* s) {
+  const size_t nb = size_t(s->n) / SAS_BLOCK;
+  const size_t BH = size_t(s->B) * s->Hkv;
+  BwdWs w{};
+  w.D_off = 0;
+  w.off_off = align_up(w.D_off + sizeof(float) * size_t(s->B) * s->Hq * s->n);
+  w.list_off = align_up(w.off_off + sizeof(int32_t) * BH * (nb + 1));
+  w.dlg_off = align_up(w.list_off + sizeof(int32_t) * BH * nb * (size_t(s->topk) + 1));
+  w.total = align_up(w.dlg_off + sas::bwd_mfma_extra_ws(s->B, s->Hq, s->Hkv, s->n, s->topk));
+  return w;
+}
+
+// ----------------------------------------------------------- decode workspace
+struct DecWs {
+  size_t idx_off, cnt_off, lg_off, lse_off, acc_off, ml_off, total;
+  int nsplit;
+};
+DecWs dec_layout(const sas_decode_shape* s) {
+  const size_t BH = size_t(s->B) * s->Hkv;
+  const size_t K = size_t(s->topk > 0 ? s->topk : 1);
+  DecWs w{};
+  w.nsplit = sas::decode_nsplit(s->B, s->Hkv, s->topk);
+  w.idx_off = 0;
+  w.cnt_off = align_up(w.idx_off + sizeof(int32_t) * BH * K);
+  w.lg_off = align_up(w.cnt_off + sizeof(int32_t) * BH);
+  w.lse_off = align_up(w.lg_off + sizeof(float) * BH * K);
+  w.acc_off = align_up(w.lse_off + sizeof(float) * BH);
+  w.ml_off = align_up(w.acc_off + sizeof(float) * size_t(s->B) * s->Hq * w.nsplit * s->d);
+  w.total = align_up(w.ml_off + sizeof(float) * size_t(s->B) * s->Hq * w.nsplit * 2);
+  return w;
+}
+
+// ----------------------------------------------------------- profiling state
+struct ProfRec {
+  const char* name;
+  hipEvent_t a, b;
+};
+struct ProfState {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  std::vector<ProfRec> pending;
+  std::vector<const char*> names;
+  std::vector<double> ms;
+  std::vector<int32_t> launches;
+  hipEvent_t open = nullptr;
+} g_prof;
+
+hipEvent_t prof_event() {
+  if (!g_prof.pool.empty()) {
+    hipEvent_t e = g_prof.pool.back();
+    g_prof.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+}  // namespace
+
+namespace sas {
+void prof_before(const char*, hipStream_t st) {
+  if (!g_prof.on) return;
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  g_prof.open = prof_event();
+  if (g_prof.open) hipEventRecord(g_prof.open, st);
+}
+void prof_after(const char* name, hipStream_t st) {
+  if (!g_prof.on) return;
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  if (!g_prof.open) return;
+  hipEvent_t e = prof_event();
+  if (!e) return;
+  hipEventRecord(e, st);
+  g_prof.pending.push_back({name, g_prof.open, e});
+  g_prof.open = nullptr;
+}
+}  // namespace sas
+
+extern "C" {
+
+int32_t sas_abi_version(void) { return 1; }
+
+const char* sas_status_string(sas_status st) {
+  switch (st) {
+    case SAS_OK: return "SAS_OK";
+    case SAS_ERR_ARG: return "SAS_ERR_ARG: invalid pointer, size or shape";
+    case SAS_ERR_DTYPE: return "SAS_ERR_DTYPE: dtype must be SAS_F32 or SAS_BF16";
+    case SAS_ERR_UNSUPPORTED: return "SAS_ERR_UNSUPPORTED: valid but not implemented";
+    case SAS_ERR_WORKSPACE: return "SAS_ERR_WORKSPACE: workspace missing or too small";
+    case SAS_ERR_HIP: return "SAS_ERR_HIP: kernel launch failed";
+    default: return "SAS: unknown status";
+  }
+}
+
+size_t sas_pool_workspace_bytes(const sas_shape* s) {
+  if (check_shape(s) != SAS_OK) return 0;
+  return align_up(2 * sizeof(float) * size_t(s->B) * s->Hkv * (s->n / SAS_BLOCK) * s->d);
+}
+
+sas_status sas_pool_scores(const sas_shape* s, const void* q, const void* k, float* out,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+  sas_status st = check_shape(s);
+  if (st != SAS_OK) return st;
+  if (!q || !k || !out) return SAS_ERR_ARG;
+  if (!ws || ws_bytes < sas_pool_workspace_bytes(s)) return SAS_ERR_WORKSPACE;
+  clear_stale_error();
+  return from_hip(sas::launch_pool(s->dtype, q, k, out, (float*)ws, s->B, s->Hq, s->Hkv, s->n,
+                                   s->d, stream));
+}
+
+sas_status sas_select(const sas_shape* s, const float* sc, int32_t* idx, int32_t* cnt,
+                      float* log_gate, float* s_lse, hipStream_t stream) {
+  sas_status st = check_shape(s);
+  if (st != SAS_OK) return st;
+  if (!sc || !cnt || !s_lse) return SAS_ERR_ARG;
+  if (s->topk > 0 && (!idx || !log_gate)) return SAS_ERR_ARG;
+  const int nb = s->n / SAS_BLOCK;
+  clear_stale_error();
+  return from_hip(sas::launch_select(sc, idx, cnt, log_gate, s_lse, s->B * s->Hkv * nb, nb, nb,
+                                     s->topk, nullptr, s->Hkv, s->n, stream));
+}
+
+sas_status sas_fwd(const sas_shape* s, const void* q, const void* k, const void* v,
+                   const int32_t* idx, const int32_t* cnt, const float* log_gate, void* o,
+                   float* lse, hipStream_t stream) {
+  sas_status st = check_shape(s);
+  if (st != SAS_OK) return st;
+  if (!q || !k || !v || !cnt || !o || !lse) return SAS_ERR_ARG;
+  if (s->topk > 0 && (!idx || !log_gate)) return SAS_ERR_ARG;
+  const float tau = tau_of(s->scale, s->d);
+  const int G = s->Hq / s->Hkv;
+  clear_stale_error();
+  if (s->dtype == SAS_BF16 && sas::mfma_supported(s->d, G))
+    return from_hip(sas::launch_fwd_mfma(q, k, v, idx, cnt, log_gate, o, lse, s->B, s->Hq, s->Hkv,
+                                         s->n, s->d, s->topk, tau, stream));
+  return from_hip(sas::launch_fwd_simt(s->dtype, q, k, v, idx, cnt, log_gate, o, lse, s->B, s->Hq,
+                                       s->Hkv, s->n, s->d, s->topk, tau, stream));
+}
+
+size_t sas_bwd_workspace_bytes(const sas_shape* s) {
+  if (check_shape(s) != SAS_OK) return 0;
+  return bwd_layout(s).total;
+}
+
+sas_status sas_bwd(const sas_shape* s, const void* q, const void* k, const void* v, const void* o,
+                   const void* dO, const float* lse, const int32_t* idx, const int32_t* cnt,
+                   const float* log_gate, const float* sc, const float* s_lse, void* dq, void* dk,
+                   void* dv, float* ds, void* ws, size_t ws_bytes, hipStream_t stream) {
+  sas_status st = check_shape(s);
+  if (st != SAS_OK) return st;
+  if (!q || !k || !v || !o || !dO || !lse || !cnt || !sc || !s_lse || !dq || !dk || !dv || !ds)
+    return SAS_ERR_ARG;
+  if (s->topk > 0 && (!idx || !log_gate)) return SAS_ERR_ARG;
+  const BwdWs w = bwd_layout(s);
+  if (!ws || ws_bytes < w.total) return SAS_ERR_WORKSPACE;
+  char* base = static_cast<char*>(ws);
+  float* Dws = reinterpret_cast<float*>(base + w.D_off);
+  int32_t* rev_off = reinterpret_cast<int32_t*>(base + w.off_off);
+  int32_t* rev_list = reinterpret_cast<int32_t*>(base + w.list_off);
+  const int nb = s->n / SAS_BLOCK;
+  const float tau = tau_of(s->scale, s->d);
+  clear_stale_error();
+  hipError_t e = sas::launch_revidx(idx, cnt, rev_off, rev_list, s->B * s->Hkv, nb, s->topk, stream);
+  if (e != hipSuccess) return from_hip(e);
+  const int G = s->Hq / s->Hkv;
+  if (s->dtype == SAS_BF16 && sas::mfma_supported(s->d, G))
+    return from_hip(sas::launch_bwd_mfma(
+        q, k, v, o, dO, lse, idx, cnt, log_gate, sc, s_lse, dq, dk, dv, ds, Dws, rev_off, rev_list,
+        reinterpret_cast<float*>(base + w.dlg_off), s->B, s->Hq, s->Hkv, s->n, s->d, s->topk, tau,
+        stream));
+  return from_hip(sas::launch_bwd_simt(s->dtype, q, k, v, o, dO, lse, idx, cnt, log_gate, sc, s_lse,
+                                       dq, dk, dv, ds, Dws, rev_off, rev_list, s->B, s->Hq, s->Hkv,
+                                       s->n, s->d, s->topk, tau, stream));
+}
+
+size_t sas_decode_workspace_bytes(const sas_decode_shape* s) {
+  if (check_dshape(s) != SAS_OK) return 0;
+  return dec_layout(s).total;
+}
+
+sas_status sas_decode(const sas_decode_shape* s, const void* q, const void* k_cache,
+                      const void* v_cache, const int32_t* seq_lens, const float* sc, void* o,
+                      int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  sas_status st = check_dshape(s);
+  if (st != SAS_OK) return st;
+  if (!q || !k_cache || !v_cache || !seq_lens || !sc || !o) return SAS_ERR_ARG;
+  const DecWs w = dec_layout(s);
+  if (!ws || ws_bytes < w.total) return SAS_ERR_WORKSPACE;
+  char* base = static_cast<char*>(ws);
+  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + w.idx_off);
+  int32_t* cnt = reinterpret_cast<int32_t*>(base + w.cnt_off);
+  float* lg = reinterpret_cast<float*>(base + w.lg_off);
+  float* lse = reinterpret_cast<float*>(base + w.lse_off);
+  float* acc = reinterpret_cast<float*>(base + w.acc_off);
+  float* ml = reinterpret_cast<float*>(base + w.ml_off);
+  const int nb = s->cap / SAS_BLOCK;
+  clear_stale_error();
+  hipError_t e = sas::launch_select(sc, idx, cnt, lg, lse, s->B * s->Hkv, nb, nb, s->topk,
+                                    seq_lens, s->Hkv, s->cap, stream);
+  if (e != hipSuccess) return from_hip(e);
+  return from_hip(sas::launch_decode(s->dtype, q, k_cache, v_cache, seq_lens, idx, cnt, lg, acc,
+                                     ml, o, s->B, s->Hq, s->Hkv, s->cap, s->d, s->topk, w.nsplit,
+                                     tau_of(s->scale, s->d), stream));
+}
+
+const char* sas_last_hip_error(void) { return hipGetErrorName(g_last_hip); }
+
+sas_status sas_prof_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  g_prof.on = on != 0;
+  return SAS_OK;
+}
+
+int32_t sas_prof_collect(const char** names, double* total_ms, int32_t* launches, int32_t max) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  for (const ProfRec& r : g_prof.pending) {
+    float ms = 0.f;
+    hipEventSynchronize(r.b);
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) ms = 0.f;
+    size_t j = 0;
+    for (; j < g_prof.names.size(); ++j)
+      if (std::strcmp(g_prof.names[j], r.name) == 0) break;
+    if (j == g_prof.names.size()) {
+      g_prof.names.push_back(r.name);
+      g_prof.ms.push_back(0.0);
+      g_prof.launches.push_back(0);
+    }
+    g_prof.ms[j] += ms;
+    g_prof.launches[j] += 1;
+    g_prof.pool.push_back(r.a);
+    g_prof.pool.push_back(r.b);
+  }
+  g_prof.pending.clear();
+  const int32_t n = int32_t(g_prof.names.size());
+  for (int32_t j = 0; j < n && j < max; ++j) {
+    if (names) names[j] = g_prof.names[j];
+    if (total_ms) total_ms[j] = g_prof.ms[j];
+    if (launches) launches[j] = g_prof.launches[j];
+  }
+  // reset the accumulators so that the next collect covers a new interval
+  g_prof.names.clear();
+  g_prof.ms.clear();
+  g_prof.launches.clear();
+  return n;
+}
+
+}  // extern "C"

@@ -1,0 +1,185 @@
+/*
+ * sas.h - C ABI of libsas: SAS gated block-sparse attention on AMD MI355X (gfx950).
+ *
+ * What is computed (sources: the Chinese review page "论文综述：SAS——通过端到端
+ * 优化上下文排序实现简单的注意力稀疏化" on paper.oopus.info, cited as [Review];
+ * the project README on gitee, cited as [README]):
+ *
+ *   The sequence is cut into blocks of b = 64 tokens [Review §2.1].  For every
+ *   (batch b, kv-head kv, 64-query block i) a score row s[b,kv,i,:] rates the
+ *   history blocks m < i [Review §2.2, selector equation].  The Top-K history
+ *   blocks are kept; each kept block m adds the log-gate
+ *       log g_m = s_m - LSE(s over ALL history blocks m' < i)
+ *   [Review §2.4, equation for log g_m] to the logits of its 64 keys; the
+ *   current block i is always kept, causally masked (key j <= query t), with
+ *   no bias (g_0 = 1); every other block is skipped:
+ *       o = softmax(tau * q K_S^T + log g_S) V_S      [Review §2.3, equation]
+ *   The backward returns dq, dk, dv and ds, where the gate gradient of a kept
+ *   block is the sum of its logit gradients [Review §2.6] pushed through the
+ *   softmax Jacobian of the normalised gate.  Top-K itself is discrete and gets
+ *   no gradient [README, figure caption (b)].
+ *
+ * Conventions shared by every entry point
+ *   - The query heads of a group share one selection: query head h reads
+ *     kv-head h / G with G = Hq / Hkv (contiguous grouping).
+ *   - tau = shape->scale, or 1/sqrt(d) when scale == 0.  The gate is never scaled.
+ *   - All tensors are dense, row-major, contiguous DEVICE buffers that the caller
+ *     owns; the library keeps no pointer after a call returns and allocates no
+ *     device memory (scratch comes from the caller's workspace argument).
+ *   - Every call validates its arguments on the host and then enqueues its
+ *     kernels on `stream` (hipStream_t; NULL = the null stream) and returns
+ *     without synchronising.  A nonzero status other than SAS_ERR_HIP means
+ *     nothing was enqueued.  SAS_ERR_HIP reports a failed launch.
+ *   - Outputs take the dtype of the inputs (q, k, v, o, dO, dq, dk, dv, decode
+ *     caches); s, log_gate, s_lse, lse and ds are always float32; idx and cnt int32.
+ *   - Calls are reentrant; calls on different streams may run concurrently as
+ *     long as their output buffers do not overlap.
+ *   - Scores must be finite (NaN/Inf in s is undefined behaviour).
+ */
+#ifndef SAS_H_
+#define SAS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t sas_status;
+#define SAS_OK 0
+#define SAS_ERR_ARG 1          /* bad pointer, size or shape */
+#define SAS_ERR_DTYPE 2        /* dtype not SAS_F32 / SAS_BF16 */
+#define SAS_ERR_UNSUPPORTED 3  /* valid but outside what the kernels implement */
+#define SAS_ERR_WORKSPACE 4    /* workspace missing or smaller than required */
+#define SAS_ERR_HIP 5          /* a kernel launch failed (hipGetLastError) */
+
+#define SAS_F32 0
+#define SAS_BF16 1
+
+#define SAS_BLOCK 64           /* tokens per block [Review §2.1] */
+#define SAS_MAX_BLOCKS 2048    /* most blocks per sequence (n or cap <= 131072) */
+
+/* Training-layer shape.  q [B,Hq,n,d]; k, v [B,Hkv,n,d].
+ * Requires B,Hq,Hkv >= 1, Hq % Hkv == 0, 1 <= Hq/Hkv <= 16, n % 64 == 0,
+ * 64 <= n <= 64*SAS_MAX_BLOCKS, d in {64,128}, 0 <= topk <= SAS_MAX_BLOCKS (a row
+ * with fewer history blocks keeps all of them), scale >= 0 and finite, dtype
+ * SAS_F32 or SAS_BF16. */
+typedef struct {
+  int32_t B, Hq, Hkv, n, d, topk;
+  float scale;
+  int32_t dtype;
+} sas_shape;
+
+/* Decode shape.  q [B,Hq,d]; k_cache, v_cache [B,Hkv,cap,d]; same limits with
+ * cap in place of n. */
+typedef struct {
+  int32_t B, Hq, Hkv, cap, d, topk;
+  float scale;
+  int32_t dtype;
+} sas_decode_shape;
+
+/* Version of this ABI (bumped on any incompatible change). */
+int32_t sas_abi_version(void);
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char* sas_status_string(sas_status st);
+
+/* ---------------------------------------------------------------- pooling
+ * Stand-in selector (mean pooling) of the 32K training workload; a score per
+ * history block from q and K_{B_m} as in [Review §2.2, selector equation].
+ *   s[b,kv,i,m] = qbar[b,kv,i] . kbar[b,kv,m] / sqrt(d)   for ALL i, m
+ * qbar = mean of q over the 64 rows of q-block i and the G heads of group kv;
+ * kbar = mean of k over the 64 rows of block m.  Means accumulate in float32.
+ *   q, k: device, shape->dtype.  s: device float32 [B,Hkv,n/64,n/64] (written).
+ *   ws: device scratch of at least sas_pool_workspace_bytes(shape) bytes. */
+size_t sas_pool_workspace_bytes(const sas_shape* shape);
+sas_status sas_pool_scores(const sas_shape* shape, const void* q, const void* k, float* s,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------- selection
+ * LSE-normalise and Top-K block-index builder [Review §2.2, §2.4].
+ * For each row (b,kv,i) with history H = {0..i-1}:
+ *   s_lse[b,kv,i]   = log sum_{m<i} exp s[b,kv,i,m]          (-inf when i == 0)
+ *   cnt[b,kv,i]     = min(topk, i)
+ *   idx[b,kv,i,:]   = the cnt history blocks with the largest scores, ties to the
+ *                     lower index (-0.0 == +0.0), listed in ascending order, then
+ *                     padded with -1 up to topk
+ *   log_gate[b,kv,i,j] = s[b,kv,i,idx[j]] - s_lse (j < cnt), -inf in the padding
+ * s: device float32 [B,Hkv,n/64,n/64]; entries m >= i are never read.
+ * idx: int32 [B,Hkv,n/64,topk]; cnt: int32 [B,Hkv,n/64];
+ * log_gate: float32 [B,Hkv,n/64,topk]; s_lse: float32 [B,Hkv,n/64] (all written).
+ * idx and log_gate may be NULL when topk == 0. */
+sas_status sas_select(const sas_shape* shape, const float* s, int32_t* idx, int32_t* cnt,
+                      float* log_gate, float* s_lse, hipStream_t stream);
+
+/* ---------------------------------------------------------------- forward
+ * Gated block-sparse attention forward [Review §2.3 equation, §2.6].
+ * For each query head h and q-block i: keys = the cnt[b,kv,i] blocks idx[b,kv,i,:]
+ * (bias log_gate) plus block i itself (bias 0, key j visible iff j <= query t).
+ *   o   [B,Hq,n,d]  dtype of q (written; bf16 rounded to nearest even)
+ *   lse [B,Hq,n]    float32 natural-log row logsumexp of the biased logits
+ * idx/cnt/log_gate as produced by sas_select (idx ascending is NOT required,
+ * but every entry j < cnt must be a block in [0, i); this is not checked on the
+ * device).  log_gate may be NULL when topk == 0. */
+sas_status sas_fwd(const sas_shape* shape, const void* q, const void* k, const void* v,
+                   const int32_t* idx, const int32_t* cnt, const float* log_gate,
+                   void* o, float* lse, hipStream_t stream);
+
+/* ---------------------------------------------------------------- backward
+ * Gradients of sum(dO * o) [Review §2.6 and the chain rule through §2.4]:
+ *   dq [B,Hq,n,d], dk, dv [B,Hkv,n,d]  (dtype of q; written, not accumulated)
+ *   ds [B,Hkv,n/64,n/64] float32: for m < i,
+ *        ds[i,m] = [m kept] dlg[i,m] - pi_i[m] * sum_{m' kept} dlg[i,m'],
+ *        pi_i = softmax of s[i, 0..i-1], dlg[i,m] = sum of the logit gradients of
+ *        the group's heads over rows of block i and keys of block m;
+ *      and ds[i,m] = 0 for m >= i (every entry is written).
+ * o and lse must come from sas_fwd on the same inputs; s, idx, cnt, log_gate
+ * and s_lse are the sas_select inputs/outputs (idx ascending, as it writes).  ws: device scratch of at least
+ * sas_bwd_workspace_bytes(shape) bytes, contents on entry irrelevant. */
+size_t sas_bwd_workspace_bytes(const sas_shape* shape);
+sas_status sas_bwd(const sas_shape* shape, const void* q, const void* k, const void* v,
+                   const void* o, const void* dO, const float* lse, const int32_t* idx,
+                   const int32_t* cnt, const float* log_gate, const float* s,
+                   const float* s_lse, void* dq, void* dk, void* dv, float* ds, void* ws,
+                   size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------- decode
+ * Single-token decode over a contiguous KV cache (the serving-side use of the
+ * same attention, [Review §2.6] and the decode-speed results of [Review §4]).
+ * Batch entry b holds seq_lens[b] tokens (1 <= seq_lens[b] <= cap); its query is
+ * token T = seq_lens[b]-1, whose current block is i = T/64 holding the tokens
+ * [64 i, seq_lens[b]).  Per kv-group: select from s[b,kv,0..i-1] exactly as
+ * sas_select; each query head attends to the kept blocks (bias log_gate) and to
+ * the current block's tokens (bias 0).
+ *   q [B,Hq,d]; k_cache, v_cache [B,Hkv,cap,d]; seq_lens int32 [B] (device);
+ *   s float32 [B,Hkv,cap/64]; o [B,Hq,d] (written).
+ *   idx_out: NULL, or int32 [B,Hkv,topk] receiving the ascending selection
+ *   (-1 padded).  ws: device scratch of sas_decode_workspace_bytes(shape) bytes.
+ * seq_lens outside [1, cap] are clamped on the device (host cannot read them). */
+size_t sas_decode_workspace_bytes(const sas_decode_shape* shape);
+sas_status sas_decode(const sas_decode_shape* shape, const void* q, const void* k_cache,
+                      const void* v_cache, const int32_t* seq_lens, const float* s, void* o,
+                      int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Name of the HIP error behind the last SAS_ERR_HIP returned on this thread
+ * ("hipSuccess" if none); static storage. */
+const char* sas_last_hip_error(void);
+
+/* ---------------------------------------------------------------- profiling
+ * Kernel-level timing for measurement tools.  When enabled, the library records
+ * a hipEvent pair around every kernel it launches afterwards (events are
+ * created lazily, outside the timed kernels) and accumulates per-kernel elapsed
+ * milliseconds when sas_prof_collect is called after the stream has drained.
+ * Not thread-safe; off by default. */
+sas_status sas_prof_enable(int32_t on);
+/* Writes up to `max` entries; returns the number of distinct kernel names seen.
+ * names[i] points to static strings; total_ms[i] is summed over launches[i]. */
+int32_t sas_prof_collect(const char** names, double* total_ms, int32_t* launches, int32_t max);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAS_H_ */

@@ -1,0 +1,111 @@
+"""C-ABI checks that need no GPU: every symbol declared in include/sas.h is
+exported by libsas.so, and invalid arguments are rejected on the host before
+any launch (these calls touch no device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_block_sparse_select_amd import _lib, api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    with open(os.path.join(ROOT, "include", "sas.h")) as f:
+        txt = f.read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(sas_[a-z_0-9]+)\s*\(", txt)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("sas_pool_scores", "sas_select", "sas_fwd", "sas_bwd", "sas_decode",
+                 "sas_bwd_workspace_bytes", "sas_status_string"):
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported():
+    L = _lib.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert set(_lib.EXPORTED) <= set(declared_functions())
+
+
+def test_abi_version_and_status_strings():
+    L = _lib.lib()
+    assert L.sas_abi_version() == 1
+    for st in range(6):
+        assert _lib.status_string(st).startswith("SAS")
+    assert "unknown" in _lib.status_string(99)
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def _sel(sh, s=FAKE, idx=FAKE, cnt=FAKE, lg=FAKE, lse=FAKE):
+    return _lib.lib().sas_select(ctypes.byref(sh), s, idx, cnt, lg, lse, None)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,n,d,K,scale,dt,expect", [
+    (1, 4, 2, 500, 128, 2, 0.0, 1, 1),      # n % 64 != 0
+    (1, 4, 3, 512, 128, 2, 0.0, 1, 1),      # Hq % Hkv != 0
+    (1, 4, 2, 512, 96, 2, 0.0, 1, 1),       # d not in {64,128}
+    (1, 4, 2, 512, 128, -1, 0.0, 1, 1),     # K < 0
+    (1, 4, 2, 512, 128, 2049, 0.0, 1, 1),   # K beyond the supported block count
+    (0, 4, 2, 512, 128, 2, 0.0, 1, 1),      # B < 1
+    (1, 34, 2, 512, 128, 2, 0.0, 1, 1),     # G > 16
+    (1, 4, 2, 512, 128, 2, -1.0, 1, 1),     # negative scale
+    (1, 4, 2, 512, 128, 2, float("nan"), 1, 1),
+    (1, 4, 2, 64 * 2049, 128, 2, 0.0, 1, 1),  # more blocks than supported
+    (1, 4, 2, 512, 128, 2, 0.0, 7, 2),      # bad dtype
+    (1, 4, 2, 0, 128, 2, 0.0, 1, 1),        # empty sequence
+])
+def test_shape_validation(B, Hq, Hkv, n, d, K, scale, dt, expect):
+    sh = _lib.SasShape(B, Hq, Hkv, n, d, K, scale, dt)
+    assert _sel(sh) == expect
+    L = _lib.lib()
+    assert L.sas_fwd(ctypes.byref(sh), *([FAKE] * 8), None) == expect
+    assert L.sas_bwd_workspace_bytes(ctypes.byref(sh)) == 0
+
+
+def test_null_pointers_rejected():
+    L = _lib.lib()
+    sh = api.make_shape(1, 4, 2, 512, 128, 2)
+    assert _sel(sh, s=None) == 1
+    assert _sel(sh, idx=None) == 1
+    assert L.sas_fwd(ctypes.byref(sh), None, *([FAKE] * 7), None) == 1
+    assert L.sas_bwd(ctypes.byref(sh), *([FAKE] * 14), None, FAKE, 1 << 40, None) == 1
+    assert L.sas_select(None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    # topk == 0 allows NULL idx / log_gate
+    sh0 = api.make_shape(1, 4, 2, 512, 128, 0)
+    assert L.sas_pool_scores(ctypes.byref(sh0), FAKE, FAKE, FAKE, None, 0, None) == 4
+
+
+def test_workspace_checks():
+    L = _lib.lib()
+    sh = api.make_shape(1, 32, 8, 32768, 128, 32)
+    need = api.sas_bwd_workspace_bytes(sh)
+    assert need > 4 * 32 * 32768      # holds at least the row statistics
+    args = [FAKE] * 15
+    assert L.sas_bwd(ctypes.byref(sh), *args, FAKE, need - 1, None) == 4
+    assert L.sas_bwd(ctypes.byref(sh), *args, None, need, None) == 4
+    pneed = api.sas_pool_workspace_bytes(sh)
+    assert L.sas_pool_scores(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, pneed - 1, None) == 4
+    dsh = api.make_decode_shape(64, 32, 8, 32768, 128, 32)
+    dneed = api.sas_decode_workspace_bytes(dsh)
+    assert dneed > 0
+    assert L.sas_decode(ctypes.byref(dsh), *([FAKE] * 7), FAKE, dneed - 1, None) == 4
+    bad = api.make_decode_shape(64, 32, 8, 1000, 128, 32)
+    assert api.sas_decode_workspace_bytes(bad) == 0
+    assert L.sas_decode(ctypes.byref(bad), *([FAKE] * 7), FAKE, 1 << 30, None) == 1
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    sh = api.make_shape(1, 1, 1, 64, 64, 0, torch.float32)
+    t = torch.zeros(64 * 64)
+    with pytest.raises(ValueError):
+        api.sas_fwd(sh, t, t, t, None, torch.zeros(1, dtype=torch.int32), None, t,
+                    torch.zeros(64))

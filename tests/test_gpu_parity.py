@@ -1,0 +1,269 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: selected block indices and counts bit-exact; bf16 workloads o max-abs
+<= 1e-2 and dq, dk, dv, ds relative-L2 <= 2e-2; the float32 workload 1e-5 for
+both.  lse / log_gate / s_lse tolerances follow from float32 accumulation.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sas_inputs as si
+from sas_run import BLOCK, dev, host, rel_l2, run_layer, tdtype
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": dict(o=1e-5, grad=1e-5, lse=1e-5), "bf16": dict(o=1e-2, grad=2e-2, lse=2e-3)}
+# bf16 outputs are stored rounded to nearest even: half an ulp is up to 2^-9 |o|,
+# which alone exceeds 1e-2 once |o| >= 2 (rows that see few keys).  The output
+# bar is therefore 1e-2 on top of the storage rounding (2^-8 |o_ref| with a 2x
+# margin for the ulp of the computed value); float32 outputs keep 1e-5.
+O_RTOL = {"f32": 0.0, "bf16": 2.0 ** -8}
+
+
+def assert_o(got, ref, dtype, what="o"):
+    err = np.abs(np.asarray(got, np.float64) - ref)
+    bound = TOL[dtype]["o"] + O_RTOL[dtype] * np.abs(ref)
+    worst = np.unravel_index(np.argmax(err - bound), err.shape)
+    assert np.all(err <= bound), (what, float(err[worst]), float(ref[worst]), worst)
+
+
+@pytest.fixture(scope="module")
+def api():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_block_sparse_select_amd as m
+    return m
+
+
+def _check_select(res, s_host, topk):
+    idx, cnt, lg, lse = oracle.select(s_host, topk)
+    assert np.array_equal(host(res["cnt"]), cnt)
+    assert np.array_equal(host(res["idx"]), idx)
+    g_lg, g_lse = host(res["log_gate"]), host(res["s_lse"])
+    assert np.array_equal(np.isneginf(g_lg), np.isneginf(lg))
+    fin = np.isfinite(lg)
+    np.testing.assert_allclose(g_lg[fin], lg[fin], rtol=1e-5, atol=1e-5)
+    assert np.array_equal(np.isneginf(g_lse), np.isneginf(lse))
+    fin = np.isfinite(lse)
+    np.testing.assert_allclose(g_lse[fin], lse[fin], rtol=1e-5, atol=1e-5)
+    return idx, cnt, lg, lse
+
+
+# ---------------------------------------------------------------- selection
+@pytest.mark.parametrize("case", ["normal", "ties", "k0", "kall", "gumbel"])
+def test_select_bitexact(api, case):
+    g = np.random.default_rng(11)
+    B, Hkv, nb, K = 2, 3, 300, 7
+    s = g.standard_normal((B, Hkv, nb, nb)).astype(np.float32)
+    if case == "ties":
+        s = np.round(s * 2).astype(np.float32)
+        z = s == 0
+        s[z] = np.where(g.random(z.sum()) < 0.5, np.float32(-0.0), np.float32(0.0))
+    if case == "k0":
+        K = 0
+    if case == "kall":
+        K = nb
+    if case == "gumbel":
+        s = (-3 * np.log(-np.log(g.random(s.shape)))).astype(np.float32)
+    sh = api.make_shape(B, 4 * Hkv, Hkv, nb * BLOCK, 128, K, torch.bfloat16)
+    st = torch.from_numpy(s).cuda()
+    sel = api.alloc_select(sh)
+    api.sas_select(sh, st, sel["idx"], sel["cnt"], sel["log_gate"], sel["s_lse"])
+    torch.cuda.synchronize()
+    _check_select(sel, s, K)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 4])
+def test_select_full_size(api, cfg):
+    w = si.WORKLOADS[cfg]
+    s = si.make_scores(w)
+    sh = api.make_shape(w.B, w.Hq, w.Hkv, w.n, w.d, w.topk, tdtype(w.dtype))
+    sel = api.alloc_select(sh)
+    api.sas_select(sh, torch.from_numpy(s).cuda(), sel["idx"], sel["cnt"], sel["log_gate"],
+                   sel["s_lse"])
+    torch.cuda.synchronize()
+    _check_select(sel, s, w.topk)
+
+
+# ---------------------------------------------------------------- pooling
+@pytest.mark.parametrize("cfg,small", [(3, True), (3, False)])
+def test_pool_parity(api, cfg, small):
+    w = si.WORKLOADS[cfg]
+    if small:
+        w = si.custom_workload(33, 1, 8, 2, 2048, 128, 4, "bf16")
+    q, k, _, _ = si.make_qkv(w, with_do=False)
+    sh = api.make_shape(w.B, w.Hq, w.Hkv, w.n, w.d, w.topk, tdtype(w.dtype))
+    s = torch.empty((w.B, w.Hkv, w.nqb, w.nqb), dtype=torch.float32, device="cuda")
+    ws = api.alloc_workspace(api.sas_pool_workspace_bytes(sh))
+    api.sas_pool_scores(sh, dev(q, tdtype(w.dtype)), dev(k, tdtype(w.dtype)), s, ws)
+    torch.cuda.synchronize()
+    ref = oracle.pool_scores(q, k, w.Hkv)
+    got = host(s)
+    assert rel_l2(got, ref) <= 1e-5
+    assert np.max(np.abs(got - ref)) <= 1e-5 * np.max(np.abs(ref))
+
+
+# ---------------------------------------------------------------- training layer, full oracle
+SMALL_CASES = {
+    "cfg1_fp32": (si.WORKLOADS[1], None),
+    "bf16_gqa4_d128": (si.custom_workload(101, 2, 8, 2, 1024, 128, 4, "bf16"), None),
+    "bf16_gqa5_d64": (si.custom_workload(102, 1, 5, 1, 640, 64, 3, "bf16"), None),
+    "bf16_single_block": (si.custom_workload(103, 1, 4, 1, 64, 128, 2, "bf16"), None),
+    "bf16_k0": (si.custom_workload(104, 1, 4, 2, 512, 128, 0, "bf16"), None),
+    "bf16_kall": (si.custom_workload(105, 1, 2, 1, 512, 128, 8, "bf16"), None),
+    "bf16_mha_d128": (si.custom_workload(106, 1, 1, 1, 768, 128, 5, "bf16"), None),
+    "bf16_heavy_gumbel": (si.custom_workload(107, 1, 4, 1, 1024, 128, 6, "bf16",
+                                             s_kind="gumbel3"), None),
+    "fp32_gqa2_d128": (si.custom_workload(108, 1, 4, 2, 384, 128, 2, "f32"), None),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL_CASES))
+def test_fwd_parity_full(api, name):
+    w, _ = SMALL_CASES[name]
+    q, k, v, _ = si.make_qkv(w, with_do=False)
+    s = si.make_scores(w)
+    dt = tdtype(w.dtype)
+    res = run_layer(api, dev(q, dt), dev(k, dt), dev(v, dt), None, torch.from_numpy(s).cuda(),
+                    w.topk, dt, bwd=False)
+    idx, cnt, lg, _ = _check_select(res, s, w.topk)
+    o, lse = oracle.fwd_gather(q, k, v, idx, cnt, lg)
+    tol = TOL[w.dtype]
+    assert_o(host(res["o"]), o, w.dtype)
+    assert np.max(np.abs(host(res["lse"]) - lse)) <= tol["lse"]
+
+
+@pytest.mark.parametrize("name", list(SMALL_CASES))
+def test_layer_parity_full(api, name):
+    w, _ = SMALL_CASES[name]
+    q, k, v, do = si.make_qkv(w)
+    s = si.make_scores(w)
+    dt = tdtype(w.dtype)
+    res = run_layer(api, dev(q, dt), dev(k, dt), dev(v, dt), dev(do, dt),
+                    torch.from_numpy(s).cuda(), w.topk, dt)
+    idx, cnt, lg, _ = _check_select(res, s, w.topk)
+    ref = oracle.sas_forward_backward(q, k, v, do, s, w.topk)
+    tol = TOL[w.dtype]
+    assert_o(host(res["o"]), ref["o"], w.dtype)
+    assert np.max(np.abs(host(res["lse"]) - ref["lse"])) <= tol["lse"]
+    for nm in ("dq", "dk", "dv", "ds"):
+        e = rel_l2(host(res[nm]), ref[nm])
+        assert e <= tol["grad"], (nm, e)
+
+
+# ---------------------------------------------------------------- full-size sampled checks
+def _sample_blocks(w, rng, n_blocks=5):
+    picks = {(0, 0, 0), (0, w.Hkv - 1, w.nqb - 1), (0, w.Hkv // 2, min(w.topk, w.nqb - 1))}
+    while len(picks) < n_blocks:
+        picks.add((int(rng.integers(w.B)), int(rng.integers(w.Hkv)), int(rng.integers(w.nqb))))
+    return sorted(picks)
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_layer_parity_full_size_sampled(api, cfg):
+    w = si.WORKLOADS[cfg]
+    q, k, v, do = si.make_qkv(w)
+    dt = tdtype(w.dtype)
+    qd, kd, vd, dod = dev(q, dt), dev(k, dt), dev(v, dt), dev(do, dt)
+    if w.s_kind == "pool":
+        res = run_layer(api, qd, kd, vd, dod, None, w.topk, dt, pool=True)
+        s = host(res["s"])      # selection parity is defined on the device scores
+    else:
+        s = si.make_scores(w)
+        res = run_layer(api, qd, kd, vd, dod, torch.from_numpy(s).cuda(), w.topk, dt)
+    idx, cnt, lg, s_lse = _check_select(res, s, w.topk)
+    rng = np.random.default_rng(cfg)
+    G = w.Hq // w.Hkv
+    tol = TOL[w.dtype]
+    o_g, lse_g, dq_g, ds_g = host(res["o"]), host(res["lse"]), host(res["dq"]), host(res["ds"])
+    for (b, kv, i) in _sample_blocks(w, rng):
+        ob, lb = oracle.fwd_gather_block(q, k, v, idx, cnt, lg, b, kv, i)
+        r = slice(i * BLOCK, (i + 1) * BLOCK)
+        hs = slice(kv * G, (kv + 1) * G)
+        assert_o(o_g[b, hs, r], ob, w.dtype, ("o", b, kv, i))
+        assert np.max(np.abs(lse_g[b, hs, r] - lb)) <= tol["lse"], (b, kv, i)
+        dqb, _, _, _, dlg = oracle.bwd_gather_block(q, k, v, do, idx, cnt, lg, b, kv, i)
+        assert rel_l2(dq_g[b, hs, r], dqb) <= tol["grad"], ("dq", b, kv, i)
+        if i > 0:
+            dlg_full = np.zeros((1, 1, w.nqb, w.topk))
+            dlg_full[0, 0, i] = dlg
+            dsr = oracle.gate_jacobian(s[b:b + 1, kv:kv + 1], s_lse[b:b + 1, kv:kv + 1],
+                                       idx[b:b + 1, kv:kv + 1], cnt[b:b + 1, kv:kv + 1],
+                                       dlg_full)[0, 0, i]
+            assert rel_l2(ds_g[b, kv, i], dsr) <= tol["grad"], ("ds", b, kv, i)
+    dk_g, dv_g = host(res["dk"]), host(res["dv"])
+    for (b, kv, m) in [(0, 0, 0), (0, w.Hkv - 1, w.nqb // 2), (0, 1, w.nqb - 1)]:
+        dkm, dvm = oracle.bwd_kv_block(q, k, v, do, idx, cnt, lg, b, kv, m)
+        r = slice(m * BLOCK, (m + 1) * BLOCK)
+        assert rel_l2(dk_g[b, kv, r], dkm) <= tol["grad"], ("dk", b, kv, m)
+        assert rel_l2(dv_g[b, kv, r], dvm) <= tol["grad"], ("dv", b, kv, m)
+
+
+# ---------------------------------------------------------------- decode
+def _decode_run(api, w, q, kc, vc, lens, s):
+    dt = tdtype(w.dtype)
+    sh = api.make_decode_shape(w.B, w.Hq, w.Hkv, w.cap, w.d, w.topk, dt)
+    o = torch.empty_like(q)
+    idx = torch.empty((w.B, w.Hkv, w.topk), dtype=torch.int32, device="cuda")
+    ws = api.alloc_workspace(api.sas_decode_workspace_bytes(sh))
+    api.sas_decode(sh, q, kc, vc, torch.from_numpy(lens).cuda(), torch.from_numpy(s).cuda(), o,
+                   idx, ws)
+    torch.cuda.synchronize()
+    return o, idx
+
+
+@pytest.mark.parametrize("dtype,G,d,cap,K", [("bf16", 4, 128, 1024, 5), ("bf16", 5, 64, 512, 3),
+                                             ("f32", 2, 64, 768, 2), ("bf16", 1, 128, 256, 0)])
+def test_decode_parity_small(api, dtype, G, d, cap, K):
+    w = si.DecodeWorkload(200 + G, 5, 2 * G, 2, cap, d, K, dtype, hist_blocks=cap // BLOCK - 1)
+    q, kc, vc, lens, s = si.make_decode_small(w)
+    lens = np.array([1, 64, 65, cap - 3, cap][:w.B], dtype=np.int32)
+    dt = tdtype(dtype)
+    o, idx = _decode_run(api, w, dev(q, dt), dev(kc, dt), dev(vc, dt), lens, s)
+    ref_o, ref_idx = oracle.decode(q, kc, vc, lens, s, K)
+    assert np.array_equal(host(idx), ref_idx)
+    assert_o(host(o), ref_o, dtype)
+
+
+def test_decode_parity_full_size(api):
+    w = si.DECODE_WORKLOAD
+    q, s = si.decode_q_and_scores(w)
+    lens = si.decode_seq_lens(w)
+    kc, vc = si.decode_cache_device(w, "cuda")
+    o, idx = _decode_run(api, w, dev(q, torch.bfloat16), kc, vc, lens, s)
+    rows = [(0, 0), (7, 3), (31, 7), (63, 5), (40, 1)]
+
+    class _Cache:
+        def __init__(self, t):
+            self.t = t
+
+        def __getitem__(self, bk):
+            return self.t[bk[0], bk[1]].float().cpu().numpy()
+
+    ref_o, ref_idx = oracle.decode(q, _Cache(kc), _Cache(vc), lens, s, w.topk, rows=rows)
+    # selection for every row (cheap) and outputs on the sampled rows
+    idx_h = host(idx)
+    for b in range(w.B):
+        for kv in range(w.Hkv):
+            ch, _, _ = oracle.select_row(s[b, kv], (int(lens[b]) - 1) // BLOCK, w.topk)
+            assert list(idx_h[b, kv, :len(ch)]) == ch
+    o_h = host(o)
+    G = w.Hq // w.Hkv
+    for (b, kv) in rows:
+        assert_o(o_h[b, kv * G:(kv + 1) * G], ref_o[b, kv * G:(kv + 1) * G], "bf16")
+
+
+# ---------------------------------------------------------------- determinism
+def test_run_twice_bitwise(api):
+    w = si.custom_workload(300, 1, 8, 2, 2048, 128, 8, "bf16")
+    q, k, v, do = si.make_qkv(w)
+    s = torch.from_numpy(si.make_scores(w)).cuda()
+    args = [dev(x, torch.bfloat16) for x in (q, k, v, do)]
+    a = run_layer(api, *args, s, w.topk, torch.bfloat16)
+    b = run_layer(api, *args, s, w.topk, torch.bfloat16)
+    for nm in ("idx", "cnt", "log_gate", "s_lse", "o", "lse", "dq", "dk", "dv", "ds"):
+        assert torch.equal(a[nm], b[nm]), nm
