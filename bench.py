@@ -1,0 +1,254 @@
+"""Benchmark of the SAS gated block-sparse attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--no-decode]
+
+A step is one pass of the training-layer hot path over one synthetic batch:
+block-score pooling (when the workload scores by pooling) -> LSE/Top-K select
+-> gated block-sparse forward -> backward (dq, dk, dv and ds).  Inputs are
+resident in HBM before the timed region; W untimed steps, then K timed steps
+between two device synchronisations.  Prints ONE JSON line.
+
+value = effective TFLOP/s: FLOPs counted on valid (query, key) pairs only
+(64*64 per kept block plus 64*65/2 for the causal current block, per query
+head), 4*d per pair for the forward and 10*d for the backward.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores, TFLOP/s
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", type=int, default=3, choices=[2, 3, 4])
+    p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    p.add_argument("--decode-steps", type=int, default=50)
+    return p.parse_args()
+
+
+def pair_count(cnt_np, G):
+    """Valid (query, key) pairs summed over query heads."""
+    import numpy as np
+    c = cnt_np.astype(np.int64)
+    return G * (int(c.sum()) * 64 * 64 + c.size * (64 * 65 // 2))
+
+
+def run_training(args, api, si, torch, np):
+    w = si.WORKLOADS[args.workload]
+    dt = torch.bfloat16
+    q, k, v, do = si.make_qkv(w)
+    dev = lambda x: torch.from_numpy(x).to("cuda").to(dt)
+    qd, kd, vd, dod = dev(q), dev(k), dev(v), dev(do)
+    host = dict(q=q, k=k, v=v, do=do)
+    del q, k, v, do
+    sh = api.make_shape(w.B, w.Hq, w.Hkv, w.n, w.d, w.topk, dt)
+    nb = w.nqb
+    pool = w.s_kind == "pool"
+    s = torch.empty((w.B, w.Hkv, nb, nb), dtype=torch.float32, device="cuda")
+    if not pool:
+        s.copy_(torch.from_numpy(si.make_scores(w)))
+    sel = api.alloc_select(sh)
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.Hq, w.n), dtype=torch.float32, device="cuda")
+    dq, dk, dv, ds = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd), torch.empty_like(s)
+    ws_pool = api.alloc_workspace(api.sas_pool_workspace_bytes(sh))
+    ws_bwd = api.alloc_workspace(api.sas_bwd_workspace_bytes(sh))
+
+    def step():
+        if pool:
+            api.sas_pool_scores(sh, qd, kd, s, ws_pool)
+        api.sas_select(sh, s, sel["idx"], sel["cnt"], sel["log_gate"], sel["s_lse"])
+        api.sas_fwd(sh, qd, kd, vd, sel["idx"], sel["cnt"], sel["log_gate"], o, lse)
+        api.sas_bwd(sh, qd, kd, vd, o, dod, lse, sel["idx"], sel["cnt"], sel["log_gate"], s,
+                    sel["s_lse"], dq, dk, dv, ds, ws_bwd)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    api.sas_prof_collect()          # drop anything recorded before
+    api.sas_prof_enable(True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    api.sas_prof_enable(False)
+    kern = api.sas_prof_collect()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+
+    cnt = sel["cnt"].cpu().numpy()
+    G = w.Hq // w.Hkv
+    pairs = pair_count(cnt, G)
+    flop_fwd = 4 * w.d * pairs
+    flop_bwd = 10 * w.d * pairs
+    per_kernel = {name: dict(avg_ms=tot / max(nl, 1), launches=nl) for name, (tot, nl) in kern.items()}
+    return dict(w=w, ms_step=ms_step, wall=wall, pairs=pairs, flop_fwd=flop_fwd, flop_bwd=flop_bwd,
+                per_kernel=per_kernel, host=host, s=s, sel=sel, steps=args.steps)
+
+
+def roofline_for(res):
+    """Dominant kernel by time; its algorithmic FLOPs per launch are the
+    contractions it performs on valid pairs: forward 2 (4d per pair), dq pass 3
+    (S, dP, dQ: 6d), dk/dv pass 4 (S, dP, dV, dK: 8d)."""
+    w = res["w"]
+    per = {"sas_fwd_mfma_kernel": 4, "sas_bwd_dq_kernel": 6, "sas_bwd_dkdv_kernel": 8}
+    pk = res["per_kernel"]
+    name = max(pk, key=lambda n: pk[n]["avg_ms"] * pk[n]["launches"])
+    if name in per:
+        flops = per[name] * w.d * res["pairs"]
+        ach = flops / (pk[name]["avg_ms"] * 1e-3) / 1e12
+        return dict(bound="mfma", achieved=round(ach, 2), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(ach / BF16_PEAK_TFLOPS, 4), traffic=None, kernel=name,
+                    avg_ms=round(pk[name]["avg_ms"], 4), flop_per_launch=flops)
+    return dict(bound="hbm", achieved=None, peak=HBM_PEAK_GBS, unit="GB/s", frac=None,
+                traffic=None, kernel=name)
+
+
+def cpu_baseline(res, np, budget_s=15.0):
+    """The oracle (numpy, float64 gather mode) on a bounded sample of the same
+    workload: whole q-blocks, forward + backward, until ~budget_s of CPU time."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    w = res["w"]
+    h = res["host"]
+    s = res["s"].cpu().numpy()
+    idx, cnt, lg, _ = oracle.select(s[:, :1], w.topk)          # kv-head 0 rows
+    G = w.Hq // w.Hkv
+    k0, v0 = h["k"][:, :1], h["v"][:, :1]
+    q0, do0 = h["q"][:, :G], h["do"][:, :G]
+    rng = np.random.default_rng(0)
+    order = rng.permutation(w.nqb)
+    t0 = time.perf_counter()
+    done, pairs = 0, 0
+    for i in order:
+        oracle.fwd_gather_block(q0, k0, v0, idx, cnt, lg, 0, 0, int(i))
+        oracle.bwd_gather_block(q0, k0, v0, do0, idx, cnt, lg, 0, 0, int(i))
+        done += 1
+        pairs += G * (int(cnt[0, 0, i]) * 4096 + 2080)
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    flops = 14 * w.d * pairs
+    return dict(value=round(flops / el / 1e12, 6), unit="TFLOP/s", cores=int(threads), kind="oracle",
+                sample=f"{done} of {w.nqb * w.Hkv * w.B} (batch, kv-head, q-block) units of the "
+                       f"{w.name} workload, kv-head 0, forward+backward in float64 gather mode, "
+                       f"{el:.1f} s")
+
+
+def run_decode(args, api, si, torch, np):
+    w = si.DECODE_WORKLOAD
+    dt = torch.bfloat16
+    qh, sh_ = si.decode_q_and_scores(w)
+    lens = si.decode_seq_lens(w)
+    kc, vc = si.decode_cache_device(w, "cuda")
+    q = torch.from_numpy(qh).cuda().to(dt)
+    s = torch.from_numpy(sh_).cuda()
+    L = torch.from_numpy(lens).cuda()
+    shp = api.make_decode_shape(w.B, w.Hq, w.Hkv, w.cap, w.d, w.topk, dt)
+    o = torch.empty_like(q)
+    idx = torch.empty((w.B, w.Hkv, w.topk), dtype=torch.int32, device="cuda")
+    ws = api.alloc_workspace(api.sas_decode_workspace_bytes(shp))
+    for _ in range(5):
+        api.sas_decode(shp, q, kc, vc, L, s, o, idx, ws)
+    torch.cuda.synchronize()
+    api.sas_prof_collect()
+    api.sas_prof_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.decode_steps):
+        api.sas_decode(shp, q, kc, vc, L, s, o, idx, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    api.sas_prof_enable(False)
+    kern = api.sas_prof_collect()
+    us = e0.elapsed_time(e1) * 1e3 / args.decode_steps
+    G = w.Hq // w.Hkv
+    kv_bytes = sum(w.Hkv * (w.topk * 64 + (int(x) - 511 * 64)) * w.d * 2 * 2 for x in lens)
+    other = q.numel() * 2 * 2 + s.numel() * 4 + idx.numel() * 4 + w.B * 4
+    alg = kv_bytes + other
+    per_kernel = {n: dict(avg_us=round(t * 1e3 / max(c, 1), 2), launches=c) for n, (t, c) in kern.items()}
+    split = per_kernel.get("sas_decode_split_kernel", {}).get("avg_us")
+    out = dict(workload=w.name, us_per_call=round(us, 2), algorithmic_bytes=alg,
+               GBs=round(alg / (us * 1e-6) / 1e9, 1),
+               frac_hbm=round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), per_kernel=per_kernel)
+    if split:
+        gbs = kv_bytes / (split * 1e-6) / 1e9
+        out["roofline"] = dict(bound="hbm", kernel="sas_decode_split_kernel", achieved=round(gbs, 1),
+                               peak=HBM_PEAK_GBS, unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4),
+                               traffic=None)
+    del kc, vc
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import gated_block_sparse_select_amd as api
+    import sas_inputs as si
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    res = run_training(args, api, si, torch, np)
+    w = res["w"]
+    total = res["flop_fwd"] + res["flop_bwd"]
+    tflops = total / (res["ms_step"] * 1e-3) / 1e12
+    line = {
+        "metric": "SAS fwd+bwd effective TFLOP/s @32K (Qwen3-8B shape) + % bf16 MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.d,
+                   "n": w.n, "block": 64, "topk": w.topk,
+                   "scores": "device mean-pool" if w.s_kind == "pool" else w.s_kind,
+                   "step": "pool+select+fwd+bwd(dq,dk,dv,ds)" if w.s_kind == "pool"
+                   else "select+fwd+bwd(dq,dk,dv,ds)"},
+        "frac_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
+        "roofline": roofline_for(res),
+        "effective_flop": {"fwd": res["flop_fwd"], "bwd": res["flop_bwd"], "pairs": res["pairs"]},
+        "per_kernel_ms": {k: round(v["avg_ms"], 4) for k, v in res["per_kernel"].items()},
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(res, np)
+    res["host"] = None
+    if not args.no_decode:
+        torch.cuda.empty_cache()
+        line["decode"] = run_decode(args, api, si, torch, np)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
