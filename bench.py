@@ -36,6 +36,8 @@ def parse():
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     p.add_argument("--decode-steps", type=int, default=50)
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="first run one 1 GiB device copy (reference for HBM byte counters)")
     return p.parse_args()
 
 
@@ -214,6 +216,14 @@ def main():
     import sas_inputs as si
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        # a plain copy of known size: 1 GiB read + 1 GiB written
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     res = run_training(args, api, si, torch, np)
     w = res["w"]
     total = res["flop_fwd"] + res["flop_bwd"]

@@ -23,7 +23,7 @@ SOURCES = ["select.hip", "pool.hip", "revidx.hip", "simt.hip", "decode.hip",
 
 ARCH = "gfx950"
 # packed fp32 ops stay off: hipcc would otherwise form v_pk_* float ops itself
-COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
+COMMON = ["-O3", "-fPIC", "-std=c++20", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wno-unused-command-line-argument", "-I", os.path.join(HERE, "..", "include")]
 

@@ -35,18 +35,18 @@ __global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ o,
     const uint16_t* __restrict__ dO, const float* __restrict__ lse,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
-    const float* __restrict__ lg, uint16_t* __restrict__ dq, float* __restrict__ Dws,
+    const float* __restrict__ lg, uint16_t* __restrict__ dq, float* __restrict__ stats,
     float* __restrict__ dlgp, int Hq, int Hkv, int n, int topk, float tau, float tau2, int BH,
-    int h_off, int hchunks, int nch) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  constexpr int ROWB = D * 2;
-  constexpr int TB = 64 * ROWB;
-  constexpr int CPR = D / 8;
-  constexpr int HALF = 64 * CPR;
-  constexpr int TOTAL = 2 * HALF;
-  constexpr int NT = 128 * GC;
-  constexpr int CPT = (TOTAL + NT - 1) / NT;
-  float* part = reinterpret_cast<float*>(smem + 4 * TB);  // [2][8] per-wave dZ sums
+    int h_off, int hchunks, int nch, int chunk0) {
+  extern __shared__ __attribute__((aligned(16))) char smem_generic[];
+  lds_char* const smem = lds_ptr(smem_generic);
+  constexpr int NS = kDqStages;
+  constexpr int TB = 64 * D * 2;
+  constexpr int JT = TB / 1024;
+  constexpr int JW = 2 * JT / (2 * GC);
+  static_assert((2 * JT) % (2 * GC) == 0, "slices must split evenly over the waves");
+  __attribute__((address_space(3))) float* part =
+      reinterpret_cast<__attribute__((address_space(3))) float*>(smem + NS * 2 * TB);  // [2][8] per-wave dZ sums
 
   const int nqb = n / SAS_BLK;
   const int G = Hq / Hkv;
@@ -61,7 +61,7 @@ __global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
   const int lr = lane & 31, hh = lane >> 5;
   const int h = kv * G + h_off + hc * GC + (wave >> 1);
   const int rt = wave & 1;
-  const int chunk = h_off / 4 + hc;
+  const int chunk = chunk0 + hc;
   const size_t rowsel = size_t(bk) * nqb + i;
   const int c_sel = cnt[rowsel];
   const int ntiles = c_sel + 1;
@@ -81,40 +81,29 @@ __global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
     for (int e = 0; e < 8; ++e) dpart += float(dop[c][e]) * float(oo[e]);
   }
   const float Drow = dpart + __shfl_xor(dpart, 32);
-  if (hh == 0) Dws[qrow] = Drow;
   const float lse2 = lse[qrow] * kLog2e;
+  if (hh == 0) {
+    // per-row statistics of this (head, q-block) for the key-block-outer pass:
+    // [lse * log2(e) for the 64 rows | D for the 64 rows]
+    float* st = stats + ((size_t(b) * Hq + h) * nqb + i) * 128;
+    st[rt * 32 + lr] = lse2;
+    st[64 + rt * 32 + lr] = Drow;
+  }
 
   const size_t kv0 = (size_t(b) * Hkv + kv) * size_t(n);
-  uint4 stg[CPT];
-  auto load_tile = [&](int t) {
+  auto issue = [&](int t, int buf) {
     const int blk = t < c_sel ? irow[t] : i;
     const uint16_t* kb = k + (kv0 + size_t(blk) * SAS_BLK) * D;
     const uint16_t* vb = v + (kv0 + size_t(blk) * SAS_BLK) * D;
+    lds_char* base = smem + buf * 2 * TB;
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int c = tid + NT * u;
-      if (c < TOTAL) {
-        const uint16_t* src = c < HALF ? kb + c * 8 : vb + (c - HALF) * 8;
-        stg[u] = *reinterpret_cast<const uint4*>(src);
-      }
+    for (int u = 0; u < JW; ++u) {
+      const int j = wave * JW + u;
+      const int T = j / JT;
+      dma_tile_slice<D>(T ? vb : kb, base + T * TB, j % JT, lane);
     }
   };
-  auto store_tile = [&](int stage) {
-    char* base = smem + stage * 2 * TB;
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int c = tid + NT * u;
-      if (c < TOTAL) {
-        const bool isv = c >= HALF;
-        const int cc = isv ? c - HALF : c;
-        *reinterpret_cast<uint4*>(base + (isv ? TB : 0) + tile_off<D>(cc / CPR, cc % CPR)) = stg[u];
-      }
-    }
-  };
-
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  for (int t = 0; t < NS - 1 && t < ntiles; ++t) issue(t, t);
 
   f32x16 dQ[D / 32];
 #pragma unroll
@@ -122,48 +111,56 @@ __global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
 #pragma unroll
     for (int j = 0; j < 16; ++j) dQ[dt][j] = 0.f;
 
+#pragma nounroll
   for (int t = 0; t < ntiles; ++t) {
-    const int stage = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
-    const char* Kt = smem + stage * 2 * TB;
-    const char* Vt = Kt + TB;
+    if (t + 1 < ntiles) vm_wait_barrier<JW * (NS - 2)>();
+    else vm_wait_barrier<0>();
+    // the barrier also published every wave's dZ sum of tile t-1
+    if (t > 0 && tid == 0) {
+      float a = 0.f;
+      for (int w = 0; w < 2 * GC; ++w) a += part[((t - 1) & 1) * 8 + w];
+      dlgp[(rowsel * nch + chunk) * topk + t - 1] = a;
+    }
+    if (t + NS - 1 < ntiles) issue(t + NS - 1, (t + NS - 1) % NS);
+    lds_cchar* Kt = smem + (t % NS) * 2 * TB;
+    lds_cchar* Vt = Kt + TB;
     const bool cur = t == c_sel;
     const float zoff = (cur ? 0.f : grow[t] * kLog2e) - lse2;
 
-    f32x16 S[2], P2[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        S[kt][j] = 0.f;
-        P2[kt][j] = 0.f;
-      }
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        S[kt] = mfma32(lds_read16(Kt, tile_off<D>(kt * 32 + lr, 2 * c + hh)), qop[c], S[kt]);
-        P2[kt] = mfma32(lds_read16(Vt, tile_off<D>(kt * 32 + lr, 2 * c + hh)), dop[c], P2[kt]);
-      }
-    }
+    // one 32-key half at a time keeps only 2 accumulator tiles live
     float zs = 0.f;
     bf16x8 dZp[4];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt) {
+      f32x16 S, P2;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        S[j] = 0.f;
+        P2[j] = 0.f;
+      }
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+        const int off = tile_off<D>(kt * 32 + lr, 2 * c + hh);
+        S = mfma32(lds_read16(Kt, off), qop[c], S);
+        P2 = mfma32(lds_read16(Vt, off), dop[c], P2);
+      }
 #pragma unroll
       for (int jc = 0; jc < 2; ++jc) {
         float x[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int j = 8 * jc + e;
-          float p = exp2f(S[kt][j] * tau2 + zoff);
+          float p = exp2f(S[j] * tau2 + zoff);
           if (cur) {
             const int key = kt * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
             if (key > rt * 32 + lr) p = 0.f;
           }
-          x[e] = p * (P2[kt][j] - Drow);
+          x[e] = p * (P2[j] - Drow);
           zs += x[e];
         }
         dZp[kt * 2 + jc] = pack_bf16x8(x);
       }
+    }
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -173,13 +170,6 @@ __global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
     if (!cur) {
       zs = wave_sum(zs);
       if (lane == 0) part[(t & 1) * 8 + wave] = zs;
-    }
-    if (t + 1 < ntiles) store_tile(stage ^ 1);
-    __syncthreads();
-    if (!cur && tid == 0) {
-      float a = 0.f;
-      for (int w = 0; w < 2 * GC; ++w) a += part[(t & 1) * 8 + w];
-      dlgp[(rowsel * nch + chunk) * topk + t] = a;
     }
   }
 
@@ -238,22 +228,26 @@ __global__ void __launch_bounds__(256) bwd_ds_kernel(const float* __restrict__ d
 
 // ------------------------------------------------------------------ dk/dv kernel
 // grid: B*Hkv*nkb workgroups of 4 waves; wave = (key half kh, row half rh).
+// The (q-block, head) steps of the reverse list stream through a ring of
+// kKvStages LDS buffers, each holding the Q and dO tiles of one (q-block, head)
+// and its row statistics.
 template <int D>
 __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
-    const float* __restrict__ lse, const float* __restrict__ Dws, const float* __restrict__ lg,
+    const float* __restrict__ stats, const float* __restrict__ lg,
     const int32_t* __restrict__ rev_off, const int32_t* __restrict__ rev_list,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int Hq, int Hkv, int n, int topk,
     float tau, float tau2) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  constexpr int ROWB = D * 2;
-  constexpr int TB = 64 * ROWB;
+  extern __shared__ __attribute__((aligned(16))) char smem_generic[];
+  lds_char* const smem = lds_ptr(smem_generic);
+  constexpr int NS = kKvStages;
+  constexpr int TB = 64 * D * 2;
   constexpr int CPR = D / 8;
-  constexpr int HALF = 64 * CPR;
-  constexpr int TOTAL = 2 * HALF;       // Q + dO chunks per step
-  constexpr int CPT = TOTAL / 256;
-  constexpr int STAGE = 2 * TB + 512;   // Q tile, dO tile, lse[64], D[64]
+  constexpr int JT = TB / 1024;
+  constexpr int JW = 2 * JT / 4;        // Q + dO slices per wave per step
+  constexpr int PER = JW + 1;           // plus one slice of row statistics
+  constexpr int STAGE = 2 * TB + 512;
 
   const int nkb = n / SAS_BLK;
   const int G = Hq / Hkv;
@@ -286,52 +280,42 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
   const int32_t e1 = rev_off[size_t(bk) * (nkb + 1) + m + 1];
   const int nsteps = (e1 - e0) * G;
 
-  uint4 stg[CPT];
-  float st_val = 0.f;
-  auto load_step = [&](int s) {
+  auto issue = [&](int s, int buf) {
     const int32_t ent = lst[e0 + s / G];
     const int iq = ent & 0xFFFF;
     const int hq = kv * G + s % G;
     const size_t row0 = (size_t(b) * Hq + hq) * n + size_t(iq) * SAS_BLK;
-    const uint16_t* qb = q + row0 * D;
-    const uint16_t* ob = dO + row0 * D;
+    lds_char* base = smem + buf * STAGE;
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int c = tid + 256 * u;
-      const uint16_t* src = c < HALF ? qb + c * 8 : ob + (c - HALF) * 8;
-      stg[u] = *reinterpret_cast<const uint4*>(src);
+    for (int u = 0; u < JW; ++u) {
+      const int j = wave * JW + u;
+      const int T = j / JT;
+      dma_tile_slice<D>((T ? dO : q) + row0 * D, base + T * TB, j % JT, lane);
     }
-    if (tid < 64) st_val = lse[row0 + tid] * kLog2e;
-    else if (tid < 128) st_val = Dws[row0 + tid - 64];
+    // 512 B of statistics: lanes 0..7 of each wave move 128 B
+    const float* st = stats + ((size_t(b) * Hq + hq) * nkb + iq) * 128 + wave * 32;
+    if (lane < 8) dma16(st + lane * 4, base + 2 * TB + wave * 128);
   };
-  auto store_step = [&](int stage) {
-    char* base = smem + stage * STAGE;
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int c = tid + 256 * u;
-      const bool iso = c >= HALF;
-      const int cc = iso ? c - HALF : c;
-      *reinterpret_cast<uint4*>(base + (iso ? TB : 0) + tile_off<D>(cc / CPR, cc % CPR)) = stg[u];
-    }
-    if (tid < 128) reinterpret_cast<float*>(base + 2 * TB)[tid] = st_val;
-  };
+  for (int t = 0; t < NS - 1 && t < nsteps; ++t) issue(t, t);
 
-  load_step(0);
-  store_step(0);
-  __syncthreads();
   const int keyw = kh * 32 + lr;  // this lane's key inside block m
+#pragma nounroll
   for (int s = 0; s < nsteps; ++s) {
-    const int stage = s & 1;
-    if (s + 1 < nsteps) load_step(s + 1);
-    const char* Qt = smem + stage * STAGE;
-    const char* Ot = Qt + TB;
-    const float* stl = reinterpret_cast<const float*>(Qt + 2 * TB);
+    const int after = min(NS - 2, nsteps - 1 - s);
+    if (after >= 2) vm_wait_barrier<PER * 2>();
+    else if (after == 1) vm_wait_barrier<PER>();
+    else vm_wait_barrier<0>();
+    if (s + NS - 1 < nsteps) issue(s + NS - 1, (s + NS - 1) % NS);
+    lds_cchar* Qt = smem + (s % NS) * STAGE;
+    lds_cchar* Ot = Qt + TB;
+    const __attribute__((address_space(3))) float* stl =
+        reinterpret_cast<const __attribute__((address_space(3))) float*>(Qt + 2 * TB);
     const int32_t ent = lst[e0 + s / G];
     const int iq = ent & 0xFFFF;
     const int slot = (ent >> 16) & 0xFFFF;
     const bool own = slot == 0xFFFF;
     const float bias2 = own ? 0.f : lg[(size_t(bk) * nkb + iq) * topk + slot] * kLog2e;
-    // own block, rows of this half all above the keys of this half: nothing visible
+    // own block: rows 0..31 see none of the keys 32..63
     const bool skip = own && kh == 1 && rh == 0;
     if (!skip) {
       f32x16 S, P2;
@@ -371,13 +355,13 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
           dK[dt] = mfma32(Zp[jc], tr_operand<D>(Qt, rh * 32 + 16 * jc, dt * 32, lane), dK[dt]);
         }
     }
-    if (s + 1 < nsteps) store_step(stage ^ 1);
-    __syncthreads();
   }
+  __syncthreads();
 
   // Reduce the two row halves through LDS ([64 keys][D] float32), then write
   // coalesced bf16 rows: first dV, then dK (scaled by tau).
-  float* red = reinterpret_cast<float*>(smem);
+  __attribute__((address_space(3))) float* red =
+      reinterpret_cast<__attribute__((address_space(3))) float*>(smem);
   const size_t out0 = ((size_t(b) * Hkv + kv) * n + size_t(m) * SAS_BLK) * D;
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
@@ -401,7 +385,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
     uint16_t* dst = (pass == 0 ? dv : dk) + out0;
     const float sc = pass == 0 ? 1.f : tau;
     for (int c = tid; c < 64 * CPR; c += 256) {
-      const float* src = red + c * 8;
+      const __attribute__((address_space(3))) float* src = red + c * 8;
       bf16x8 r;
 #pragma unroll
       for (int e = 0; e < 8; ++e) r[e] = (__bf16)(src[e] * sc);
@@ -412,48 +396,45 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
 }
 
 // ------------------------------------------------------------------ host side
-template <class K>
-static void allow_lds(K kernel, size_t bytes) {
-  if (bytes > 65536)
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
-}
-
 template <int D, int GC>
 static void dq_launch(int nblocks, const void* q, const void* k, const void* v, const void* o,
                       const void* dO, const float* lse, const int32_t* idx, const int32_t* cnt,
-                      const float* lg, void* dq, float* Dws, float* dlgp, int Hq, int Hkv, int n,
+                      const float* lg, void* dq, float* stats, float* dlgp, int Hq, int Hkv, int n,
                       int topk, float tau, float tau2, int BH, int h_off, int hchunks, int nch,
-                      hipStream_t st) {
-  const size_t shm = size_t(4) * 64 * D * 2 + 64;
+                      int chunk0, hipStream_t st) {
+  const size_t shm = size_t(kDqStages) * 2 * 64 * D * 2 + 64;
   auto kern = bwd_dq_kernel<D, GC>;
   allow_lds(kern, shm);
   hipLaunchKernelGGL(kern, dim3(nblocks), dim3(128 * GC), shm, st, (const uint16_t*)q,
                      (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o,
-                     (const uint16_t*)dO, lse, idx, cnt, lg, (uint16_t*)dq, Dws, dlgp, Hq, Hkv, n,
-                     topk, tau, tau2, BH, h_off, hchunks, nch);
+                     (const uint16_t*)dO, lse, idx, cnt, lg, (uint16_t*)dq, stats, dlgp, Hq, Hkv,
+                     n, topk, tau, tau2, BH, h_off, hchunks, nch, chunk0);
 }
 
 template <int D>
 static void dq_dispatch(int gc, int nblocks, const void* q, const void* k, const void* v,
                         const void* o, const void* dO, const float* lse, const int32_t* idx,
-                        const int32_t* cnt, const float* lg, void* dq, float* Dws, float* dlgp,
+                        const int32_t* cnt, const float* lg, void* dq, float* stats, float* dlgp,
                         int Hq, int Hkv, int n, int topk, float tau, float tau2, int BH, int h_off,
-                        int hchunks, int nch, hipStream_t st) {
-#define SAS_DQ_ARGS nblocks, q, k, v, o, dO, lse, idx, cnt, lg, dq, Dws, dlgp, Hq, Hkv, n, topk, \
-                    tau, tau2, BH, h_off, hchunks, nch, st
+                        int hchunks, int nch, int chunk0, hipStream_t st) {
+#define SAS_DQ_ARGS nblocks, q, k, v, o, dO, lse, idx, cnt, lg, dq, stats, dlgp, Hq, Hkv, n, \
+                    topk, tau, tau2, BH, h_off, hchunks, nch, chunk0, st
   switch (gc) {
     case 1: dq_launch<D, 1>(SAS_DQ_ARGS); break;
     case 2: dq_launch<D, 2>(SAS_DQ_ARGS); break;
-    case 3: dq_launch<D, 3>(SAS_DQ_ARGS); break;
     default: dq_launch<D, 4>(SAS_DQ_ARGS); break;
   }
 #undef SAS_DQ_ARGS
 }
 
+static int n_head_chunks(int G) {
+  int nch = 0;
+  for (const HeadChunks& hc : head_chunks(G)) nch += hc.count;
+  return nch;
+}
+
 size_t bwd_mfma_extra_ws(int B, int Hq, int Hkv, int n, int topk) {
-  const int G = Hq / Hkv;
-  const int nch = (G + 3) / 4;
+  const int nch = n_head_chunks(Hq / Hkv);
   return sizeof(float) * size_t(B) * Hkv * (n / SAS_BLK) * nch * size_t(topk > 0 ? topk : 1);
 }
 
@@ -461,25 +442,22 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
                            const void* dO, const float* lse, const int32_t* idx,
                            const int32_t* cnt, const float* lg, const float* s,
                            const float* s_lse, void* dq, void* dk, void* dv, float* ds,
-                           float* Dws, const int32_t* rev_off, const int32_t* rev_list,
+                           float* stats, const int32_t* rev_off, const int32_t* rev_list,
                            float* dlgp, int B, int Hq, int Hkv, int n, int d, int topk, float tau,
                            hipStream_t st) {
   const int G = Hq / Hkv;
   const int nqb = n / SAS_BLK;
   const int BH = B * Hkv;
   const float tau2 = tau * kLog2e;
-  const int full = G / 4, rem = G % 4;
-  const int nch = full + (rem > 0 ? 1 : 0);
+  const int nch = n_head_chunks(G);
   const int K = topk > 0 ? topk : 1;
   {
     ProfScope ps("sas_bwd_dq_kernel", st);
-    if (full > 0) {
-      if (d == 128) dq_dispatch<128>(4, BH * nqb * full, q, k, v, o, dO, lse, idx, cnt, lg, dq, Dws, dlgp, Hq, Hkv, n, K, tau, tau2, BH, 0, full, nch, st);
-      else dq_dispatch<64>(4, BH * nqb * full, q, k, v, o, dO, lse, idx, cnt, lg, dq, Dws, dlgp, Hq, Hkv, n, K, tau, tau2, BH, 0, full, nch, st);
-    }
-    if (rem > 0) {
-      if (d == 128) dq_dispatch<128>(rem, BH * nqb, q, k, v, o, dO, lse, idx, cnt, lg, dq, Dws, dlgp, Hq, Hkv, n, K, tau, tau2, BH, 4 * full, 1, nch, st);
-      else dq_dispatch<64>(rem, BH * nqb, q, k, v, o, dO, lse, idx, cnt, lg, dq, Dws, dlgp, Hq, Hkv, n, K, tau, tau2, BH, 4 * full, 1, nch, st);
+    int chunk0 = 0;
+    for (const HeadChunks& hc : head_chunks(G)) {
+      if (d == 128) dq_dispatch<128>(hc.gc, BH * nqb * hc.count, q, k, v, o, dO, lse, idx, cnt, lg, dq, stats, dlgp, Hq, Hkv, n, K, tau, tau2, BH, hc.h_off, hc.count, nch, chunk0, st);
+      else dq_dispatch<64>(hc.gc, BH * nqb * hc.count, q, k, v, o, dO, lse, idx, cnt, lg, dq, stats, dlgp, Hq, Hkv, n, K, tau, tau2, BH, hc.h_off, hc.count, nch, chunk0, st);
+      chunk0 += hc.count;
     }
   }
   hipError_t e = hipGetLastError();
@@ -493,19 +471,19 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
   if (e != hipSuccess) return e;
   {
     ProfScope ps("sas_bwd_dkdv_kernel", st);
-    const size_t shm = size_t(2) * (2 * 64 * d * 2 + 512);
+    const size_t shm = size_t(kKvStages) * (2 * 64 * d * 2 + 512);
     if (d == 128) {
       auto kern = bwd_dkdv_kernel<128>;
       allow_lds(kern, shm);
       hipLaunchKernelGGL(kern, dim3(BH * nqb), dim3(256), shm, st, (const uint16_t*)q,
-                         (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO, lse, Dws, lg,
+                         (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO, stats, lg,
                          rev_off, rev_list, (uint16_t*)dk, (uint16_t*)dv, Hq, Hkv, n, topk, tau,
                          tau2);
     } else {
       auto kern = bwd_dkdv_kernel<64>;
       allow_lds(kern, shm);
       hipLaunchKernelGGL(kern, dim3(BH * nqb), dim3(256), shm, st, (const uint16_t*)q,
-                         (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO, lse, Dws, lg,
+                         (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO, stats, lg,
                          rev_off, rev_list, (uint16_t*)dk, (uint16_t*)dv, Hq, Hkv, n, topk, tau,
                          tau2);
     }

@@ -20,6 +20,8 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
 
 SAS_DEV f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -45,13 +47,48 @@ SAS_DEV int tile_off(int row, int ch) {
   return row * (D * 2) + ((ch ^ swz<D>(row)) << 4);
 }
 
-SAS_DEV bf16x8 lds_read16(const char* base, int off) {
-  return *reinterpret_cast<const bf16x8*>(base + off);
+// LDS tiles are addressed through address_space(3) pointers so that no
+// generic-to-local conversion is emitted per access.
+typedef const __attribute__((address_space(3))) char lds_cchar;
+
+SAS_DEV lds_char* lds_ptr(char* generic_smem) { return (lds_char*)generic_smem; }
+
+// Integer LDS byte addresses: the backend folds "address + constant" into the
+// 16-bit offset field of the DS instruction, so a per-lane base plus
+// compile-time tile/chunk offsets costs no VALU per read.
+// LDS byte addresses are below 2^18; the mask lets the compiler prove the sign
+// bit is clear, which DS offset folding requires.
+constexpr uint32_t kLdsAddrMask = (1u << 18) - 1;
+SAS_DEV uint32_t lds_addr(lds_cchar* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>(p)) & kLdsAddrMask;
+}
+SAS_DEV bf16x8 lds_read16_at(uint32_t a) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(uintptr_t(a));
+}
+SAS_DEV bf16x4 lds_read_tr_at(uint32_t a) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      reinterpret_cast<__attribute__((address_space(3))) bf16x4*>(uintptr_t(a)));
+}
+// Hide a value from the optimiser (so "base + lane offset" stays one register
+// and only the small per-access constant goes to the DS offset field).
+SAS_DEV uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
 }
 
-SAS_DEV bf16x4 lds_read_tr(const char* base, int off) {
+SAS_DEV bf16x8 tr_pair_at(uint32_t a0, uint32_t a1) {
+  const bf16x4 a = lds_read_tr_at(a0);
+  const bf16x4 b = lds_read_tr_at(a1);
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+SAS_DEV bf16x8 lds_read16(lds_cchar* base, int off) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(base + off);
+}
+
+SAS_DEV bf16x4 lds_read_tr(lds_cchar* base, int off) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-      (__attribute__((address_space(3))) bf16x4*)((lds_char*)base + off));
+      (__attribute__((address_space(3))) bf16x4*)(base + off));
 }
 
 // Transposed operand of a row-major [64 keys][D] tile: 8 keys x one column per
@@ -60,7 +97,7 @@ SAS_DEV bf16x4 lds_read_tr(const char* base, int off) {
 // tile.  Lane l gets keys kbase + 4*(l/32) + {0..3} and kbase + 8 + 4*(l/32) +
 // {0..3} of column col0 + l%32.
 template <int D>
-SAS_DEV bf16x8 tr_operand(const char* tile, int kbase, int col0, int lane) {
+SAS_DEV bf16x8 tr_operand(lds_cchar* tile, int kbase, int col0, int lane) {
   const int i = lane & 15, hh = lane >> 5, dh = (lane >> 4) & 1;
   const int col = col0 + dh * 16 + (i & 3) * 4;
   const int r0 = kbase + 4 * hh + (i >> 2);
@@ -69,6 +106,129 @@ SAS_DEV bf16x8 tr_operand(const char* tile, int kbase, int col0, int lane) {
   const bf16x4 a = lds_read_tr(tile, tile_off<D>(r0, col >> 3) + sub);
   const bf16x4 b = lds_read_tr(tile, tile_off<D>(r1, col >> 3) + sub);
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// ---------------------------------------------------------------- LDS DMA ring
+// GLOBAL_LOAD_LDS_DWORDX4 (checked on the device): lane l's 16 bytes land at
+// LDS address base + 16*l (base is wave-uniform); inactive lanes write nothing.
+// The loads count in vmcnt like any vector load but need no registers, so a
+// workgroup can keep several tiles in flight.
+SAS_DEV void dma16(const void* g, lds_char* l) {
+  __builtin_amdgcn_global_load_lds((glb_void*)g, (lds_void*)l, 16, 0, 0);
+}
+
+// Slice jj (1 KB) of a 64 x D bf16 tile whose rows are contiguous in global
+// memory (row stride D elements), written to LDS in the swizzled layout: each
+// lane fetches the logical chunk that belongs at its physical slot.
+template <int D>
+SAS_DEV void dma_tile_slice(const uint16_t* gtile, lds_char* ltile, int jj, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int RPI = 64 / CPR;  // rows per 1 KB slice
+  const int r = jj * RPI + lane / CPR;
+  const int c = (lane % CPR) ^ swz<D>(r);
+  dma16(gtile + r * D + c * 8, ltile + jj * 1024);
+}
+
+// Wait until at most N of this wave's vector memory operations are
+// outstanding and all its LDS operations are done, then barrier.  Raw
+// s_barrier: __syncthreads() adds a release fence that waits for every
+// outstanding load (vmcnt(0)) and would drain the DMA ring.  The empty asm
+// statements keep the compiler from moving memory operations across.
+template <int N>
+SAS_DEV void vm_wait_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+constexpr int kFwdStages = 3;   // K/V tile ring depth of the forward
+constexpr int kDqStages = 2;    // K/V tile ring depth of the dq pass (register-bound)
+constexpr int kKvStages = 4;    // Q/dO tile ring depth of the key-block-outer kernel
+
+// Host: a query-head group of G heads is covered by launches of 4-, 2- and
+// 1-head workgroups (so the DMA slices split evenly over the waves).
+struct HeadChunks {
+  int gc, h_off, count;  // heads per workgroup, first head, chunks in launch
+};
+inline int head_chunk_list(int G, HeadChunks* out) {
+  int nlist = 0, h = 0;
+  for (int gc = 4; gc >= 1; gc >>= 1) {
+    const int c = (G - h) / gc;
+    if (c > 0) {
+      out[nlist++] = HeadChunks{gc, h, c};
+      h += c * gc;
+    }
+  }
+  return nlist;
+}
+struct HeadChunkSet {
+  HeadChunks v[3];
+  int nv;
+  const HeadChunks* begin() const { return v; }
+  const HeadChunks* end() const { return v + nv; }
+};
+inline HeadChunkSet head_chunks(int G) {
+  HeadChunkSet s{};
+  s.nv = head_chunk_list(G, s.v);
+  return s;
+}
+
+template <class K>
+inline void allow_lds(K kernel, size_t bytes) {
+  if (bytes > 65536)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
+}
+
+// Transposed operand read with precomputed per-lane offsets (see tr_offsets).
+SAS_DEV bf16x8 tr_operand_at(lds_cchar* tile, int off0, int off1) {
+  const bf16x4 a = lds_read_tr(tile, off0);
+  const bf16x4 b = lds_read_tr(tile, off1);
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Per-lane byte offsets of the two DS_READ_B64_TR_B16 reads of tr_operand for a
+// 16-row chunk starting at row 0 and the 32-column tile dt.  For a chunk that
+// starts at row kbase (a multiple of 16) the offsets are kbase*2*D larger: the
+// swizzle depends on row % 16 only.
+template <int D>
+SAS_DEV void tr_offsets(int lane, int (&off)[D / 32][2]) {
+  const int i = lane & 15, hh = lane >> 5, dh = (lane >> 4) & 1;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const int r = 4 * hh + (i >> 2) + 8 * w;
+      const int col = dt * 32 + dh * 16 + (i & 3) * 4;
+      off[dt][w] = (tile_off<D>(r, col >> 3) + ((i & 1) << 3)) & int(kLdsAddrMask);
+    }
+}
+
+// Per-lane byte offsets of the 16-byte row reads of rows r0 + (lane % 32),
+// chunks 2c + lane/32 (c < D/16), for r0 a multiple of 16.
+template <int D>
+SAS_DEV void row_offsets(int lane, int (&off)[D / 16]) {
+  const int lr = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) off[c] = tile_off<D>(lr, 2 * c + hh) & int(kLdsAddrMask);
+}
+
+// 2^x on the transcendental unit without the denormal range fix-up of exp2f
+// (softmax weights below 2^-126 flush to zero, which is harmless).
+SAS_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// Sum of the 8 bf16 values (accumulated in float32) added to acc.
+SAS_DEV float sum_bf16x8(const bf16x8& v, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
+  return acc;
 }
 
 SAS_DEV bf16x8 pack_bf16x8(const float* x) {

@@ -15,6 +15,9 @@
 // K/V tiles are double-buffered in LDS; the next tile's global loads are in
 // flight while the current one is computed.  Softmax runs in the exp2 domain.
 // Workgroups are issued largest q-block first (most tiles first).
+#include <type_traits>
+#include <utility>
+
 #include "launch.h"
 #include "mfma_common.h"
 
@@ -27,14 +30,13 @@ __global__ void __launch_bounds__(128 * GC) fwd_mfma_kernel(
     const int32_t* __restrict__ cnt, const float* __restrict__ lg, uint16_t* __restrict__ o,
     float* __restrict__ lse, int Hq, int Hkv, int n, int topk, float tau2, int BH, int h_off,
     int hchunks) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  constexpr int ROWB = D * 2;
-  constexpr int TB = 64 * ROWB;          // bytes of one 64 x D tile
-  constexpr int CPR = D / 8;             // 16-byte chunks per row
-  constexpr int HALF = 64 * CPR;         // chunks per tile
-  constexpr int TOTAL = 2 * HALF;        // K + V chunks per stage
-  constexpr int NT = 128 * GC;
-  constexpr int CPT = (TOTAL + NT - 1) / NT;
+  extern __shared__ __attribute__((aligned(16))) char smem_generic[];
+  lds_char* const smem = lds_ptr(smem_generic);
+  constexpr int NS = kFwdStages;
+  constexpr int TB = 64 * D * 2;          // bytes of one 64 x D tile
+  constexpr int JT = TB / 1024;           // 1 KB DMA slices per tile
+  constexpr int JW = 2 * JT / (2 * GC);   // slices per wave per stage (K and V)
+  static_assert((2 * JT) % (2 * GC) == 0, "slices must split evenly over the waves");
 
   const int nqb = n / SAS_BLK;
   const int G = Hq / Hkv;
@@ -62,39 +64,40 @@ __global__ void __launch_bounds__(128 * GC) fwd_mfma_kernel(
     qop[c] = *reinterpret_cast<const bf16x8*>(q + qrow * D + c * 16 + hh * 8);
 
   const size_t kv0 = (size_t(b) * Hkv + kv) * size_t(n);
-  uint4 stg[CPT];
-  auto load_tile = [&](int t) {
+  auto issue = [&](int t, int buf) __attribute__((always_inline)) {
     const int blk = t < c_sel ? irow[t] : i;
     const uint16_t* kb = k + (kv0 + size_t(blk) * SAS_BLK) * D;
     const uint16_t* vb = v + (kv0 + size_t(blk) * SAS_BLK) * D;
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int c = tid + NT * u;
-      if (c < TOTAL) {
-        const uint16_t* src = c < HALF ? kb + c * 8 : vb + (c - HALF) * 8;
-        stg[u] = *reinterpret_cast<const uint4*>(src);
-      }
+    for (int u = 0; u < JW; ++u) {
+      const int j = wave * JW + u;
+      const int T = j / JT;
+      dma_tile_slice<D>(T ? vb : kb, smem + (T * NS + buf) * TB, j % JT, lane);
     }
   };
-  auto store_tile = [&](int stage) {
-    char* base = smem + stage * 2 * TB;
+
+  for (int t = 0; t < NS - 1 && t < ntiles; ++t) issue(t, t);
+
+  // per-lane LDS addresses of stage 0; other stages / halves / chunks add
+  // compile-time offsets below 64 KB that fold into the DS instructions
+  uint32_t ka[D / 16], va[D / 32][2];
+  {
+    int koff[D / 16], voff[D / 32][2];
+    row_offsets<D>(lane, koff);
+    tr_offsets<D>(lane, voff);
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int c = tid + NT * u;
-      if (c < TOTAL) {
-        const bool isv = c >= HALF;
-        const int cc = isv ? c - HALF : c;
-        const int row = cc / CPR, col = cc % CPR;
-        const int off = tile_off<D>(row, col);
-        *reinterpret_cast<uint4*>(base + (isv ? TB : 0) + off) = stg[u];
-      }
-    }
-  };
+    for (int c = 0; c < D / 16; ++c) ka[c] = opaque(lds_addr(smem) + uint32_t(koff[c]));
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int w = 0; w < 2; ++w) va[dt][w] = opaque(lds_addr(smem) + NS * TB + uint32_t(voff[dt][w]));
+  }
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
+  // Running row max in the exp2 domain.  It is raised only when a tile's max
+  // exceeds it by more than kRescaleSlack (wave-uniform decision), so most
+  // tiles skip the O rescale; weights stay below 2^kRescaleSlack, and the
+  // final O / l is exact whatever max was used.
+  constexpr float kRescaleSlack = 8.0f;
   float mrow = -INFINITY, lrow = 0.f;
   f32x16 O[D / 32];
 #pragma unroll
@@ -102,13 +105,10 @@ __global__ void __launch_bounds__(128 * GC) fwd_mfma_kernel(
 #pragma unroll
     for (int j = 0; j < 16; ++j) O[dt][j] = 0.f;
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int stage = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
-    const char* Kt = smem + stage * 2 * TB;
-    const char* Vt = Kt + TB;
-    const bool cur = t == c_sel;
-    const float bias2 = cur ? 0.f : grow[t] * kLog2e;
+  // One tile from ring stage ST (compile-time, so every LDS address is a
+  // per-lane register plus an immediate offset).  CUR: the causal current block.
+  auto tile = [&]<int ST, bool CUR>(int t) __attribute__((always_inline)) {
+    const float bias2 = CUR ? 0.f : grow[t] * kLog2e;
 
     f32x16 S[2];
 #pragma unroll
@@ -117,31 +117,33 @@ __global__ void __launch_bounds__(128 * GC) fwd_mfma_kernel(
       for (int j = 0; j < 16; ++j) S[kt][j] = 0.f;
 #pragma unroll
       for (int c = 0; c < D / 16; ++c)
-        S[kt] = mfma32(lds_read16(Kt, tile_off<D>(kt * 32 + lr, 2 * c + hh)), qop[c], S[kt]);
+        S[kt] = mfma32(lds_read16_at(ka[c] + ST * TB + kt * 32 * D * 2), qop[c], S[kt]);
+    }
+    if (CUR) {  // causal mask of the current block: key j visible iff j <= row
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (kt * 32 + 8 * (j >> 2) + 4 * hh + (j & 3) > rt * 32 + lr) S[kt][j] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        float z = S[kt][j] * tau2 + bias2;
-        if (cur) {
-          const int key = kt * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
-          if (key > rt * 32 + lr) z = -INFINITY;
-        }
-        S[kt][j] = z;
-        mx = fmaxf(mx, z);
-      }
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, S[kt][j]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(mrow, mx);
-    const float alpha = exp2f(mrow - mnew);
-    mrow = mnew;
-    lrow *= alpha;
+    const float mt = mx * tau2 + bias2;   // tau2 > 0: max commutes with the affine map
+    if (__any(mt > mrow + kRescaleSlack)) {
+      const float mnew = fmaxf(mrow, mt);
+      const float alpha = fast_exp2(mrow - mnew);
+      mrow = mnew;
+      lrow *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+      for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) O[dt][j] *= alpha;
-
+        for (int j = 0; j < 16; ++j) O[dt][j] *= alpha;
+    }
+    const float c0 = bias2 - mrow;
     bf16x8 P[4];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -149,21 +151,40 @@ __global__ void __launch_bounds__(128 * GC) fwd_mfma_kernel(
       for (int jc = 0; jc < 2; ++jc) {
         float p[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = exp2f(S[kt][8 * jc + e] - mnew);
-          lrow += p[e];
-        }
+        for (int e = 0; e < 8; ++e) p[e] = fast_exp2(__builtin_fmaf(S[kt][8 * jc + e], tau2, c0));
         P[kt * 2 + jc] = pack_bf16x8(p);
+        lrow = sum_bf16x8(P[kt * 2 + jc], lrow);   // normalise by the weights actually used
       }
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int ch = 0; ch < 4; ++ch)
-        O[dt] = mfma32(tr_operand<D>(Vt, ch * 16, dt * 32, lane), P[ch], O[dt]);
+        O[dt] = mfma32(tr_pair_at(va[dt][0] + ST * TB + ch * 16 * D * 2,
+                                  va[dt][1] + ST * TB + ch * 16 * D * 2),
+                       P[ch], O[dt]);
+  };
+  // Tile t of the kept blocks: its DMA landed (and the buffer it replaces is
+  // free) after the wait + barrier; then the tile NS-1 ahead is put in flight.
+  auto kept = [&]<int ST>(int t) __attribute__((always_inline)) {
+    vm_wait_barrier<JW * (NS - 2)>();
+    if (t + NS - 1 < ntiles) issue(t + NS - 1, (ST + NS - 1) % NS);
+    tile.template operator()<ST, false>(t);
+  };
+  auto ring = [&]<int... S>(int t0, std::integer_sequence<int, S...>) __attribute__((always_inline)) {
+    (kept.template operator()<S>(t0 + S), ...);
+  };
 
-    if (t + 1 < ntiles) store_tile(stage ^ 1);
-    __syncthreads();
-  }
+  int t = 0;
+#pragma nounroll
+  for (; t + NS <= c_sel; t += NS) ring(t, std::make_integer_sequence<int, NS>{});
+  // t % NS == 0 here; finish the kept tiles, then the current block
+  [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
+    ((t + S < c_sel ? kept.template operator()<S>(t + S) : void()), ...);
+  }(std::make_integer_sequence<int, NS - 1>{});
+  vm_wait_barrier<0>();
+  [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
+    ((c_sel % NS == S ? tile.template operator()<S, true>(c_sel) : void()), ...);
+  }(std::make_integer_sequence<int, NS>{});
 
   lrow += __shfl_xor(lrow, 32);
   const float inv = 1.f / lrow;
@@ -187,8 +208,10 @@ static void fwd_launch(int nblocks, const void* q, const void* k, const void* v,
                        const int32_t* idx, const int32_t* cnt, const float* lg, void* o, float* lse,
                        int Hq, int Hkv, int n, int topk, float tau2, int BH, int h_off,
                        int hchunks, hipStream_t st) {
-  const size_t shm = size_t(4) * 64 * D * 2;
-  hipLaunchKernelGGL((fwd_mfma_kernel<D, GC>), dim3(nblocks), dim3(128 * GC), shm, st,
+  const size_t shm = size_t(kFwdStages) * 2 * 64 * D * 2;
+  auto kern = fwd_mfma_kernel<D, GC>;
+  allow_lds(kern, shm);
+  hipLaunchKernelGGL(kern, dim3(nblocks), dim3(128 * GC), shm, st,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, cnt, lg,
                      (uint16_t*)o, lse, Hq, Hkv, n, topk, tau2, BH, h_off, hchunks);
 }
@@ -201,7 +224,6 @@ static void fwd_dispatch(int gc, int nblocks, const void* q, const void* k, cons
   switch (gc) {
     case 1: fwd_launch<D, 1>(nblocks, q, k, v, idx, cnt, lg, o, lse, Hq, Hkv, n, topk, tau2, BH, h_off, hchunks, st); break;
     case 2: fwd_launch<D, 2>(nblocks, q, k, v, idx, cnt, lg, o, lse, Hq, Hkv, n, topk, tau2, BH, h_off, hchunks, st); break;
-    case 3: fwd_launch<D, 3>(nblocks, q, k, v, idx, cnt, lg, o, lse, Hq, Hkv, n, topk, tau2, BH, h_off, hchunks, st); break;
     default: fwd_launch<D, 4>(nblocks, q, k, v, idx, cnt, lg, o, lse, Hq, Hkv, n, topk, tau2, BH, h_off, hchunks, st); break;
   }
 }
@@ -214,15 +236,10 @@ hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, const in
   const int nqb = n / SAS_BLK;
   const int BH = B * Hkv;
   const float tau2 = tau * kLog2e;
-  const int full = G / 4, rem = G % 4;
-  // heads [0, 4*full) in chunks of 4, then the remaining rem heads
-  if (full > 0) {
-    if (d == 128) fwd_dispatch<128>(4, BH * nqb * full, q, k, v, idx, cnt, lg, o, lse, Hq, Hkv, n, topk, tau2, BH, 0, full, st);
-    else fwd_dispatch<64>(4, BH * nqb * full, q, k, v, idx, cnt, lg, o, lse, Hq, Hkv, n, topk, tau2, BH, 0, full, st);
-  }
-  if (rem > 0) {
-    if (d == 128) fwd_dispatch<128>(rem, BH * nqb, q, k, v, idx, cnt, lg, o, lse, Hq, Hkv, n, topk, tau2, BH, 4 * full, 1, st);
-    else fwd_dispatch<64>(rem, BH * nqb, q, k, v, idx, cnt, lg, o, lse, Hq, Hkv, n, topk, tau2, BH, 4 * full, 1, st);
+  // heads in chunks of 4, then 2, then 1 (each launch covers hchunks chunks)
+  for (const HeadChunks& hc : head_chunks(G)) {
+    if (d == 128) fwd_dispatch<128>(hc.gc, BH * nqb * hc.count, q, k, v, idx, cnt, lg, o, lse, Hq, Hkv, n, topk, tau2, BH, hc.h_off, hc.count, st);
+    else fwd_dispatch<64>(hc.gc, BH * nqb * hc.count, q, k, v, idx, cnt, lg, o, lse, Hq, Hkv, n, topk, tau2, BH, hc.h_off, hc.count, st);
   }
   return hipGetLastError();
 }

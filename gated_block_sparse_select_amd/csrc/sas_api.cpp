@@ -85,7 +85,8 @@ BwdWs bwd_layout(const sas_shape* s) {
   const size_t BH = size_t(s->B) * s->Hkv;
   BwdWs w{};
   w.D_off = 0;
-  w.off_off = align_up(w.D_off + sizeof(float) * size_t(s->B) * s->Hq * s->n);
+  // row statistics: SIMT path D [B,Hq,n]; MFMA path [lse*log2e | D] per 64 rows
+  w.off_off = align_up(w.D_off + 2 * sizeof(float) * size_t(s->B) * s->Hq * s->n);
   w.list_off = align_up(w.off_off + sizeof(int32_t) * BH * (nb + 1));
   w.dlg_off = align_up(w.list_off + sizeof(int32_t) * BH * nb * (size_t(s->topk) + 1));
   w.total = align_up(w.dlg_off + sas::bwd_mfma_extra_ws(s->B, s->Hq, s->Hkv, s->n, s->topk));
