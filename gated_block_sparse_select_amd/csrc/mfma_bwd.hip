@@ -23,6 +23,9 @@
 //    registers - no atomics, so the result is deterministic.
 // The split recomputes S and dP in both passes (7 tile products instead of 5)
 // in exchange for no atomics and no per-pair partial buffers.
+#include <type_traits>
+#include <utility>
+
 #include "launch.h"
 #include "mfma_common.h"
 
@@ -91,19 +94,32 @@ __global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
   }
 
   const size_t kv0 = (size_t(b) * Hkv + kv) * size_t(n);
-  auto issue = [&](int t, int buf) {
+  // LDS: K tiles of the NS stages, then the V tiles
+  auto issue = [&](int t, int buf) __attribute__((always_inline)) {
     const int blk = t < c_sel ? irow[t] : i;
     const uint16_t* kb = k + (kv0 + size_t(blk) * SAS_BLK) * D;
     const uint16_t* vb = v + (kv0 + size_t(blk) * SAS_BLK) * D;
-    lds_char* base = smem + buf * 2 * TB;
 #pragma unroll
     for (int u = 0; u < JW; ++u) {
       const int j = wave * JW + u;
       const int T = j / JT;
-      dma_tile_slice<D>(T ? vb : kb, base + T * TB, j % JT, lane);
+      dma_tile_slice<D>(T ? vb : kb, smem + (T * NS + buf) * TB, j % JT, lane);
     }
   };
   for (int t = 0; t < NS - 1 && t < ntiles; ++t) issue(t, t);
+
+  uint32_t ka[D / 16], ta[D / 32][2];
+  {
+    int koff[D / 16], toff[D / 32][2];
+    row_offsets<D>(lane, koff);
+    tr_offsets<D>(lane, toff);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) ka[c] = opaque(lds_addr(smem) + uint32_t(koff[c]));
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int w = 0; w < 2; ++w) ta[dt][w] = opaque(lds_addr(smem) + uint32_t(toff[dt][w]));
+  }
 
   f32x16 dQ[D / 32];
 #pragma unroll
@@ -111,27 +127,14 @@ __global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
 #pragma unroll
     for (int j = 0; j < 16; ++j) dQ[dt][j] = 0.f;
 
-#pragma nounroll
-  for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) vm_wait_barrier<JW * (NS - 2)>();
-    else vm_wait_barrier<0>();
-    // the barrier also published every wave's dZ sum of tile t-1
-    if (t > 0 && tid == 0) {
-      float a = 0.f;
-      for (int w = 0; w < 2 * GC; ++w) a += part[((t - 1) & 1) * 8 + w];
-      dlgp[(rowsel * nch + chunk) * topk + t - 1] = a;
-    }
-    if (t + NS - 1 < ntiles) issue(t + NS - 1, (t + NS - 1) % NS);
-    lds_cchar* Kt = smem + (t % NS) * 2 * TB;
-    lds_cchar* Vt = Kt + TB;
-    const bool cur = t == c_sel;
-    const float zoff = (cur ? 0.f : grow[t] * kLog2e) - lse2;
-
-    // one 32-key half at a time keeps only 2 accumulator tiles live
+  // one tile from ring stage ST (compile-time: LDS offsets fold into the DS
+  // instructions); CUR = the causal current block
+  auto tile = [&]<int ST, bool CUR>(int t) __attribute__((always_inline)) {
+    const float zoff = (CUR ? 0.f : grow[t] * kLog2e) - lse2;
     float zs = 0.f;
     bf16x8 dZp[4];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < 2; ++kt) {   // one 32-key half at a time
       f32x16 S, P2;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
@@ -140,9 +143,8 @@ __global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
       }
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
-        const int off = tile_off<D>(kt * 32 + lr, 2 * c + hh);
-        S = mfma32(lds_read16(Kt, off), qop[c], S);
-        P2 = mfma32(lds_read16(Vt, off), dop[c], P2);
+        S = mfma32(lds_read16_at(ka[c] + ST * TB + kt * 32 * D * 2), qop[c], S);
+        P2 = mfma32(lds_read16_at(ka[c] + (NS + ST) * TB + kt * 32 * D * 2), dop[c], P2);
       }
 #pragma unroll
       for (int jc = 0; jc < 2; ++jc) {
@@ -150,11 +152,8 @@ __global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int j = 8 * jc + e;
-          float p = exp2f(S[j] * tau2 + zoff);
-          if (cur) {
-            const int key = kt * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
-            if (key > rt * 32 + lr) p = 0.f;
-          }
+          float p = fast_exp2(__builtin_fmaf(S[j], tau2, zoff));
+          if (CUR && kt * 32 + 8 * (j >> 2) + 4 * hh + (j & 3) > rt * 32 + lr) p = 0.f;
           x[e] = p * (P2[j] - Drow);
           zs += x[e];
         }
@@ -165,13 +164,44 @@ __global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int ch = 0; ch < 4; ++ch)
-        dQ[dt] = mfma32(tr_operand<D>(Kt, ch * 16, dt * 32, lane), dZp[ch], dQ[dt]);
-
-    if (!cur) {
+        dQ[dt] = mfma32(tr_pair_at(ta[dt][0] + ST * TB + ch * 16 * D * 2,
+                                   ta[dt][1] + ST * TB + ch * 16 * D * 2),
+                        dZp[ch], dQ[dt]);
+    if (!CUR) {
       zs = wave_sum(zs);
       if (lane == 0) part[(t & 1) * 8 + wave] = zs;
     }
+  };
+  // kept tile t: wait for it (and for the buffer it replaces to be free),
+  // publish the block gate gradient of tile t-1, refill, compute
+  auto kept = [&]<int ST>(int t) __attribute__((always_inline)) {
+    vm_wait_barrier<JW * (NS - 2)>();
+    if (t > 0 && tid == 0) {
+      float a = 0.f;
+      for (int w = 0; w < 2 * GC; ++w) a += part[((t - 1) & 1) * 8 + w];
+      dlgp[(rowsel * nch + chunk) * topk + t - 1] = a;
+    }
+    if (t + NS - 1 < ntiles) issue(t + NS - 1, (ST + NS - 1) % NS);
+    tile.template operator()<ST, false>(t);
+  };
+  int t = 0;
+#pragma nounroll
+  for (; t + NS <= c_sel; t += NS)
+    [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
+      (kept.template operator()<S>(t + S), ...);
+    }(std::make_integer_sequence<int, NS>{});
+  [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
+    ((t + S < c_sel ? kept.template operator()<S>(t + S) : void()), ...);
+  }(std::make_integer_sequence<int, NS - 1>{});
+  vm_wait_barrier<0>();
+  if (c_sel > 0 && tid == 0) {
+    float a = 0.f;
+    for (int w = 0; w < 2 * GC; ++w) a += part[((c_sel - 1) & 1) * 8 + w];
+    dlgp[(rowsel * nch + chunk) * topk + c_sel - 1] = a;
   }
+  [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
+    ((c_sel % NS == S ? tile.template operator()<S, true>(c_sel) : void()), ...);
+  }(std::make_integer_sequence<int, NS>{});
 
   uint16_t* drow = dq + qrow * D;
 #pragma unroll
@@ -230,7 +260,9 @@ __global__ void __launch_bounds__(256) bwd_ds_kernel(const float* __restrict__ d
 // grid: B*Hkv*nkb workgroups of 4 waves; wave = (key half kh, row half rh).
 // The (q-block, head) steps of the reverse list stream through a ring of
 // kKvStages LDS buffers, each holding the Q and dO tiles of one (q-block, head)
-// and its row statistics.
+// and its row statistics; the block's own V tile sits in LDS after the ring
+// (its K rows stay in registers as the S = Q K^T operand).
+// LDS: ring stage s at s*STAGE = [Q tile | dO tile | lse*log2e[64] | D[64]].
 template <int D>
 __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -242,12 +274,14 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
   extern __shared__ __attribute__((aligned(16))) char smem_generic[];
   lds_char* const smem = lds_ptr(smem_generic);
   constexpr int NS = kKvStages;
-  constexpr int TB = 64 * D * 2;
+  constexpr int ROWB = D * 2;
+  constexpr int TB = 64 * ROWB;
   constexpr int CPR = D / 8;
   constexpr int JT = TB / 1024;
   constexpr int JW = 2 * JT / 4;        // Q + dO slices per wave per step
   constexpr int PER = JW + 1;           // plus one slice of row statistics
   constexpr int STAGE = 2 * TB + 512;
+  constexpr int VT = NS * STAGE;        // the block's own V tile
 
   const int nkb = n / SAS_BLK;
   const int G = Hq / Hkv;
@@ -259,13 +293,16 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
   const int lr = lane & 31, hh = lane >> 5;
   const int kh = wave & 1, rh = wave >> 1;
 
-  const size_t krow = (size_t(b) * Hkv + kv) * n + size_t(m) * SAS_BLK + kh * 32 + lr;
-  bf16x8 kop[D / 16], vop[D / 16];
+  const size_t kvrow0 = (size_t(b) * Hkv + kv) * n + size_t(m) * SAS_BLK;
+  const size_t krow = kvrow0 + kh * 32 + lr;
+  bf16x8 kop[D / 16];
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
+  for (int c = 0; c < D / 16; ++c)
     kop[c] = *reinterpret_cast<const bf16x8*>(k + krow * D + c * 16 + hh * 8);
-    vop[c] = *reinterpret_cast<const bf16x8*>(v + krow * D + c * 16 + hh * 8);
-  }
+  // own V tile -> LDS (swizzled), read back as the dP = dO V^T operand
+#pragma unroll
+  for (int u = 0; u < JT / 4; ++u) dma_tile_slice<D>(v + kvrow0 * D, smem + VT, wave * (JT / 4) + u, lane);
+
   f32x16 dK[D / 32], dV[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
@@ -280,7 +317,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
   const int32_t e1 = rev_off[size_t(bk) * (nkb + 1) + m + 1];
   const int nsteps = (e1 - e0) * G;
 
-  auto issue = [&](int s, int buf) {
+  auto issue = [&](int s, int buf) __attribute__((always_inline)) {
     const int32_t ent = lst[e0 + s / G];
     const int iq = ent & 0xFFFF;
     const int hq = kv * G + s % G;
@@ -298,63 +335,99 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
   };
   for (int t = 0; t < NS - 1 && t < nsteps; ++t) issue(t, t);
 
+  // per-lane LDS addresses (stage 0); every other offset is an immediate
+  uint32_t qa[D / 16], ta[D / 32][2], va[D / 16];
+  {
+    int roff[D / 16], toff[D / 32][2];
+    row_offsets<D>(lane, roff);
+    tr_offsets<D>(lane, toff);
+    const uint32_t base = lds_addr(smem) + uint32_t(rh * 32 * ROWB);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      qa[c] = opaque(base + uint32_t(roff[c]));
+      va[c] = opaque(lds_addr(smem) + VT + uint32_t(kh * 32 * ROWB + roff[c]));
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int w = 0; w < 2; ++w) ta[dt][w] = opaque(base + uint32_t(toff[dt][w]));
+  }
+  // row statistics of rows rh*32 + 8*jg + 4*hh + 0..3 (16 B each group)
+  const uint32_t sa = opaque(lds_addr(smem) + 2 * TB + uint32_t((rh * 32 + 4 * hh) * 4));
   const int keyw = kh * 32 + lr;  // this lane's key inside block m
-#pragma nounroll
-  for (int s = 0; s < nsteps; ++s) {
+
+  auto step = [&](int s, auto own_tag) __attribute__((always_inline)) {
+    constexpr bool OWN = decltype(own_tag)::value;
+    const uint32_t sb = uint32_t((s % NS) * STAGE);
+    const int32_t ent = lst[e0 + s / G];
+    const int iq = ent & 0xFFFF;
+    const int slot = (ent >> 16) & 0xFFFF;
+    const float bias2 = OWN ? 0.f : lg[(size_t(bk) * nkb + iq) * topk + slot] * kLog2e;
+    // own block: rows 0..31 see none of the keys 32..63
+    if (OWN && kh == 1 && rh == 0) return;
+    f32x16 S, P2;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      S[j] = 0.f;
+      P2[j] = 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const uint32_t a = opaque(qa[c] + sb);
+      S = mfma32(lds_read16_at(a), kop[c], S);
+      P2 = mfma32(lds_read16_at(a + TB), lds_read16_at(va[c]), P2);
+    }
+    // S[row][key]: lane l, reg j: row = rh*32 + 8(j/4) + 4hh + j%4, key = keyw
+    const uint32_t sas = opaque(sa + sb);
+    bf16x8 Pp[2], Zp[2];
+#pragma unroll
+    for (int jc = 0; jc < 2; ++jc) {
+      float pv[8], zv[8];
+#pragma unroll
+      for (int g2 = 0; g2 < 2; ++g2) {
+        const int jg = 2 * jc + g2;
+        typedef __attribute__((ext_vector_type(4))) float f32x4;
+        const f32x4 lv = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(uintptr_t(sas + jg * 32));
+        const f32x4 dv4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(uintptr_t(sas + 256 + jg * 32));
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int j = 4 * jg + r4;
+          float p = fast_exp2(__builtin_fmaf(S[j], tau2, bias2 - lv[r4]));
+          if (OWN && keyw > rh * 32 + 8 * jg + 4 * hh + r4) p = 0.f;
+          pv[4 * g2 + r4] = p;
+          zv[4 * g2 + r4] = p * (P2[j] - dv4[r4]);
+        }
+      }
+      Pp[jc] = pack_bf16x8(pv);
+      Zp[jc] = pack_bf16x8(zv);
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const uint32_t a0 = opaque(ta[dt][0] + sb), a1 = opaque(ta[dt][1] + sb);
+#pragma unroll
+      for (int jc = 0; jc < 2; ++jc) {
+        dV[dt] = mfma32(Pp[jc], tr_pair_at(a0 + TB + jc * 16 * ROWB, a1 + TB + jc * 16 * ROWB), dV[dt]);
+        dK[dt] = mfma32(Zp[jc], tr_pair_at(a0 + jc * 16 * ROWB, a1 + jc * 16 * ROWB), dK[dt]);
+      }
+    }
+  };
+  // the own block (always the first list entry) is the first G steps
+  auto waitfor = [&](int s) __attribute__((always_inline)) {
     const int after = min(NS - 2, nsteps - 1 - s);
     if (after >= 2) vm_wait_barrier<PER * 2>();
     else if (after == 1) vm_wait_barrier<PER>();
     else vm_wait_barrier<0>();
     if (s + NS - 1 < nsteps) issue(s + NS - 1, (s + NS - 1) % NS);
-    lds_cchar* Qt = smem + (s % NS) * STAGE;
-    lds_cchar* Ot = Qt + TB;
-    const __attribute__((address_space(3))) float* stl =
-        reinterpret_cast<const __attribute__((address_space(3))) float*>(Qt + 2 * TB);
-    const int32_t ent = lst[e0 + s / G];
-    const int iq = ent & 0xFFFF;
-    const int slot = (ent >> 16) & 0xFFFF;
-    const bool own = slot == 0xFFFF;
-    const float bias2 = own ? 0.f : lg[(size_t(bk) * nkb + iq) * topk + slot] * kLog2e;
-    // own block: rows 0..31 see none of the keys 32..63
-    const bool skip = own && kh == 1 && rh == 0;
-    if (!skip) {
-      f32x16 S, P2;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        S[j] = 0.f;
-        P2[j] = 0.f;
-      }
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        const int off = tile_off<D>(rh * 32 + lr, 2 * c + hh);
-        S = mfma32(lds_read16(Qt, off), kop[c], S);
-        P2 = mfma32(lds_read16(Ot, off), vop[c], P2);
-      }
-      // S[row][key]: lane l, reg j: row = rh*32 + 8(j/4) + 4hh + j%4, key = keyw
-      bf16x8 Pp[2], Zp[2];
-#pragma unroll
-      for (int jc = 0; jc < 2; ++jc) {
-        float pv[8], zv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = 8 * jc + e;
-          const int row = rh * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
-          float p = exp2f(S[j] * tau2 + bias2 - stl[row]);
-          if (own && keyw > row) p = 0.f;
-          pv[e] = p;
-          zv[e] = p * (P2[j] - stl[64 + row]);
-        }
-        Pp[jc] = pack_bf16x8(pv);
-        Zp[jc] = pack_bf16x8(zv);
-      }
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int jc = 0; jc < 2; ++jc) {
-          dV[dt] = mfma32(Pp[jc], tr_operand<D>(Ot, rh * 32 + 16 * jc, dt * 32, lane), dV[dt]);
-          dK[dt] = mfma32(Zp[jc], tr_operand<D>(Qt, rh * 32 + 16 * jc, dt * 32, lane), dK[dt]);
-        }
-    }
+  };
+#pragma nounroll
+  for (int s = 0; s < G; ++s) {
+    waitfor(s);
+    step(s, std::true_type{});
+  }
+#pragma nounroll
+  for (int s = G; s < nsteps; ++s) {
+    waitfor(s);
+    step(s, std::false_type{});
   }
   __syncthreads();
 
@@ -362,7 +435,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
   // coalesced bf16 rows: first dV, then dK (scaled by tau).
   __attribute__((address_space(3))) float* red =
       reinterpret_cast<__attribute__((address_space(3))) float*>(smem);
-  const size_t out0 = ((size_t(b) * Hkv + kv) * n + size_t(m) * SAS_BLK) * D;
+  const size_t out0 = kvrow0 * D;
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     const f32x16* acc = pass == 0 ? dV : dK;
@@ -471,7 +544,7 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
   if (e != hipSuccess) return e;
   {
     ProfScope ps("sas_bwd_dkdv_kernel", st);
-    const size_t shm = size_t(kKvStages) * (2 * 64 * d * 2 + 512);
+    const size_t shm = size_t(kKvStages) * (2 * 64 * d * 2 + 512) + 64 * d * 2;
     if (d == 128) {
       auto kern = bwd_dkdv_kernel<128>;
       allow_lds(kern, shm);
