@@ -41,15 +41,14 @@ __global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
     const float* __restrict__ lg, uint16_t* __restrict__ dq, float* __restrict__ stats,
     float* __restrict__ dlgp, int Hq, int Hkv, int n, int topk, float tau, float tau2, int BH,
     int h_off, int hchunks, int nch, int chunk0) {
-  extern __shared__ __attribute__((aligned(16))) char smem_generic[];
-  lds_char* const smem = lds_ptr(smem_generic);
   constexpr int NS = kDqStages;
-  constexpr int TB = 64 * D * 2;
+  constexpr int ROWB = D * 2;
+  constexpr int TB = 64 * ROWB;
   constexpr int JT = TB / 1024;
   constexpr int JW = 2 * JT / (2 * GC);
   static_assert((2 * JT) % (2 * GC) == 0, "slices must split evenly over the waves");
-  __attribute__((address_space(3))) float* part =
-      reinterpret_cast<__attribute__((address_space(3))) float*>(smem + NS * 2 * TB);  // [2][8] per-wave dZ sums
+  constexpr int TK = 200, TV = 201;       // LDS buffer tags: K tiles, V tiles
+  __shared__ float part[2][8];            // per-wave dZ sums of the last two tiles
 
   const int nqb = n / SAS_BLK;
   const int G = Hq / Hkv;
@@ -94,31 +93,33 @@ __global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
   }
 
   const size_t kv0 = (size_t(b) * Hkv + kv) * size_t(n);
-  // LDS: K tiles of the NS stages, then the V tiles
-  auto issue = [&](int t, int buf) __attribute__((always_inline)) {
+  auto issue = [&]<int BUF>(int t) __attribute__((always_inline)) {
     const int blk = t < c_sel ? irow[t] : i;
     const uint16_t* kb = k + (kv0 + size_t(blk) * SAS_BLK) * D;
     const uint16_t* vb = v + (kv0 + size_t(blk) * SAS_BLK) * D;
 #pragma unroll
     for (int u = 0; u < JW; ++u) {
       const int j = wave * JW + u;
-      const int T = j / JT;
-      dma_tile_slice<D>(T ? vb : kb, smem + (T * NS + buf) * TB, j % JT, lane);
+      if (j < JT) dma_tile_slice<D>(kb, stage_buf<TK, BUF, TB>(), j, lane);
+      else dma_tile_slice<D>(vb, stage_buf<TV, BUF, TB>(), j - JT, lane);
     }
   };
-  for (int t = 0; t < NS - 1 && t < ntiles; ++t) issue(t, t);
+  issue.template operator()<0>(0);
+  if constexpr (NS > 2) {
+    if (1 < ntiles) issue.template operator()<1>(1);
+  }
 
-  uint32_t ka[D / 16], ta[D / 32][2];
+  uint32_t ko[D / 16], to[D / 32][2];
   {
     int koff[D / 16], toff[D / 32][2];
     row_offsets<D>(lane, koff);
     tr_offsets<D>(lane, toff);
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) ka[c] = opaque(lds_addr(smem) + uint32_t(koff[c]));
+    for (int c = 0; c < D / 16; ++c) ko[c] = lane_off(koff[c]);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int w = 0; w < 2; ++w) ta[dt][w] = opaque(lds_addr(smem) + uint32_t(toff[dt][w]));
+      for (int w = 0; w < 2; ++w) to[dt][w] = lane_off(toff[dt][w]);
   }
 
   f32x16 dQ[D / 32];
@@ -127,9 +128,10 @@ __global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
 #pragma unroll
     for (int j = 0; j < 16; ++j) dQ[dt][j] = 0.f;
 
-  // one tile from ring stage ST (compile-time: LDS offsets fold into the DS
-  // instructions); CUR = the causal current block
+  // one tile from ring stage ST; CUR = the causal current block
   auto tile = [&]<int ST, bool CUR>(int t) __attribute__((always_inline)) {
+    lds_cchar* Kt = stage_buf<TK, ST, TB>();
+    lds_cchar* Vt = stage_buf<TV, ST, TB>();
     const float zoff = (CUR ? 0.f : grow[t] * kLog2e) - lse2;
     float zs = 0.f;
     bf16x8 dZp[4];
@@ -143,8 +145,8 @@ __global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
       }
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
-        S = mfma32(lds_read16_at(ka[c] + ST * TB + kt * 32 * D * 2), qop[c], S);
-        P2 = mfma32(lds_read16_at(ka[c] + (NS + ST) * TB + kt * 32 * D * 2), dop[c], P2);
+        S = mfma32(ld16(Kt + kt * 32 * ROWB, ko[c]), qop[c], S);
+        P2 = mfma32(ld16(Vt + kt * 32 * ROWB, ko[c]), dop[c], P2);
       }
 #pragma unroll
       for (int jc = 0; jc < 2; ++jc) {
@@ -164,24 +166,25 @@ __global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int ch = 0; ch < 4; ++ch)
-        dQ[dt] = mfma32(tr_pair_at(ta[dt][0] + ST * TB + ch * 16 * D * 2,
-                                   ta[dt][1] + ST * TB + ch * 16 * D * 2),
-                        dZp[ch], dQ[dt]);
+        dQ[dt] = mfma32(ldtr_pair(Kt + ch * 16 * ROWB, to[dt][0], to[dt][1]), dZp[ch], dQ[dt]);
     if (!CUR) {
       zs = wave_sum(zs);
-      if (lane == 0) part[(t & 1) * 8 + wave] = zs;
+      if (lane == 0) part[t & 1][wave] = zs;
     }
   };
-  // kept tile t: wait for it (and for the buffer it replaces to be free),
-  // publish the block gate gradient of tile t-1, refill, compute
+  auto publish = [&](int t) __attribute__((always_inline)) {   // gate gradient of tile t
+    if (tid == 0) {
+      float a = 0.f;
+      for (int w = 0; w < 2 * GC; ++w) a += part[t & 1][w];
+      dlgp[(rowsel * nch + chunk) * topk + t] = a;
+    }
+  };
+  // kept tile t in stage ST: wait for it (and for the stage it refills to be
+  // free), publish the gate gradient of tile t-1, refill, compute
   auto kept = [&]<int ST>(int t) __attribute__((always_inline)) {
     vm_wait_barrier<JW * (NS - 2)>();
-    if (t > 0 && tid == 0) {
-      float a = 0.f;
-      for (int w = 0; w < 2 * GC; ++w) a += part[((t - 1) & 1) * 8 + w];
-      dlgp[(rowsel * nch + chunk) * topk + t - 1] = a;
-    }
-    if (t + NS - 1 < ntiles) issue(t + NS - 1, (ST + NS - 1) % NS);
+    if (t > 0) publish(t - 1);
+    if (t + NS - 1 < ntiles) issue.template operator()<(ST + NS - 1) % NS>(t + NS - 1);
     tile.template operator()<ST, false>(t);
   };
   int t = 0;
@@ -194,11 +197,7 @@ __global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
     ((t + S < c_sel ? kept.template operator()<S>(t + S) : void()), ...);
   }(std::make_integer_sequence<int, NS - 1>{});
   vm_wait_barrier<0>();
-  if (c_sel > 0 && tid == 0) {
-    float a = 0.f;
-    for (int w = 0; w < 2 * GC; ++w) a += part[((c_sel - 1) & 1) * 8 + w];
-    dlgp[(rowsel * nch + chunk) * topk + c_sel - 1] = a;
-  }
+  if (c_sel > 0) publish(c_sel - 1);
   [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
     ((c_sel % NS == S ? tile.template operator()<S, true>(c_sel) : void()), ...);
   }(std::make_integer_sequence<int, NS>{});
@@ -259,10 +258,9 @@ __global__ void __launch_bounds__(256) bwd_ds_kernel(const float* __restrict__ d
 // ------------------------------------------------------------------ dk/dv kernel
 // grid: B*Hkv*nkb workgroups of 4 waves; wave = (key half kh, row half rh).
 // The (q-block, head) steps of the reverse list stream through a ring of
-// kKvStages LDS buffers, each holding the Q and dO tiles of one (q-block, head)
-// and its row statistics; the block's own V tile sits in LDS after the ring
-// (its K rows stay in registers as the S = Q K^T operand).
-// LDS: ring stage s at s*STAGE = [Q tile | dO tile | lse*log2e[64] | D[64]].
+// kKvStages stages, each holding the Q and dO tiles of one (q-block, head) and
+// its row statistics [lse*log2e | D]; the block's own V tile sits in LDS (its
+// K rows stay in registers as the S = Q K^T operand).
 template <int D>
 __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -271,8 +269,6 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
     const int32_t* __restrict__ rev_off, const int32_t* __restrict__ rev_list,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int Hq, int Hkv, int n, int topk,
     float tau, float tau2) {
-  extern __shared__ __attribute__((aligned(16))) char smem_generic[];
-  lds_char* const smem = lds_ptr(smem_generic);
   constexpr int NS = kKvStages;
   constexpr int ROWB = D * 2;
   constexpr int TB = 64 * ROWB;
@@ -280,8 +276,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
   constexpr int JT = TB / 1024;
   constexpr int JW = 2 * JT / 4;        // Q + dO slices per wave per step
   constexpr int PER = JW + 1;           // plus one slice of row statistics
-  constexpr int STAGE = 2 * TB + 512;
-  constexpr int VT = NS * STAGE;        // the block's own V tile
+  constexpr int TQ = 300, TO = 301, TS = 302, TVV = 303;   // LDS buffer tags
 
   const int nkb = n / SAS_BLK;
   const int G = Hq / Hkv;
@@ -299,9 +294,9 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
 #pragma unroll
   for (int c = 0; c < D / 16; ++c)
     kop[c] = *reinterpret_cast<const bf16x8*>(k + krow * D + c * 16 + hh * 8);
-  // own V tile -> LDS (swizzled), read back as the dP = dO V^T operand
+  lds_char* Vown = stage_buf<TVV, 0, TB>();
 #pragma unroll
-  for (int u = 0; u < JT / 4; ++u) dma_tile_slice<D>(v + kvrow0 * D, smem + VT, wave * (JT / 4) + u, lane);
+  for (int u = 0; u < JT / 4; ++u) dma_tile_slice<D>(v + kvrow0 * D, Vown, wave * (JT / 4) + u, lane);
 
   f32x16 dK[D / 32], dV[D / 32];
 #pragma unroll
@@ -317,54 +312,55 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
   const int32_t e1 = rev_off[size_t(bk) * (nkb + 1) + m + 1];
   const int nsteps = (e1 - e0) * G;
 
-  auto issue = [&](int s, int buf) __attribute__((always_inline)) {
+  auto issue = [&]<int BUF>(int s) __attribute__((always_inline)) {
     const int32_t ent = lst[e0 + s / G];
     const int iq = ent & 0xFFFF;
     const int hq = kv * G + s % G;
     const size_t row0 = (size_t(b) * Hq + hq) * n + size_t(iq) * SAS_BLK;
-    lds_char* base = smem + buf * STAGE;
 #pragma unroll
     for (int u = 0; u < JW; ++u) {
       const int j = wave * JW + u;
-      const int T = j / JT;
-      dma_tile_slice<D>((T ? dO : q) + row0 * D, base + T * TB, j % JT, lane);
+      if (j < JT) dma_tile_slice<D>(q + row0 * D, stage_buf<TQ, BUF, TB>(), j, lane);
+      else dma_tile_slice<D>(dO + row0 * D, stage_buf<TO, BUF, TB>(), j - JT, lane);
     }
     // 512 B of statistics: lanes 0..7 of each wave move 128 B
     const float* st = stats + ((size_t(b) * Hq + hq) * nkb + iq) * 128 + wave * 32;
-    if (lane < 8) dma16(st + lane * 4, base + 2 * TB + wave * 128);
+    if (lane < 8) dma16(st + lane * 4, stage_buf<TS, BUF, 512>() + wave * 128);
   };
-  for (int t = 0; t < NS - 1 && t < nsteps; ++t) issue(t, t);
+  [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
+    ((S < nsteps ? issue.template operator()<S>(S) : void()), ...);
+  }(std::make_integer_sequence<int, NS - 1>{});
 
-  // per-lane LDS addresses (stage 0); every other offset is an immediate
-  uint32_t qa[D / 16], ta[D / 32][2], va[D / 16];
+  uint32_t qo[D / 16], to[D / 32][2], vo[D / 16];
   {
     int roff[D / 16], toff[D / 32][2];
     row_offsets<D>(lane, roff);
     tr_offsets<D>(lane, toff);
-    const uint32_t base = lds_addr(smem) + uint32_t(rh * 32 * ROWB);
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
-      qa[c] = opaque(base + uint32_t(roff[c]));
-      va[c] = opaque(lds_addr(smem) + VT + uint32_t(kh * 32 * ROWB + roff[c]));
+      qo[c] = lane_off(rh * 32 * ROWB + roff[c]);
+      vo[c] = lane_off(kh * 32 * ROWB + roff[c]);
     }
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int w = 0; w < 2; ++w) ta[dt][w] = opaque(base + uint32_t(toff[dt][w]));
+      for (int w = 0; w < 2; ++w) to[dt][w] = lane_off(rh * 32 * ROWB + toff[dt][w]);
   }
-  // row statistics of rows rh*32 + 8*jg + 4*hh + 0..3 (16 B each group)
-  const uint32_t sa = opaque(lds_addr(smem) + 2 * TB + uint32_t((rh * 32 + 4 * hh) * 4));
+  // row statistics of rows rh*32 + 8*jg + 4*hh + 0..3 (16 B per group)
+  const uint32_t so = lane_off((rh * 32 + 4 * hh) * 4);
   const int keyw = kh * 32 + lr;  // this lane's key inside block m
 
-  auto step = [&](int s, auto own_tag) __attribute__((always_inline)) {
-    constexpr bool OWN = decltype(own_tag)::value;
-    const uint32_t sb = uint32_t((s % NS) * STAGE);
+  auto step = [&]<int ST>(int s) __attribute__((always_inline)) {
+    lds_cchar* Qt = stage_buf<TQ, ST, TB>();
+    lds_cchar* Ot = stage_buf<TO, ST, TB>();
+    lds_cchar* St = stage_buf<TS, ST, 512>();
     const int32_t ent = lst[e0 + s / G];
     const int iq = ent & 0xFFFF;
     const int slot = (ent >> 16) & 0xFFFF;
-    const float bias2 = OWN ? 0.f : lg[(size_t(bk) * nkb + iq) * topk + slot] * kLog2e;
+    const bool own = slot == 0xFFFF;   // the block's own (causal) current block
+    const float bias2 = own ? 0.f : lg[(size_t(bk) * nkb + iq) * topk + slot] * kLog2e;
     // own block: rows 0..31 see none of the keys 32..63
-    if (OWN && kh == 1 && rh == 0) return;
+    if (own && kh == 1 && rh == 0) return;
     f32x16 S, P2;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -373,12 +369,11 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
     }
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
-      const uint32_t a = opaque(qa[c] + sb);
-      S = mfma32(lds_read16_at(a), kop[c], S);
-      P2 = mfma32(lds_read16_at(a + TB), lds_read16_at(va[c]), P2);
+      S = mfma32(ld16(Qt, qo[c]), kop[c], S);
+      P2 = mfma32(ld16(Ot, qo[c]), ld16(Vown, vo[c]), P2);
     }
     // S[row][key]: lane l, reg j: row = rh*32 + 8(j/4) + 4hh + j%4, key = keyw
-    const uint32_t sas = opaque(sa + sb);
+    typedef __attribute__((ext_vector_type(4))) float f32x4;
     bf16x8 Pp[2], Zp[2];
 #pragma unroll
     for (int jc = 0; jc < 2; ++jc) {
@@ -386,14 +381,13 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
 #pragma unroll
       for (int g2 = 0; g2 < 2; ++g2) {
         const int jg = 2 * jc + g2;
-        typedef __attribute__((ext_vector_type(4))) float f32x4;
-        const f32x4 lv = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(uintptr_t(sas + jg * 32));
-        const f32x4 dv4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(uintptr_t(sas + 256 + jg * 32));
+        const f32x4 lv = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(St + so + jg * 32);
+        const f32x4 dv4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(St + so + 256 + jg * 32);
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const int j = 4 * jg + r4;
           float p = fast_exp2(__builtin_fmaf(S[j], tau2, bias2 - lv[r4]));
-          if (OWN && keyw > rh * 32 + 8 * jg + 4 * hh + r4) p = 0.f;
+          if (own && keyw > rh * 32 + 8 * jg + 4 * hh + r4) p = 0.f;
           pv[4 * g2 + r4] = p;
           zv[4 * g2 + r4] = p * (P2[j] - dv4[r4]);
         }
@@ -402,49 +396,52 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
       Zp[jc] = pack_bf16x8(zv);
     }
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-      const uint32_t a0 = opaque(ta[dt][0] + sb), a1 = opaque(ta[dt][1] + sb);
+    for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int jc = 0; jc < 2; ++jc) {
-        dV[dt] = mfma32(Pp[jc], tr_pair_at(a0 + TB + jc * 16 * ROWB, a1 + TB + jc * 16 * ROWB), dV[dt]);
-        dK[dt] = mfma32(Zp[jc], tr_pair_at(a0 + jc * 16 * ROWB, a1 + jc * 16 * ROWB), dK[dt]);
+        dV[dt] = mfma32(Pp[jc], ldtr_pair(Ot + jc * 16 * ROWB, to[dt][0], to[dt][1]), dV[dt]);
+        dK[dt] = mfma32(Zp[jc], ldtr_pair(Qt + jc * 16 * ROWB, to[dt][0], to[dt][1]), dK[dt]);
       }
-    }
   };
-  // the own block (always the first list entry) is the first G steps
-  auto waitfor = [&](int s) __attribute__((always_inline)) {
+  // step s in stage ST: wait for its DMA (and for the stage it refills to be
+  // free), refill the stage NS-1 ahead, compute
+  auto run = [&]<int ST>(int s) __attribute__((always_inline)) {
     const int after = min(NS - 2, nsteps - 1 - s);
     if (after >= 2) vm_wait_barrier<PER * 2>();
     else if (after == 1) vm_wait_barrier<PER>();
     else vm_wait_barrier<0>();
-    if (s + NS - 1 < nsteps) issue(s + NS - 1, (s + NS - 1) % NS);
+    if (s + NS - 1 < nsteps) issue.template operator()<(ST + NS - 1) % NS>(s + NS - 1);
+    step.template operator()<ST>(s);
   };
+  int s = 0;
 #pragma nounroll
-  for (int s = 0; s < G; ++s) {
-    waitfor(s);
-    step(s, std::true_type{});
-  }
-#pragma nounroll
-  for (int s = G; s < nsteps; ++s) {
-    waitfor(s);
-    step(s, std::false_type{});
-  }
+  for (; s + NS <= nsteps; s += NS)
+    [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
+      (run.template operator()<S>(s + S), ...);
+    }(std::make_integer_sequence<int, NS>{});
+  [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
+    ((s + S < nsteps ? run.template operator()<S>(s + S) : void()), ...);
+  }(std::make_integer_sequence<int, NS - 1>{});
   __syncthreads();
 
-  // Reduce the two row halves through LDS ([64 keys][D] float32), then write
-  // coalesced bf16 rows: first dV, then dK (scaled by tau).
-  __attribute__((address_space(3))) float* red =
-      reinterpret_cast<__attribute__((address_space(3))) float*>(smem);
+  // Reduce the two row halves through LDS (float32 [32 keys][D] per key half,
+  // in the stage-0 Q / dO buffers), then write coalesced bf16 rows: first dV,
+  // then dK (scaled by tau).
+  __attribute__((address_space(3))) float* red[2] = {
+      reinterpret_cast<__attribute__((address_space(3))) float*>(stage_buf<TQ, 0, TB>()),
+      reinterpret_cast<__attribute__((address_space(3))) float*>(stage_buf<TO, 0, TB>())};
+  static_assert(32 * D * 4 <= TB, "reduction buffer");
   const size_t out0 = kvrow0 * D;
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     const f32x16* acc = pass == 0 ? dV : dK;
+    __attribute__((address_space(3))) float* rk = red[kh];
     if (rh == 1) {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-          red[(kh * 32 + 8 * (j >> 2) + 4 * hh + (j & 3)) * D + dt * 32 + lr] = acc[dt][j];
+          rk[(8 * (j >> 2) + 4 * hh + (j & 3)) * D + dt * 32 + lr] = acc[dt][j];
     }
     __syncthreads();
     if (rh == 0) {
@@ -452,13 +449,14 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-          red[(kh * 32 + 8 * (j >> 2) + 4 * hh + (j & 3)) * D + dt * 32 + lr] += acc[dt][j];
+          rk[(8 * (j >> 2) + 4 * hh + (j & 3)) * D + dt * 32 + lr] += acc[dt][j];
     }
     __syncthreads();
     uint16_t* dst = (pass == 0 ? dv : dk) + out0;
     const float sc = pass == 0 ? 1.f : tau;
     for (int c = tid; c < 64 * CPR; c += 256) {
-      const __attribute__((address_space(3))) float* src = red + c * 8;
+      const int key = c / CPR;
+      const __attribute__((address_space(3))) float* src = red[key >> 5] + (key & 31) * D + (c % CPR) * 8;
       bf16x8 r;
 #pragma unroll
       for (int e = 0; e < 8; ++e) r[e] = (__bf16)(src[e] * sc);
@@ -475,10 +473,7 @@ static void dq_launch(int nblocks, const void* q, const void* k, const void* v, 
                       const float* lg, void* dq, float* stats, float* dlgp, int Hq, int Hkv, int n,
                       int topk, float tau, float tau2, int BH, int h_off, int hchunks, int nch,
                       int chunk0, hipStream_t st) {
-  const size_t shm = size_t(kDqStages) * 2 * 64 * D * 2 + 64;
-  auto kern = bwd_dq_kernel<D, GC>;
-  allow_lds(kern, shm);
-  hipLaunchKernelGGL(kern, dim3(nblocks), dim3(128 * GC), shm, st, (const uint16_t*)q,
+  hipLaunchKernelGGL((bwd_dq_kernel<D, GC>), dim3(nblocks), dim3(128 * GC), 0, st, (const uint16_t*)q,
                      (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o,
                      (const uint16_t*)dO, lse, idx, cnt, lg, (uint16_t*)dq, stats, dlgp, Hq, Hkv,
                      n, topk, tau, tau2, BH, h_off, hchunks, nch, chunk0);
@@ -544,18 +539,13 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
   if (e != hipSuccess) return e;
   {
     ProfScope ps("sas_bwd_dkdv_kernel", st);
-    const size_t shm = size_t(kKvStages) * (2 * 64 * d * 2 + 512) + 64 * d * 2;
     if (d == 128) {
-      auto kern = bwd_dkdv_kernel<128>;
-      allow_lds(kern, shm);
-      hipLaunchKernelGGL(kern, dim3(BH * nqb), dim3(256), shm, st, (const uint16_t*)q,
+      hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3(BH * nqb), dim3(256), 0, st, (const uint16_t*)q,
                          (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO, stats, lg,
                          rev_off, rev_list, (uint16_t*)dk, (uint16_t*)dv, Hq, Hkv, n, topk, tau,
                          tau2);
     } else {
-      auto kern = bwd_dkdv_kernel<64>;
-      allow_lds(kern, shm);
-      hipLaunchKernelGGL(kern, dim3(BH * nqb), dim3(256), shm, st, (const uint16_t*)q,
+      hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3(BH * nqb), dim3(256), 0, st, (const uint16_t*)q,
                          (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO, stats, lg,
                          rev_off, rev_list, (uint16_t*)dk, (uint16_t*)dv, Hq, Hkv, n, topk, tau,
                          tau2);

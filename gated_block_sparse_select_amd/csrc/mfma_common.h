@@ -69,13 +69,6 @@ SAS_DEV bf16x4 lds_read_tr_at(uint32_t a) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
       reinterpret_cast<__attribute__((address_space(3))) bf16x4*>(uintptr_t(a)));
 }
-// Hide a value from the optimiser (so "base + lane offset" stays one register
-// and only the small per-access constant goes to the DS offset field).
-SAS_DEV uint32_t opaque(uint32_t x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
-
 SAS_DEV bf16x8 tr_pair_at(uint32_t a0, uint32_t a1) {
   const bf16x4 a = lds_read_tr_at(a0);
   const bf16x4 b = lds_read_tr_at(a1);
@@ -141,6 +134,45 @@ SAS_DEV void vm_wait_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+}
+
+// Hide a value from the optimiser (so "base + lane offset" stays one register
+// and only the small per-access constant goes to the DS offset field).
+SAS_DEV uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// ---------------------------------------------------------------- LDS ring buffers
+// Every ring stage (and tile kind) is its own __shared__ variable, reached
+// with a compile-time stage index.  The compiler then knows which buffer an
+// LDS read touches and which buffers in-flight DMA writes, and waits only for
+// the DMA that filled the stage being read (with one LDS variable and a
+// runtime stage index it drains every outstanding load before each
+// transposed read).
+template <int TAG, int ST, int BYTES>
+SAS_DEV lds_char* stage_buf() {
+  __shared__ __attribute__((aligned(16))) char buf[BYTES];
+  return (lds_char*)buf;
+}
+
+// Per-lane byte offset kept in a register: hidden from re-association and
+// masked so that the compiler can prove it non-negative, which lets every
+// "buffer + offset + constant" access fold the constant into the DS
+// instruction's offset field.
+SAS_DEV uint32_t lane_off(int raw) { return opaque(uint32_t(raw)) & kLdsAddrMask; }
+
+SAS_DEV bf16x8 ld16(lds_cchar* base, uint32_t off) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(base + off);
+}
+SAS_DEV bf16x4 ldtr(lds_cchar* base, uint32_t off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (__attribute__((address_space(3))) bf16x4*)(base + off));
+}
+SAS_DEV bf16x8 ldtr_pair(lds_cchar* base, uint32_t off0, uint32_t off1) {
+  const bf16x4 a = ldtr(base, off0);
+  const bf16x4 b = ldtr(base, off1);
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 constexpr int kFwdStages = 3;   // K/V tile ring depth of the forward

@@ -30,13 +30,13 @@ __global__ void __launch_bounds__(128 * GC) fwd_mfma_kernel(
     const int32_t* __restrict__ cnt, const float* __restrict__ lg, uint16_t* __restrict__ o,
     float* __restrict__ lse, int Hq, int Hkv, int n, int topk, float tau2, int BH, int h_off,
     int hchunks) {
-  extern __shared__ __attribute__((aligned(16))) char smem_generic[];
-  lds_char* const smem = lds_ptr(smem_generic);
   constexpr int NS = kFwdStages;
-  constexpr int TB = 64 * D * 2;          // bytes of one 64 x D tile
+  constexpr int ROWB = D * 2;
+  constexpr int TB = 64 * ROWB;           // bytes of one 64 x D tile
   constexpr int JT = TB / 1024;           // 1 KB DMA slices per tile
   constexpr int JW = 2 * JT / (2 * GC);   // slices per wave per stage (K and V)
   static_assert((2 * JT) % (2 * GC) == 0, "slices must split evenly over the waves");
+  constexpr int TK = 100, TV = 101;       // LDS buffer tags: K tiles, V tiles
 
   const int nqb = n / SAS_BLK;
   const int G = Hq / Hkv;
@@ -64,33 +64,32 @@ __global__ void __launch_bounds__(128 * GC) fwd_mfma_kernel(
     qop[c] = *reinterpret_cast<const bf16x8*>(q + qrow * D + c * 16 + hh * 8);
 
   const size_t kv0 = (size_t(b) * Hkv + kv) * size_t(n);
-  auto issue = [&](int t, int buf) __attribute__((always_inline)) {
+  // tile t -> ring stage BUF: K and V of block idx[t] (or the current block)
+  auto issue = [&]<int BUF>(int t) __attribute__((always_inline)) {
     const int blk = t < c_sel ? irow[t] : i;
     const uint16_t* kb = k + (kv0 + size_t(blk) * SAS_BLK) * D;
     const uint16_t* vb = v + (kv0 + size_t(blk) * SAS_BLK) * D;
 #pragma unroll
     for (int u = 0; u < JW; ++u) {
       const int j = wave * JW + u;
-      const int T = j / JT;
-      dma_tile_slice<D>(T ? vb : kb, smem + (T * NS + buf) * TB, j % JT, lane);
+      if (j < JT) dma_tile_slice<D>(kb, stage_buf<TK, BUF, TB>(), j, lane);
+      else dma_tile_slice<D>(vb, stage_buf<TV, BUF, TB>(), j - JT, lane);
     }
   };
+  issue.template operator()<0>(0);
+  if (1 < ntiles) issue.template operator()<1>(1);
 
-  for (int t = 0; t < NS - 1 && t < ntiles; ++t) issue(t, t);
-
-  // per-lane LDS addresses of stage 0; other stages / halves / chunks add
-  // compile-time offsets below 64 KB that fold into the DS instructions
-  uint32_t ka[D / 16], va[D / 32][2];
+  uint32_t ko[D / 16], vo[D / 32][2];
   {
     int koff[D / 16], voff[D / 32][2];
     row_offsets<D>(lane, koff);
     tr_offsets<D>(lane, voff);
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) ka[c] = opaque(lds_addr(smem) + uint32_t(koff[c]));
+    for (int c = 0; c < D / 16; ++c) ko[c] = lane_off(koff[c]);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int w = 0; w < 2; ++w) va[dt][w] = opaque(lds_addr(smem) + NS * TB + uint32_t(voff[dt][w]));
+      for (int w = 0; w < 2; ++w) vo[dt][w] = lane_off(voff[dt][w]);
   }
 
   // Running row max in the exp2 domain.  It is raised only when a tile's max
@@ -105,9 +104,10 @@ __global__ void __launch_bounds__(128 * GC) fwd_mfma_kernel(
 #pragma unroll
     for (int j = 0; j < 16; ++j) O[dt][j] = 0.f;
 
-  // One tile from ring stage ST (compile-time, so every LDS address is a
-  // per-lane register plus an immediate offset).  CUR: the causal current block.
+  // one tile from ring stage ST; CUR: the causal current block
   auto tile = [&]<int ST, bool CUR>(int t) __attribute__((always_inline)) {
+    lds_cchar* Kt = stage_buf<TK, ST, TB>();
+    lds_cchar* Vt = stage_buf<TV, ST, TB>();
     const float bias2 = CUR ? 0.f : grow[t] * kLog2e;
 
     f32x16 S[2];
@@ -117,7 +117,7 @@ __global__ void __launch_bounds__(128 * GC) fwd_mfma_kernel(
       for (int j = 0; j < 16; ++j) S[kt][j] = 0.f;
 #pragma unroll
       for (int c = 0; c < D / 16; ++c)
-        S[kt] = mfma32(lds_read16_at(ka[c] + ST * TB + kt * 32 * D * 2), qop[c], S[kt]);
+        S[kt] = mfma32(ld16(Kt + kt * 32 * ROWB, ko[c]), qop[c], S[kt]);
     }
     if (CUR) {  // causal mask of the current block: key j visible iff j <= row
 #pragma unroll
@@ -159,24 +159,22 @@ __global__ void __launch_bounds__(128 * GC) fwd_mfma_kernel(
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int ch = 0; ch < 4; ++ch)
-        O[dt] = mfma32(tr_pair_at(va[dt][0] + ST * TB + ch * 16 * D * 2,
-                                  va[dt][1] + ST * TB + ch * 16 * D * 2),
-                       P[ch], O[dt]);
+        O[dt] = mfma32(ldtr_pair(Vt + ch * 16 * ROWB, vo[dt][0], vo[dt][1]), P[ch], O[dt]);
   };
-  // Tile t of the kept blocks: its DMA landed (and the buffer it replaces is
-  // free) after the wait + barrier; then the tile NS-1 ahead is put in flight.
+  // kept tile t in stage ST: its DMA landed (and the stage it refills is free)
+  // after the wait + barrier; then the tile NS-1 ahead is put in flight
   auto kept = [&]<int ST>(int t) __attribute__((always_inline)) {
     vm_wait_barrier<JW * (NS - 2)>();
-    if (t + NS - 1 < ntiles) issue(t + NS - 1, (ST + NS - 1) % NS);
+    if (t + NS - 1 < ntiles) issue.template operator()<(ST + NS - 1) % NS>(t + NS - 1);
     tile.template operator()<ST, false>(t);
-  };
-  auto ring = [&]<int... S>(int t0, std::integer_sequence<int, S...>) __attribute__((always_inline)) {
-    (kept.template operator()<S>(t0 + S), ...);
   };
 
   int t = 0;
 #pragma nounroll
-  for (; t + NS <= c_sel; t += NS) ring(t, std::make_integer_sequence<int, NS>{});
+  for (; t + NS <= c_sel; t += NS)
+    [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
+      (kept.template operator()<S>(t + S), ...);
+    }(std::make_integer_sequence<int, NS>{});
   // t % NS == 0 here; finish the kept tiles, then the current block
   [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
     ((t + S < c_sel ? kept.template operator()<S>(t + S) : void()), ...);
@@ -208,10 +206,7 @@ static void fwd_launch(int nblocks, const void* q, const void* k, const void* v,
                        const int32_t* idx, const int32_t* cnt, const float* lg, void* o, float* lse,
                        int Hq, int Hkv, int n, int topk, float tau2, int BH, int h_off,
                        int hchunks, hipStream_t st) {
-  const size_t shm = size_t(kFwdStages) * 2 * 64 * D * 2;
-  auto kern = fwd_mfma_kernel<D, GC>;
-  allow_lds(kern, shm);
-  hipLaunchKernelGGL(kern, dim3(nblocks), dim3(128 * GC), shm, st,
+  hipLaunchKernelGGL((fwd_mfma_kernel<D, GC>), dim3(nblocks), dim3(128 * GC), 0, st,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, cnt, lg,
                      (uint16_t*)o, lse, Hq, Hkv, n, topk, tau2, BH, h_off, hchunks);
 }
