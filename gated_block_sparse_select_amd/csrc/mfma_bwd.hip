@@ -28,6 +28,7 @@
 
 #include "launch.h"
 #include "mfma_common.h"
+#include "sas.h"
 
 namespace sas {
 
@@ -86,10 +87,10 @@ __global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
   const float lse2 = lse[qrow] * kLog2e;
   if (hh == 0) {
     // per-row statistics of this (head, q-block) for the key-block-outer pass:
-    // [lse * log2(e) for the 64 rows | D for the 64 rows]
+    // [-lse / tau for the 64 rows | -D for the 64 rows]
     float* st = stats + ((size_t(b) * Hq + h) * nqb + i) * 128;
-    st[rt * 32 + lr] = lse2;
-    st[64 + rt * 32 + lr] = Drow;
+    st[rt * 32 + lr] = -lse[qrow] / tau;
+    st[64 + rt * 32 + lr] = -Drow;
   }
 
   const size_t kv0 = (size_t(b) * Hkv + kv) * size_t(n);
@@ -259,8 +260,19 @@ __global__ void __launch_bounds__(256) bwd_ds_kernel(const float* __restrict__ d
 // grid: B*Hkv*nkb workgroups of 4 waves; wave = (key half kh, row half rh).
 // The (q-block, head) steps of the reverse list stream through a ring of
 // kKvStages stages, each holding the Q and dO tiles of one (q-block, head) and
-// its row statistics [lse*log2e | D]; the block's own V tile sits in LDS (its
-// K rows stay in registers as the S = Q K^T operand).
+// its row statistics [-lse/tau | -D]; the K and V rows of the wave's key half
+// stay in registers.  The statistics are the start values of the two
+// accumulators, so S = Q K^T - lse/tau (tau2*S + bias2 is the base-2 log of
+// P) and dP = dO V^T - D come out of the matrix cores ready for the
+// elementwise step.
+//
+// Each step runs in four phases fenced with sched_barrier: S and dP (LDS
+// reads two 16-column chunks ahead of the products that use them), P and dZ
+// of rows 0..15 of the wave's 32, the dV/dK products of those rows overlapped
+// with P and dZ of rows 16..31, then the dV/dK products of rows 16..31.  The
+// list entries (q-block and base-2 log-gate) are staged in LDS first, so the
+// loop issues no scalar memory loads (those return out of order and would
+// force every LDS wait to drain all outstanding LDS reads).
 template <int D>
 __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -270,13 +282,14 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int Hq, int Hkv, int n, int topk,
     float tau, float tau2) {
   constexpr int NS = kKvStages;
+  static_assert(NS == 4, "stage arithmetic below assumes a 4-stage ring");
   constexpr int ROWB = D * 2;
   constexpr int TB = 64 * ROWB;
   constexpr int CPR = D / 8;
   constexpr int JT = TB / 1024;
   constexpr int JW = 2 * JT / 4;        // Q + dO slices per wave per step
-  constexpr int PER = JW + 1;           // plus one slice of row statistics
-  constexpr int TQ = 300, TO = 301, TS = 302, TVV = 303;   // LDS buffer tags
+  constexpr int PER = JW + 1;           // plus the row statistics
+  constexpr int TQ = 300, TO = 301, TS = 302;   // LDS buffer tags
 
   const int nkb = n / SAS_BLK;
   const int G = Hq / Hkv;
@@ -284,19 +297,18 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
   const int m = blockIdx.x % nkb;
   const int b = bk / Hkv, kv = bk % Hkv;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lr = lane & 31, hh = lane >> 5;
   const int kh = wave & 1, rh = wave >> 1;
 
   const size_t kvrow0 = (size_t(b) * Hkv + kv) * n + size_t(m) * SAS_BLK;
   const size_t krow = kvrow0 + kh * 32 + lr;
-  bf16x8 kop[D / 16];
+  bf16x8 kop[D / 16], vop[D / 16];
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c)
+  for (int c = 0; c < D / 16; ++c) {
     kop[c] = *reinterpret_cast<const bf16x8*>(k + krow * D + c * 16 + hh * 8);
-  lds_char* Vown = stage_buf<TVV, 0, TB>();
-#pragma unroll
-  for (int u = 0; u < JT / 4; ++u) dma_tile_slice<D>(v + kvrow0 * D, Vown, wave * (JT / 4) + u, lane);
+    vop[c] = *reinterpret_cast<const bf16x8*>(v + krow * D + c * 16 + hh * 8);
+  }
 
   f32x16 dK[D / 32], dV[D / 32];
 #pragma unroll
@@ -307,121 +319,207 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
       dV[dt][j] = 0.f;
     }
 
+  // list entries of this key block -> LDS: q-block and base-2 log-gate
+  // (0 for the own block, entry 0)
+  __shared__ int2 meta[SAS_MAX_BLOCKS];
   const int32_t* lst = rev_list + size_t(bk) * nkb * (topk + 1);
   const int32_t e0 = rev_off[size_t(bk) * (nkb + 1) + m];
   const int32_t e1 = rev_off[size_t(bk) * (nkb + 1) + m + 1];
+  for (int e = tid; e < e1 - e0; e += 256) {
+    const int32_t ent = lst[e0 + e];
+    const int iq = ent & 0xFFFF, slot = (ent >> 16) & 0xFFFF;
+    const float b2 = slot == 0xFFFF ? 0.f : lg[(size_t(bk) * nkb + iq) * topk + slot] * kLog2e;
+    meta[e] = make_int2(iq, __float_as_int(b2));
+  }
+  __syncthreads();
   const int nsteps = (e1 - e0) * G;
+  const int nmain = nsteps - G;
 
-  auto issue = [&]<int BUF>(int s) __attribute__((always_inline)) {
-    const int32_t ent = lst[e0 + s / G];
-    const int iq = ent & 0xFFFF;
-    const int hq = kv * G + s % G;
-    const size_t row0 = (size_t(b) * Hq + hq) * n + size_t(iq) * SAS_BLK;
+  // DMA cursor: the next step to issue, as (list entry, head).  The first
+  // half of the waves move Q slices, the others dO slices; every wave moves
+  // the 256 B of row statistics of its row half (lane l: word l%32 of the
+  // -lse/tau rows for l < 32, of the -D rows for l >= 32).
+  static_assert(JW % 4 == 0, "slice groups must start at a multiple of 4");
+  int ie = 0, ih = 0;
+  const bool q_side = wave * JW < JT;
+  const int slice0 = (wave * JW) % JT;
+  const size_t hstride = size_t(n) * D * 2;
+  const char* src_base = reinterpret_cast<const char*>(q_side ? q : dO) +
+                         (size_t(b) * Hq + kv * G) * hstride + slice0 * 1024;
+  const float* st_base = stats + (size_t(b) * Hq + kv * G) * size_t(nkb) * 128 + rh * 32 +
+                         (lane >> 5) * 64 + (lane & 31);
+  uint32_t pat[4];
+  dma_lane_pattern<D>(lane, pat);
+  auto issue = [&]<int BUF>() __attribute__((always_inline)) {
+    const int iq = __builtin_amdgcn_readfirstlane(meta[ie].x);
+    const char* tile = src_base + size_t(ih) * hstride + size_t(iq) * SAS_BLK * D * 2;
+    lds_char* dst = (q_side ? stage_buf<TQ, BUF, TB>() : stage_buf<TO, BUF, TB>()) + slice0 * 1024;
 #pragma unroll
-    for (int u = 0; u < JW; ++u) {
-      const int j = wave * JW + u;
-      if (j < JT) dma_tile_slice<D>(q + row0 * D, stage_buf<TQ, BUF, TB>(), j, lane);
-      else dma_tile_slice<D>(dO + row0 * D, stage_buf<TO, BUF, TB>(), j - JT, lane);
+    for (int u = 0; u < JW; ++u) dma16(tile + u * 1024 + pat[u & 3], dst + u * 1024);
+    __builtin_amdgcn_global_load_lds(
+        (glb_void*)(st_base + (size_t(ih) * nkb + iq) * 128),
+        (lds_void*)(stage_buf<TS, BUF, 1024>() + wave * 256), 4, 0, 0);
+    if (++ih == G) {
+      ih = 0;
+      ++ie;
     }
-    // 512 B of statistics: lanes 0..7 of each wave move 128 B
-    const float* st = stats + ((size_t(b) * Hq + hq) * nkb + iq) * 128 + wave * 32;
-    if (lane < 8) dma16(st + lane * 4, stage_buf<TS, BUF, 512>() + wave * 128);
   };
+  // wait until the loads of all but the `ahead` most recently issued steps
+  // have landed, then barrier
+  auto wait_ahead = [&](int ahead) __attribute__((always_inline)) {
+    if (ahead >= 2) vm_wait_barrier<2 * PER>();
+    else if (ahead == 1) vm_wait_barrier<PER>();
+    else vm_wait_barrier<0>();
+  };
+
   [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
-    ((S < nsteps ? issue.template operator()<S>(S) : void()), ...);
+    ((S < nsteps ? issue.template operator()<S>() : void()), ...);
   }(std::make_integer_sequence<int, NS - 1>{});
 
-  uint32_t qo[D / 16], to[D / 32][2], vo[D / 16];
+  uint32_t qo[D / 16], to[D / 32][2];
   {
     int roff[D / 16], toff[D / 32][2];
     row_offsets<D>(lane, roff);
     tr_offsets<D>(lane, toff);
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      qo[c] = lane_off(rh * 32 * ROWB + roff[c]);
-      vo[c] = lane_off(kh * 32 * ROWB + roff[c]);
-    }
+    for (int c = 0; c < D / 16; ++c) qo[c] = lane_off(rh * 32 * ROWB + roff[c]);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int w = 0; w < 2; ++w) to[dt][w] = lane_off(rh * 32 * ROWB + toff[dt][w]);
   }
-  // row statistics of rows rh*32 + 8*jg + 4*hh + 0..3 (16 B per group)
-  const uint32_t so = lane_off((rh * 32 + 4 * hh) * 4);
-  const int keyw = kh * 32 + lr;  // this lane's key inside block m
+  // statistics of rows rh*32 + 8*jg + 4*hh + 0..3 (16 B per group jg) in this
+  // wave's 256 B copy
+  const uint32_t so = lane_off(wave * 256 + 4 * hh * 4);
+  typedef __attribute__((ext_vector_type(4))) float f32x4;
+  typedef const __attribute__((address_space(3))) f32x4 lds_f32x4;
 
-  auto step = [&]<int ST>(int s) __attribute__((always_inline)) {
+  // P and dZ = P o (dP - D) of row chunk jc as bf16 operands (register
+  // j = 8*jc + e holds row rh*32 + 8*(j/4) + 4*hh + j%4 of this lane's key)
+  auto elementwise = [&]<bool OWN, int JC>(const f32x16& S, const f32x16& P2, float bias2,
+                                           bf16x8& Pp, bf16x8& Zp) __attribute__((always_inline)) {
+    float pv[8], zv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = 8 * JC + e;
+      float p = fast_exp2(__builtin_fmaf(S[j], tau2, bias2));
+      if (OWN && kh * 32 + lr > rh * 32 + 8 * (j >> 2) + 4 * hh + (j & 3)) p = 0.f;
+      pv[e] = p;
+      zv[e] = p * P2[j];
+    }
+    Pp = pack_bf16x8(pv);
+    Zp = pack_bf16x8(zv);
+  };
+
+  auto step = [&]<int ST, bool OWN>(float bias2) __attribute__((always_inline)) {
+    constexpr int NC = D / 16;
+    constexpr int NT = D / 32;
     lds_cchar* Qt = stage_buf<TQ, ST, TB>();
     lds_cchar* Ot = stage_buf<TO, ST, TB>();
-    lds_cchar* St = stage_buf<TS, ST, 512>();
-    const int32_t ent = lst[e0 + s / G];
-    const int iq = ent & 0xFFFF;
-    const int slot = (ent >> 16) & 0xFFFF;
-    const bool own = slot == 0xFFFF;   // the block's own (causal) current block
-    const float bias2 = own ? 0.f : lg[(size_t(bk) * nkb + iq) * topk + slot] * kLog2e;
-    // own block: rows 0..31 see none of the keys 32..63
-    if (own && kh == 1 && rh == 0) return;
+    lds_cchar* St = stage_buf<TS, ST, 1024>();
+    // phase 1: S = Q K^T - lse/tau, dP = dO V^T - D
     f32x16 S, P2;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      S[j] = 0.f;
-      P2[j] = 0.f;
-    }
+    for (int jg = 0; jg < 4; ++jg) {
+      const f32x4 l4 = *reinterpret_cast<lds_f32x4*>(St + so + jg * 32);
+      const f32x4 d4 = *reinterpret_cast<lds_f32x4*>(St + so + 128 + jg * 32);
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      S = mfma32(ld16(Qt, qo[c]), kop[c], S);
-      P2 = mfma32(ld16(Ot, qo[c]), ld16(Vown, vo[c]), P2);
-    }
-    // S[row][key]: lane l, reg j: row = rh*32 + 8(j/4) + 4hh + j%4, key = keyw
-    typedef __attribute__((ext_vector_type(4))) float f32x4;
-    bf16x8 Pp[2], Zp[2];
-#pragma unroll
-    for (int jc = 0; jc < 2; ++jc) {
-      float pv[8], zv[8];
-#pragma unroll
-      for (int g2 = 0; g2 < 2; ++g2) {
-        const int jg = 2 * jc + g2;
-        const f32x4 lv = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(St + so + jg * 32);
-        const f32x4 dv4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(St + so + 256 + jg * 32);
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int j = 4 * jg + r4;
-          float p = fast_exp2(__builtin_fmaf(S[j], tau2, bias2 - lv[r4]));
-          if (own && keyw > rh * 32 + 8 * jg + 4 * hh + r4) p = 0.f;
-          pv[4 * g2 + r4] = p;
-          zv[4 * g2 + r4] = p * (P2[j] - dv4[r4]);
-        }
+      for (int r = 0; r < 4; ++r) {
+        S[4 * jg + r] = l4[r];
+        P2[4 * jg + r] = d4[r];
       }
-      Pp[jc] = pack_bf16x8(pv);
-      Zp[jc] = pack_bf16x8(zv);
+    }
+    bf16x8 qa[NC], oa[NC];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      qa[c] = ld16(Qt, qo[c]);
+      oa[c] = ld16(Ot, qo[c]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (c + 2 < NC) {
+        qa[c + 2] = ld16(Qt, qo[c + 2]);
+        oa[c + 2] = ld16(Ot, qo[c + 2]);
+      }
+      S = mfma32(qa[c], kop[c], S);
+      P2 = mfma32(oa[c], vop[c], P2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // phase 2: transposed operands of rows 0..15, P and dZ of rows 0..15
+    bf16x8 tO0[NT], tQ0[NT], tO1[NT], tQ1[NT];
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt) {
+      tO0[dt] = ldtr_pair(Ot, to[dt][0], to[dt][1]);
+      tQ0[dt] = ldtr_pair(Qt, to[dt][0], to[dt][1]);
+    }
+    bf16x8 Pp0, Zp0, Pp1, Zp1;
+    elementwise.template operator()<OWN, 0>(S, P2, bias2, Pp0, Zp0);
+    __builtin_amdgcn_sched_barrier(0);
+    // phase 3: dV/dK of rows 0..15 with P, dZ and operands of rows 16..31
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt) {
+      tO1[dt] = ldtr_pair(Ot + 16 * ROWB, to[dt][0], to[dt][1]);
+      tQ1[dt] = ldtr_pair(Qt + 16 * ROWB, to[dt][0], to[dt][1]);
     }
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+    for (int dt = 0; dt < NT; ++dt) {
+      dV[dt] = mfma32(Pp0, tO0[dt], dV[dt]);
+      dK[dt] = mfma32(Zp0, tQ0[dt], dK[dt]);
+    }
+    elementwise.template operator()<OWN, 1>(S, P2, bias2, Pp1, Zp1);
 #pragma unroll
-      for (int jc = 0; jc < 2; ++jc) {
-        dV[dt] = mfma32(Pp[jc], ldtr_pair(Ot + jc * 16 * ROWB, to[dt][0], to[dt][1]), dV[dt]);
-        dK[dt] = mfma32(Zp[jc], ldtr_pair(Qt + jc * 16 * ROWB, to[dt][0], to[dt][1]), dK[dt]);
-      }
+    for (int i = 0; i < 2 * NT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one matrix product
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six vector ops
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // phase 4: dV/dK of rows 16..31
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt) {
+      dV[dt] = mfma32(Pp1, tO1[dt], dV[dt]);
+      dK[dt] = mfma32(Zp1, tQ1[dt], dK[dt]);
+    }
   };
+
   // step s in stage ST: wait for its DMA (and for the stage it refills to be
-  // free), refill the stage NS-1 ahead, compute
-  auto run = [&]<int ST>(int s) __attribute__((always_inline)) {
-    const int after = min(NS - 2, nsteps - 1 - s);
-    if (after >= 2) vm_wait_barrier<PER * 2>();
-    else if (after == 1) vm_wait_barrier<PER>();
-    else vm_wait_barrier<0>();
-    if (s + NS - 1 < nsteps) issue.template operator()<(ST + NS - 1) % NS>(s + NS - 1);
-    step.template operator()<ST>(s);
+  // free), refill the stage NS-1 ahead, compute.  Steps 0..G-1 are the own
+  // block (no gate, causal mask; rows 0..31 see none of the keys 32..63, so
+  // that wave sits them out).
+  int ce = 0, chd = 0;   // list entry / head of the step being computed
+  auto run = [&]<int ST, bool STEADY>(int s) __attribute__((always_inline)) {
+    if (STEADY) vm_wait_barrier<(NS - 2) * PER>();
+    else wait_ahead(min(NS - 2, nsteps - 1 - s));
+    if (STEADY || s + NS - 1 < nsteps) issue.template operator()<(ST + NS - 1) % NS>();
+    const float bias2 = __int_as_float(meta[ce].y);
+    if (++chd == G) {
+      chd = 0;
+      ++ce;
+    }
+    if (!STEADY && s < G) {
+      if (!(kh == 1 && rh == 0)) step.template operator()<ST, true>(0.f);
+    } else {
+      step.template operator()<ST, false>(bias2);
+    }
   };
   int s = 0;
+  // own-block steps and the ring tail use the checked form
 #pragma nounroll
-  for (; s + NS <= nsteps; s += NS)
+  for (; s < G; s += NS)
     [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
-      (run.template operator()<S>(s + S), ...);
+      ((s + S < nsteps ? run.template operator()<S, false>(s + S) : void()), ...);
     }(std::make_integer_sequence<int, NS>{});
-  [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
-    ((s + S < nsteps ? run.template operator()<S>(s + S) : void()), ...);
-  }(std::make_integer_sequence<int, NS - 1>{});
+#pragma nounroll
+  for (; s + 2 * NS - 2 < nsteps; s += NS)
+    [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
+      (run.template operator()<S, true>(s + S), ...);
+    }(std::make_integer_sequence<int, NS>{});
+#pragma nounroll
+  for (; s < nsteps; s += NS)
+    [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
+      ((s + S < nsteps ? run.template operator()<S, false>(s + S) : void()), ...);
+    }(std::make_integer_sequence<int, NS>{});
   __syncthreads();
 
   // Reduce the two row halves through LDS (float32 [32 keys][D] per key half,

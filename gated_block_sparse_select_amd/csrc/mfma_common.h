@@ -122,6 +122,23 @@ SAS_DEV void dma_tile_slice(const uint16_t* gtile, lds_char* ltile, int jj, int 
   dma16(gtile + r * D + c * 8, ltile + jj * 1024);
 }
 
+// Per-lane byte offset, inside a 1 KB slice of a swizzled 64 x D tile, of the
+// chunk lane `lane` moves for slices jj = t (mod 4): the swizzle of a slice's
+// rows depends on jj mod 4 only, so slice jj of a tile at global address g
+// is lane-wise g + 1024*jj + pat[jj % 4] (same logical chunk as
+// dma_tile_slice).
+template <int D>
+SAS_DEV void dma_lane_pattern(int lane, uint32_t (&pat)[4]) {
+  constexpr int CPR = D / 8;
+  constexpr int RPI = 64 / CPR;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int r = t * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ swz<D>(r);
+    pat[t] = uint32_t((lane / CPR) * D * 2 + c * 16);
+  }
+}
+
 // Wait until at most N of this wave's vector memory operations are
 // outstanding and all its LDS operations are done, then barrier.  Raw
 // s_barrier: __syncthreads() adds a release fence that waits for every
