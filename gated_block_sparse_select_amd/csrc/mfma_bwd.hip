@@ -339,23 +339,20 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
   // half of the waves move Q slices, the others dO slices; every wave moves
   // the 256 B of row statistics of its row half (lane l: word l%32 of the
   // -lse/tau rows for l < 32, of the -D rows for l >= 32).
-  static_assert(JW % 4 == 0, "slice groups must start at a multiple of 4");
   int ie = 0, ih = 0;
   const bool q_side = wave * JW < JT;
   const int slice0 = (wave * JW) % JT;
   const size_t hstride = size_t(n) * D * 2;
   const char* src_base = reinterpret_cast<const char*>(q_side ? q : dO) +
-                         (size_t(b) * Hq + kv * G) * hstride + slice0 * 1024;
+                         (size_t(b) * Hq + kv * G) * hstride;
   const float* st_base = stats + (size_t(b) * Hq + kv * G) * size_t(nkb) * 128 + rh * 32 +
                          (lane >> 5) * 64 + (lane & 31);
   uint32_t pat[4];
-  dma_lane_pattern<D>(lane, pat);
+  dma_lane_pattern<D>(lane, slice0, pat);
   auto issue = [&]<int BUF>() __attribute__((always_inline)) {
     const int iq = __builtin_amdgcn_readfirstlane(meta[ie].x);
     const char* tile = src_base + size_t(ih) * hstride + size_t(iq) * SAS_BLK * D * 2;
-    lds_char* dst = (q_side ? stage_buf<TQ, BUF, TB>() : stage_buf<TO, BUF, TB>()) + slice0 * 1024;
-#pragma unroll
-    for (int u = 0; u < JW; ++u) dma16(tile + u * 1024 + pat[u & 3], dst + u * 1024);
+    dma_slices<JW>(tile, q_side ? stage_buf<TQ, BUF, TB>() : stage_buf<TO, BUF, TB>(), slice0, pat);
     __builtin_amdgcn_global_load_lds(
         (glb_void*)(st_base + (size_t(ih) * nkb + iq) * 128),
         (lds_void*)(stage_buf<TS, BUF, 1024>() + wave * 256), 4, 0, 0);

@@ -122,21 +122,31 @@ SAS_DEV void dma_tile_slice(const uint16_t* gtile, lds_char* ltile, int jj, int 
   dma16(gtile + r * D + c * 8, ltile + jj * 1024);
 }
 
-// Per-lane byte offset, inside a 1 KB slice of a swizzled 64 x D tile, of the
-// chunk lane `lane` moves for slices jj = t (mod 4): the swizzle of a slice's
-// rows depends on jj mod 4 only, so slice jj of a tile at global address g
-// is lane-wise g + 1024*jj + pat[jj % 4] (same logical chunk as
-// dma_tile_slice).
+// Per-lane byte offsets, inside a 1 KB slice of a swizzled 64 x D tile, of
+// the chunk lane `lane` moves (same logical chunk as dma_tile_slice).  The
+// swizzle of a slice's rows depends on the slice index mod 4 only, so slice
+// first + u of a tile at global address g is lane-wise
+// g + 1024*(first + u) + pat[u % 4].
 template <int D>
-SAS_DEV void dma_lane_pattern(int lane, uint32_t (&pat)[4]) {
+SAS_DEV void dma_lane_pattern(int lane, int first, uint32_t (&pat)[4]) {
   constexpr int CPR = D / 8;
   constexpr int RPI = 64 / CPR;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int r = t * RPI + lane / CPR;
+    const int r = (first + t) * RPI + lane / CPR;
     const int c = (lane % CPR) ^ swz<D>(r);
     pat[t] = uint32_t((lane / CPR) * D * 2 + c * 16);
   }
+}
+
+// A contiguous run of N slices, first .. first+N-1, of the tile at gtile
+// (wave-uniform) into the LDS tile ltile.
+template <int N>
+SAS_DEV void dma_slices(const void* gtile, lds_char* ltile, int first, const uint32_t (&pat)[4]) {
+  const char* g = reinterpret_cast<const char*>(gtile) + first * 1024;
+  lds_char* l = ltile + first * 1024;
+#pragma unroll
+  for (int u = 0; u < N; ++u) dma16(g + u * 1024 + pat[u & 3], l + u * 1024);
 }
 
 // Wait until at most N of this wave's vector memory operations are
