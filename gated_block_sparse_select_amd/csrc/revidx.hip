@@ -6,84 +6,114 @@
 // where slot is m's position in idx[i,:] (0xFFFF for the own block), so the
 // consumer can read that pair's log-gate directly.
 //
-// One workgroup per (batch, kv-head).  Counts come from LDS atomics (order
-// independent), offsets from a prefix sum, and the lists are filled in
-// ascending i from an LDS bitmap rebuilt per chunk of 128 q-blocks, so the
-// output is deterministic.
+// One workgroup per (batch, kv-head).  List lengths come from LDS atomics
+// (order independent) and a parallel prefix sum.  The lists are then filled
+// in chunks of 64 q-blocks: a 64-bit LDS mask per key block marks the rows of
+// the chunk that selected it, and each (row, slot) pair of the chunk writes
+// its entry at the list cursor plus the number of earlier rows in the mask,
+// so every list comes out ascending and the output is deterministic.
 #include "common.h"
 #include "launch.h"
 
 namespace sas {
 
 constexpr int kRevMaxNb = 2048;
-constexpr int kChunk = 128;               // q-blocks per bitmap chunk
-constexpr int kWords = kChunk / 32;
+constexpr int kRevThreads = 1024;
+constexpr int kChunkRows = 64;            // q-blocks per fill chunk (one mask bit each)
 
-__global__ void __launch_bounds__(1024) revidx_kernel(const int32_t* __restrict__ idx,
-                                                      const int32_t* __restrict__ cnt,
-                                                      int32_t* __restrict__ rev_off,
-                                                      int32_t* __restrict__ rev_list, int nb,
-                                                      int topk) {
+__global__ void __launch_bounds__(kRevThreads) revidx_kernel(const int32_t* __restrict__ idx,
+                                                            const int32_t* __restrict__ cnt,
+                                                            int32_t* __restrict__ rev_off,
+                                                            int32_t* __restrict__ rev_list,
+                                                            int nb, int topk) {
   __shared__ int32_t cursor[kRevMaxNb + 1];
-  __shared__ uint32_t bits[kRevMaxNb * kWords];
+  __shared__ unsigned long long rows[kRevMaxNb];
+  __shared__ int32_t wtot[kRevThreads / 64];
   const int bh = blockIdx.x;
   const int32_t* I = idx + size_t(bh) * nb * topk;
   const int32_t* C = cnt + size_t(bh) * nb;
   int32_t* off = rev_off + size_t(bh) * (nb + 1);
   int32_t* list = rev_list + size_t(bh) * nb * (topk + 1);
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wid = tid >> 6;
 
-  for (int m = tid; m <= nb; m += blockDim.x) cursor[m] = (m < nb) ? 1 : 0;
+  // list lengths: the own block plus every row that kept m
+  for (int m = tid; m <= nb; m += kRevThreads) cursor[m] = (m < nb) ? 1 : 0;
   __syncthreads();
-  for (int e = tid; e < nb * topk; e += blockDim.x) {
-    const int i = e / topk, sl = e % topk;
-    if (sl < C[i]) atomicAdd(&cursor[I[e]], 1);
-  }
-  __syncthreads();
-  // exclusive prefix sum over nb+1 entries (single thread: nb <= 2048)
-  if (tid == 0) {
-    int run = 0;
-    for (int m = 0; m <= nb; ++m) {
-      const int c = cursor[m];
-      cursor[m] = run;
-      run += c;
+  if (topk > 0) {
+    for (int e = tid; e < nb * topk; e += kRevThreads) {
+      const int i = e / topk, sl = e - i * topk;
+      if (sl < C[i]) atomicAdd(&cursor[I[e]], 1);
     }
   }
   __syncthreads();
-  for (int m = tid; m <= nb; m += blockDim.x) off[m] = cursor[m];
-  for (int m = tid; m < nb; m += blockDim.x) list[cursor[m]] = m | int32_t(0xFFFF0000u);
-  __syncthreads();
-  for (int m = tid; m < nb; m += blockDim.x) cursor[m] += 1;
 
-  for (int c0 = 0; c0 < nb; c0 += kChunk) {
-    for (int w = tid; w < nb * kWords; w += blockDim.x) bits[w] = 0u;
+  // exclusive prefix sum of cursor[0..nb]: PER consecutive entries per
+  // thread, an inclusive scan across each wave, then across the waves
+  constexpr int PER = (kRevMaxNb + 1 + kRevThreads - 1) / kRevThreads;
+  int v[PER], tot = 0;
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int j = tid * PER + p;
+    v[p] = j <= nb ? cursor[j] : 0;
+    tot += v[p];
+  }
+  int x = tot;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wtot[wid] = x;
+  __syncthreads();
+  if (wid == 0) {
+    int w = lane < kRevThreads / 64 ? wtot[lane] : 0;
+    int xs = w;
+#pragma unroll
+    for (int o = 1; o < kRevThreads / 64; o <<= 1) {
+      const int y = __shfl_up(xs, o);
+      if (lane >= o) xs += y;
+    }
+    if (lane < kRevThreads / 64) wtot[lane] = xs - w;   // exclusive over waves
+  }
+  __syncthreads();
+  int run = wtot[wid] + x - tot;
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int j = tid * PER + p;
+    if (j <= nb) cursor[j] = run;
+    run += v[p];
+  }
+  __syncthreads();
+  for (int m = tid; m <= nb; m += kRevThreads) {
+    off[m] = cursor[m];
+    if (m < nb) {
+      list[cursor[m]] = m | int32_t(0xFFFF0000u);
+      cursor[m] += 1;
+    }
+  }
+  __syncthreads();
+  if (topk == 0) return;
+
+  for (int c0 = 0; c0 < nb; c0 += kChunkRows) {
+    const int c1 = min(nb, c0 + kChunkRows);
+    for (int m = tid; m < nb; m += kRevThreads) rows[m] = 0ull;
     __syncthreads();
-    const int c1 = min(nb, c0 + kChunk);
-    for (int e = c0 * topk + tid; e < c1 * topk; e += blockDim.x) {
-      const int i = e / topk, sl = e % topk;
-      if (sl < C[i]) atomicOr(&bits[I[e] * kWords + (i - c0) / 32], 1u << ((i - c0) & 31));
+    for (int e = c0 * topk + tid; e < c1 * topk; e += kRevThreads) {
+      const int i = e / topk, sl = e - i * topk;
+      if (sl < C[i]) atomicOr(&rows[I[e]], 1ull << (i - c0));
     }
     __syncthreads();
-    for (int m = tid; m < nb; m += blockDim.x) {
-      int cur = cursor[m];
-      for (int w = 0; w < kWords; ++w) {
-        uint32_t x = bits[m * kWords + w];
-        while (x) {
-          const int bpos = __ffs(x) - 1;
-          x &= x - 1;
-          const int i = c0 + w * 32 + bpos;
-          // m's slot in the ascending row idx[i, 0..cnt)
-          int lo = 0, hi = C[i] - 1;
-          const int32_t* row = I + size_t(i) * topk;
-          while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (row[mid] < m) lo = mid + 1; else hi = mid;
-          }
-          list[cur++] = i | (lo << 16);
-        }
+    for (int e = c0 * topk + tid; e < c1 * topk; e += kRevThreads) {
+      const int i = e / topk, sl = e - i * topk;
+      if (sl < C[i]) {
+        const int m = I[e];
+        const unsigned long long before = rows[m] & ((1ull << (i - c0)) - 1ull);
+        list[cursor[m] + __popcll(before)] = i | (sl << 16);
       }
-      cursor[m] = cur;
     }
+    __syncthreads();
+    for (int m = tid; m < nb; m += kRevThreads) cursor[m] += __popcll(rows[m]);
     __syncthreads();
   }
 }
@@ -91,8 +121,8 @@ __global__ void __launch_bounds__(1024) revidx_kernel(const int32_t* __restrict_
 hipError_t launch_revidx(const int32_t* idx, const int32_t* cnt, int32_t* rev_off,
                          int32_t* rev_list, int BH, int nb, int topk, hipStream_t st) {
   ProfScope ps("sas_revidx_kernel", st);
-  hipLaunchKernelGGL(revidx_kernel, dim3(BH), dim3(1024), 0, st, idx, cnt, rev_off, rev_list, nb,
-                     topk);
+  hipLaunchKernelGGL(revidx_kernel, dim3(BH), dim3(kRevThreads), 0, st, idx, cnt, rev_off, rev_list,
+                     nb, topk);
   return hipGetLastError();
 }
 
