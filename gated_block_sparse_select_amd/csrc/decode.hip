@@ -19,7 +19,7 @@
 namespace sas {
 
 template <class E>
-struct Vec16;  // one 16-byte chunk of elements, unpacked to float
+struct Vec16;  // one 16-byte chunk of elements
 template <>
 struct Vec16<ElemBF16> {
   static constexpr int N = 8;
@@ -31,6 +31,16 @@ struct Vec16<ElemBF16> {
       o[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
     }
   }
+  // acc + dot(q, k) over the 8 elements, accumulated in float32
+  static SAS_DEV float dot(const uint4& q, const uint4& k, float acc) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf2;
+    const uint32_t qw[4] = {q.x, q.y, q.z, q.w}, kw[4] = {k.x, k.y, k.z, k.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, qw[e]),
+                                            __builtin_bit_cast(bf2, kw[e]), acc, false);
+    return acc;
+  }
 };
 template <>
 struct Vec16<ElemF32> {
@@ -39,11 +49,41 @@ struct Vec16<ElemF32> {
     o[0] = __uint_as_float(u.x); o[1] = __uint_as_float(u.y);
     o[2] = __uint_as_float(u.z); o[3] = __uint_as_float(u.w);
   }
+  static SAS_DEV float dot(const uint4& q, const uint4& k, float acc) {
+    acc = __builtin_fmaf(__uint_as_float(q.x), __uint_as_float(k.x), acc);
+    acc = __builtin_fmaf(__uint_as_float(q.y), __uint_as_float(k.y), acc);
+    acc = __builtin_fmaf(__uint_as_float(q.z), __uint_as_float(k.z), acc);
+    return __builtin_fmaf(__uint_as_float(q.w), __uint_as_float(k.w), acc);
+  }
 };
 
+// Sum over aligned groups of W lanes (W = 8, 16 or 32) with DPP lane
+// permutations: swap neighbours, swap pairs, mirror within 8, mirror within
+// 16 (then one swap across the two rows of 16 for W = 32).
+template <int CTRL>
+SAS_DEV float dpp_add(float x) {
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                           0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+template <int W>
+SAS_DEV float group_sum(float x) {
+  static_assert(W == 8 || W == 16 || W == 32, "group width");
+  x = dpp_add<0xB1>(x);     // quad_perm [1,0,3,2]
+  x = dpp_add<0x4E>(x);     // quad_perm [2,3,0,1]
+  x = dpp_add<0x141>(x);    // row_half_mirror
+  if (W >= 16) x = dpp_add<0x140>(x);   // row_mirror
+  if (W == 32) x += __shfl_xor(x, 16);
+  return x;
+}
+
 // grid: B*Hkv*nsplit workgroups of 256 threads.
-// Thread t owns element group dg = t % CPR (EPC elements) of keys
-// kg + (256/CPR)*u, u < KPT, in every tile.
+// Thread t owns chunk dg = t % CPR (EPC elements) of keys kg + KG*u, u < KPT,
+// of every tile, kg = t / CPR: a group of CPR lanes reads one key row (256 B
+// at d = 128 bf16) and the tile is one contiguous stretch of the cache.  Each
+// key group keeps its own online softmax (running max, sum, output chunk) for
+// all G heads, so tiles need no workgroup barrier; the next tile's K/V chunks
+// are loaded while the current one is computed.  The KG groups are merged
+// once, through LDS, at the end.
 template <class E, int D, int GMAX>
 __global__ void __launch_bounds__(256) decode_split_kernel(
     const typename E::T* __restrict__ q, const typename E::T* __restrict__ kc,
@@ -61,7 +101,6 @@ __global__ void __launch_bounds__(256) decode_split_kernel(
   const int G = Hq / Hkv;
   const int t = threadIdx.x;
   const int dg = t % CPR, kg = t / CPR;
-  const int wave = t >> 6;
 
   int L = seq_lens[b];
   L = L < 1 ? 1 : (L > cap ? cap : L);
@@ -71,133 +110,119 @@ __global__ void __launch_bounds__(256) decode_split_kernel(
   const int per = (ntiles + nsplit - 1) / nsplit;
   const int t0 = split * per, t1 = min(ntiles, t0 + per);
 
-  // query values of this thread's element group for all heads, pre-scaled by
-  // tau*log2(e) so scores are in the exp2 domain
-  float qv[GMAX][EPC];
+  // this thread's chunk of every head's query (scores are scaled by
+  // tau*log2(e) afterwards, so they are in the exp2 domain)
+  uint4 qv[GMAX];
 #pragma unroll
-  for (int g = 0; g < GMAX; ++g) {
-    if (g < G) {
-      const typename E::T* qp = q + (size_t(b) * Hq + kv * G + g) * D + dg * EPC;
-      float tmp[EPC];
-      Vec16<E>::unpack(*reinterpret_cast<const uint4*>(qp), tmp);
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) qv[g][e] = tmp[e] * tau2;
-    }
-  }
+  for (int g = 0; g < GMAX; ++g)
+    qv[g] = g < G ? *reinterpret_cast<const uint4*>(q + (size_t(b) * Hq + kv * G + g) * D + dg * EPC)
+                  : make_uint4(0u, 0u, 0u, 0u);
   float acc[GMAX][EPC];
-  float mrun[GMAX], lpart[GMAX];
+  float mrun[GMAX], lrun[GMAX];
 #pragma unroll
   for (int g = 0; g < GMAX; ++g) {
     mrun[g] = -INFINITY;
-    lpart[g] = 0.f;
+    lrun[g] = 0.f;
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[g][e] = 0.f;
   }
-  __shared__ float red[4][GMAX];
 
   const size_t cache0 = (size_t(b) * Hkv + kv) * size_t(cap) * D;
-  for (int tile = t0; tile < t1; ++tile) {
-    const int blk = tile < c_sel ? idx[size_t(bk) * topk + tile] : icur;
-    const float bias2 = tile < c_sel ? lg[size_t(bk) * topk + tile] * kLog2e : 0.f;
-    const int nvalid = tile < c_sel ? SAS_BLK : L - icur * SAS_BLK;
-    const typename E::T* kt = kc + cache0 + size_t(blk) * SAS_BLK * D;
-    const typename E::T* vt = vc + cache0 + size_t(blk) * SAS_BLK * D;
-    uint4 kr[KPT], vr[KPT];
+  const int32_t* irow = idx + size_t(bk) * topk;
+  const float* grow = lg + size_t(bk) * topk;
+  auto tile_block = [&](int tile) __attribute__((always_inline)) {
+    return tile < c_sel ? irow[tile] : icur;
+  };
+  uint4 kr[KPT], vr[KPT];
+  auto load = [&](int tile) __attribute__((always_inline)) {
+    const size_t base = cache0 + size_t(tile_block(tile)) * SAS_BLK * D;
+    const uint4* kt = reinterpret_cast<const uint4*>(kc + base);
+    const uint4* vt = reinterpret_cast<const uint4*>(vc + base);
 #pragma unroll
     for (int u = 0; u < KPT; ++u) {
-      const int c = u * 256 + t;  // chunk index inside the contiguous tile
-      kr[u] = reinterpret_cast<const uint4*>(kt)[c];
-      vr[u] = reinterpret_cast<const uint4*>(vt)[c];
+      kr[u] = kt[u * 256 + t];
+      vr[u] = vt[u * 256 + t];
     }
+  };
+  if (t0 < t1) load(t0);
+  for (int tile = t0; tile < t1; ++tile) {
+    uint4 kc_[KPT], vc_[KPT];
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      kc_[u] = kr[u];
+      vc_[u] = vr[u];
+    }
+    if (tile + 1 < t1) load(tile + 1);
+    const float bias2 = tile < c_sel ? grow[tile] * kLog2e : 0.f;
+    const int nvalid = tile < c_sel ? SAS_BLK : L - icur * SAS_BLK;
     float sc[KPT][GMAX];
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      float kx[EPC];
-      Vec16<E>::unpack(kr[u], kx);
+    for (int u = 0; u < KPT; ++u)
 #pragma unroll
-      for (int g = 0; g < GMAX; ++g) {
-        float a = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) a += qv[g][e] * kx[e];
-        sc[u][g] = a;
-      }
-    }
-    // sum over the CPR lanes holding one key row
-#pragma unroll
-    for (int o = 1; o < CPR; o <<= 1)
-#pragma unroll
-      for (int u = 0; u < KPT; ++u)
-#pragma unroll
-        for (int g = 0; g < GMAX; ++g) sc[u][g] += __shfl_xor(sc[u][g], o);
-    float tmax[GMAX];
-#pragma unroll
-    for (int g = 0; g < GMAX; ++g) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int u = 0; u < KPT; ++u) {
-        const int key = kg + KG * u;
-        sc[u][g] = key < nvalid ? sc[u][g] + bias2 : -INFINITY;
-        mx = fmaxf(mx, sc[u][g]);
-      }
-      for (int o = CPR; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-      tmax[g] = mx;
-    }
-    __syncthreads();
-    if ((t & 63) == 0)
-#pragma unroll
-      for (int g = 0; g < GMAX; ++g) red[wave][g] = tmax[g];
-    __syncthreads();
+      for (int g = 0; g < GMAX; ++g) sc[u][g] = group_sum<CPR>(Vec16<E>::dot(qv[g], kc_[u], 0.f));
 #pragma unroll
     for (int g = 0; g < GMAX; ++g) {
       if (g >= G) continue;
-      const float mt = fmaxf(fmaxf(red[0][g], red[1][g]), fmaxf(red[2][g], red[3][g]));
+      float mt = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < KPT; ++u) {
+        sc[u][g] = kg + KG * u < nvalid ? __builtin_fmaf(sc[u][g], tau2, bias2) : -INFINITY;
+        mt = fmaxf(mt, sc[u][g]);
+      }
+      if (mt == -INFINITY) continue;   // no valid key of this group in the tile
       const float mnew = fmaxf(mrun[g], mt);
       const float corr = exp2f(mrun[g] - mnew);
       mrun[g] = mnew;
-      lpart[g] *= corr;
+      lrun[g] *= corr;
 #pragma unroll
       for (int e = 0; e < EPC; ++e) acc[g][e] *= corr;
 #pragma unroll
       for (int u = 0; u < KPT; ++u) {
         const float p = exp2f(sc[u][g] - mnew);
-        lpart[g] += p;
+        lrun[g] += p;
         float vx[EPC];
-        Vec16<E>::unpack(vr[u], vx);
+        Vec16<E>::unpack(vc_[u], vx);
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[g][e] += p * vx[e];
+        for (int e = 0; e < EPC; ++e) acc[g][e] = __builtin_fmaf(p, vx[e], acc[g][e]);
       }
     }
   }
-  // reduce acc / lpart over the KG key groups that share an element group
-  __shared__ float racc[GMAX][D];
-  __shared__ float rl[GMAX];
-  for (int x = t; x < GMAX * D; x += 256) racc[x / D][x % D] = 0.f;
-  if (t < GMAX) rl[t] = 0.f;
+
+  // merge the KG key groups: M = max of the group maxima, each group's sum
+  // and output chunk scaled by 2^(m_k - M)
+  __shared__ float sm[KG][GMAX], sl[KG][GMAX];
+  __shared__ float sacc[KG][GMAX][D];
+#pragma unroll
+  for (int g = 0; g < GMAX; ++g) {
+    if (g >= G) continue;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) sacc[kg][g][dg * EPC + e] = acc[g][e];
+    if (dg == 0) {
+      sm[kg][g] = mrun[g];
+      sl[kg][g] = lrun[g];
+    }
+  }
   __syncthreads();
-  for (int k2 = 0; k2 < KG; ++k2) {
-    if (kg == k2) {
-#pragma unroll
-      for (int g = 0; g < GMAX; ++g) {
-        if (g >= G) continue;
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) racc[g][dg * EPC + e] += acc[g][e];
-        if (dg == 0) rl[g] += lpart[g];
-      }
-    }
-    __syncthreads();
-  }
   for (int x = t; x < G * D; x += 256) {
     const int g = x / D, c = x % D;
-    part_acc[((size_t(b) * Hq + kv * G + g) * nsplit + split) * D + c] = racc[g][c];
-  }
-  if (t == 0) {
-    // thread 0 holds the workgroup-wide running max of every head
+    float M = -INFINITY;
 #pragma unroll
-    for (int g = 0; g < GMAX; ++g) {
-      if (g >= G) continue;
-      const size_t pi = ((size_t(b) * Hq + kv * G + g) * nsplit + split) * 2;
-      part_ml[pi] = (t0 < t1) ? mrun[g] : -INFINITY;
-      part_ml[pi + 1] = rl[g];
+    for (int k = 0; k < KG; ++k) M = fmaxf(M, sm[k][g]);
+    float a = 0.f, l = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int k = 0; k < KG; ++k) {
+        if (sm[k][g] == -INFINITY) continue;
+        const float w = exp2f(sm[k][g] - M);
+        a = __builtin_fmaf(w, sacc[k][g][c], a);
+        l = __builtin_fmaf(w, sl[k][g], l);
+      }
+    }
+    const size_t pb = (size_t(b) * Hq + kv * G + g) * nsplit + split;
+    part_acc[pb * D + c] = a;
+    if (c == 0) {
+      part_ml[pb * 2] = M;
+      part_ml[pb * 2 + 1] = l;
     }
   }
 }
