@@ -6,7 +6,8 @@
 // with m = j*64 + lane, so scanning j ascending and lanes ascending visits m in
 // ascending order.  Each candidate gets a 32-bit order-preserving key of its
 // float value (-0.0 canonicalised to +0.0); a 32-step bitwise search with wave
-// population counts finds the K-th largest key T exactly; all keys > T are
+// population counts (ballots, so the counting stays in scalar registers)
+// finds the K-th largest key T exactly; all keys > T are
 // kept, and keys == T are kept lowest index first until K blocks are chosen.
 // The kept blocks are then compacted in ascending order with ballots.  Every
 // comparison is on the exact float bits, so the result is bit-identical to a
@@ -22,7 +23,7 @@ SAS_DEV uint32_t order_key(float x) {
 }
 
 template <int CPL>
-__global__ void __launch_bounds__(256) select_kernel(const float* __restrict__ s,
+__global__ void __launch_bounds__(64) select_kernel(const float* __restrict__ s,
                                                      int32_t* __restrict__ idx,
                                                      int32_t* __restrict__ cnt,
                                                      float* __restrict__ lg,
@@ -30,9 +31,8 @@ __global__ void __launch_bounds__(256) select_kernel(const float* __restrict__ s
                                                      int nqb, int nkb, int topk,
                                                      const int32_t* __restrict__ seq_lens,
                                                      int hkv, int cap) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  const int lane = threadIdx.x;
+  const int row = blockIdx.x;
   int i;
   if (seq_lens) {
     int L = seq_lens[row / hkv];
@@ -70,14 +70,13 @@ __global__ void __launch_bounds__(256) select_kernel(const float* __restrict__ s
       const uint32_t c = T | (1u << bit);
       int n_ge = 0;
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) n_ge += key[j] >= c;
-      n_ge = wave_sum_i(n_ge);
+      for (int j = 0; j < CPL; ++j) n_ge += __popcll(__ballot(key[j] >= c));
       if (n_ge >= keff) T = c;
     }
     int n_gt = 0;
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) n_gt += key[j] > T;
-    need_eq = keff - wave_sum_i(n_gt);
+    for (int j = 0; j < CPL; ++j) n_gt += __popcll(__ballot(key[j] > T));
+    need_eq = keff - n_gt;
   }
 
   int32_t* irow = idx ? idx + size_t(row) * topk : nullptr;
@@ -118,8 +117,8 @@ __global__ void __launch_bounds__(256) select_kernel(const float* __restrict__ s
 template <int CPL>
 static void go(const float* s, int32_t* idx, int32_t* cnt, float* lg, float* slse, int rows,
                int nqb, int nkb, int topk, const int32_t* sl, int hkv, int cap, hipStream_t st) {
-  hipLaunchKernelGGL(select_kernel<CPL>, dim3((rows + 3) / 4), dim3(256), 0, st, s, idx, cnt, lg,
-                     slse, rows, nqb, nkb, topk, sl, hkv, cap);
+  hipLaunchKernelGGL(select_kernel<CPL>, dim3(rows), dim3(64), 0, st, s, idx, cnt, lg, slse, rows,
+                     nqb, nkb, topk, sl, hkv, cap);
 }
 
 hipError_t launch_select(const float* s, int32_t* idx, int32_t* cnt, float* lg, float* slse,
