@@ -113,9 +113,9 @@ KERNEL_SOURCES = {
     "sas_bwd_dkdv_kernel": ["mfma_bwd.hip", "mfma_common.h", "common.h", "launch.h"],
     "sas_bwd_dq_kernel": ["mfma_bwd.hip", "mfma_common.h", "common.h", "launch.h"],
     "sas_fwd_mfma_kernel": ["mfma_fwd.hip", "mfma_common.h", "common.h", "launch.h"],
-    "sas_decode_split_kernel": ["decode.hip", "common.h", "launch.h"],
+    "sas_decode_kernel": ["decode.hip", "select_row.h", "common.h", "launch.h"],
     "sas_pool_means_kernel": ["pool.hip", "common.h", "launch.h"],
-    "sas_select_kernel": ["select.hip", "common.h", "launch.h"],
+    "sas_select_kernel": ["select.hip", "select_row.h", "common.h", "launch.h"],
 }
 
 
@@ -227,15 +227,15 @@ def run_decode(args, api, si, torch, np):
     other = q.numel() * 2 * 2 + s.numel() * 4 + idx.numel() * 4 + w.B * 4
     alg = kv_bytes + other
     per_kernel = {n: dict(avg_us=round(t * 1e3 / max(c, 1), 2), launches=c) for n, (t, c) in kern.items()}
-    split = per_kernel.get("sas_decode_split_kernel", {}).get("avg_us")
+    split = per_kernel.get("sas_decode_kernel", {}).get("avg_us")
     out = dict(workload=w.name, us_per_call=round(us, 2), algorithmic_bytes=alg,
                GBs=round(alg / (us * 1e-6) / 1e9, 1),
                frac_hbm=round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), per_kernel=per_kernel)
     if split:
         gbs = kv_bytes / (split * 1e-6) / 1e9
-        out["roofline"] = dict(bound="hbm", kernel="sas_decode_split_kernel", achieved=round(gbs, 1),
+        out["roofline"] = dict(bound="hbm", kernel="sas_decode_kernel", achieved=round(gbs, 1),
                                peak=HBM_PEAK_GBS, unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4),
-                               traffic=measured_traffic("sas_decode_split_kernel"),
+                               traffic=measured_traffic("sas_decode_kernel"),
                                algorithmic_bytes=kv_bytes, avg_us=split)
     del kc, vc
     torch.cuda.empty_cache()

@@ -32,6 +32,10 @@ struct ElemBF16 {
   static SAS_DEV void st(T* p, float v) { *p = f32_to_bf16(v); }
 };
 
+// 2^x on the transcendental unit without the denormal range fix-up of exp2f
+// (softmax weights below 2^-126 flush to zero, which is harmless).
+SAS_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // ------------------------------------------------------------- wave64 reductions
 SAS_DEV float wave_max(float v) {
 #pragma unroll

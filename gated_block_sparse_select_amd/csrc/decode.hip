@@ -7,16 +7,20 @@
 //
 // The step is HBM-bound (one pass over the kept K/V tiles), so it runs on the
 // vector units with perfectly coalesced 16-byte loads: a 64-token tile of one
-// kv-head is one contiguous 64*d element chunk of the cache.
-//   1. select (select.hip, decode rows) -> idx / log-gate in the workspace;
-//   2. split kernel: grid (b, kv, split); each workgroup streams a contiguous
-//      range of the (cnt+1) tiles for all G query heads of the group and
-//      writes an unnormalised partial (acc, running max, running sum);
-//   3. combine kernel: merges the splits per query head.
+// kv-head is one contiguous 64*d element chunk of the cache.  One kernel does
+// the whole step for a (b, kv-group, split): wave 0 selects the row's blocks
+// into LDS (select_row), then the workgroup streams its share of the kept
+// tiles plus the current block with two tiles of loads in flight.  When one
+// workgroup covers a whole row (enough rows to fill the GPU) it writes o
+// directly; otherwise it writes an unnormalised partial (output, max, sum)
+// and a combine kernel merges the splits.
 #include "common.h"
 #include "launch.h"
+#include "sas.h"
+#include "select_row.h"
 
 namespace sas {
+
 
 template <class E>
 struct Vec16;  // one 16-byte chunk of elements
@@ -81,16 +85,17 @@ SAS_DEV float group_sum(float x) {
 // of every tile, kg = t / CPR: a group of CPR lanes reads one key row (256 B
 // at d = 128 bf16) and the tile is one contiguous stretch of the cache.  Each
 // key group keeps its own online softmax (running max, sum, output chunk) for
-// all G heads, so tiles need no workgroup barrier; the next tile's K/V chunks
-// are loaded while the current one is computed.  The KG groups are merged
-// once, through LDS, at the end.
-template <class E, int D, int GMAX>
-__global__ void __launch_bounds__(256) decode_split_kernel(
+// all G heads, so tiles need no workgroup barrier.  Three register buffers
+// rotate (the tile loop is unrolled by 3) so that the loads of the next two
+// tiles are in flight while one is computed.  The KG groups are merged once,
+// through LDS, at the end.
+template <class E, int D, int GMAX, int CPL>
+__global__ void __launch_bounds__(256) decode_kernel(
     const typename E::T* __restrict__ q, const typename E::T* __restrict__ kc,
     const typename E::T* __restrict__ vc, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
-    const float* __restrict__ lg, float* __restrict__ part_acc, float* __restrict__ part_ml,
-    int Hq, int Hkv, int cap, int topk, int nsplit, float tau2) {
+    const float* __restrict__ s, int32_t* __restrict__ idx_out, typename E::T* __restrict__ o,
+    float* __restrict__ part_acc, float* __restrict__ part_ml, int Hq, int Hkv, int cap, int topk,
+    int nsplit, float tau2) {
   constexpr int EPC = Vec16<E>::N;        // elements per 16-byte chunk
   constexpr int CPR = D / EPC;            // chunks per key row
   constexpr int KG = 256 / CPR;           // key groups per workgroup
@@ -101,14 +106,11 @@ __global__ void __launch_bounds__(256) decode_split_kernel(
   const int G = Hq / Hkv;
   const int t = threadIdx.x;
   const int dg = t % CPR, kg = t / CPR;
+  const int wave = t >> 6, lane = t & 63;
 
   int L = seq_lens[b];
   L = L < 1 ? 1 : (L > cap ? cap : L);
   const int icur = (L - 1) / SAS_BLK;
-  const int c_sel = cnt[bk];
-  const int ntiles = c_sel + 1;
-  const int per = (ntiles + nsplit - 1) / nsplit;
-  const int t0 = split * per, t1 = min(ntiles, t0 + per);
 
   // this thread's chunk of every head's query (scores are scaled by
   // tau*log2(e) afterwards, so they are in the exp2 domain)
@@ -117,6 +119,30 @@ __global__ void __launch_bounds__(256) decode_split_kernel(
   for (int g = 0; g < GMAX; ++g)
     qv[g] = g < G ? *reinterpret_cast<const uint4*>(q + (size_t(b) * Hq + kv * G + g) * D + dg * EPC)
                   : make_uint4(0u, 0u, 0u, 0u);
+
+  // selection of this row: kept blocks and base-2 log-gates in LDS
+  __shared__ int32_t sblk[SAS_MAX_BLOCKS];
+  __shared__ float sgate[SAS_MAX_BLOCKS];
+  __shared__ int scnt;
+  if (wave == 0) {
+    int32_t* orow = (idx_out != nullptr && split == 0) ? idx_out + size_t(bk) * topk : nullptr;
+    float lse;
+    const int keff = select_row<CPL>(s + size_t(bk) * (cap / SAS_BLK), icur, topk, lane, lse,
+                                     [&](int pos, int m, float g) {
+                                       sblk[pos] = m;
+                                       sgate[pos] = g * kLog2e;
+                                       if (orow) orow[pos] = m;
+                                     });
+    if (orow)
+      for (int p = keff + lane; p < topk; p += 64) orow[p] = -1;
+    if (lane == 0) scnt = keff;
+  }
+  __syncthreads();
+  const int c_sel = scnt;
+  const int ntiles = c_sel + 1;
+  const int per = (ntiles + nsplit - 1) / nsplit;
+  const int t0 = split * per, t1 = min(ntiles, t0 + per);
+
   float acc[GMAX][EPC];
   float mrun[GMAX], lrun[GMAX];
 #pragma unroll
@@ -128,38 +154,27 @@ __global__ void __launch_bounds__(256) decode_split_kernel(
   }
 
   const size_t cache0 = (size_t(b) * Hkv + kv) * size_t(cap) * D;
-  const int32_t* irow = idx + size_t(bk) * topk;
-  const float* grow = lg + size_t(bk) * topk;
-  auto tile_block = [&](int tile) __attribute__((always_inline)) {
-    return tile < c_sel ? irow[tile] : icur;
-  };
-  uint4 kr[KPT], vr[KPT];
-  auto load = [&](int tile) __attribute__((always_inline)) {
-    const size_t base = cache0 + size_t(tile_block(tile)) * SAS_BLK * D;
+  uint4 kb[3][KPT], vb[3][KPT];
+  auto load = [&]<int B>(int tile) __attribute__((always_inline)) {
+    const int blk = tile < c_sel ? sblk[tile] : icur;
+    const size_t base = cache0 + size_t(blk) * SAS_BLK * D;
     const uint4* kt = reinterpret_cast<const uint4*>(kc + base);
     const uint4* vt = reinterpret_cast<const uint4*>(vc + base);
 #pragma unroll
     for (int u = 0; u < KPT; ++u) {
-      kr[u] = kt[u * 256 + t];
-      vr[u] = vt[u * 256 + t];
+      kb[B][u] = kt[u * 256 + t];
+      vb[B][u] = vt[u * 256 + t];
     }
   };
-  if (t0 < t1) load(t0);
-  for (int tile = t0; tile < t1; ++tile) {
-    uint4 kc_[KPT], vc_[KPT];
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      kc_[u] = kr[u];
-      vc_[u] = vr[u];
-    }
-    if (tile + 1 < t1) load(tile + 1);
-    const float bias2 = tile < c_sel ? grow[tile] * kLog2e : 0.f;
+  auto compute = [&]<int B>(int tile) __attribute__((always_inline)) {
+    const float bias2 = tile < c_sel ? sgate[tile] : 0.f;
     const int nvalid = tile < c_sel ? SAS_BLK : L - icur * SAS_BLK;
     float sc[KPT][GMAX];
 #pragma unroll
     for (int u = 0; u < KPT; ++u)
 #pragma unroll
-      for (int g = 0; g < GMAX; ++g) sc[u][g] = group_sum<CPR>(Vec16<E>::dot(qv[g], kc_[u], 0.f));
+      for (int g = 0; g < GMAX; ++g)
+        sc[u][g] = g < G ? group_sum<CPR>(Vec16<E>::dot(qv[g], kb[B][u], 0.f)) : 0.f;
 #pragma unroll
     for (int g = 0; g < GMAX; ++g) {
       if (g >= G) continue;
@@ -171,22 +186,36 @@ __global__ void __launch_bounds__(256) decode_split_kernel(
       }
       if (mt == -INFINITY) continue;   // no valid key of this group in the tile
       const float mnew = fmaxf(mrun[g], mt);
-      const float corr = exp2f(mrun[g] - mnew);
+      const float corr = fast_exp2(mrun[g] - mnew);
       mrun[g] = mnew;
       lrun[g] *= corr;
 #pragma unroll
       for (int e = 0; e < EPC; ++e) acc[g][e] *= corr;
 #pragma unroll
       for (int u = 0; u < KPT; ++u) {
-        const float p = exp2f(sc[u][g] - mnew);
+        const float p = fast_exp2(sc[u][g] - mnew);
         lrun[g] += p;
         float vx[EPC];
-        Vec16<E>::unpack(vc_[u], vx);
+        Vec16<E>::unpack(vb[B][u], vx);
 #pragma unroll
         for (int e = 0; e < EPC; ++e) acc[g][e] = __builtin_fmaf(p, vx[e], acc[g][e]);
       }
     }
+  };
+  if (t0 < t1) load.template operator()<0>(t0);
+  if (t0 + 1 < t1) load.template operator()<1>(t0 + 1);
+  if (t0 + 2 < t1) load.template operator()<2>(t0 + 2);
+  int tile = t0;
+  for (; tile + 3 <= t1; tile += 3) {
+    compute.template operator()<0>(tile);
+    if (tile + 3 < t1) load.template operator()<0>(tile + 3);
+    compute.template operator()<1>(tile + 1);
+    if (tile + 4 < t1) load.template operator()<1>(tile + 4);
+    compute.template operator()<2>(tile + 2);
+    if (tile + 5 < t1) load.template operator()<2>(tile + 5);
   }
+  if (tile < t1) compute.template operator()<0>(tile);
+  if (tile + 1 < t1) compute.template operator()<1>(tile + 1);
 
   // merge the KG key groups: M = max of the group maxima, each group's sum
   // and output chunk scaled by 2^(m_k - M)
@@ -213,16 +242,21 @@ __global__ void __launch_bounds__(256) decode_split_kernel(
 #pragma unroll
       for (int k = 0; k < KG; ++k) {
         if (sm[k][g] == -INFINITY) continue;
-        const float w = exp2f(sm[k][g] - M);
+        const float w = fast_exp2(sm[k][g] - M);
         a = __builtin_fmaf(w, sacc[k][g][c], a);
         l = __builtin_fmaf(w, sl[k][g], l);
       }
     }
-    const size_t pb = (size_t(b) * Hq + kv * G + g) * nsplit + split;
-    part_acc[pb * D + c] = a;
-    if (c == 0) {
-      part_ml[pb * 2] = M;
-      part_ml[pb * 2 + 1] = l;
+    const size_t bh = size_t(b) * Hq + kv * G + g;
+    if (nsplit == 1) {
+      E::st(o + bh * D + c, a / l);   // the current block always has a valid key
+    } else {
+      const size_t pb = bh * nsplit + split;
+      part_acc[pb * D + c] = a;
+      if (c == 0) {
+        part_ml[pb * 2] = M;
+        part_ml[pb * 2 + 1] = l;
+      }
     }
   }
 }
@@ -241,7 +275,7 @@ __global__ void __launch_bounds__(128) decode_combine_kernel(const float* __rest
   for (int sp = 0; sp < nsplit; ++sp) {
     const float m = part_ml[(bh * nsplit + sp) * 2];
     if (m == -INFINITY) continue;
-    const float w = exp2f(m - M);
+    const float w = fast_exp2(m - M);
     l += w * part_ml[(bh * nsplit + sp) * 2 + 1];
     a += w * part_acc[(bh * nsplit + sp) * D + c];
   }
@@ -249,55 +283,63 @@ __global__ void __launch_bounds__(128) decode_combine_kernel(const float* __rest
 }
 
 int decode_nsplit(int B, int Hkv, int topk) {
+  // one workgroup per row when there are enough rows to fill the GPU (two
+  // per CU); otherwise split each row's tiles over several workgroups
   const int pairs = B * Hkv;
-  int ns = (2048 + pairs - 1) / pairs;
+  int ns = (512 + pairs - 1) / pairs;
   if (ns > topk + 1) ns = topk + 1;
   if (ns < 1) ns = 1;
   return ns;
 }
 
-template <class E, int D, int GMAX>
-static void split_go(const void* q, const void* kc, const void* vc, const int32_t* sl,
-                     const int32_t* idx, const int32_t* cnt, const float* lg, float* pa,
-                     float* pm, int B, int Hq, int Hkv, int cap, int topk, int ns, float tau2,
-                     hipStream_t st) {
+template <class E, int D, int GMAX, int CPL>
+static void dec_go(const void* q, const void* kc, const void* vc, const int32_t* sl,
+                   const float* s, int32_t* idx_out, void* o, float* pa, float* pm, int B,
+                   int Hq, int Hkv, int cap, int topk, int ns, float tau2, hipStream_t st) {
   using T = typename E::T;
-  hipLaunchKernelGGL((decode_split_kernel<E, D, GMAX>), dim3(B * Hkv * ns), dim3(256), 0, st,
-                     (const T*)q, (const T*)kc, (const T*)vc, sl, idx, cnt, lg, pa, pm, Hq, Hkv,
-                     cap, topk, ns, tau2);
+  hipLaunchKernelGGL((decode_kernel<E, D, GMAX, CPL>), dim3(B * Hkv * ns), dim3(256), 0, st,
+                     (const T*)q, (const T*)kc, (const T*)vc, sl, s, idx_out, (T*)o, pa, pm, Hq,
+                     Hkv, cap, topk, ns, tau2);
+}
+
+template <class E, int D, int CPL>
+static void dec_g(int G, const void* q, const void* kc, const void* vc, const int32_t* sl,
+                  const float* s, int32_t* idx_out, void* o, float* pa, float* pm, int B, int Hq,
+                  int Hkv, int cap, int topk, int ns, float tau2, hipStream_t st) {
+  if (G <= 4) dec_go<E, D, 4, CPL>(q, kc, vc, sl, s, idx_out, o, pa, pm, B, Hq, Hkv, cap, topk, ns, tau2, st);
+  else if (G <= 8) dec_go<E, D, 8, CPL>(q, kc, vc, sl, s, idx_out, o, pa, pm, B, Hq, Hkv, cap, topk, ns, tau2, st);
+  else dec_go<E, D, 16, CPL>(q, kc, vc, sl, s, idx_out, o, pa, pm, B, Hq, Hkv, cap, topk, ns, tau2, st);
 }
 
 template <class E, int D>
-static void split_g(int G, const void* q, const void* kc, const void* vc, const int32_t* sl,
-                    const int32_t* idx, const int32_t* cnt, const float* lg, float* pa, float* pm,
-                    int B, int Hq, int Hkv, int cap, int topk, int ns, float tau2,
-                    hipStream_t st) {
-  if (G <= 1) split_go<E, D, 1>(q, kc, vc, sl, idx, cnt, lg, pa, pm, B, Hq, Hkv, cap, topk, ns, tau2, st);
-  else if (G <= 2) split_go<E, D, 2>(q, kc, vc, sl, idx, cnt, lg, pa, pm, B, Hq, Hkv, cap, topk, ns, tau2, st);
-  else if (G <= 4) split_go<E, D, 4>(q, kc, vc, sl, idx, cnt, lg, pa, pm, B, Hq, Hkv, cap, topk, ns, tau2, st);
-  else if (G <= 8) split_go<E, D, 8>(q, kc, vc, sl, idx, cnt, lg, pa, pm, B, Hq, Hkv, cap, topk, ns, tau2, st);
-  else split_go<E, D, 16>(q, kc, vc, sl, idx, cnt, lg, pa, pm, B, Hq, Hkv, cap, topk, ns, tau2, st);
+static void dec_c(int G, const void* q, const void* kc, const void* vc, const int32_t* sl,
+                  const float* s, int32_t* idx_out, void* o, float* pa, float* pm, int B, int Hq,
+                  int Hkv, int cap, int topk, int ns, float tau2, hipStream_t st) {
+  // candidates per lane of the select: history rows hold up to cap/64 - 1 blocks
+  if (select_cpl(cap / SAS_BLK) <= 8)
+    dec_g<E, D, 8>(G, q, kc, vc, sl, s, idx_out, o, pa, pm, B, Hq, Hkv, cap, topk, ns, tau2, st);
+  else
+    dec_g<E, D, 32>(G, q, kc, vc, sl, s, idx_out, o, pa, pm, B, Hq, Hkv, cap, topk, ns, tau2, st);
 }
 
 hipError_t launch_decode(int dtype, const void* q, const void* kc, const void* vc,
-                         const int32_t* seq_lens, const int32_t* idx, const int32_t* cnt,
-                         const float* lg, float* part_acc, float* part_ml, void* o, int B, int Hq,
-                         int Hkv, int cap, int d, int topk, int nsplit, float tau,
-                         hipStream_t st) {
+                         const int32_t* seq_lens, const float* s, int32_t* idx_out,
+                         float* part_acc, float* part_ml, void* o, int B, int Hq, int Hkv,
+                         int cap, int d, int topk, int nsplit, float tau, hipStream_t st) {
   const int G = Hq / Hkv;
   const float tau2 = tau * kLog2e;
   {
-    ProfScope ps("sas_decode_split_kernel", st);
+    ProfScope ps("sas_decode_kernel", st);
     if (dtype == 1) {
-      if (d == 128) split_g<ElemBF16, 128>(G, q, kc, vc, seq_lens, idx, cnt, lg, part_acc, part_ml, B, Hq, Hkv, cap, topk, nsplit, tau2, st);
-      else split_g<ElemBF16, 64>(G, q, kc, vc, seq_lens, idx, cnt, lg, part_acc, part_ml, B, Hq, Hkv, cap, topk, nsplit, tau2, st);
+      if (d == 128) dec_c<ElemBF16, 128>(G, q, kc, vc, seq_lens, s, idx_out, o, part_acc, part_ml, B, Hq, Hkv, cap, topk, nsplit, tau2, st);
+      else dec_c<ElemBF16, 64>(G, q, kc, vc, seq_lens, s, idx_out, o, part_acc, part_ml, B, Hq, Hkv, cap, topk, nsplit, tau2, st);
     } else {
-      if (d == 128) split_g<ElemF32, 128>(G, q, kc, vc, seq_lens, idx, cnt, lg, part_acc, part_ml, B, Hq, Hkv, cap, topk, nsplit, tau2, st);
-      else split_g<ElemF32, 64>(G, q, kc, vc, seq_lens, idx, cnt, lg, part_acc, part_ml, B, Hq, Hkv, cap, topk, nsplit, tau2, st);
+      if (d == 128) dec_c<ElemF32, 128>(G, q, kc, vc, seq_lens, s, idx_out, o, part_acc, part_ml, B, Hq, Hkv, cap, topk, nsplit, tau2, st);
+      else dec_c<ElemF32, 64>(G, q, kc, vc, seq_lens, s, idx_out, o, part_acc, part_ml, B, Hq, Hkv, cap, topk, nsplit, tau2, st);
     }
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || nsplit == 1) return e;
   {
     ProfScope ps("sas_decode_combine_kernel", st);
     if (dtype == 1) {

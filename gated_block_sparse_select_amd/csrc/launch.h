@@ -52,9 +52,8 @@ hipError_t launch_bwd_simt(int dtype, const void* q, const void* k, const void* 
 // ---- decode (decode.hip)
 int decode_nsplit(int B, int Hkv, int topk);
 hipError_t launch_decode(int dtype, const void* q, const void* kc, const void* vc,
-                         const int32_t* seq_lens, const int32_t* idx, const int32_t* cnt,
-                         const float* lg, float* part_acc, float* part_ml, void* o, int B, int Hq,
-                         int Hkv, int cap, int d, int topk, int nsplit, float tau,
-                         hipStream_t st);
+                         const int32_t* seq_lens, const float* s, int32_t* idx_out,
+                         float* part_acc, float* part_ml, void* o, int B, int Hq, int Hkv,
+                         int cap, int d, int topk, int nsplit, float tau, hipStream_t st);
 
 }  // namespace sas

@@ -274,9 +274,6 @@ SAS_DEV void row_offsets(int lane, int (&off)[D / 16]) {
   for (int c = 0; c < D / 16; ++c) off[c] = tile_off<D>(lr, 2 * c + hh) & int(kLdsAddrMask);
 }
 
-// 2^x on the transcendental unit without the denormal range fix-up of exp2f
-// (softmax weights below 2^-126 flush to zero, which is harmless).
-SAS_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 

@@ -94,22 +94,19 @@ BwdWs bwd_layout(const sas_shape* s) {
 }
 
 // ----------------------------------------------------------- decode workspace
+// Partial outputs (and per-split max / sum) when a row's tiles are split over
+// several workgroups; a small minimum otherwise.
 struct DecWs {
-  size_t idx_off, cnt_off, lg_off, lse_off, acc_off, ml_off, total;
+  size_t acc_off, ml_off, total;
   int nsplit;
 };
 DecWs dec_layout(const sas_decode_shape* s) {
-  const size_t BH = size_t(s->B) * s->Hkv;
-  const size_t K = size_t(s->topk > 0 ? s->topk : 1);
   DecWs w{};
   w.nsplit = sas::decode_nsplit(s->B, s->Hkv, s->topk);
-  w.idx_off = 0;
-  w.cnt_off = align_up(w.idx_off + sizeof(int32_t) * BH * K);
-  w.lg_off = align_up(w.cnt_off + sizeof(int32_t) * BH);
-  w.lse_off = align_up(w.lg_off + sizeof(float) * BH * K);
-  w.acc_off = align_up(w.lse_off + sizeof(float) * BH);
-  w.ml_off = align_up(w.acc_off + sizeof(float) * size_t(s->B) * s->Hq * w.nsplit * s->d);
-  w.total = align_up(w.ml_off + sizeof(float) * size_t(s->B) * s->Hq * w.nsplit * 2);
+  const size_t parts = w.nsplit > 1 ? size_t(s->B) * s->Hq * w.nsplit : 0;
+  w.acc_off = 0;
+  w.ml_off = align_up(w.acc_off + sizeof(float) * parts * s->d);
+  w.total = align_up(w.ml_off + sizeof(float) * parts * 2 + 1);
   return w;
 }
 
@@ -272,19 +269,11 @@ sas_status sas_decode(const sas_decode_shape* s, const void* q, const void* k_ca
   const DecWs w = dec_layout(s);
   if (!ws || ws_bytes < w.total) return SAS_ERR_WORKSPACE;
   char* base = static_cast<char*>(ws);
-  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + w.idx_off);
-  int32_t* cnt = reinterpret_cast<int32_t*>(base + w.cnt_off);
-  float* lg = reinterpret_cast<float*>(base + w.lg_off);
-  float* lse = reinterpret_cast<float*>(base + w.lse_off);
   float* acc = reinterpret_cast<float*>(base + w.acc_off);
   float* ml = reinterpret_cast<float*>(base + w.ml_off);
-  const int nb = s->cap / SAS_BLOCK;
   clear_stale_error();
-  hipError_t e = sas::launch_select(sc, idx, cnt, lg, lse, s->B * s->Hkv, nb, nb, s->topk,
-                                    seq_lens, s->Hkv, s->cap, stream);
-  if (e != hipSuccess) return from_hip(e);
-  return from_hip(sas::launch_decode(s->dtype, q, k_cache, v_cache, seq_lens, idx, cnt, lg, acc,
-                                     ml, o, s->B, s->Hq, s->Hkv, s->cap, s->d, s->topk, w.nsplit,
+  return from_hip(sas::launch_decode(s->dtype, q, k_cache, v_cache, seq_lens, sc, idx_out, acc, ml,
+                                     o, s->B, s->Hq, s->Hkv, s->cap, s->d, s->topk, w.nsplit,
                                      tau_of(s->scale, s->d), stream));
 }
 
