@@ -257,7 +257,7 @@ __global__ void __launch_bounds__(256) bwd_ds_kernel(const float* __restrict__ d
 }
 
 // ------------------------------------------------------------------ dk/dv kernel
-// grid: B*Hkv*nkb workgroups of 4 waves; wave = (key half kh, row half rh).
+// grid: nkb*B*Hkv workgroups of 4 waves; wave = (key half kh, row half rh).
 // The (q-block, head) steps of the reverse list stream through a ring of
 // kKvStages stages, each holding the Q and dO tiles of one (q-block, head) and
 // its row statistics [-lse/tau | -D]; the K and V rows of the wave's key half
@@ -293,8 +293,15 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
 
   const int nkb = n / SAS_BLK;
   const int G = Hq / Hkv;
-  const int bk = blockIdx.x / nkb;
-  const int m = blockIdx.x % nkb;
+  // key-block-major grid: consecutive workgroups take the same key block of
+  // consecutive (batch, kv-head) pairs.  Workgroups are dealt round-robin to
+  // the XCDs, so one XCD serves one kv-head's key blocks m, m+1, ... at a
+  // time; their reverse lists walk similar q-block ranges in ascending order,
+  // so a Q/dO tile one of them loads is often still in that XCD's L2 when the
+  // next needs it.  It also starts the longest lists (small m) first.
+  const int BH = gridDim.x / nkb;
+  const int m = blockIdx.x / BH;
+  const int bk = blockIdx.x % BH;
   const int b = bk / Hkv, kv = bk % Hkv;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
