@@ -119,6 +119,15 @@ __global__ void __launch_bounds__(128 * GC) fwd_mfma_kernel(
       for (int c = 0; c < D / 16; ++c)
         S[kt] = mfma32(ld16(Kt + kt * 32 * ROWB, ko[c]), qop[c], S[kt]);
     }
+    // K-chunk reads run 4 products ahead of the products that use them
+#pragma unroll
+    for (int x = 0; x < 4; ++x) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int x = 0; x < D / 8 - 4; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     if (CUR) {  // causal mask of the current block: key j visible iff j <= row
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -160,6 +169,15 @@ __global__ void __launch_bounds__(128 * GC) fwd_mfma_kernel(
 #pragma unroll
       for (int ch = 0; ch < 4; ++ch)
         O[dt] = mfma32(ldtr_pair(Vt + ch * 16 * ROWB, vo[dt][0], vo[dt][1]), P[ch], O[dt]);
+    // transposed V reads run 4 products ahead
+#pragma unroll
+    for (int x = 0; x < 8; ++x) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int x = 0; x < D / 8 - 4; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   };
   // kept tile t in stage ST: its DMA landed (and the stage it refills is free)
   // after the wait + barrier; then the tile NS-1 ahead is put in flight
