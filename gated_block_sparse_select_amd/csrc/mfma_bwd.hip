@@ -47,7 +47,7 @@ __global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
   constexpr int TB = 64 * ROWB;
   constexpr int JT = TB / 1024;
   constexpr int JW = 2 * JT / (2 * GC);
-  static_assert((2 * JT) % (2 * GC) == 0, "slices must split evenly over the waves");
+  static_assert((2 * JT) % (2 * GC) == 0 && JT % JW == 0, "slices must split evenly over the waves");
   constexpr int TK = 200, TV = 201;       // LDS buffer tags: K tiles, V tiles
   __shared__ float part[2][8];            // per-wave dZ sums of the last two tiles
 
@@ -94,16 +94,16 @@ __global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
   }
 
   const size_t kv0 = (size_t(b) * Hkv + kv) * size_t(n);
+  // the first half of the waves move K slices, the others V slices
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const bool k_side = wv * JW < JT;
+  const int slice0 = (wv * JW) % JT;
+  uint32_t pat[4];
+  dma_lane_pattern<D>(lane, slice0, pat);
   auto issue = [&]<int BUF>(int t) __attribute__((always_inline)) {
     const int blk = t < c_sel ? irow[t] : i;
-    const uint16_t* kb = k + (kv0 + size_t(blk) * SAS_BLK) * D;
-    const uint16_t* vb = v + (kv0 + size_t(blk) * SAS_BLK) * D;
-#pragma unroll
-    for (int u = 0; u < JW; ++u) {
-      const int j = wave * JW + u;
-      if (j < JT) dma_tile_slice<D>(kb, stage_buf<TK, BUF, TB>(), j, lane);
-      else dma_tile_slice<D>(vb, stage_buf<TV, BUF, TB>(), j - JT, lane);
-    }
+    const uint16_t* src = (k_side ? k : v) + (kv0 + size_t(blk) * SAS_BLK) * D;
+    dma_slices<JW>(src, k_side ? stage_buf<TK, BUF, TB>() : stage_buf<TV, BUF, TB>(), slice0, pat);
   };
   issue.template operator()<0>(0);
   if constexpr (NS > 2) {
@@ -352,8 +352,8 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
   const size_t hstride = size_t(n) * D * 2;
   const char* src_base = reinterpret_cast<const char*>(q_side ? q : dO) +
                          (size_t(b) * Hq + kv * G) * hstride;
-  const float* st_base = stats + (size_t(b) * Hq + kv * G) * size_t(nkb) * 128 + rh * 32 +
-                         (lane >> 5) * 64 + (lane & 31);
+  const float* st_base = stats + (size_t(b) * Hq + kv * G) * size_t(nkb) * 128 + rh * 32;
+  const uint32_t st_lane = uint32_t(((lane >> 5) * 64 + (lane & 31)) * 4);
   uint32_t pat[4];
   dma_lane_pattern<D>(lane, slice0, pat);
   auto issue = [&]<int BUF>() __attribute__((always_inline)) {
@@ -361,7 +361,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
     const char* tile = src_base + size_t(ih) * hstride + size_t(iq) * SAS_BLK * D * 2;
     dma_slices<JW>(tile, q_side ? stage_buf<TQ, BUF, TB>() : stage_buf<TO, BUF, TB>(), slice0, pat);
     __builtin_amdgcn_global_load_lds(
-        (glb_void*)(st_base + (size_t(ih) * nkb + iq) * 128),
+        (glb_void*)(uniform_ptr(st_base + (size_t(ih) * nkb + iq) * 128) + opaque(st_lane)),
         (lds_void*)(stage_buf<TS, BUF, 1024>() + wave * 256), 4, 0, 0);
     if (++ih == G) {
       ih = 0;

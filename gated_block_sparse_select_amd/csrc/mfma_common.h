@@ -110,20 +110,10 @@ SAS_DEV void dma16(const void* g, lds_char* l) {
   __builtin_amdgcn_global_load_lds((glb_void*)g, (lds_void*)l, 16, 0, 0);
 }
 
-// Slice jj (1 KB) of a 64 x D bf16 tile whose rows are contiguous in global
-// memory (row stride D elements), written to LDS in the swizzled layout: each
-// lane fetches the logical chunk that belongs at its physical slot.
-template <int D>
-SAS_DEV void dma_tile_slice(const uint16_t* gtile, lds_char* ltile, int jj, int lane) {
-  constexpr int CPR = D / 8;
-  constexpr int RPI = 64 / CPR;  // rows per 1 KB slice
-  const int r = jj * RPI + lane / CPR;
-  const int c = (lane % CPR) ^ swz<D>(r);
-  dma16(gtile + r * D + c * 8, ltile + jj * 1024);
-}
-
 // Per-lane byte offsets, inside a 1 KB slice of a swizzled 64 x D tile, of
-// the chunk lane `lane` moves (same logical chunk as dma_tile_slice).  The
+// the chunk lane `lane` moves, for tiles whose rows are contiguous in global
+// memory (row stride D elements) written to LDS in the swizzled layout: each
+// lane fetches the logical chunk that belongs at its physical slot.  The
 // swizzle of a slice's rows depends on the slice index mod 4 only, so slice
 // first + u of a tile at global address g is lane-wise
 // g + 1024*(first + u) + pat[u % 4].
@@ -139,6 +129,24 @@ SAS_DEV void dma_lane_pattern(int lane, int first, uint32_t (&pat)[4]) {
   }
 }
 
+// Hide a value from the optimiser (so "base + lane offset" stays one register
+// and only the small per-access constant goes to the DS offset field).
+SAS_DEV uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// A wave-uniform global address, held in SGPRs: a DMA from it plus a 32-bit
+// lane offset issues in the scalar-base + vector-offset form, with no
+// per-lane 64-bit address arithmetic.  Only for addresses every lane of the
+// wave shares.
+SAS_DEV const char* uniform_ptr(const void* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32));
+  return reinterpret_cast<const char*>((uint64_t(hi) << 32) | lo);
+}
+
 // A contiguous run of N slices, first .. first+N-1, of the tile at gtile
 // (wave-uniform) into the LDS tile ltile.
 template <int N>
@@ -146,7 +154,7 @@ SAS_DEV void dma_slices(const void* gtile, lds_char* ltile, int first, const uin
   const char* g = reinterpret_cast<const char*>(gtile) + first * 1024;
   lds_char* l = ltile + first * 1024;
 #pragma unroll
-  for (int u = 0; u < N; ++u) dma16(g + u * 1024 + pat[u & 3], l + u * 1024);
+  for (int u = 0; u < N; ++u) dma16(uniform_ptr(g + u * 1024) + opaque(pat[u & 3]), l + u * 1024);
 }
 
 // Wait until at most N of this wave's vector memory operations are
@@ -163,12 +171,6 @@ SAS_DEV void vm_wait_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Hide a value from the optimiser (so "base + lane offset" stays one register
-// and only the small per-access constant goes to the DS offset field).
-SAS_DEV uint32_t opaque(uint32_t x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
 
 // ---------------------------------------------------------------- LDS ring buffers
 // Every ring stage (and tile kind) is its own __shared__ variable, reached

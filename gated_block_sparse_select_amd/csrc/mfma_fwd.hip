@@ -35,7 +35,7 @@ __global__ void __launch_bounds__(128 * GC) fwd_mfma_kernel(
   constexpr int TB = 64 * ROWB;           // bytes of one 64 x D tile
   constexpr int JT = TB / 1024;           // 1 KB DMA slices per tile
   constexpr int JW = 2 * JT / (2 * GC);   // slices per wave per stage (K and V)
-  static_assert((2 * JT) % (2 * GC) == 0, "slices must split evenly over the waves");
+  static_assert((2 * JT) % (2 * GC) == 0 && JT % JW == 0, "slices must split evenly over the waves");
   constexpr int TK = 100, TV = 101;       // LDS buffer tags: K tiles, V tiles
 
   const int nqb = n / SAS_BLK;
@@ -65,16 +65,17 @@ __global__ void __launch_bounds__(128 * GC) fwd_mfma_kernel(
 
   const size_t kv0 = (size_t(b) * Hkv + kv) * size_t(n);
   // tile t -> ring stage BUF: K and V of block idx[t] (or the current block)
+  // the first half of the waves move K slices, the others V slices (JW
+  // divides JT, so no wave straddles the two)
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const bool k_side = wv * JW < JT;
+  const int slice0 = (wv * JW) % JT;
+  uint32_t pat[4];
+  dma_lane_pattern<D>(lane, slice0, pat);
   auto issue = [&]<int BUF>(int t) __attribute__((always_inline)) {
     const int blk = t < c_sel ? irow[t] : i;
-    const uint16_t* kb = k + (kv0 + size_t(blk) * SAS_BLK) * D;
-    const uint16_t* vb = v + (kv0 + size_t(blk) * SAS_BLK) * D;
-#pragma unroll
-    for (int u = 0; u < JW; ++u) {
-      const int j = wave * JW + u;
-      if (j < JT) dma_tile_slice<D>(kb, stage_buf<TK, BUF, TB>(), j, lane);
-      else dma_tile_slice<D>(vb, stage_buf<TV, BUF, TB>(), j - JT, lane);
-    }
+    const uint16_t* src = (k_side ? k : v) + (kv0 + size_t(blk) * SAS_BLK) * D;
+    dma_slices<JW>(src, k_side ? stage_buf<TK, BUF, TB>() : stage_buf<TV, BUF, TB>(), slice0, pat);
   };
   issue.template operator()<0>(0);
   if (1 < ntiles) issue.template operator()<1>(1);
