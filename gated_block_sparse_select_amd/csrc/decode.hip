@@ -14,6 +14,9 @@
 // workgroup covers a whole row (enough rows to fill the GPU) it writes o
 // directly; otherwise it writes an unnormalised partial (output, max, sum)
 // and a combine kernel merges the splits.
+#include <type_traits>
+#include <utility>
+
 #include "common.h"
 #include "launch.h"
 #include "sas.h"
@@ -85,9 +88,9 @@ SAS_DEV float group_sum(float x) {
 // of every tile, kg = t / CPR: a group of CPR lanes reads one key row (256 B
 // at d = 128 bf16) and the tile is one contiguous stretch of the cache.  Each
 // key group keeps its own online softmax (running max, sum, output chunk) for
-// all G heads, so tiles need no workgroup barrier.  Three register buffers
-// rotate (the tile loop is unrolled by 3) so that the loads of the next two
-// tiles are in flight while one is computed.  The KG groups are merged once,
+// all G heads, so tiles need no workgroup barrier.  NB register buffers
+// rotate (the tile loop is unrolled by NB) so that the loads of the next
+// NB-1 tiles are in flight while one is computed.  The KG groups are merged once,
 // through LDS, at the end.
 template <class E, int D, int GMAX, int CPL>
 __global__ void __launch_bounds__(256) decode_kernel(
@@ -154,7 +157,9 @@ __global__ void __launch_bounds__(256) decode_kernel(
   }
 
   const size_t cache0 = (size_t(b) * Hkv + kv) * size_t(cap) * D;
-  uint4 kb[3][KPT], vb[3][KPT];
+  // register buffers: NB-1 tiles of loads stay in flight while one is computed
+  constexpr int NB = 3;
+  uint4 kb[NB][KPT], vb[NB][KPT];
   auto load = [&]<int B>(int tile) __attribute__((always_inline)) {
     const int blk = tile < c_sel ? sblk[tile] : icur;
     const size_t base = cache0 + size_t(blk) * SAS_BLK * D;
@@ -166,6 +171,12 @@ __global__ void __launch_bounds__(256) decode_kernel(
       vb[B][u] = vt[u * 256 + t];
     }
   };
+  // Lazy running max (exp2 domain): raised only when a tile's max exceeds it
+  // by more than kSlack somewhere in the wave, so most tiles skip the rescale;
+  // weights stay below 2^kSlack and the final acc / l is exact whatever max
+  // was used.
+  constexpr float kSlack = 8.f;
+  constexpr bool kBF16 = std::is_same<E, ElemBF16>::value;
   auto compute = [&]<int B>(int tile) __attribute__((always_inline)) {
     const float bias2 = tile < c_sel ? sgate[tile] : 0.f;
     const int nvalid = tile < c_sel ? SAS_BLK : L - icur * SAS_BLK;
@@ -175,6 +186,22 @@ __global__ void __launch_bounds__(256) decode_kernel(
 #pragma unroll
       for (int g = 0; g < GMAX; ++g)
         sc[u][g] = g < G ? group_sum<CPR>(Vec16<E>::dot(qv[g], kb[B][u], 0.f)) : 0.f;
+    // bf16: V of key pairs (2x, 2x+1) regrouped once per tile, shared by all
+    // heads: word w of vp[x][h] holds elements 2w+h of the two keys, so
+    // acc += p0 v0 + p1 v1 is one v_dot2_f32_bf16 per element.
+    uint32_t vp[KPT / 2][2][4];
+    if constexpr (kBF16) {
+#pragma unroll
+      for (int x = 0; x < KPT / 2; ++x) {
+        const uint4 a = vb[B][2 * x], c = vb[B][2 * x + 1];
+        const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, cw[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          vp[x][0][w] = __builtin_amdgcn_perm(cw[w], aw[w], 0x05040100u);
+          vp[x][1][w] = __builtin_amdgcn_perm(cw[w], aw[w], 0x07060302u);
+        }
+      }
+    }
 #pragma unroll
     for (int g = 0; g < GMAX; ++g) {
       if (g >= G) continue;
@@ -185,37 +212,56 @@ __global__ void __launch_bounds__(256) decode_kernel(
         mt = fmaxf(mt, sc[u][g]);
       }
       if (mt == -INFINITY) continue;   // no valid key of this group in the tile
-      const float mnew = fmaxf(mrun[g], mt);
-      const float corr = fast_exp2(mrun[g] - mnew);
-      mrun[g] = mnew;
-      lrun[g] *= corr;
+      if (__any(mt > mrun[g] + kSlack)) {
+        const float mnew = fmaxf(mrun[g], mt);
+        const float corr = fast_exp2(mrun[g] - mnew);
+        mrun[g] = mnew;
+        lrun[g] *= corr;
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) acc[g][e] *= corr;
+        for (int e = 0; e < EPC; ++e) acc[g][e] *= corr;
+      }
+      if constexpr (kBF16) {
+        typedef __attribute__((ext_vector_type(2))) __bf16 bf2;
+        const bf2 ones = __builtin_bit_cast(bf2, 0x3F803F80u);
 #pragma unroll
-      for (int u = 0; u < KPT; ++u) {
-        const float p = fast_exp2(sc[u][g] - mnew);
-        lrun[g] += p;
-        float vx[EPC];
-        Vec16<E>::unpack(vb[B][u], vx);
+        for (int x = 0; x < KPT / 2; ++x) {
+          // the weights actually used (bf16) also form the normaliser
+          const bf2 pp = {(__bf16)fast_exp2(sc[2 * x][g] - mrun[g]),
+                          (__bf16)fast_exp2(sc[2 * x + 1][g] - mrun[g])};
+          lrun[g] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lrun[g], false);
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[g][e] = __builtin_fmaf(p, vx[e], acc[g][e]);
+          for (int w = 0; w < 4; ++w)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              acc[g][2 * w + h] = __builtin_amdgcn_fdot2_f32_bf16(
+                  pp, __builtin_bit_cast(bf2, vp[x][h][w]), acc[g][2 * w + h], false);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) {
+          const float p = fast_exp2(sc[u][g] - mrun[g]);
+          lrun[g] += p;
+          float vx[EPC];
+          Vec16<E>::unpack(vb[B][u], vx);
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) acc[g][e] = __builtin_fmaf(p, vx[e], acc[g][e]);
+        }
       }
     }
   };
-  if (t0 < t1) load.template operator()<0>(t0);
-  if (t0 + 1 < t1) load.template operator()<1>(t0 + 1);
-  if (t0 + 2 < t1) load.template operator()<2>(t0 + 2);
+  [&]<int... X>(std::integer_sequence<int, X...>) __attribute__((always_inline)) {
+    ((t0 + X < t1 ? load.template operator()<X>(t0 + X) : void()), ...);
+  }(std::make_integer_sequence<int, NB>{});
   int tile = t0;
-  for (; tile + 3 <= t1; tile += 3) {
-    compute.template operator()<0>(tile);
-    if (tile + 3 < t1) load.template operator()<0>(tile + 3);
-    compute.template operator()<1>(tile + 1);
-    if (tile + 4 < t1) load.template operator()<1>(tile + 4);
-    compute.template operator()<2>(tile + 2);
-    if (tile + 5 < t1) load.template operator()<2>(tile + 5);
-  }
-  if (tile < t1) compute.template operator()<0>(tile);
-  if (tile + 1 < t1) compute.template operator()<1>(tile + 1);
+  for (; tile + NB <= t1; tile += NB)
+    [&]<int... X>(std::integer_sequence<int, X...>) __attribute__((always_inline)) {
+      ((compute.template operator()<X>(tile + X),
+        (tile + X + NB < t1 ? load.template operator()<X>(tile + X + NB) : void())),
+       ...);
+    }(std::make_integer_sequence<int, NB>{});
+  [&]<int... X>(std::integer_sequence<int, X...>) __attribute__((always_inline)) {
+    ((tile + X < t1 ? compute.template operator()<X>(tile + X) : void()), ...);
+  }(std::make_integer_sequence<int, NB - 1>{});
 
   // merge the KG key groups: M = max of the group maxima, each group's sum
   // and output chunk scaled by 2^(m_k - M)
