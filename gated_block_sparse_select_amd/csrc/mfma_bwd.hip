@@ -139,10 +139,11 @@ __global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {   // one 32-key half at a time
       f32x16 S, P2;
+      // dP starts at -D (this lane's row), so the products give dP - D
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         S[j] = 0.f;
-        P2[j] = 0.f;
+        P2[j] = -Drow;
       }
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
@@ -157,10 +158,10 @@ __global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
           const int j = 8 * jc + e;
           float p = fast_exp2(__builtin_fmaf(S[j], tau2, zoff));
           if (CUR && kt * 32 + 8 * (j >> 2) + 4 * hh + (j & 3) > rt * 32 + lr) p = 0.f;
-          x[e] = p * (P2[j] - Drow);
-          zs += x[e];
+          x[e] = p * P2[j];
         }
         dZp[kt * 2 + jc] = pack_bf16x8(x);
+        zs = sum_bf16x8(dZp[kt * 2 + jc], zs);   // the block-gate gradient of the dZ used
       }
     }
 #pragma unroll
