@@ -119,6 +119,8 @@ SMALL_CASES = {
     "bf16_heavy_gumbel": (si.custom_workload(107, 1, 4, 1, 1024, 128, 6, "bf16",
                                              s_kind="gumbel3"), None),
     "fp32_gqa2_d128": (si.custom_workload(108, 1, 4, 2, 384, 128, 2, "f32"), None),
+    # 16 query heads per kv-head: four head chunks in the forward and dq
+    "bf16_gqa16_d128": (si.custom_workload(109, 1, 16, 1, 512, 128, 3, "bf16"), None),
 }
 
 
@@ -217,7 +219,8 @@ def _decode_run(api, w, q, kc, vc, lens, s):
 
 
 @pytest.mark.parametrize("dtype,G,d,cap,K", [("bf16", 4, 128, 1024, 5), ("bf16", 5, 64, 512, 3),
-                                             ("f32", 2, 64, 768, 2), ("bf16", 1, 128, 256, 0)])
+                                             ("f32", 2, 64, 768, 2), ("bf16", 1, 128, 256, 0),
+                                             ("bf16", 12, 128, 512, 4)])
 def test_decode_parity_small(api, dtype, G, d, cap, K):
     w = si.DecodeWorkload(200 + G, 5, 2 * G, 2, cap, d, K, dtype, hist_blocks=cap // BLOCK - 1)
     q, kc, vc, lens, s = si.make_decode_small(w)
