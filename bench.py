@@ -252,7 +252,7 @@ def run_decode(args, api, si, torch, np):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+        print(json.dumps({"error": "bench.py runs on one GPU only; run with --gpus 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import numpy as np
