@@ -18,7 +18,8 @@ BLOCK = 64
 EXPORTED = [
     "sas_abi_version", "sas_status_string", "sas_pool_workspace_bytes", "sas_pool_scores",
     "sas_select", "sas_fwd", "sas_bwd_workspace_bytes", "sas_bwd",
-    "sas_decode_workspace_bytes", "sas_decode", "sas_prof_enable", "sas_prof_collect",
+    "sas_decode_workspace_bytes", "sas_decode", "sas_decode_paged_workspace_bytes",
+    "sas_decode_paged", "sas_prof_enable", "sas_prof_collect",
     "sas_last_hip_error",
 ]
 
@@ -32,6 +33,13 @@ class SasShape(ctypes.Structure):
 class SasDecodeShape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
                 ("cap", ctypes.c_int32), ("d", ctypes.c_int32), ("topk", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+class SasDecodePagedShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+                ("max_blocks", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("topk", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("dtype", ctypes.c_int32)]
 
 
@@ -77,6 +85,11 @@ def lib() -> ctypes.CDLL:
         L.sas_decode_workspace_bytes.argtypes = [dp]
         L.sas_decode.restype = i32
         L.sas_decode.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, st]
+        pp = ctypes.POINTER(SasDecodePagedShape)
+        L.sas_decode_paged_workspace_bytes.restype = sz
+        L.sas_decode_paged_workspace_bytes.argtypes = [pp]
+        L.sas_decode_paged.restype = i32
+        L.sas_decode_paged.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, st]
         L.sas_last_hip_error.restype = ctypes.c_char_p
         L.sas_prof_enable.restype = i32
         L.sas_prof_enable.argtypes = [i32]

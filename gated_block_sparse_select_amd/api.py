@@ -12,7 +12,7 @@ import ctypes
 
 import torch
 
-from ._lib import (BLOCK, SAS_BF16, SAS_F32, SasDecodeShape, SasError, SasShape, lib,
+from ._lib import (BLOCK, SAS_BF16, SAS_F32, SasDecodePagedShape, SasDecodeShape, SasError, SasShape, lib,
                    status_string)
 
 _DT = {torch.float32: SAS_F32, torch.bfloat16: SAS_BF16}
@@ -53,6 +53,11 @@ def make_shape(B, Hq, Hkv, n, d, topk, dtype=torch.bfloat16, scale=0.0) -> SasSh
 
 def make_decode_shape(B, Hq, Hkv, cap, d, topk, dtype=torch.bfloat16, scale=0.0) -> SasDecodeShape:
     return SasDecodeShape(B, Hq, Hkv, cap, d, topk, float(scale), _DT[dtype])
+
+
+def make_decode_paged_shape(B, Hq, Hkv, max_blocks, num_pages, d, topk, dtype=torch.bfloat16,
+                            scale=0.0) -> SasDecodePagedShape:
+    return SasDecodePagedShape(B, Hq, Hkv, max_blocks, num_pages, d, topk, float(scale), _DT[dtype])
 
 
 def shape_of(q: torch.Tensor, k: torch.Tensor, topk: int, scale: float = 0.0) -> SasShape:
@@ -156,6 +161,28 @@ def sas_decode(shape: SasDecodeShape, q, k_cache, v_cache, seq_lens, s, o, idx_o
                          _stream(stream)), "sas_decode")
 
 
+def sas_decode_paged_workspace_bytes(shape: SasDecodePagedShape) -> int:
+    return int(lib().sas_decode_paged_workspace_bytes(ctypes.byref(shape)))
+
+
+def sas_decode_paged(shape: SasDecodePagedShape, q, k_pages, v_pages, page_table, seq_lens, s, o,
+                     idx_out, ws, stream=None):
+    dt = _dt(shape)
+    pool = shape.num_pages * shape.Hkv * BLOCK * shape.d
+    _check(q, "q", dt, shape.B * shape.Hq * shape.d)
+    _check(k_pages, "k_pages", dt, pool)
+    _check(v_pages, "v_pages", dt, pool)
+    _check(page_table, "page_table", torch.int32, shape.B * shape.max_blocks)
+    _check(seq_lens, "seq_lens", torch.int32, shape.B)
+    _check(s, "s", torch.float32, shape.B * shape.Hkv * shape.max_blocks)
+    _check(o, "o", dt, shape.B * shape.Hq * shape.d)
+    _check(idx_out, "idx_out", torch.int32, shape.B * shape.Hkv * shape.topk)
+    _check(ws, "ws", torch.uint8)
+    _ok(lib().sas_decode_paged(ctypes.byref(shape), _ptr(q), _ptr(k_pages), _ptr(v_pages),
+                               _ptr(page_table), _ptr(seq_lens), _ptr(s), _ptr(o), _ptr(idx_out),
+                               _ptr(ws), ws.numel(), _stream(stream)), "sas_decode_paged")
+
+
 def sas_prof_enable(on: bool):
     _ok(lib().sas_prof_enable(1 if on else 0), "sas_prof_enable")
 
@@ -184,8 +211,10 @@ def alloc_workspace(nbytes: int, device="cuda"):
 
 
 __all__ = [
-    "make_shape", "make_decode_shape", "shape_of", "sas_pool_workspace_bytes", "sas_pool_scores",
-    "sas_select", "sas_fwd", "sas_bwd_workspace_bytes", "sas_bwd", "sas_decode_workspace_bytes",
-    "sas_decode", "sas_prof_enable", "sas_prof_collect", "alloc_select", "alloc_workspace",
-    "status_string", "SasError", "SasShape", "SasDecodeShape",
+    "make_shape", "make_decode_shape", "make_decode_paged_shape", "shape_of",
+    "sas_pool_workspace_bytes", "sas_pool_scores", "sas_select", "sas_fwd",
+    "sas_bwd_workspace_bytes", "sas_bwd", "sas_decode_workspace_bytes", "sas_decode",
+    "sas_decode_paged_workspace_bytes", "sas_decode_paged", "sas_prof_enable", "sas_prof_collect",
+    "alloc_select", "alloc_workspace", "status_string", "SasError", "SasShape", "SasDecodeShape",
+    "SasDecodePagedShape",
 ]

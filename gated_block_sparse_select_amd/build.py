@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libsas.so")
 BUILD = os.path.join(HERE, "_build")
 
-SOURCES = ["select.hip", "pool.hip", "revidx.hip", "simt.hip", "decode.hip",
+SOURCES = ["select.hip", "pool.hip", "revidx.hip", "simt.hip", "decode.hip", "decode_paged.hip",
            "mfma_fwd.hip", "mfma_bwd.hip", "sas_api.cpp"]
 
 ARCH = "gfx950"

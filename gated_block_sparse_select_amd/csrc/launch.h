@@ -56,4 +56,11 @@ hipError_t launch_decode(int dtype, const void* q, const void* kc, const void* v
                          float* part_acc, float* part_ml, void* o, int B, int Hq, int Hkv,
                          int cap, int d, int topk, int nsplit, float tau, hipStream_t st);
 
+// ---- paged decode (decode_paged.hip)
+hipError_t launch_decode_paged(int dtype, const void* q, const void* k_pages, const void* v_pages,
+                               const int32_t* page_table, int num_pages, const int32_t* seq_lens,
+                               const float* s, int32_t* idx_out, float* part_acc, float* part_ml,
+                               void* o, int B, int Hq, int Hkv, int max_blocks, int d, int topk,
+                               int nsplit, float tau, hipStream_t st);
+
 }  // namespace sas

@@ -62,6 +62,31 @@ sas_status check_dshape(const sas_decode_shape* s) {
   return SAS_OK;
 }
 
+sas_status check_pshape(const sas_decode_paged_shape* s) {
+  if (!s) return SAS_ERR_ARG;
+  if (s->dtype != SAS_F32 && s->dtype != SAS_BF16) return SAS_ERR_DTYPE;
+  if (s->max_blocks < 1 || s->max_blocks > SAS_MAX_DECODE_BLOCKS || s->num_pages < 1)
+    return SAS_ERR_ARG;
+  // the remaining limits are those of a decode shape whose cap is one block
+  if (!shape_ok_common(s->B, s->Hq, s->Hkv, SAS_BLOCK, s->d, s->topk, s->scale)) return SAS_ERR_ARG;
+  if (int64_t(s->B) * s->Hkv * s->max_blocks > (int64_t(1) << 30)) return SAS_ERR_ARG;
+  return SAS_OK;
+}
+
+// the paged decode's workspace is laid out like the contiguous decode's
+sas_decode_shape as_decode_shape(const sas_decode_paged_shape* s) {
+  sas_decode_shape d{};
+  d.B = s->B;
+  d.Hq = s->Hq;
+  d.Hkv = s->Hkv;
+  d.cap = SAS_BLOCK;
+  d.d = s->d;
+  d.topk = s->topk;
+  d.scale = s->scale;
+  d.dtype = s->dtype;
+  return d;
+}
+
 float tau_of(float scale, int d) { return scale > 0.f ? scale : 1.0f / std::sqrt(float(d)); }
 
 thread_local hipError_t g_last_hip = hipSuccess;
@@ -275,6 +300,32 @@ sas_status sas_decode(const sas_decode_shape* s, const void* q, const void* k_ca
   return from_hip(sas::launch_decode(s->dtype, q, k_cache, v_cache, seq_lens, sc, idx_out, acc, ml,
                                      o, s->B, s->Hq, s->Hkv, s->cap, s->d, s->topk, w.nsplit,
                                      tau_of(s->scale, s->d), stream));
+}
+
+size_t sas_decode_paged_workspace_bytes(const sas_decode_paged_shape* s) {
+  if (check_pshape(s) != SAS_OK) return 0;
+  const sas_decode_shape d = as_decode_shape(s);
+  return dec_layout(&d).total;
+}
+
+sas_status sas_decode_paged(const sas_decode_paged_shape* s, const void* q, const void* k_pages,
+                            const void* v_pages, const int32_t* page_table,
+                            const int32_t* seq_lens, const float* sc, void* o, int32_t* idx_out,
+                            void* ws, size_t ws_bytes, hipStream_t stream) {
+  sas_status st = check_pshape(s);
+  if (st != SAS_OK) return st;
+  if (!q || !k_pages || !v_pages || !page_table || !seq_lens || !sc || !o) return SAS_ERR_ARG;
+  const sas_decode_shape d = as_decode_shape(s);
+  const DecWs w = dec_layout(&d);
+  if (!ws || ws_bytes < w.total) return SAS_ERR_WORKSPACE;
+  char* base = static_cast<char*>(ws);
+  float* acc = reinterpret_cast<float*>(base + w.acc_off);
+  float* ml = reinterpret_cast<float*>(base + w.ml_off);
+  clear_stale_error();
+  return from_hip(sas::launch_decode_paged(s->dtype, q, k_pages, v_pages, page_table, s->num_pages,
+                                           seq_lens, sc, idx_out, acc, ml, o, s->B, s->Hq, s->Hkv,
+                                           s->max_blocks, s->d, s->topk, w.nsplit,
+                                           tau_of(s->scale, s->d), stream));
 }
 
 const char* sas_last_hip_error(void) { return hipGetErrorName(g_last_hip); }

@@ -87,6 +87,123 @@ SAS_DEV int select_row(const float* __restrict__ srow, int i, int topk, int lane
   return keff;
 }
 
+// The same selection by a workgroup of NW waves, for rows of up to
+// NW*64*CPL candidates (long decode contexts).  Wave w holds the contiguous
+// candidates [w*64*CPL, (w+1)*64*CPL), m = w*64*CPL + j*64 + lane, so waves in
+// order, then j, then lanes visit m ascending.  The maximum, the exp sum
+// (summed in wave order, so the result is deterministic) and every count of
+// the threshold search are combined across waves through red, an LDS array of
+// at least 6*NW words; each of the 32 search rounds costs one barrier (its
+// counts alternate between two slots, so a slot is rewritten only after every
+// wave has read it).  Ties at the threshold and output positions follow from
+// the per-wave counts of the waves before.  Every thread of the workgroup must
+// call it (it contains __syncthreads).
+template <int CPL, int NW, class Emit>
+SAS_DEV int select_row_wg(const float* __restrict__ srow, int i, int topk, int wave, int lane,
+                          float& lse, __attribute__((address_space(3))) float* red, Emit&& emit) {
+  __attribute__((address_space(3))) int* ired =
+      reinterpret_cast<__attribute__((address_space(3))) int*>(red);
+  const int m0 = wave * 64 * CPL;
+  float val[CPL];
+  uint32_t key[CPL];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int m = m0 + j * 64 + lane;
+    const bool ok = m < i;
+    val[j] = ok ? srow[m] : -INFINITY;
+    key[j] = ok ? order_key(val[j]) : 0u;
+    mx = fmaxf(mx, val[j]);
+  }
+  mx = wave_max(mx);
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  float gmx = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) gmx = fmaxf(gmx, red[w]);
+  float se = 0.f;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j)
+    if (m0 + j * 64 + lane < i) se += expf(val[j] - gmx);
+  se = wave_sum(se);
+  if (lane == 0) red[NW + wave] = se;
+  __syncthreads();
+  float gse = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) gse += red[NW + w];
+  lse = (i > 0) ? gmx + logf(gse) : -INFINITY;
+
+  const int keff = topk < i ? topk : i;
+  uint32_t T = 0u;
+  int need_eq = 0;
+  const bool search = keff < i && keff > 0;   // uniform over the workgroup
+  if (search) {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = T | (1u << bit);
+      int n = 0;
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) n += __popcll(__ballot(key[j] >= c));
+      const int slot = 2 * NW + (bit & 1) * NW;
+      if (lane == 0) ired[slot + wave] = n;
+      __syncthreads();
+      int tot = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) tot += ired[slot + w];
+      if (tot >= keff) T = c;
+    }
+  }
+  // per-wave counts above and at the threshold (waves before this one decide
+  // its tie budget and its first output position)
+  int gt = 0, eqn = 0;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    gt += __popcll(__ballot(key[j] > T));
+    eqn += __popcll(__ballot(search && key[j] == T));
+  }
+  if (lane == 0) {
+    ired[4 * NW + wave] = gt;
+    ired[5 * NW + wave] = eqn;
+  }
+  __syncthreads();
+  int n_gt = 0, eq_before = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) n_gt += ired[4 * NW + w];
+  if (search) need_eq = keff - n_gt;
+  int base = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    if (w >= wave) break;
+    const int e_w = ired[5 * NW + w];
+    if (keff == i) {
+      base += min(64 * CPL, max(0, i - w * 64 * CPL));
+    } else if (search) {
+      base += ired[4 * NW + w] + min(e_w, max(0, need_eq - eq_before));
+    }
+    eq_before += e_w;
+  }
+
+  int eq_seen = eq_before;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int m = m0 + j * 64 + lane;
+    bool take;
+    if (keff == 0) {
+      take = false;
+    } else if (keff == i) {
+      take = m < i;
+    } else {
+      const bool eq = key[j] == T;
+      const uint64_t eqm = __ballot(eq);
+      take = key[j] > T || (eq && eq_seen + mask_rank(eqm) < need_eq);
+      eq_seen += __popcll(eqm);
+    }
+    const uint64_t tm = __ballot(take);
+    if (take) emit(base + mask_rank(tm), m, val[j] - lse);
+    base += __popcll(tm);
+  }
+  return keff;
+}
+
 // candidates per lane for history rows of up to nkb blocks
 inline int select_cpl(int nkb) {
   const int need = (nkb + 63) / 64;

@@ -80,6 +80,20 @@ typedef struct {
   int32_t dtype;
 } sas_decode_shape;
 
+#define SAS_MAX_DECODE_BLOCKS 8192  /* most blocks per sequence in paged decode (context <= 524288) */
+
+/* Paged decode shape.  The KV cache is a pool of num_pages pages, each holding
+ * one 64-token block of every kv-head: k_pages, v_pages [num_pages,Hkv,64,d].
+ * Block m of sequence b lives in page page_table[b,m] (int32 [B,max_blocks]).
+ * q [B,Hq,d]; s float32 [B,Hkv,max_blocks].  Same limits as sas_shape with
+ * 64*max_blocks in place of n, except 1 <= max_blocks <= SAS_MAX_DECODE_BLOCKS;
+ * num_pages >= 1; 0 <= topk <= SAS_MAX_BLOCKS. */
+typedef struct {
+  int32_t B, Hq, Hkv, max_blocks, num_pages, d, topk;
+  float scale;
+  int32_t dtype;
+} sas_decode_paged_shape;
+
 /* Version of this ABI (bumped on any incompatible change). */
 int32_t sas_abi_version(void);
 
@@ -162,6 +176,25 @@ size_t sas_decode_workspace_bytes(const sas_decode_shape* shape);
 sas_status sas_decode(const sas_decode_shape* shape, const void* q, const void* k_cache,
                       const void* v_cache, const int32_t* seq_lens, const float* s, void* o,
                       int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------- paged decode
+ * sas_decode over a paged KV pool, the serving-side cache of [Review §2.6]:
+ * the same selection and attention with cap = 64*max_blocks, where the K/V
+ * rows of token t of sequence b are k_pages[page_table[b,t/64], kv, t%64, :]
+ * (likewise v_pages).  Only the table entries of each row's kept blocks and
+ * current block are read.  Entries outside [0, num_pages) are clamped on the
+ * device: nothing outside the pool is read, and rows that use such entries get
+ * unspecified values.  Rows of more than SAS_MAX_BLOCKS history blocks are
+ * selected by a whole workgroup (long contexts up to 512K tokens).
+ *   seq_lens int32 [B] (device), clamped into [1, 64*max_blocks];
+ *   idx_out: NULL, or int32 [B,Hkv,topk] receiving the ascending block indices
+ *   (not pages), -1 padded; o [B,Hq,d] (written).
+ *   ws: device scratch of sas_decode_paged_workspace_bytes(shape) bytes. */
+size_t sas_decode_paged_workspace_bytes(const sas_decode_paged_shape* shape);
+sas_status sas_decode_paged(const sas_decode_paged_shape* shape, const void* q,
+                            const void* k_pages, const void* v_pages, const int32_t* page_table,
+                            const int32_t* seq_lens, const float* s, void* o, int32_t* idx_out,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Name of the HIP error behind the last SAS_ERR_HIP returned on this thread
  * ("hipSuccess" if none); static storage. */

@@ -34,7 +34,7 @@ import numpy as np
 
 BLOCK = 64
 
-TID_Q, TID_K, TID_V, TID_S, TID_DO, TID_LEN = 0, 1, 2, 3, 4, 5
+TID_Q, TID_K, TID_V, TID_S, TID_DO, TID_LEN, TID_PAGES = 0, 1, 2, 3, 4, 5, 6
 
 
 @dataclasses.dataclass(frozen=True)
@@ -182,6 +182,29 @@ def make_decode_small(w: DecodeWorkload):
 def decode_seq_lens(w: DecodeWorkload) -> np.ndarray:
     L = rng(w.cfg, TID_LEN).integers(1, BLOCK + 1, size=w.B)
     return (w.hist_blocks * BLOCK + L).astype(np.int32)
+
+
+def make_decode_paged(cfg: int, B: int, Hq: int, Hkv: int, max_blocks: int, num_pages: int,
+                      d: int, dtype: str = "bf16", seq_lens=None):
+    """Inputs of a paged decode, all on the host: q [B,Hq,d]; k_pages, v_pages
+    [num_pages,Hkv,64,d]; page_table int32 [B,max_blocks]; seq_lens int32 [B];
+    s [B,Hkv,max_blocks].  When the pool holds at least B*max_blocks pages each
+    block gets its own page (a random permutation, the rest of the pool
+    unused); otherwise blocks draw pages at random and share them, as copies of
+    a common prefix would.  seq_lens default to random lengths in
+    [1, 64*max_blocks]."""
+    q = _store(_normal(cfg, TID_Q, (B, Hq, d)), dtype)
+    kp = _store(_normal(cfg, TID_K, (num_pages, Hkv, BLOCK, d)), dtype)
+    vp = _store(_normal(cfg, TID_V, (num_pages, Hkv, BLOCK, d)), dtype)
+    s = _normal(cfg, TID_S, (B, Hkv, max_blocks))
+    g = rng(cfg, TID_PAGES)
+    if num_pages >= B * max_blocks:
+        table = g.permutation(num_pages)[:B * max_blocks].reshape(B, max_blocks)
+    else:
+        table = g.integers(0, num_pages, size=(B, max_blocks))
+    if seq_lens is None:
+        seq_lens = rng(cfg, TID_LEN).integers(1, BLOCK * max_blocks + 1, size=B)
+    return (q, kp, vp, table.astype(np.int32), np.asarray(seq_lens, dtype=np.int32), s)
 
 
 def decode_q_and_scores(w: DecodeWorkload):

@@ -102,6 +102,39 @@ def test_workspace_checks():
     assert L.sas_decode(ctypes.byref(bad), *([FAKE] * 7), FAKE, 1 << 30, None) == 1
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,maxb,pages,d,K,dt,expect", [
+    (2, 8, 2, 8192, 100, 128, 32, 1, 0),     # 512K-token rows: accepted
+    (2, 8, 2, 8193, 100, 128, 32, 1, 1),     # more blocks than SAS_MAX_DECODE_BLOCKS
+    (2, 8, 2, 0, 100, 128, 32, 1, 1),        # no blocks
+    (2, 8, 2, 64, 0, 128, 32, 1, 1),         # empty pool
+    (2, 8, 2, 64, 100, 96, 32, 1, 1),        # d not in {64,128}
+    (2, 8, 3, 64, 100, 128, 32, 1, 1),       # Hq % Hkv != 0
+    (2, 8, 2, 64, 100, 128, 2049, 1, 1),     # topk beyond SAS_MAX_BLOCKS
+    (2, 8, 2, 64, 100, 128, 32, 5, 2),       # bad dtype
+])
+def test_paged_decode_shape_validation(B, Hq, Hkv, maxb, pages, d, K, dt, expect):
+    L = _lib.lib()
+    sh = _lib.SasDecodePagedShape(B, Hq, Hkv, maxb, pages, d, K, 0.0, dt)
+    need = L.sas_decode_paged_workspace_bytes(ctypes.byref(sh))
+    assert (need > 0) == (expect == 0)
+    if expect:   # every pointer non-NULL and the workspace large: only the shape decides
+        assert L.sas_decode_paged(ctypes.byref(sh), *([FAKE] * 8), FAKE, 1 << 40, None) == expect
+
+
+def test_paged_decode_pointer_and_workspace_checks():
+    L = _lib.lib()
+    sh = api.make_decode_paged_shape(4, 32, 8, 8192, 1 << 16, 128, 32)
+    need = api.sas_decode_paged_workspace_bytes(sh)
+    assert need > 0
+    ptrs = [FAKE] * 8
+    for j in range(7):   # q, k_pages, v_pages, page_table, seq_lens, s, o are required
+        bad = list(ptrs)
+        bad[j] = None
+        assert L.sas_decode_paged(ctypes.byref(sh), *bad, FAKE, need, None) == 1
+    assert L.sas_decode_paged(ctypes.byref(sh), *ptrs, FAKE, need - 1, None) == 4
+    assert L.sas_decode_paged(ctypes.byref(sh), *ptrs, None, need, None) == 4
+
+
 def test_binding_rejects_host_tensors():
     import torch
     sh = api.make_shape(1, 1, 1, 64, 64, 0, torch.float32)

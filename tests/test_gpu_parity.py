@@ -260,6 +260,80 @@ def test_decode_parity_full_size(api):
         assert_o(o_h[b, kv * G:(kv + 1) * G], ref_o[b, kv * G:(kv + 1) * G], "bf16")
 
 
+# ---------------------------------------------------------------- paged decode
+class _PagedRows:
+    """[b, kv] -> sequence b's [cap, d] cache seen through its page table, with
+    out-of-range entries clipped into the pool as the library specifies (an
+    input view for the oracle, which itself only knows contiguous caches)."""
+
+    def __init__(self, pages, table):
+        self.pages = pages
+        self.table = np.clip(table, 0, pages.shape[0] - 1)
+
+    def __getitem__(self, bk):
+        b, kv = bk
+        pages, pt = self.pages, self.table[b]
+
+        class _Rows:
+            def __getitem__(self, cols):
+                cols = np.asarray(cols)
+                return pages[pt[cols // BLOCK], kv, cols % BLOCK]
+
+        return _Rows()
+
+
+def _decode_paged_run(api, dtype, q, kp, vp, table, lens, s, K):
+    B, Hq, d = q.shape
+    num_pages, Hkv = kp.shape[:2]
+    max_blocks = table.shape[1]
+    dt = tdtype(dtype)
+    shp = api.make_decode_paged_shape(B, Hq, Hkv, max_blocks, num_pages, d, K, dt)
+    qd = dev(q, dt)
+    o = torch.empty_like(qd)
+    idx = torch.full((B, Hkv, K), -7, dtype=torch.int32, device="cuda")
+    ws = api.alloc_workspace(api.sas_decode_paged_workspace_bytes(shp))
+    api.sas_decode_paged(shp, qd, dev(kp, dt), dev(vp, dt), torch.from_numpy(table).cuda(),
+                         torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda(),
+                         torch.from_numpy(s).cuda(), o, idx, ws)
+    torch.cuda.synchronize()
+    return host(o), host(idx)
+
+
+@pytest.mark.parametrize("dtype,G,d,max_blocks,num_pages,K", [
+    ("bf16", 4, 128, 40, 400, 5),    # a page of its own for every block
+    ("bf16", 2, 64, 24, 30, 3),      # blocks share pages
+    ("f32", 2, 64, 16, 64, 2),
+    ("bf16", 5, 128, 20, 100, 0)])
+def test_decode_paged_parity_small(api, dtype, G, d, max_blocks, num_pages, K):
+    B, Hkv = 4, 2
+    q, kp, vp, table, lens, s = si.make_decode_paged(400 + max_blocks, B, G * Hkv, Hkv, max_blocks,
+                                                     num_pages, d, dtype)
+    lens[0], lens[1] = 1, BLOCK * max_blocks          # shortest and longest rows
+    table[2, :] = np.where(np.arange(max_blocks) % 3 == 0, -5, table[2, :])
+    table[3, 1] = num_pages + 7                       # entries outside the pool are clamped
+    o, idx = _decode_paged_run(api, dtype, q, kp, vp, table, lens, s, K)
+    ref_o, ref_idx = oracle.decode(q, _PagedRows(kp, table), _PagedRows(vp, table), lens, s, K)
+    assert np.array_equal(idx, ref_idx)
+    assert_o(o, ref_o, dtype)
+
+
+@pytest.mark.parametrize("ties,K", [(False, 32), (True, 32), (False, 0), (True, 2048)])
+def test_decode_paged_long_context(api, ties, K):
+    """Rows of up to 8191 history blocks (512K tokens), selected by the whole
+    workgroup; with ties, equal scores straddle the waves' candidate ranges."""
+    B, Hq, Hkv, d = 3, 4, 2, 64
+    max_blocks, num_pages = 8192, 4096
+    lens = [BLOCK * max_blocks, 300000, 1000]
+    q, kp, vp, table, lens, s = si.make_decode_paged(450 + K, B, Hq, Hkv, max_blocks, num_pages, d,
+                                                     "bf16", seq_lens=lens)
+    if ties:
+        s = np.round(s * 2).astype(np.float32)
+    o, idx = _decode_paged_run(api, "bf16", q, kp, vp, table, lens, s, K)
+    ref_o, ref_idx = oracle.decode(q, _PagedRows(kp, table), _PagedRows(vp, table), lens, s, K)
+    assert np.array_equal(idx, ref_idx)
+    assert_o(o, ref_o, "bf16")
+
+
 # ---------------------------------------------------------------- determinism
 def test_run_twice_bitwise(api):
     w = si.custom_workload(300, 1, 8, 2, 2048, 128, 8, "bf16")
