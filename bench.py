@@ -11,6 +11,10 @@ between two device synchronisations.  Prints ONE JSON line.
 value = effective TFLOP/s: FLOPs counted on valid (query, key) pairs only
 (64*64 per kept block plus 64*65/2 for the causal current block, per query
 head), 4*d per pair for the forward and 10*d for the backward.
+
+Unless --no-decode is given the line also carries "decode" (batch 64, 32K
+contiguous cache: us per call, GB/s, the decode kernel's roofline) and
+"decode_paged" (one 512K-token sequence in a paged pool: us per call, GB/s).
 """
 from __future__ import annotations
 
@@ -249,6 +253,63 @@ def run_decode(args, api, si, torch, np):
     return out
 
 
+def run_decode_paged(args, api, si, torch, np):
+    """Long-context paged decode (select over every history block fused in):
+    us per call, and GB/s of the bytes a call must read (kept K/V rows, score
+    rows, page-table entries, q) over that time."""
+    w = si.PAGED_DECODE_WORKLOAD
+    dt = torch.bfloat16
+    qh, table, lens, sh_ = si.paged_decode_host(w)
+    kp, vp = si.paged_pool_device(w, "cuda")
+    q = torch.from_numpy(qh).cuda().to(dt)
+    pt = torch.from_numpy(table).cuda()
+    L = torch.from_numpy(lens).cuda()
+    s = torch.from_numpy(sh_).cuda()
+    shp = api.make_decode_paged_shape(w.B, w.Hq, w.Hkv, w.max_blocks, w.num_pages, w.d, w.topk, dt)
+    o = torch.empty_like(q)
+    idx = torch.empty((w.B, w.Hkv, w.topk), dtype=torch.int32, device="cuda")
+    ws = api.alloc_workspace(api.sas_decode_paged_workspace_bytes(shp))
+
+    def call():
+        api.sas_decode_paged(shp, q, kp, vp, pt, L, s, o, idx, ws)
+
+    for _ in range(20):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.decode_steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.decode_steps
+    api.sas_prof_collect()
+    api.sas_prof_enable(True)
+    for _ in range(args.decode_steps):
+        call()
+    torch.cuda.synchronize()
+    api.sas_prof_enable(False)
+    kern = api.sas_prof_collect()
+    kept = 0
+    for x in lens:
+        icur = (int(x) - 1) // 64
+        kept += w.Hkv * (min(w.topk, icur) * 64 + (int(x) - 64 * icur))
+    icur0 = (int(lens[0]) - 1) // 64
+    kv_bytes = kept * w.d * 2 * 2
+    score_bytes = sum(w.Hkv * ((int(x) - 1) // 64) * 4 for x in lens)
+    other = q.numel() * 2 * 2 + w.B * w.Hkv * (w.topk + 1) * 4 * 2 + w.B * 4
+    alg = kv_bytes + score_bytes + other
+    per_kernel = {n: dict(avg_us=round(t * 1e3 / max(c, 1), 2), launches=c) for n, (t, c) in kern.items()}
+    out = dict(workload=w.name, us_per_call=round(us, 2), algorithmic_bytes=alg,
+               GBs=round(alg / (us * 1e-6) / 1e9, 1),
+               frac_hbm=round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), per_kernel=per_kernel,
+               history_blocks_per_row=icur0, kept_blocks_per_row=min(w.topk, icur0) + 1,
+               pool_pages=w.num_pages)
+    del kp, vp
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -302,6 +363,7 @@ def main():
     if not args.no_decode:
         torch.cuda.empty_cache()
         line["decode"] = run_decode(args, api, si, torch, np)
+        line["decode_paged"] = run_decode_paged(args, api, si, torch, np)
     print(json.dumps(line), flush=True)
 
 

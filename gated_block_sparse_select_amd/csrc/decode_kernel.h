@@ -345,17 +345,29 @@ __global__ void __launch_bounds__(128) decode_combine_kernel(const float* __rest
                                                              const float* __restrict__ part_ml,
                                                              typename E::T* __restrict__ o,
                                                              int nsplit) {
+  // the splits' (max, sum) pairs go to LDS with parallel loads, so the merge
+  // below issues its partial-output loads back to back instead of one
+  // dependent load per split (decode_nsplit never exceeds 512)
+  __shared__ float sm[512], sl[512];
   const size_t bh = blockIdx.x;
   const int c = threadIdx.x;
+  for (int sp = c; sp < nsplit; sp += D) {
+    sm[sp] = part_ml[(bh * nsplit + sp) * 2];
+    sl[sp] = part_ml[(bh * nsplit + sp) * 2 + 1];
+  }
+  __syncthreads();
   float M = -INFINITY;
-  for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, part_ml[(bh * nsplit + sp) * 2]);
+  for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, sm[sp]);
   float l = 0.f, a = 0.f;
+#pragma unroll 8
   for (int sp = 0; sp < nsplit; ++sp) {
-    const float m = part_ml[(bh * nsplit + sp) * 2];
-    if (m == -INFINITY) continue;
-    const float w = fast_exp2(m - M);
-    l += w * part_ml[(bh * nsplit + sp) * 2 + 1];
-    a += w * part_acc[(bh * nsplit + sp) * D + c];
+    const float m = sm[sp];
+    const float x = part_acc[(bh * nsplit + sp) * D + c];
+    if (m != -INFINITY) {   // a split without keys contributes nothing
+      const float w = fast_exp2(m - M);
+      l += w * sl[sp];
+      a += w * x;
+    }
   }
   E::st(o + bh * D + c, a / l);
 }

@@ -97,6 +97,34 @@ WORKLOADS = {
 DECODE_WORKLOAD = DecodeWorkload(5, 64, 32, 8, 32768, 128, 32)
 
 
+@dataclasses.dataclass(frozen=True)
+class PagedDecodeWorkload:
+    """Long-context paged decode: B sequences of about 64*max_blocks tokens in
+    a pool of B*max_blocks one-block pages (every block its own page, the pages
+    of a sequence scattered over the pool)."""
+    cfg: int
+    B: int
+    Hq: int
+    Hkv: int
+    max_blocks: int
+    d: int
+    topk: int
+    dtype: str = "bf16"
+
+    @property
+    def name(self) -> str:
+        return (f"decode-paged-qwen3-8b-B{self.B}-ctx{self.max_blocks * BLOCK}-K{self.topk}")
+
+    @property
+    def num_pages(self) -> int:
+        return self.B * self.max_blocks
+
+
+# Qwen3-8B attention shape, one sequence of a 512K-token context (the batch-1,
+# 512K decode setting of the SAS review page, §4)
+PAGED_DECODE_WORKLOAD = PagedDecodeWorkload(6, 1, 32, 8, 8192, 128, 32)
+
+
 def rng(cfg: int, tid: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(cfg), int(tid)])))
 
@@ -205,6 +233,36 @@ def make_decode_paged(cfg: int, B: int, Hq: int, Hkv: int, max_blocks: int, num_
     if seq_lens is None:
         seq_lens = rng(cfg, TID_LEN).integers(1, BLOCK * max_blocks + 1, size=B)
     return (q, kp, vp, table.astype(np.int32), np.asarray(seq_lens, dtype=np.int32), s)
+
+
+def paged_decode_host(w: PagedDecodeWorkload):
+    """q [B,Hq,d], page_table int32 [B,max_blocks] (a random permutation of the
+    pool), seq_lens int32 [B] (the last block partly filled) and
+    s [B,Hkv,max_blocks]; the pages themselves come from paged_pool_device."""
+    q = _store(_normal(w.cfg, TID_Q, (w.B, w.Hq, w.d)), w.dtype)
+    s = _normal(w.cfg, TID_S, (w.B, w.Hkv, w.max_blocks))
+    table = rng(w.cfg, TID_PAGES).permutation(w.num_pages).reshape(w.B, w.max_blocks)
+    L = (w.max_blocks - 1) * BLOCK + rng(w.cfg, TID_LEN).integers(1, BLOCK + 1, size=w.B)
+    return q, table.astype(np.int32), L.astype(np.int32), s
+
+
+def paged_pool_device(w: PagedDecodeWorkload, device):
+    """k_pages, v_pages [num_pages,Hkv,64,d] drawn on the device with seeded
+    torch generators, filled in slices to bound the float32 temporary."""
+    import torch
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    out = []
+    for tid in (TID_K, TID_V):
+        g = torch.Generator(device=device)
+        g.manual_seed(1_000_003 * w.cfg + tid)
+        t = torch.empty((w.num_pages, w.Hkv, BLOCK, w.d), dtype=dt, device=device)
+        step = 4096
+        for p0 in range(0, w.num_pages, step):
+            p1 = min(w.num_pages, p0 + step)
+            t[p0:p1].copy_(torch.randn((p1 - p0, w.Hkv, BLOCK, w.d), generator=g, device=device,
+                                       dtype=torch.float32))
+        out.append(t)
+    return out[0], out[1]
 
 
 def decode_q_and_scores(w: DecodeWorkload):
