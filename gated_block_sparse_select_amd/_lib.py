@@ -17,7 +17,7 @@ BLOCK = 64
 
 EXPORTED = [
     "sas_abi_version", "sas_status_string", "sas_pool_workspace_bytes", "sas_pool_scores",
-    "sas_select", "sas_fwd", "sas_bwd_workspace_bytes", "sas_bwd",
+    "sas_select", "sas_mask_documents", "sas_fwd", "sas_bwd_workspace_bytes", "sas_bwd",
     "sas_decode_workspace_bytes", "sas_decode", "sas_decode_paged_workspace_bytes",
     "sas_decode_paged", "sas_prof_enable", "sas_prof_collect",
     "sas_last_hip_error",
@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
         L.sas_pool_scores.argtypes = [sp, vp, vp, vp, vp, sz, st]
         L.sas_select.restype = i32
         L.sas_select.argtypes = [sp, vp, vp, vp, vp, vp, st]
+        L.sas_mask_documents.restype = i32
+        L.sas_mask_documents.argtypes = [sp, vp, vp, st]
         L.sas_fwd.restype = i32
         L.sas_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, st]
         L.sas_bwd_workspace_bytes.restype = sz

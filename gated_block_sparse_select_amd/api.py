@@ -97,6 +97,37 @@ def sas_select(shape: SasShape, s, idx, cnt, log_gate, s_lse, stream=None):
                          _ptr(s_lse), _stream(stream)), "sas_select")
 
 
+def sas_mask_documents(shape: SasShape, doc_first, s, stream=None):
+    nb = shape.n // BLOCK
+    _check(doc_first, "doc_first", torch.int32, shape.B * nb)
+    _check(s, "s", torch.float32, shape.B * shape.Hkv * nb * nb)
+    _ok(lib().sas_mask_documents(ctypes.byref(shape), _ptr(doc_first), _ptr(s), _stream(stream)),
+        "sas_mask_documents")
+
+
+def doc_first_from_cu_seqlens(cu_seqlens, n: int):
+    """doc_first [len(cu_seqlens), n/64] int32 (host) from per-entry document
+    token offsets: cu_seqlens[b] is a nondecreasing list starting at 0 whose
+    entries are multiples of 64 and at most n (the last document runs to n)."""
+    if n % BLOCK:
+        raise ValueError("n must be a multiple of 64")
+    nb = n // BLOCK
+    out = torch.empty((len(cu_seqlens), nb), dtype=torch.int32)
+    for b, offs in enumerate(cu_seqlens):
+        offs = [int(x) for x in offs]
+        if not offs or offs[0] != 0 or any(x % BLOCK or x > n for x in offs) or \
+                any(y < x for x, y in zip(offs, offs[1:])):
+            raise ValueError(f"cu_seqlens[{b}] must start at 0, be nondecreasing, "
+                             "hold multiples of 64 and stay <= n")
+        first = 0
+        starts = {x // BLOCK for x in offs}
+        for i in range(nb):
+            if i in starts:
+                first = i
+            out[b, i] = first
+    return out
+
+
 def sas_fwd(shape: SasShape, q, k, v, idx, cnt, log_gate, o, lse, stream=None):
     dt = _dt(shape)
     nb = shape.n // BLOCK
@@ -212,7 +243,8 @@ def alloc_workspace(nbytes: int, device="cuda"):
 
 __all__ = [
     "make_shape", "make_decode_shape", "make_decode_paged_shape", "shape_of",
-    "sas_pool_workspace_bytes", "sas_pool_scores", "sas_select", "sas_fwd",
+    "sas_pool_workspace_bytes", "sas_pool_scores", "sas_select", "sas_mask_documents",
+    "doc_first_from_cu_seqlens", "sas_fwd",
     "sas_bwd_workspace_bytes", "sas_bwd", "sas_decode_workspace_bytes", "sas_decode",
     "sas_decode_paged_workspace_bytes", "sas_decode_paged", "sas_prof_enable", "sas_prof_collect",
     "alloc_select", "alloc_workspace", "status_string", "SasError", "SasShape", "SasDecodeShape",

@@ -23,6 +23,8 @@ struct ProfScope {
 // ---- selection (select.hip)
 // Training rows: rows = B*Hkv*nqb, q-block i = row % nqb, row stride nkb.
 // Decode rows (seq_lens != nullptr): rows = B*Hkv, i = (clamp(len,1,cap)-1)/64.
+hipError_t launch_mask_documents(const int32_t* doc_first, float* s, int B, int hkv, int nb,
+                                 hipStream_t st);
 hipError_t launch_select(const float* s, int32_t* idx, int32_t* cnt, float* log_gate,
                          float* s_lse, int rows, int nqb, int nkb, int topk,
                          const int32_t* seq_lens, int hkv, int cap, hipStream_t st);

@@ -247,9 +247,10 @@ __global__ void __launch_bounds__(256) bwd_ds_kernel(const float* __restrict__ d
   __syncthreads();
   const float tot = tot_s;
   const float sl_ = s_lse[row];
+  const int hist = sl_ > -INFINITY ? i : 0;   // a row without candidates has no gate
   for (int m = threadIdx.x; m < nqb; m += 256) {
     float val = 0.f;
-    if (m < i) {
+    if (m < hist) {
       const int sm = slot_of[m];
       val = (sm >= 0 ? dl[sm] : 0.f) - expf(s[row * nqb + m] - sl_) * tot;
     }

@@ -227,6 +227,15 @@ sas_status sas_select(const sas_shape* s, const float* sc, int32_t* idx, int32_t
                                      s->topk, nullptr, s->Hkv, s->n, stream));
 }
 
+sas_status sas_mask_documents(const sas_shape* s, const int32_t* doc_first, float* sc,
+                              hipStream_t stream) {
+  sas_status st = check_shape(s);
+  if (st != SAS_OK) return st;
+  if (!doc_first || !sc) return SAS_ERR_ARG;
+  clear_stale_error();
+  return from_hip(sas::launch_mask_documents(doc_first, sc, s->B, s->Hkv, s->n / SAS_BLOCK, stream));
+}
+
 sas_status sas_fwd(const sas_shape* s, const void* q, const void* k, const void* v,
                    const int32_t* idx, const int32_t* cnt, const float* log_gate, void* o,
                    float* lse, hipStream_t stream) {

@@ -65,4 +65,27 @@ hipError_t launch_select(const float* s, int32_t* idx, int32_t* cnt, float* lg, 
   return hipGetLastError();
 }
 
+// Packed batches: s[b,kv,i,m] = -inf for m < first block of block i's
+// document, which takes those blocks out of row i's candidates.  One 256-thread
+// workgroup per score row; a row writes at most i floats.
+__global__ void __launch_bounds__(256) mask_documents_kernel(const int32_t* __restrict__ doc_first,
+                                                             float* __restrict__ s, int hkv,
+                                                             int nb) {
+  const size_t row = blockIdx.x;          // (b, kv, i)
+  const int i = int(row % nb);
+  const int b = int(row / (size_t(nb) * hkv));
+  int f = doc_first[size_t(b) * nb + i];
+  f = f < 0 ? 0 : (f > i ? i : f);
+  float* srow = s + row * nb;
+  for (int m = threadIdx.x; m < f; m += 256) srow[m] = -INFINITY;
+}
+
+hipError_t launch_mask_documents(const int32_t* doc_first, float* s, int B, int hkv, int nb,
+                                 hipStream_t st) {
+  ProfScope ps("sas_mask_documents_kernel", st);
+  hipLaunchKernelGGL(mask_documents_kernel, dim3(size_t(B) * hkv * nb), dim3(256), 0, st,
+                     doc_first, s, hkv, nb);
+  return hipGetLastError();
+}
+
 }  // namespace sas

@@ -10,7 +10,10 @@
 // largest key T exactly; all keys > T are kept, and keys == T are kept lowest
 // index first until K blocks are chosen.  The kept blocks are emitted in
 // ascending order.  Every comparison is on the exact float bits, so the
-// result is bit-identical to a sort by (score desc, index asc).
+// result is bit-identical to a sort by (score desc, index asc).  A score of
+// -inf marks a block that is not a candidate (in a packed batch, a block of
+// an earlier document): it is left out of the LSE and never kept, so a row
+// keeps min(K, finite scores) blocks and a row without one gets LSE -inf.
 #pragma once
 
 #include "common.h"
@@ -22,36 +25,38 @@ SAS_DEV uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Selects min(topk, i) of the blocks m < i of srow.  emit(pos, m, log_gate)
-// is called by the lane holding the pos-th kept block (pos ascending with m).
-// Returns the number kept (wave-uniform); lse receives LSE(srow[0..i)), -inf
-// for i == 0.
+// Selects min(topk, candidates) of the blocks m < i of srow.  emit(pos, m,
+// log_gate) is called by the lane holding the pos-th kept block (pos
+// ascending with m).  Returns the number kept (wave-uniform); lse receives
+// the LSE over the candidates, -inf if there is none.
 template <int CPL, class Emit>
 SAS_DEV int select_row(const float* __restrict__ srow, int i, int topk, int lane, float& lse,
                        Emit&& emit) {
   float val[CPL];
   uint32_t key[CPL];
   float mx = -INFINITY;
+  int nc = 0;   // candidates: m < i with a finite score
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
     const int m = j * 64 + lane;
-    const bool ok = m < i;
-    val[j] = ok ? srow[m] : -INFINITY;
-    key[j] = ok ? order_key(val[j]) : 0u;  // 0 is below every finite key
+    val[j] = m < i ? srow[m] : -INFINITY;
+    const bool ok = val[j] > -INFINITY;
+    key[j] = ok ? order_key(val[j]) : 0u;  // 0 is below every candidate's key
+    nc += __popcll(__ballot(ok));
     mx = fmaxf(mx, val[j]);
   }
   mx = wave_max(mx);
   float se = 0.f;
 #pragma unroll
   for (int j = 0; j < CPL; ++j)
-    if (j * 64 + lane < i) se += expf(val[j] - mx);
+    if (key[j] != 0u) se += expf(val[j] - mx);
   se = wave_sum(se);
-  lse = (i > 0) ? mx + logf(se) : -INFINITY;
+  lse = nc > 0 ? mx + logf(se) : -INFINITY;
 
-  const int keff = topk < i ? topk : i;
-  uint32_t T = 0u;  // keep every valid key when keff == i
+  const int keff = topk < nc ? topk : nc;
+  uint32_t T = 0u;  // every candidate is kept when keff == nc
   int need_eq = 0;
-  if (keff < i && keff > 0) {
+  if (keff < nc && keff > 0) {
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t c = T | (1u << bit);
       int n_ge = 0;
@@ -72,8 +77,8 @@ SAS_DEV int select_row(const float* __restrict__ srow, int i, int topk, int lane
     bool take;
     if (keff == 0) {
       take = false;
-    } else if (keff == i) {
-      take = m < i;
+    } else if (keff == nc) {
+      take = key[j] != 0u;
     } else {
       const bool eq = key[j] == T;
       const uint64_t eqm = __ballot(eq);
@@ -93,7 +98,7 @@ SAS_DEV int select_row(const float* __restrict__ srow, int i, int topk, int lane
 // order, then j, then lanes visit m ascending.  The maximum, the exp sum
 // (summed in wave order, so the result is deterministic) and every count of
 // the threshold search are combined across waves through red, an LDS array of
-// at least 6*NW words; each of the 32 search rounds costs one barrier (its
+// at least 7*NW words; each of the 32 search rounds costs one barrier (its
 // counts alternate between two slots, so a slot is rewritten only after every
 // wave has read it).  Ties at the threshold and output positions follow from
 // the per-wave counts of the waves before.  Every thread of the workgroup must
@@ -107,36 +112,45 @@ SAS_DEV int select_row_wg(const float* __restrict__ srow, int i, int topk, int w
   float val[CPL];
   uint32_t key[CPL];
   float mx = -INFINITY;
+  int ncw = 0;   // this wave's candidates (m < i, finite score)
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
     const int m = m0 + j * 64 + lane;
-    const bool ok = m < i;
-    val[j] = ok ? srow[m] : -INFINITY;
+    val[j] = m < i ? srow[m] : -INFINITY;
+    const bool ok = val[j] > -INFINITY;
     key[j] = ok ? order_key(val[j]) : 0u;
+    ncw += __popcll(__ballot(ok));
     mx = fmaxf(mx, val[j]);
   }
   mx = wave_max(mx);
-  if (lane == 0) red[wave] = mx;
+  if (lane == 0) {
+    red[wave] = mx;
+    ired[6 * NW + wave] = ncw;
+  }
   __syncthreads();
   float gmx = -INFINITY;
+  int nc = 0;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) gmx = fmaxf(gmx, red[w]);
+  for (int w = 0; w < NW; ++w) {
+    gmx = fmaxf(gmx, red[w]);
+    nc += ired[6 * NW + w];
+  }
   float se = 0.f;
 #pragma unroll
   for (int j = 0; j < CPL; ++j)
-    if (m0 + j * 64 + lane < i) se += expf(val[j] - gmx);
+    if (key[j] != 0u) se += expf(val[j] - gmx);
   se = wave_sum(se);
   if (lane == 0) red[NW + wave] = se;
   __syncthreads();
   float gse = 0.f;
 #pragma unroll
   for (int w = 0; w < NW; ++w) gse += red[NW + w];
-  lse = (i > 0) ? gmx + logf(gse) : -INFINITY;
+  lse = nc > 0 ? gmx + logf(gse) : -INFINITY;
 
-  const int keff = topk < i ? topk : i;
+  const int keff = topk < nc ? topk : nc;
   uint32_t T = 0u;
   int need_eq = 0;
-  const bool search = keff < i && keff > 0;   // uniform over the workgroup
+  const bool search = keff < nc && keff > 0;   // uniform over the workgroup
   if (search) {
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t c = T | (1u << bit);
@@ -174,8 +188,8 @@ SAS_DEV int select_row_wg(const float* __restrict__ srow, int i, int topk, int w
   for (int w = 0; w < NW; ++w) {
     if (w >= wave) break;
     const int e_w = ired[5 * NW + w];
-    if (keff == i) {
-      base += min(64 * CPL, max(0, i - w * 64 * CPL));
+    if (keff == nc) {
+      base += ired[6 * NW + w];
     } else if (search) {
       base += ired[4 * NW + w] + min(e_w, max(0, need_eq - eq_before));
     }
@@ -189,8 +203,8 @@ SAS_DEV int select_row_wg(const float* __restrict__ srow, int i, int topk, int w
     bool take;
     if (keff == 0) {
       take = false;
-    } else if (keff == i) {
-      take = m < i;
+    } else if (keff == nc) {
+      take = key[j] != 0u;
     } else {
       const bool eq = key[j] == T;
       const uint64_t eqm = __ballot(eq);

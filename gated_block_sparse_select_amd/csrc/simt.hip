@@ -178,9 +178,10 @@ __global__ void __launch_bounds__(1024) bwd_dq_simt_kernel(
   const float sl = s_lse[rowsel];
   const float* srow = s + rowsel * nqb;
   float* dsrow = ds + rowsel * nqb;
+  const int hist = sl > -INFINITY ? i : 0;   // a row without candidates has no gate
   for (int m = threadIdx.x; m < nqb; m += blockDim.x) {
     float val = 0.f;
-    if (m < i) {
+    if (m < hist) {
       const int sl_m = slot_of[m];
       val = (sl_m >= 0 ? dlg_s[sl_m] : 0.f) - expf(srow[m] - sl) * tot;
     }

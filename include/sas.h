@@ -34,7 +34,10 @@
  *     caches); s, log_gate, s_lse, lse and ds are always float32; idx and cnt int32.
  *   - Calls are reentrant; calls on different streams may run concurrently as
  *     long as their output buffers do not overlap.
- *   - Scores must be finite (NaN/Inf in s is undefined behaviour).
+ *   - A score of -inf marks a history block that is not a candidate (in a
+ *     packed batch, a block of an earlier document): it is left out of the
+ *     gate's LSE, never kept, and gets ds = 0.  Other scores must be finite
+ *     (NaN or +inf in s is undefined behaviour).
  */
 #ifndef SAS_H_
 #define SAS_H_
@@ -114,10 +117,10 @@ sas_status sas_pool_scores(const sas_shape* shape, const void* q, const void* k,
 
 /* ---------------------------------------------------------------- selection
  * LSE-normalise and Top-K block-index builder [Review §2.2, §2.4].
- * For each row (b,kv,i) with history H = {0..i-1}:
- *   s_lse[b,kv,i]   = log sum_{m<i} exp s[b,kv,i,m]          (-inf when i == 0)
- *   cnt[b,kv,i]     = min(topk, i)
- *   idx[b,kv,i,:]   = the cnt history blocks with the largest scores, ties to the
+ * For each row (b,kv,i) with candidates C = {m < i : s[b,kv,i,m] > -inf}:
+ *   s_lse[b,kv,i]   = log sum_{m in C} exp s[b,kv,i,m]       (-inf when C is empty)
+ *   cnt[b,kv,i]     = min(topk, |C|)
+ *   idx[b,kv,i,:]   = the cnt candidates with the largest scores, ties to the
  *                     lower index (-0.0 == +0.0), listed in ascending order, then
  *                     padded with -1 up to topk
  *   log_gate[b,kv,i,j] = s[b,kv,i,idx[j]] - s_lse (j < cnt), -inf in the padding
@@ -127,6 +130,23 @@ sas_status sas_pool_scores(const sas_shape* shape, const void* q, const void* k,
  * idx and log_gate may be NULL when topk == 0. */
 sas_status sas_select(const sas_shape* shape, const float* s, int32_t* idx, int32_t* cnt,
                       float* log_gate, float* s_lse, hipStream_t stream);
+
+/* ---------------------------------------------------------------- packed batches
+ * Several documents packed into one sequence, each starting on a block
+ * boundary (pad a document to a multiple of 64 tokens; its padding sits after
+ * its last real token, so causal masking keeps it out of every real row).  A
+ * q-block attends only to blocks of its own document [Review §2.2 and §2.4,
+ * applied per document]: this call sets, in place,
+ *   s[b,kv,i,m] = -inf   for m < doc_first[b,i]
+ * and leaves every other entry unchanged; sas_select, sas_fwd, sas_bwd and
+ * sas_decode then treat those blocks as non-candidates (see the -inf rule
+ * above), so the packed run gives each document what a run over it alone gives.
+ *   doc_first: device int32 [B,n/64], the first block of the document holding
+ *              block i (0 <= doc_first[b,i] <= i; other values are clamped to
+ *              that range).
+ *   s: device float32 [B,Hkv,n/64,n/64], modified in place. */
+sas_status sas_mask_documents(const sas_shape* shape, const int32_t* doc_first, float* s,
+                              hipStream_t stream);
 
 /* ---------------------------------------------------------------- forward
  * Gated block-sparse attention forward [Review §2.3 equation, §2.6].
@@ -146,8 +166,9 @@ sas_status sas_fwd(const sas_shape* shape, const void* q, const void* k, const v
  *   dq [B,Hq,n,d], dk, dv [B,Hkv,n,d]  (dtype of q; written, not accumulated)
  *   ds [B,Hkv,n/64,n/64] float32: for m < i,
  *        ds[i,m] = [m kept] dlg[i,m] - pi_i[m] * sum_{m' kept} dlg[i,m'],
- *        pi_i = softmax of s[i, 0..i-1], dlg[i,m] = sum of the logit gradients of
- *        the group's heads over rows of block i and keys of block m;
+ *        pi_i = softmax of s[i,:] over the row's candidates (0 elsewhere, and
+ *        0 in a row without candidates), dlg[i,m] = sum of the logit gradients
+ *        of the group's heads over rows of block i and keys of block m;
  *      and ds[i,m] = 0 for m >= i (every entry is written).
  * o and lse must come from sas_fwd on the same inputs; s, idx, cnt, log_gate
  * and s_lse are the sas_select inputs/outputs (idx ascending, as it writes).  ws: device scratch of at least

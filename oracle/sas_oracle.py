@@ -37,6 +37,9 @@ notes):
   and current block i.
 * the LSE runs over all history blocks, selected or not; with fewer than K
   history blocks all of them are selected (still gated).
+* a score of -inf marks a history block that is not a candidate: no part of
+  the LSE, never kept, ds = 0; a packed batch of block-aligned documents puts
+  -inf on every block of an earlier document (``mask_documents``).
 * ties in s go to the lower block index; -0.0 and +0.0 are equal.
 * idx lists the selected blocks in ascending order, padded with -1; padded
   log_gate entries are -inf; s_lse of a row with no history is -inf.
@@ -94,17 +97,43 @@ def select_row(srow, i: int, topk: int):
     [Review §2.2]: keep the Top-K history blocks by score.  [Review §2.4]:
     log g_m = s_m - LSE over all history blocks.  Ranking key (-s_m, m) makes
     ties go to the lower index; adding +0.0 turns -0.0 into +0.0 first.
+    A score of -inf marks a block that is not a candidate (in a packed batch,
+    a block of an earlier document): it takes no part in the LSE and is never
+    kept, so a row keeps min(K, number of finite scores) blocks, and a row
+    with no finite score keeps none and has s_lse = -inf.
     Pinned by: a sort-free rank-count brute force, integer and signed-zero tie
-    fixtures, shift invariance, permutation covariance, K = 0 and K >= i.
+    fixtures, shift invariance, permutation covariance, K = 0 and K >= i, and
+    packed documents matching separate runs.
     """
-    if i == 0:
-        return [], [], NEG_INF
     h = _f64(srow[:i]) + 0.0
-    mx = float(h.max())
-    s_lse = mx + math.log(float(np.sum(np.exp(h - mx))))
-    order = sorted(range(i), key=lambda m: (-h[m], m))
-    chosen = sorted(order[:min(topk, i)])
+    cand = [m for m in range(i) if h[m] > NEG_INF]
+    if not cand:
+        return [], [], NEG_INF
+    hc = h[cand]
+    mx = float(hc.max())
+    s_lse = mx + math.log(float(np.sum(np.exp(hc - mx))))
+    order = sorted(cand, key=lambda m: (-h[m], m))
+    chosen = sorted(order[:min(topk, len(cand))])
     return chosen, [float(h[m]) - s_lse for m in chosen], s_lse
+
+
+def mask_documents(s, doc_first):
+    """Packed batch: return a copy of s with s[b,kv,i,m] = -inf for every
+    m < doc_first[b,i] (the blocks of earlier documents), clamped to
+    0 <= doc_first <= i.
+
+    [Review §2.2, §2.4] applied per document: a q-block's candidates and its
+    gate normalisation are its own document's earlier blocks.  Pinned by the
+    packed-documents test: a packed run through this mask equals, block for
+    block, separate runs over each document, with zero ds across documents.
+    """
+    out = _f64(s).copy()
+    B, Hkv, NQB, _ = out.shape
+    for b in range(B):
+        for i in range(NQB):
+            f = min(max(int(doc_first[b][i]), 0), i)
+            out[b, :, i, :f] = NEG_INF
+    return out
 
 
 def select(s, topk: int):
@@ -259,7 +288,9 @@ def gate_jacobian(s, s_lse, idx, cnt, dlg):
 
     log g_m = s_m - LSE(s_H) for m in H_i, so for every history block m:
     ds[i, m] = [m selected] dlg[i, m] - pi_i[m] * sum_{m' selected} dlg[i, m'],
-    pi_i = softmax(s[i, H_i]) = exp(s - s_lse).  Entries m >= i are 0.
+    pi_i = softmax(s[i, H_i]) = exp(s - s_lse).  Entries m >= i are 0, and so
+    are blocks with s = -inf (not candidates, pi = 0) and rows with no
+    candidate at all (no gate, s_lse = -inf).
     Pinned by finite differences through select + forward, and by
     sum_m ds[i, m] = 0.
     """
@@ -270,6 +301,8 @@ def gate_jacobian(s, s_lse, idx, cnt, dlg):
         for kv in range(Hkv):
             for i in range(1, NQB):
                 c = int(cnt[b, kv, i])
+                if s_lse[b, kv, i] == NEG_INF:
+                    continue
                 pi = np.exp(s[b, kv, i, :i] - s_lse[b, kv, i])
                 tot = float(np.sum(dlg[b, kv, i, :c]))
                 ds[b, kv, i, :i] = -pi * tot

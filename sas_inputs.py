@@ -34,7 +34,7 @@ import numpy as np
 
 BLOCK = 64
 
-TID_Q, TID_K, TID_V, TID_S, TID_DO, TID_LEN, TID_PAGES = 0, 1, 2, 3, 4, 5, 6
+TID_Q, TID_K, TID_V, TID_S, TID_DO, TID_LEN, TID_PAGES, TID_DOCS = 0, 1, 2, 3, 4, 5, 6, 7
 
 
 @dataclasses.dataclass(frozen=True)
@@ -51,6 +51,7 @@ class Workload:
     qkv_std: float = 1.0
     s_kind: str = "normal"   # "normal" | "pool" | "gumbel3"
     s_std: float = 1.0
+    packed: bool = False     # each batch entry packs several documents (make_doc_first)
 
     @property
     def nqb(self) -> int:
@@ -83,6 +84,7 @@ WORKLOAD_NAMES = {
     2: "qwen3-4b-layer-n8192-K16",
     3: "qwen3-8b-layer-n32768-K32",
     4: "qwen3-14b-layer-n32768-K64",
+    7: "qwen3-8b-layer-n32768-K32-packed",
     5: "decode-qwen3-8b-B64-cache32768-K32",
 }
 
@@ -92,6 +94,7 @@ WORKLOADS = {
                 s_kind="normal", s_std=math.sqrt(2.0)),
     3: Workload(3, 1, 32, 8, 32768, 128, 32, "bf16", s_kind="pool"),
     4: Workload(4, 1, 40, 8, 32768, 128, 64, "bf16", s_kind="gumbel3"),
+    7: Workload(7, 1, 32, 8, 32768, 128, 32, "bf16", s_kind="normal", packed=True),
 }
 
 DECODE_WORKLOAD = DecodeWorkload(5, 64, 32, 8, 32768, 128, 32)
@@ -190,10 +193,42 @@ def make_scores(w: Workload) -> np.ndarray | None:
 
 def custom_workload(seed: int, B: int, Hq: int, Hkv: int, n: int, d: int, topk: int,
                     dtype: str = "bf16", s_kind: str = "normal", qkv_std: float = 1.0,
-                    s_std: float = 1.0) -> Workload:
+                    s_std: float = 1.0, packed: bool = False) -> Workload:
     """A smaller workload with the same value distributions (parity tests)."""
     return Workload(seed, B, Hq, Hkv, n, d, topk, dtype, qkv_std=qkv_std,
-                    s_kind=s_kind, s_std=s_std)
+                    s_kind=s_kind, s_std=s_std, packed=packed)
+
+
+# ---------------------------------------------------------------- packed documents
+def doc_first_of(doc_blocks) -> np.ndarray:
+    """int32 [sum(doc_blocks)]: the first block of the document holding each
+    block, for documents of doc_blocks[j] blocks laid end to end."""
+    first, start = [], 0
+    for nb in doc_blocks:
+        first += [start] * int(nb)
+        start += int(nb)
+    return np.array(first, dtype=np.int32)
+
+
+def packed_doc_blocks(cfg: int, b: int, nb: int) -> list[int]:
+    """Document lengths (in blocks) of batch entry b: log-uniform between one
+    block and the whole sequence, drawn until the nb blocks are filled (the
+    last document is cut at the end), so long and short documents mix."""
+    g = np.random.default_rng([cfg, TID_DOCS, b])
+    out, left = [], nb
+    while left > 0:
+        ln = int(np.exp(g.uniform(0.0, math.log(nb + 1))))
+        ln = max(1, min(ln, left))
+        out.append(ln)
+        left -= ln
+    return out
+
+
+def make_doc_first(w: Workload) -> np.ndarray | None:
+    """doc_first [B, NQB] int32 of a packed workload, None otherwise."""
+    if not w.packed:
+        return None
+    return np.stack([doc_first_of(packed_doc_blocks(w.cfg, b, w.nqb)) for b in range(w.B)])
 
 
 # ---------------------------------------------------------------- decode

@@ -28,10 +28,11 @@ def tdtype(w_dtype: str):
     return torch.float32 if w_dtype == "f32" else torch.bfloat16
 
 
-def run_layer(api, q, k, v, do, s, topk, dtype, scale=0.0, pool=False, bwd=True):
-    """Run (pool) -> select -> fwd (-> bwd) on device tensors; returns a dict of
-    device tensors.  q,k,v,do are device tensors; s is a device float32 tensor
-    or None when pool=True."""
+def run_layer(api, q, k, v, do, s, topk, dtype, scale=0.0, pool=False, bwd=True, doc_first=None):
+    """Run (pool) -> (mask documents) -> select -> fwd (-> bwd) on device
+    tensors; returns a dict of device tensors.  q,k,v,do are device tensors; s
+    is a device float32 tensor (masked in place when doc_first, a device int32
+    [B, n/64] tensor, is given) or None when pool=True."""
     B, Hq, n, d = q.shape
     Hkv = k.shape[1]
     nb = n // BLOCK
@@ -41,6 +42,8 @@ def run_layer(api, q, k, v, do, s, topk, dtype, scale=0.0, pool=False, bwd=True)
         s = torch.empty((B, Hkv, nb, nb), dtype=torch.float32, device="cuda")
         ws = api.alloc_workspace(api.sas_pool_workspace_bytes(sh))
         api.sas_pool_scores(sh, q, k, s, ws)
+    if doc_first is not None:
+        api.sas_mask_documents(sh, doc_first, s)
     out["s"] = s
     sel = api.alloc_select(sh)
     api.sas_select(sh, s, sel["idx"], sel["cnt"], sel["log_gate"], sel["s_lse"])

@@ -78,6 +78,11 @@ def test_null_pointers_rejected():
     assert L.sas_fwd(ctypes.byref(sh), None, *([FAKE] * 7), None) == 1
     assert L.sas_bwd(ctypes.byref(sh), *([FAKE] * 14), None, FAKE, 1 << 40, None) == 1
     assert L.sas_select(None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert L.sas_mask_documents(ctypes.byref(sh), None, FAKE, None) == 1
+    assert L.sas_mask_documents(ctypes.byref(sh), FAKE, None, None) == 1
+    assert L.sas_mask_documents(None, FAKE, FAKE, None) == 1
+    bad = api.make_shape(1, 4, 2, 500, 128, 2)     # n not a multiple of 64
+    assert L.sas_mask_documents(ctypes.byref(bad), FAKE, FAKE, None) == 1
     # topk == 0 allows NULL idx / log_gate
     sh0 = api.make_shape(1, 4, 2, 512, 128, 0)
     assert L.sas_pool_scores(ctypes.byref(sh0), FAKE, FAKE, FAKE, None, 0, None) == 4
@@ -142,3 +147,11 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(ValueError):
         api.sas_fwd(sh, t, t, t, None, torch.zeros(1, dtype=torch.int32), None, t,
                     torch.zeros(64))
+
+
+def test_doc_first_from_cu_seqlens():
+    df = api.doc_first_from_cu_seqlens([[0, 192, 256], [0], [0, 64, 64, 512]], 512)
+    assert df.tolist() == [[0, 0, 0, 3, 4, 4, 4, 4], [0] * 8, [0, 1, 1, 1, 1, 1, 1, 1]]
+    for bad in ([[64, 128]], [[0, 100]], [[0, 256, 128]], [[0, 576]]):
+        with pytest.raises(ValueError):
+            api.doc_first_from_cu_seqlens(bad, 512)

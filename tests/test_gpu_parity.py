@@ -89,6 +89,20 @@ def test_select_full_size(api, cfg):
     _check_select(sel, s, w.topk)
 
 
+def test_mask_documents_bitexact(api):
+    g = np.random.default_rng(12)
+    B, Hkv, nb = 3, 2, 200
+    s = g.standard_normal((B, Hkv, nb, nb)).astype(np.float32)
+    df = np.stack([si.doc_first_of(si.packed_doc_blocks(12, b, nb)) for b in range(B)])
+    df[2, ::7] = np.where(np.arange(0, nb, 7) % 2, -3, nb + 5)   # clamped into [0, i]
+    sh = api.make_shape(B, 2 * Hkv, Hkv, nb * BLOCK, 128, 4, torch.bfloat16)
+    st = torch.from_numpy(s).cuda()
+    api.sas_mask_documents(sh, torch.from_numpy(df).cuda(), st)
+    torch.cuda.synchronize()
+    ref = oracle.mask_documents(s, df).astype(np.float32)
+    assert np.array_equal(host(st), ref)
+
+
 # ---------------------------------------------------------------- pooling
 @pytest.mark.parametrize("cfg,small", [(3, True), (3, False)])
 def test_pool_parity(api, cfg, small):
@@ -121,17 +135,33 @@ SMALL_CASES = {
     "fp32_gqa2_d128": (si.custom_workload(108, 1, 4, 2, 384, 128, 2, "f32"), None),
     # 16 query heads per kv-head: four head chunks in the forward and dq
     "bf16_gqa16_d128": (si.custom_workload(109, 1, 16, 1, 512, 128, 3, "bf16"), None),
+    # packed documents (scores of earlier documents masked to -inf on the device)
+    "bf16_packed_gqa4_d128": (si.custom_workload(110, 2, 8, 2, 1536, 128, 4, "bf16",
+                                                 packed=True), None),
+    "fp32_packed_d64": (si.custom_workload(111, 1, 2, 1, 1024, 64, 3, "f32", packed=True), None),
 }
+
+
+def _scores(w):
+    """(device scores as the library should receive them, doc_first on the
+    device or None, host scores after the oracle's document mask)."""
+    s = si.make_scores(w)
+    df = si.make_doc_first(w)
+    if df is None:
+        return torch.from_numpy(s).cuda(), None, s
+    return (torch.from_numpy(s).cuda(), torch.from_numpy(df).cuda(),
+            oracle.mask_documents(s, df).astype(np.float32))
 
 
 @pytest.mark.parametrize("name", list(SMALL_CASES))
 def test_fwd_parity_full(api, name):
     w, _ = SMALL_CASES[name]
     q, k, v, _ = si.make_qkv(w, with_do=False)
-    s = si.make_scores(w)
+    sd, df, s = _scores(w)
     dt = tdtype(w.dtype)
-    res = run_layer(api, dev(q, dt), dev(k, dt), dev(v, dt), None, torch.from_numpy(s).cuda(),
-                    w.topk, dt, bwd=False)
+    res = run_layer(api, dev(q, dt), dev(k, dt), dev(v, dt), None, sd, w.topk, dt, bwd=False,
+                    doc_first=df)
+    assert np.array_equal(host(res["s"]), s)
     idx, cnt, lg, _ = _check_select(res, s, w.topk)
     o, lse = oracle.fwd_gather(q, k, v, idx, cnt, lg)
     tol = TOL[w.dtype]
@@ -143,10 +173,10 @@ def test_fwd_parity_full(api, name):
 def test_layer_parity_full(api, name):
     w, _ = SMALL_CASES[name]
     q, k, v, do = si.make_qkv(w)
-    s = si.make_scores(w)
+    sd, df, s = _scores(w)
     dt = tdtype(w.dtype)
-    res = run_layer(api, dev(q, dt), dev(k, dt), dev(v, dt), dev(do, dt),
-                    torch.from_numpy(s).cuda(), w.topk, dt)
+    res = run_layer(api, dev(q, dt), dev(k, dt), dev(v, dt), dev(do, dt), sd, w.topk, dt,
+                    doc_first=df)
     idx, cnt, lg, _ = _check_select(res, s, w.topk)
     ref = oracle.sas_forward_backward(q, k, v, do, s, w.topk)
     tol = TOL[w.dtype]
@@ -155,6 +185,9 @@ def test_layer_parity_full(api, name):
     for nm in ("dq", "dk", "dv", "ds"):
         e = rel_l2(host(res[nm]), ref[nm])
         assert e <= tol["grad"], (nm, e)
+    if df is not None:   # no gradient reaches another document's blocks
+        ds_g = host(res["ds"])
+        assert np.all(ds_g[np.isneginf(s)] == 0.0)
 
 
 # ---------------------------------------------------------------- full-size sampled checks
@@ -165,24 +198,32 @@ def _sample_blocks(w, rng, n_blocks=5):
     return sorted(picks)
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4])
+@pytest.mark.parametrize("cfg", [2, 3, 4, 7])
 def test_layer_parity_full_size_sampled(api, cfg):
     w = si.WORKLOADS[cfg]
     q, k, v, do = si.make_qkv(w)
     dt = tdtype(w.dtype)
     qd, kd, vd, dod = dev(q, dt), dev(k, dt), dev(v, dt), dev(do, dt)
+    df = None
     if w.s_kind == "pool":
         res = run_layer(api, qd, kd, vd, dod, None, w.topk, dt, pool=True)
         s = host(res["s"])      # selection parity is defined on the device scores
     else:
-        s = si.make_scores(w)
-        res = run_layer(api, qd, kd, vd, dod, torch.from_numpy(s).cuda(), w.topk, dt)
+        sd, df, s = _scores(w)
+        res = run_layer(api, qd, kd, vd, dod, sd, w.topk, dt, doc_first=df)
+        assert np.array_equal(host(res["s"]), s)
     idx, cnt, lg, s_lse = _check_select(res, s, w.topk)
     rng = np.random.default_rng(cfg)
     G = w.Hq // w.Hkv
     tol = TOL[w.dtype]
     o_g, lse_g, dq_g, ds_g = host(res["o"]), host(res["lse"]), host(res["dq"]), host(res["ds"])
-    for (b, kv, i) in _sample_blocks(w, rng):
+    picks = _sample_blocks(w, rng)
+    if df is not None:
+        # a document's first block (no candidates) and the block after it
+        starts = [i for i in range(1, w.nqb) if df[0, i] == i and i + 1 < w.nqb]
+        picks += [(0, 1, starts[0]), (0, 2, starts[0] + 1), (0, 3, starts[-1])]
+        assert np.all(ds_g[np.isneginf(s)] == 0.0)
+    for (b, kv, i) in picks:
         ob, lb = oracle.fwd_gather_block(q, k, v, idx, cnt, lg, b, kv, i)
         r = slice(i * BLOCK, (i + 1) * BLOCK)
         hs = slice(kv * G, (kv + 1) * G)
@@ -331,6 +372,52 @@ def test_decode_paged_long_context(api, ties, K):
     o, idx = _decode_paged_run(api, "bf16", q, kp, vp, table, lens, s, K)
     ref_o, ref_idx = oracle.decode(q, _PagedRows(kp, table), _PagedRows(vp, table), lens, s, K)
     assert np.array_equal(idx, ref_idx)
+    assert_o(o, ref_o, "bf16")
+
+
+def _mask_history(s, g, first):
+    """-inf on the blocks before first[b] (an earlier document) and on a
+    random tenth of the rest."""
+    s = s.copy()
+    for b in range(s.shape[0]):
+        s[b, :, :first[b]] = -np.inf
+    s[g.random(s.shape) < 0.1] = -np.inf
+    return s
+
+
+def test_decode_masked_scores(api):
+    """Decode rows whose history holds non-candidate (-inf) blocks, one row
+    with none left (only the current block is attended)."""
+    w = si.DecodeWorkload(260, 5, 8, 2, 1024, 128, 5, "bf16", hist_blocks=15)
+    q, kc, vc, lens, s = si.make_decode_small(w)
+    g = np.random.default_rng(260)
+    s = _mask_history(s, g, [0, 3, 9, 15, 1])
+    s[4] = -np.inf
+    dt = tdtype(w.dtype)
+    o, idx = _decode_run(api, w, dev(q, dt), dev(kc, dt), dev(vc, dt), lens, s)
+    ref_o, ref_idx = oracle.decode(q, kc, vc, lens, s, w.topk)
+    assert np.array_equal(host(idx), ref_idx)
+    assert np.all(host(idx)[4] == -1)
+    assert_o(host(o), ref_o, "bf16")
+
+
+def test_decode_paged_masked_long_context(api):
+    """The workgroup selection over up to 8191 history blocks with -inf
+    blocks: fewer candidates than K in one row, none in another."""
+    B, Hq, Hkv, d, K = 4, 4, 2, 64, 32
+    max_blocks, num_pages = 8192, 4096
+    lens = [BLOCK * max_blocks, 300000, 200000, 5000]
+    q, kp, vp, table, lens, s = si.make_decode_paged(470, B, Hq, Hkv, max_blocks, num_pages, d,
+                                                     "bf16", seq_lens=lens)
+    g = np.random.default_rng(470)
+    s = _mask_history(s, g, [4000, 0, 3120, 0])
+    s[1, :, :4680] = -np.inf                     # row 1: at most 7 candidates left (< K)
+    s[1, :, 4680:4692] = g.standard_normal((Hkv, 12)).astype(np.float32)
+    s[3] = -np.inf                               # row 3: no candidate
+    o, idx = _decode_paged_run(api, "bf16", q, kp, vp, table, lens, s, K)
+    ref_o, ref_idx = oracle.decode(q, _PagedRows(kp, table), _PagedRows(vp, table), lens, s, K)
+    assert np.array_equal(idx, ref_idx)
+    assert np.all(idx[3] == -1)
     assert_o(o, ref_o, "bf16")
 
 
