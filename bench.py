@@ -38,6 +38,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", type=int, default=3, choices=[2, 3, 4])
     p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-full-range", action="store_true", help="skip the full-range (K = n/64) line")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     p.add_argument("--decode-steps", type=int, default=50)
     p.add_argument("--copy-calibration", action="store_true",
@@ -52,8 +53,10 @@ def pair_count(cnt_np, G):
     return G * (int(c.sum()) * 64 * 64 + c.size * (64 * 65 // 2))
 
 
-def run_training(args, api, si, torch, np):
-    w = si.WORKLOADS[args.workload]
+def run_training(args, api, si, torch, np, w=None, steps=None, warmup=None):
+    w = si.WORKLOADS[args.workload] if w is None else w
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
     dt = torch.bfloat16
     q, k, v, do = si.make_qkv(w)
     dev = lambda x: torch.from_numpy(x).to("cuda").to(dt)
@@ -81,7 +84,7 @@ def run_training(args, api, si, torch, np):
         api.sas_bwd(sh, qd, kd, vd, o, dod, lse, sel["idx"], sel["cnt"], sel["log_gate"], s,
                     sel["s_lse"], dq, dk, dv, ds, ws_bwd)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     api.sas_prof_collect()          # drop anything recorded before
@@ -90,14 +93,14 @@ def run_training(args, api, si, torch, np):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     api.sas_prof_enable(False)
     kern = api.sas_prof_collect()
-    ms_step = ev0.elapsed_time(ev1) / args.steps
+    ms_step = ev0.elapsed_time(ev1) / steps
 
     cnt = sel["cnt"].cpu().numpy()
     G = w.Hq // w.Hkv
@@ -106,7 +109,22 @@ def run_training(args, api, si, torch, np):
     flop_bwd = 10 * w.d * pairs
     per_kernel = {name: dict(avg_ms=tot / max(nl, 1), launches=nl) for name, (tot, nl) in kern.items()}
     return dict(w=w, ms_step=ms_step, wall=wall, pairs=pairs, flop_fwd=flop_fwd, flop_bwd=flop_bwd,
-                per_kernel=per_kernel, host=host, s=s, sel=sel, steps=args.steps)
+                per_kernel=per_kernel, host=host, s=s, sel=sel, steps=steps)
+
+
+def run_full_range(args, api, si, torch, np):
+    """Full-range gated attention (every history block kept with its gate) on
+    the 32K layer: the same kernels with K = n/64."""
+    w = si.WORKLOADS[8]
+    res = run_training(args, api, si, torch, np, w=w, steps=max(1, args.steps // 4), warmup=1)
+    total = res["flop_fwd"] + res["flop_bwd"]
+    tf = total / (res["ms_step"] * 1e-3) / 1e12
+    out = {"workload": w.name, "topk": w.topk, "steps": res["steps"],
+           "ms_per_step": round(res["ms_step"], 3), "TFLOPs": round(tf, 1),
+           "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+           "per_kernel_ms": {k: round(v["avg_ms"], 3) for k, v in res["per_kernel"].items()}}
+    res.clear()
+    return out
 
 
 # Translation units of the kernels whose HBM traffic the committed counter
@@ -359,7 +377,11 @@ def main():
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(res, np)
-    res["host"] = None
+    res.clear()
+    torch.cuda.empty_cache()
+    if not args.no_full_range:
+        line["full_range"] = run_full_range(args, api, si, torch, np)
+        torch.cuda.empty_cache()
     if not args.no_decode:
         torch.cuda.empty_cache()
         line["decode"] = run_decode(args, api, si, torch, np)

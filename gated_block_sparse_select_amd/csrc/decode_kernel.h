@@ -163,7 +163,7 @@ __global__ void __launch_bounds__(256) decode_kernel(
       if (lane == 0) scnt = keff;
     }
   } else {
-    __shared__ float sel_red[7 * SW];
+    __shared__ float sel_red[6 * SW];
     float lse;
     const int keff = select_row_wg<CPL, SW>(srow, icur, topk, wave, lane, lse,
                                             (__attribute__((address_space(3))) float*)sel_red, emit);

@@ -25,71 +25,74 @@ SAS_DEV uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// order_key(-inf): below the key of every finite score, which is at least
+// order_key(-FLT_MAX) = kNoKey + 1.  A key <= kNoKey is not a candidate.
+constexpr uint32_t kNoKey = 0x007FFFFFu;
+
 // Selects min(topk, candidates) of the blocks m < i of srow.  emit(pos, m,
 // log_gate) is called by the lane holding the pos-th kept block (pos
 // ascending with m).  Returns the number kept (wave-uniform); lse receives
 // the LSE over the candidates, -inf if there is none.
+//
+// Non-candidates (m >= i or a score of -inf) carry key kNoKey, below every
+// candidate's key, so the search ends with T <= kNoKey exactly when fewer
+// than topk candidates exist, and then every key > kNoKey is kept.  The number kept is the
+// running output position, so no separate candidate count is needed.
 template <int CPL, class Emit>
 SAS_DEV int select_row(const float* __restrict__ srow, int i, int topk, int lane, float& lse,
                        Emit&& emit) {
   float val[CPL];
   uint32_t key[CPL];
   float mx = -INFINITY;
-  int nc = 0;   // candidates: m < i with a finite score
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
     const int m = j * 64 + lane;
     val[j] = m < i ? srow[m] : -INFINITY;
-    const bool ok = val[j] > -INFINITY;
-    key[j] = ok ? order_key(val[j]) : 0u;  // 0 is below every candidate's key
-    nc += __popcll(__ballot(ok));
+    key[j] = order_key(val[j]);
     mx = fmaxf(mx, val[j]);
   }
   mx = wave_max(mx);
   float se = 0.f;
 #pragma unroll
-  for (int j = 0; j < CPL; ++j)
-    if (key[j] != 0u) se += expf(val[j] - mx);
+  for (int j = 0; j < CPL; ++j) se += expf(val[j] - mx);   // -inf terms add 0
   se = wave_sum(se);
-  lse = nc > 0 ? mx + logf(se) : -INFINITY;
+  lse = mx > -INFINITY ? mx + logf(se) : -INFINITY;
 
-  const int keff = topk < nc ? topk : nc;
-  uint32_t T = 0u;  // every candidate is kept when keff == nc
+  // keep keys > T, then keys == T lowest index first until need_eq are kept;
+  // topk == 0 keeps nothing (no key exceeds ~0), topk >= i every candidate
+  uint32_t T = topk > 0 ? kNoKey : ~0u;
   int need_eq = 0;
-  if (keff < nc && keff > 0) {
+  if (topk > 0 && topk < i) {
+    uint32_t th = 0u;   // largest th with at least topk keys >= th
     for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t c = T | (1u << bit);
+      const uint32_t c = th | (1u << bit);
       int n_ge = 0;
 #pragma unroll
       for (int j = 0; j < CPL; ++j) n_ge += __popcll(__ballot(key[j] >= c));
-      if (n_ge >= keff) T = c;
+      if (n_ge >= topk) th = c;
     }
-    int n_gt = 0;
+    if (th > kNoKey) {
+      T = th;
+      int n_gt = 0;
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) n_gt += __popcll(__ballot(key[j] > T));
-    need_eq = keff - n_gt;
+      for (int j = 0; j < CPL; ++j) n_gt += __popcll(__ballot(key[j] > T));
+      need_eq = topk - n_gt;
+    }
   }
 
   int base = 0, eq_seen = 0;
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
     const int m = j * 64 + lane;
-    bool take;
-    if (keff == 0) {
-      take = false;
-    } else if (keff == nc) {
-      take = key[j] != 0u;
-    } else {
-      const bool eq = key[j] == T;
-      const uint64_t eqm = __ballot(eq);
-      take = key[j] > T || (eq && eq_seen + mask_rank(eqm) < need_eq);
-      eq_seen += __popcll(eqm);
-    }
+    const bool eq = key[j] == T;
+    const uint64_t eqm = __ballot(eq);
+    const bool take = key[j] > T || (eq && eq_seen + mask_rank(eqm) < need_eq);
+    eq_seen += __popcll(eqm);
     const uint64_t tm = __ballot(take);
     if (take) emit(base + mask_rank(tm), m, val[j] - lse);
     base += __popcll(tm);
   }
-  return keff;
+  return base;
 }
 
 // The same selection by a workgroup of NW waves, for rows of up to
@@ -98,7 +101,7 @@ SAS_DEV int select_row(const float* __restrict__ srow, int i, int topk, int lane
 // order, then j, then lanes visit m ascending.  The maximum, the exp sum
 // (summed in wave order, so the result is deterministic) and every count of
 // the threshold search are combined across waves through red, an LDS array of
-// at least 7*NW words; each of the 32 search rounds costs one barrier (its
+// at least 6*NW words; each of the 32 search rounds costs one barrier (its
 // counts alternate between two slots, so a slot is rewritten only after every
 // wave has read it).  Ties at the threshold and output positions follow from
 // the per-wave counts of the waves before.  Every thread of the workgroup must
@@ -112,48 +115,36 @@ SAS_DEV int select_row_wg(const float* __restrict__ srow, int i, int topk, int w
   float val[CPL];
   uint32_t key[CPL];
   float mx = -INFINITY;
-  int ncw = 0;   // this wave's candidates (m < i, finite score)
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
     const int m = m0 + j * 64 + lane;
     val[j] = m < i ? srow[m] : -INFINITY;
-    const bool ok = val[j] > -INFINITY;
-    key[j] = ok ? order_key(val[j]) : 0u;
-    ncw += __popcll(__ballot(ok));
+    key[j] = order_key(val[j]);
     mx = fmaxf(mx, val[j]);
   }
   mx = wave_max(mx);
-  if (lane == 0) {
-    red[wave] = mx;
-    ired[6 * NW + wave] = ncw;
-  }
+  if (lane == 0) red[wave] = mx;
   __syncthreads();
   float gmx = -INFINITY;
-  int nc = 0;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    gmx = fmaxf(gmx, red[w]);
-    nc += ired[6 * NW + w];
-  }
+  for (int w = 0; w < NW; ++w) gmx = fmaxf(gmx, red[w]);
   float se = 0.f;
 #pragma unroll
-  for (int j = 0; j < CPL; ++j)
-    if (key[j] != 0u) se += expf(val[j] - gmx);
+  for (int j = 0; j < CPL; ++j) se += expf(val[j] - gmx);   // -inf terms add 0
   se = wave_sum(se);
   if (lane == 0) red[NW + wave] = se;
   __syncthreads();
   float gse = 0.f;
 #pragma unroll
   for (int w = 0; w < NW; ++w) gse += red[NW + w];
-  lse = nc > 0 ? gmx + logf(gse) : -INFINITY;
+  lse = gmx > -INFINITY ? gmx + logf(gse) : -INFINITY;
 
-  const int keff = topk < nc ? topk : nc;
-  uint32_t T = 0u;
-  int need_eq = 0;
-  const bool search = keff < nc && keff > 0;   // uniform over the workgroup
+  uint32_t T = topk > 0 ? kNoKey : ~0u;
+  const bool search = topk > 0 && topk < i;   // uniform over the workgroup
+  uint32_t th = 0u;   // largest th with at least topk keys >= th
   if (search) {
     for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t c = T | (1u << bit);
+      const uint32_t c = th | (1u << bit);
       int n = 0;
 #pragma unroll
       for (int j = 0; j < CPL; ++j) n += __popcll(__ballot(key[j] >= c));
@@ -163,16 +154,19 @@ SAS_DEV int select_row_wg(const float* __restrict__ srow, int i, int topk, int w
       int tot = 0;
 #pragma unroll
       for (int w = 0; w < NW; ++w) tot += ired[slot + w];
-      if (tot >= keff) T = c;
+      if (tot >= topk) th = c;
     }
   }
-  // per-wave counts above and at the threshold (waves before this one decide
-  // its tie budget and its first output position)
+  // ties are kept only when the search found a candidate threshold (at least
+  // topk candidates); per-wave counts above and at it (the waves before this
+  // one decide its tie budget and its first output position)
+  const bool ties = search && th > kNoKey;
+  if (ties) T = th;
   int gt = 0, eqn = 0;
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
     gt += __popcll(__ballot(key[j] > T));
-    eqn += __popcll(__ballot(search && key[j] == T));
+    eqn += __popcll(__ballot(ties && key[j] == T));
   }
   if (lane == 0) {
     ired[4 * NW + wave] = gt;
@@ -182,17 +176,13 @@ SAS_DEV int select_row_wg(const float* __restrict__ srow, int i, int topk, int w
   int n_gt = 0, eq_before = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) n_gt += ired[4 * NW + w];
-  if (search) need_eq = keff - n_gt;
+  const int need_eq = ties ? topk - n_gt : 0;
   int base = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
     if (w >= wave) break;
     const int e_w = ired[5 * NW + w];
-    if (keff == nc) {
-      base += ired[6 * NW + w];
-    } else if (search) {
-      base += ired[4 * NW + w] + min(e_w, max(0, need_eq - eq_before));
-    }
+    base += ired[4 * NW + w] + min(e_w, max(0, need_eq - eq_before));
     eq_before += e_w;
   }
 
@@ -200,22 +190,15 @@ SAS_DEV int select_row_wg(const float* __restrict__ srow, int i, int topk, int w
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
     const int m = m0 + j * 64 + lane;
-    bool take;
-    if (keff == 0) {
-      take = false;
-    } else if (keff == nc) {
-      take = key[j] != 0u;
-    } else {
-      const bool eq = key[j] == T;
-      const uint64_t eqm = __ballot(eq);
-      take = key[j] > T || (eq && eq_seen + mask_rank(eqm) < need_eq);
-      eq_seen += __popcll(eqm);
-    }
+    const bool eq = ties && key[j] == T;
+    const uint64_t eqm = __ballot(eq);
+    const bool take = key[j] > T || (eq && eq_seen + mask_rank(eqm) < need_eq);
+    eq_seen += __popcll(eqm);
     const uint64_t tm = __ballot(take);
     if (take) emit(base + mask_rank(tm), m, val[j] - lse);
     base += __popcll(tm);
   }
-  return keff;
+  return n_gt + need_eq;
 }
 
 // candidates per lane for history rows of up to nkb blocks

@@ -85,6 +85,8 @@ WORKLOAD_NAMES = {
     3: "qwen3-8b-layer-n32768-K32",
     4: "qwen3-14b-layer-n32768-K64",
     7: "qwen3-8b-layer-n32768-K32-packed",
+    8: "qwen3-8b-layer-n32768-full",
+    9: "qwen3-4b-layer-n8192-full",
     5: "decode-qwen3-8b-B64-cache32768-K32",
 }
 
@@ -95,6 +97,10 @@ WORKLOADS = {
     3: Workload(3, 1, 32, 8, 32768, 128, 32, "bf16", s_kind="pool"),
     4: Workload(4, 1, 40, 8, 32768, 128, 64, "bf16", s_kind="gumbel3"),
     7: Workload(7, 1, 32, 8, 32768, 128, 32, "bf16", s_kind="normal", packed=True),
+    # full-range gated attention: K covers every history block
+    8: Workload(8, 1, 32, 8, 32768, 128, 512, "bf16", s_kind="pool"),
+    9: Workload(9, 1, 32, 8, 8192, 128, 128, "bf16", qkv_std=1 / math.sqrt(2),
+                s_kind="normal", s_std=math.sqrt(2.0)),
 }
 
 DECODE_WORKLOAD = DecodeWorkload(5, 64, 32, 8, 32768, 128, 32)
