@@ -48,6 +48,17 @@ notes):
   holds the tokens [64*(T//64), seq_len); its history is the blocks before it.
 * pooling stand-in selector: s[i, m] = mean_{G heads, 64 rows}(q) .
   mean_{64 rows}(k_m) / sqrt(d), for every (i, m) pair.
+* gate variants of the ablations [Review §2.3, §2.4, §2.5 and the ablation
+  table of §4]; the selection is the same Top-K for all of them:
+  - "softmax" (the method): log g_m = s_m - LSE(s_H), inside the softmax;
+  - "sigmoid": log g_m = log sigmoid(s_m), inside the softmax, each block on
+    its own (no normalisation over the history);
+  - "hard": the kept blocks enter with g = 1 (no bias) and the backward is
+    a straight-through estimator in log space: the gradient a kept block's
+    bias receives is passed to the softmax log-gate s_m - LSE(s_H);
+  - "external": g_m = exp(s_m - LSE(s_H)) scales the values of block m after
+    an unbiased softmax over the kept and current keys (the current block has
+    g = 1), o = sum_j P_j g_(block j) v_j.
 
 Every function here is pinned by the CPU tests in ``tests/test_oracle_*.py``
 (brute force, closed forms, invariants, library special cases, finite
@@ -89,10 +100,24 @@ def pool_scores(q, k, Hkv: int):
 
 
 # ============================================================== selection
-def select_row(srow, i: int, topk: int):
+def _log_gate(h, s_lse, gate: str):
+    """Forward log-gate of a kept block with score h (see the gate variants in
+    the module header)."""
+    if gate in ("softmax", "external"):
+        return float(h) - s_lse
+    if gate == "sigmoid":
+        return min(float(h), 0.0) - math.log1p(math.exp(-abs(float(h))))
+    if gate == "hard":
+        return 0.0
+    raise ValueError(gate)
+
+
+def select_row(srow, i: int, topk: int, gate: str = "softmax"):
     """Select for one query block i from its score row (length >= i).
 
     Returns (chosen ascending list, log_gate list aligned with it, s_lse).
+    The log-gates follow ``gate`` (module header); s_lse is the LSE over the
+    candidates for every variant.
 
     [Review §2.2]: keep the Top-K history blocks by score.  [Review §2.4]:
     log g_m = s_m - LSE over all history blocks.  Ranking key (-s_m, m) makes
@@ -114,7 +139,7 @@ def select_row(srow, i: int, topk: int):
     s_lse = mx + math.log(float(np.sum(np.exp(hc - mx))))
     order = sorted(cand, key=lambda m: (-h[m], m))
     chosen = sorted(order[:min(topk, len(cand))])
-    return chosen, [float(h[m]) - s_lse for m in chosen], s_lse
+    return chosen, [_log_gate(h[m], s_lse, gate) for m in chosen], s_lse
 
 
 def mask_documents(s, doc_first):
@@ -136,7 +161,7 @@ def mask_documents(s, doc_first):
     return out
 
 
-def select(s, topk: int):
+def select(s, topk: int, gate: str = "softmax"):
     """idx [B,Hkv,NQB,K] int32 (ascending, -1 padded), cnt [B,Hkv,NQB] int32,
     log_gate [B,Hkv,NQB,K] float64 (-inf padded), s_lse [B,Hkv,NQB] float64.
 
@@ -152,7 +177,7 @@ def select(s, topk: int):
     for b in range(B):
         for kv in range(Hkv):
             for i in range(NQB):
-                ch, g, l = select_row(s[b, kv, i], i, K)
+                ch, g, l = select_row(s[b, kv, i], i, K, gate)
                 c = len(ch)
                 cnt[b, kv, i] = c
                 idx[b, kv, i, :c] = ch
@@ -189,9 +214,21 @@ def _softmax_rows(Z):
     return np.exp(Z - L), L[..., 0]
 
 
-def fwd_dense(q, k, v, idx, cnt, log_gate, scale=None):
+def _placed(A, gate: str):
+    """(logit bias, value weights) of the dense bias A for the gate's place:
+    inside the softmax the bias is A and the weights are 1; outside it the
+    logits keep only the mask (0 or -inf) and each key's value is scaled by
+    g = exp(A) (1 for the current block, 0 where masked)."""
+    if gate == "external":
+        return np.where(np.isfinite(A), 0.0, NEG_INF), np.exp(A)
+    return A, np.ones_like(A)
+
+
+def fwd_dense(q, k, v, idx, cnt, log_gate, scale=None, gate: str = "softmax"):
     """Dense definition: for each query head h (kv-head h // G),
     Z = tau Q_h K^T + A, L = rowwise logsumexp(Z), O_h = exp(Z - L) V.
+    For the external gate, Z keeps only A's mask and O_h = (exp(Z - L) o W) V
+    with W = exp(A) (module header).
 
     [Review §2.3] equation for o_SAS with the bias A of ``bias_matrix``.
     Returns (o [B,Hq,n,d], lse [B,Hq,n]) in float64.  Pinned by: K = 0 equals
@@ -208,18 +245,19 @@ def fwd_dense(q, k, v, idx, cnt, log_gate, scale=None):
     lse = np.zeros((B, Hq, n))
     for b in range(B):
         for kv in range(Hkv):
-            A = bias_matrix(n, idx[b, kv], cnt[b, kv], log_gate[b, kv])
+            A, W = _placed(bias_matrix(n, idx[b, kv], cnt[b, kv], log_gate[b, kv]), gate)
             for g in range(G):
                 h = kv * G + g
                 P, L = _softmax_rows(tau * q[b, h] @ k[b, kv].T + A)
-                o[b, h] = P @ v[b, kv]
+                o[b, h] = (P * W) @ v[b, kv]
                 lse[b, h] = L
     return o, lse
 
 
 def _gather_cols(i: int, idx_row, cnt_row, lg_row):
     """Key columns of q-block i (selected blocks in slot order, then the
-    current block) with their per-column bias and block slot (-1 = current)."""
+    current block) with their per-column log-gate (0 for the current block)
+    and block slot (-1 = current)."""
     cols, bias, slot = [], [], []
     for sl in range(int(cnt_row[i])):
         m = int(idx_row[i, sl])
@@ -244,7 +282,15 @@ def _block_logits(qi, kc, bias, slot, tau):
     return Z
 
 
-def fwd_gather_block(q, k, v, idx, cnt, log_gate, b: int, kv: int, i: int, scale=None):
+def _placed_cols(lgc, gate: str):
+    """(logit bias, value weights) of gathered columns with log-gates lgc."""
+    if gate == "external":
+        return np.zeros_like(lgc), np.exp(lgc)
+    return lgc, np.ones_like(lgc)
+
+
+def fwd_gather_block(q, k, v, idx, cnt, log_gate, b: int, kv: int, i: int, scale=None,
+                     gate: str = "softmax"):
     """Gather-mode forward of one (batch, kv-group, q-block): the formula of
     ``fwd_dense`` evaluated only on columns whose bias is finite, which is
     exact because exp(-inf) = 0.  Returns (o [G,64,d], lse [G,64])."""
@@ -253,8 +299,9 @@ def fwd_gather_block(q, k, v, idx, cnt, log_gate, b: int, kv: int, i: int, scale
     Hkv = k.shape[1]
     G = Hq // Hkv
     tau = (1.0 / math.sqrt(d)) if not scale else float(scale)
-    cols, bias, slot = _gather_cols(i, idx[b, kv], cnt[b, kv], log_gate[b, kv])
-    kc, vc = k[b, kv, cols], v[b, kv, cols]
+    cols, lgc, slot = _gather_cols(i, idx[b, kv], cnt[b, kv], log_gate[b, kv])
+    bias, w = _placed_cols(lgc, gate)
+    kc, vc = k[b, kv, cols], v[b, kv, cols] * w[:, None]
     r = slice(i * BLOCK, (i + 1) * BLOCK)
     o = np.zeros((G, BLOCK, d))
     lse = np.zeros((G, BLOCK))
@@ -265,7 +312,7 @@ def fwd_gather_block(q, k, v, idx, cnt, log_gate, b: int, kv: int, i: int, scale
     return o, lse
 
 
-def fwd_gather(q, k, v, idx, cnt, log_gate, scale=None, blocks=None):
+def fwd_gather(q, k, v, idx, cnt, log_gate, scale=None, blocks=None, gate: str = "softmax"):
     """Gather-mode forward over all q-blocks (or the (b, kv, i) list given)."""
     B, Hq, n, d = np.shape(q)
     Hkv = np.shape(k)[1]
@@ -275,7 +322,7 @@ def fwd_gather(q, k, v, idx, cnt, log_gate, scale=None, blocks=None):
     todo = blocks if blocks is not None else [
         (b, kv, i) for b in range(B) for kv in range(Hkv) for i in range(n // BLOCK)]
     for (b, kv, i) in todo:
-        ob, lb = fwd_gather_block(q, k, v, idx, cnt, log_gate, b, kv, i, scale)
+        ob, lb = fwd_gather_block(q, k, v, idx, cnt, log_gate, b, kv, i, scale, gate)
         r = slice(i * BLOCK, (i + 1) * BLOCK)
         o[b, kv * G:(kv + 1) * G, r] = ob
         lse[b, kv * G:(kv + 1) * G, r] = lb
@@ -283,7 +330,7 @@ def fwd_gather(q, k, v, idx, cnt, log_gate, scale=None, blocks=None):
 
 
 # ============================================================== backward
-def gate_jacobian(s, s_lse, idx, cnt, dlg):
+def gate_jacobian(s, s_lse, idx, cnt, dlg, gate: str = "softmax"):
     """ds from the per-slot gate gradient dlg (chain rule through [Review §2.4]).
 
     log g_m = s_m - LSE(s_H) for m in H_i, so for every history block m:
@@ -293,10 +340,23 @@ def gate_jacobian(s, s_lse, idx, cnt, dlg):
     candidate at all (no gate, s_lse = -inf).
     Pinned by finite differences through select + forward, and by
     sum_m ds[i, m] = 0.
+
+    The "external" gate has the same log-gate, and "hard" passes its bias
+    gradient to that log-gate (straight-through), so both use this Jacobian.
+    For "sigmoid", d log sigmoid(s)/ds = sigmoid(-s) and blocks do not
+    interact: ds[i, m] = [m selected] dlg[i, m] sigmoid(-s[i, m]).
     """
     s = _f64(s)
     B, Hkv, NQB, NKB = s.shape
     ds = np.zeros((B, Hkv, NQB, NKB))
+    if gate == "sigmoid":
+        for b in range(B):
+            for kv in range(Hkv):
+                for i in range(NQB):
+                    for sl in range(int(cnt[b, kv, i])):
+                        m = int(idx[b, kv, i, sl])
+                        ds[b, kv, i, m] = dlg[b, kv, i, sl] / (1.0 + math.exp(s[b, kv, i, m]))
+        return ds
     for b in range(B):
         for kv in range(Hkv):
             for i in range(1, NQB):
@@ -311,7 +371,7 @@ def gate_jacobian(s, s_lse, idx, cnt, dlg):
     return ds
 
 
-def bwd_dense(q, k, v, do, idx, cnt, log_gate, scale=None):
+def bwd_dense(q, k, v, do, idx, cnt, log_gate, scale=None, gate: str = "softmax"):
     """Analytic backward of the dense definition (no autograd).
 
     With P = softmax(Z), O = P V and upstream dO:
@@ -319,6 +379,9 @@ def bwd_dense(q, k, v, do, idx, cnt, log_gate, scale=None):
       dQ_h = tau dZ K, dK = tau sum_h dZ^T Q_h, dV = sum_h P^T dO_h,
       dlg[i, slot] = sum over the group's heads, rows t of block i and columns
       j of the slot's block m of dZ[t, j]  ([Review §2.6] block-sum rule).
+    External gate (O = (P o W) V): dP = (dO V^T) o W, dV = sum_h (P o W)^T dO_h,
+    and the log-gate gradient of a block is the sum of P o dP over its
+    columns (d/dlog g of g * P dP).
     Returns (dq, dk, dv, dlg [B,Hkv,NQB,K]) in float64.  Pinned by central
     finite differences in float64 and by the row identity sum_j dZ[t, j] = 0.
     """
@@ -332,25 +395,28 @@ def bwd_dense(q, k, v, do, idx, cnt, log_gate, scale=None):
     dlg = np.zeros((B, Hkv, n // BLOCK, K))
     for b in range(B):
         for kv in range(Hkv):
-            A = bias_matrix(n, idx[b, kv], cnt[b, kv], log_gate[b, kv])
+            A, W = _placed(bias_matrix(n, idx[b, kv], cnt[b, kv], log_gate[b, kv]), gate)
             for g in range(G):
                 h = kv * G + g
                 P, _ = _softmax_rows(tau * q[b, h] @ k[b, kv].T + A)
-                O = P @ v[b, kv]
+                O = (P * W) @ v[b, kv]
                 D = np.sum(do[b, h] * O, axis=1, keepdims=True)
-                dZ = P * (do[b, h] @ v[b, kv].T - D)
+                dP = (do[b, h] @ v[b, kv].T) * W
+                dZ = P * (dP - D)
                 dq[b, h] = tau * dZ @ k[b, kv]
                 dk[b, kv] += tau * dZ.T @ q[b, h]
-                dv[b, kv] += P.T @ do[b, h]
+                dv[b, kv] += (P * W).T @ do[b, h]
+                G_ = P * dP if gate == "external" else dZ
                 for i in range(n // BLOCK):
                     r = slice(i * BLOCK, (i + 1) * BLOCK)
                     for sl in range(int(cnt[b, kv, i])):
                         m = int(idx[b, kv, i, sl])
-                        dlg[b, kv, i, sl] += dZ[r, m * BLOCK:(m + 1) * BLOCK].sum()
+                        dlg[b, kv, i, sl] += G_[r, m * BLOCK:(m + 1) * BLOCK].sum()
     return dq, dk, dv, dlg
 
 
-def bwd_gather_block(q, k, v, do, idx, cnt, log_gate, b: int, kv: int, i: int, scale=None):
+def bwd_gather_block(q, k, v, do, idx, cnt, log_gate, b: int, kv: int, i: int, scale=None,
+                     gate: str = "softmax"):
     """Backward contributions of one (batch, kv-group, q-block) in gather mode.
 
     Returns (dq [G,64,d], cols, dk_cols [len(cols),d], dv_cols, dlg_row [K]):
@@ -363,8 +429,9 @@ def bwd_gather_block(q, k, v, do, idx, cnt, log_gate, b: int, kv: int, i: int, s
     G = Hq // Hkv
     K = idx.shape[-1]
     tau = (1.0 / math.sqrt(d)) if not scale else float(scale)
-    cols, bias, slot = _gather_cols(i, idx[b, kv], cnt[b, kv], log_gate[b, kv])
-    kc, vc = k[b, kv, cols], v[b, kv, cols]
+    cols, lgc, slot = _gather_cols(i, idx[b, kv], cnt[b, kv], log_gate[b, kv])
+    bias, w = _placed_cols(lgc, gate)
+    kc, vc = k[b, kv, cols], v[b, kv, cols] * w[:, None]
     r = slice(i * BLOCK, (i + 1) * BLOCK)
     dq = np.zeros((G, BLOCK, d))
     dkc = np.zeros((len(cols), d))
@@ -375,17 +442,18 @@ def bwd_gather_block(q, k, v, do, idx, cnt, log_gate, b: int, kv: int, i: int, s
         P, _ = _softmax_rows(_block_logits(q[b, h, r], kc, bias, slot, tau))
         O = P @ vc
         D = np.sum(do[b, h, r] * O, axis=1, keepdims=True)
-        dZ = P * (do[b, h, r] @ vc.T - D)
+        dP = do[b, h, r] @ vc.T
+        dZ = P * (dP - D)
         dq[g] = tau * dZ @ kc
         dkc += tau * dZ.T @ q[b, h, r]
-        dvc += P.T @ do[b, h, r]
-        colsum = dZ.sum(axis=0)
+        dvc += w[:, None] * (P.T @ do[b, h, r])
+        colsum = (P * dP if gate == "external" else dZ).sum(axis=0)
         for sl in range(int(cnt[b, kv, i])):
             dlg[sl] += colsum[slot == sl].sum()
     return dq, cols, dkc, dvc, dlg
 
 
-def bwd_gather(q, k, v, do, idx, cnt, log_gate, scale=None, blocks=None):
+def bwd_gather(q, k, v, do, idx, cnt, log_gate, scale=None, blocks=None, gate: str = "softmax"):
     """Gather-mode backward over all q-blocks (or the listed (b, kv, i)).
 
     With ``blocks`` given, dq is exact on those q-blocks' rows only and dk/dv
@@ -401,7 +469,8 @@ def bwd_gather(q, k, v, do, idx, cnt, log_gate, scale=None, blocks=None):
     todo = blocks if blocks is not None else [
         (b, kv, i) for b in range(B) for kv in range(Hkv) for i in range(n // BLOCK)]
     for (b, kv, i) in todo:
-        dqb, cols, dkc, dvc, dl = bwd_gather_block(q, k, v, do, idx, cnt, log_gate, b, kv, i, scale)
+        dqb, cols, dkc, dvc, dl = bwd_gather_block(q, k, v, do, idx, cnt, log_gate, b, kv, i, scale,
+                                                   gate)
         dq[b, kv * G:(kv + 1) * G, i * BLOCK:(i + 1) * BLOCK] = dqb
         np.add.at(dk[b, kv], cols, dkc)
         np.add.at(dv[b, kv], cols, dvc)
@@ -418,7 +487,8 @@ def reverse_lists(idx, cnt, b: int, kv: int, m: int):
     return [m] + out
 
 
-def bwd_kv_block(q, k, v, do, idx, cnt, log_gate, b: int, kv: int, m: int, scale=None):
+def bwd_kv_block(q, k, v, do, idx, cnt, log_gate, b: int, kv: int, m: int, scale=None,
+                 gate: str = "softmax"):
     """dk, dv [64, d] of key block m of (b, kv), summed over every q-block
     that reads it (sampled full-size checks)."""
     d = np.shape(q)[3]
@@ -426,7 +496,8 @@ def bwd_kv_block(q, k, v, do, idx, cnt, log_gate, b: int, kv: int, m: int, scale
     dv = np.zeros((BLOCK, d))
     rows = np.arange(m * BLOCK, (m + 1) * BLOCK)
     for i in reverse_lists(idx, cnt, b, kv, m):
-        _, cols, dkc, dvc, _ = bwd_gather_block(q, k, v, do, idx, cnt, log_gate, b, kv, i, scale)
+        _, cols, dkc, dvc, _ = bwd_gather_block(q, k, v, do, idx, cnt, log_gate, b, kv, i, scale,
+                                                gate)
         sel = np.isin(cols, rows)
         pos = cols[sel] - m * BLOCK
         np.add.at(dk, pos, dkc[sel])
@@ -435,27 +506,30 @@ def bwd_kv_block(q, k, v, do, idx, cnt, log_gate, b: int, kv: int, m: int, scale
 
 
 # ============================================================== full pipeline
-def sas_forward_backward(q, k, v, do, s, topk: int, scale=None, mode: str = "gather"):
+def sas_forward_backward(q, k, v, do, s, topk: int, scale=None, mode: str = "gather",
+                         gate: str = "softmax"):
     """select -> forward -> backward -> ds, everything float64.
     Returns a dict with idx, cnt, log_gate, s_lse, o, lse, dq, dk, dv, dlg, ds."""
-    idx, cnt, lg, s_lse = select(s, topk)
+    idx, cnt, lg, s_lse = select(s, topk, gate)
     if mode == "dense":
-        o, lse = fwd_dense(q, k, v, idx, cnt, lg, scale)
-        dq, dk, dv, dlg = bwd_dense(q, k, v, do, idx, cnt, lg, scale)
+        o, lse = fwd_dense(q, k, v, idx, cnt, lg, scale, gate)
+        dq, dk, dv, dlg = bwd_dense(q, k, v, do, idx, cnt, lg, scale, gate)
     else:
-        o, lse = fwd_gather(q, k, v, idx, cnt, lg, scale)
-        dq, dk, dv, dlg = bwd_gather(q, k, v, do, idx, cnt, lg, scale)
-    ds = gate_jacobian(s, s_lse, idx, cnt, dlg)
+        o, lse = fwd_gather(q, k, v, idx, cnt, lg, scale, gate=gate)
+        dq, dk, dv, dlg = bwd_gather(q, k, v, do, idx, cnt, lg, scale, gate=gate)
+    ds = gate_jacobian(s, s_lse, idx, cnt, dlg, gate)
     return dict(idx=idx, cnt=cnt, log_gate=lg, s_lse=s_lse, o=o, lse=lse,
                 dq=dq, dk=dk, dv=dv, dlg=dlg, ds=ds)
 
 
 # ============================================================== decode
-def decode(q, k_cache, v_cache, seq_lens, s, topk: int, scale=None, rows=None):
+def decode(q, k_cache, v_cache, seq_lens, s, topk: int, scale=None, rows=None,
+           gate: str = "softmax"):
     """Single-token decode.  For batch entry b the query is token
     T = seq_len - 1 in block i = T // 64; kv-group kv selects from s[b, kv, :i]
     exactly as ``select_row``; each query head h of the group attends to the
-    selected blocks (bias log_gate) and to keys [64 i, seq_len) (bias 0).
+    selected blocks (bias log_gate) and to keys [64 i, seq_len) (bias 0); the
+    external gate scales the selected blocks' values instead.
 
     ``rows`` limits the work to a list of (b, kv); k_cache/v_cache may then be
     dicts {(b, kv): (k [cap,d] or block-indexable array)} - any object with
@@ -475,17 +549,17 @@ def decode(q, k_cache, v_cache, seq_lens, s, topk: int, scale=None, rows=None):
         L = int(seq_lens[b])
         T = L - 1
         i = T // BLOCK
-        chosen, lg, _ = select_row(s[b, kv], i, K)
+        chosen, lg, _ = select_row(s[b, kv], i, K, gate)
         idx[b, kv, :len(chosen)] = chosen
         kc_all, vc_all = k_cache[b, kv], v_cache[b, kv]
         cols = [np.arange(m * BLOCK, (m + 1) * BLOCK) for m in chosen]
-        bias = [np.full(BLOCK, g) for g in lg]
+        lgc = [np.full(BLOCK, g) for g in lg]
         cols.append(np.arange(i * BLOCK, L))
-        bias.append(np.zeros(L - i * BLOCK))
+        lgc.append(np.zeros(L - i * BLOCK))
         cols = np.concatenate(cols)
-        bias = np.concatenate(bias)
+        bias, w = _placed_cols(np.concatenate(lgc), gate)
         kc = _f64(kc_all[cols])
-        vc = _f64(vc_all[cols])
+        vc = _f64(vc_all[cols]) * w[:, None]
         for g in range(G):
             h = kv * G + g
             z = tau * kc @ q[b, h] + bias
