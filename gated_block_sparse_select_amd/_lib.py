@@ -13,6 +13,10 @@ LIB_PATH = os.path.join(HERE, "libsas.so")
 
 SAS_OK, SAS_ERR_ARG, SAS_ERR_DTYPE, SAS_ERR_UNSUPPORTED, SAS_ERR_WORKSPACE, SAS_ERR_HIP = range(6)
 SAS_F32, SAS_BF16 = 0, 1
+SAS_GATE_SOFTMAX, SAS_GATE_SIGMOID, SAS_GATE_HARD, SAS_GATE_EXTERNAL = range(4)
+GATES = {"softmax": SAS_GATE_SOFTMAX, "sigmoid": SAS_GATE_SIGMOID, "hard": SAS_GATE_HARD,
+         "external": SAS_GATE_EXTERNAL}
+ABI_VERSION = 2
 BLOCK = 64
 
 EXPORTED = [
@@ -27,20 +31,20 @@ EXPORTED = [
 class SasShape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
                 ("n", ctypes.c_int32), ("d", ctypes.c_int32), ("topk", ctypes.c_int32),
-                ("scale", ctypes.c_float), ("dtype", ctypes.c_int32)]
+                ("scale", ctypes.c_float), ("dtype", ctypes.c_int32), ("gate", ctypes.c_int32)]
 
 
 class SasDecodeShape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
                 ("cap", ctypes.c_int32), ("d", ctypes.c_int32), ("topk", ctypes.c_int32),
-                ("scale", ctypes.c_float), ("dtype", ctypes.c_int32)]
+                ("scale", ctypes.c_float), ("dtype", ctypes.c_int32), ("gate", ctypes.c_int32)]
 
 
 class SasDecodePagedShape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
                 ("max_blocks", ctypes.c_int32), ("num_pages", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("topk", ctypes.c_int32),
-                ("scale", ctypes.c_float), ("dtype", ctypes.c_int32)]
+                ("scale", ctypes.c_float), ("dtype", ctypes.c_int32), ("gate", ctypes.c_int32)]
 
 
 class SasError(RuntimeError):
@@ -67,6 +71,9 @@ def lib() -> ctypes.CDLL:
         sp = ctypes.POINTER(SasShape)
         dp = ctypes.POINTER(SasDecodeShape)
         L.sas_abi_version.restype = i32
+        if L.sas_abi_version() != ABI_VERSION:
+            raise ImportError(f"{LIB_PATH} implements ABI {L.sas_abi_version()}, this binding "
+                              f"needs {ABI_VERSION}: rebuild the library")
         L.sas_status_string.restype = ctypes.c_char_p
         L.sas_status_string.argtypes = [i32]
         L.sas_pool_workspace_bytes.restype = sz

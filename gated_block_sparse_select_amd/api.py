@@ -12,7 +12,7 @@ import ctypes
 
 import torch
 
-from ._lib import (BLOCK, SAS_BF16, SAS_F32, SasDecodePagedShape, SasDecodeShape, SasError, SasShape, lib,
+from ._lib import (BLOCK, GATES, SAS_BF16, SAS_F32, SasDecodePagedShape, SasDecodeShape, SasError, SasShape, lib,
                    status_string)
 
 _DT = {torch.float32: SAS_F32, torch.bfloat16: SAS_BF16}
@@ -47,22 +47,32 @@ def _ok(st, where):
         raise SasError(st, where)
 
 
-def make_shape(B, Hq, Hkv, n, d, topk, dtype=torch.bfloat16, scale=0.0) -> SasShape:
-    return SasShape(B, Hq, Hkv, n, d, topk, float(scale), _DT[dtype])
+def _gate(gate) -> int:
+    """Gate kind: one of "softmax", "sigmoid", "hard", "external", or its
+    SAS_GATE_* code (other integers are passed through for the library to
+    reject)."""
+    return GATES[gate] if isinstance(gate, str) else int(gate)
 
 
-def make_decode_shape(B, Hq, Hkv, cap, d, topk, dtype=torch.bfloat16, scale=0.0) -> SasDecodeShape:
-    return SasDecodeShape(B, Hq, Hkv, cap, d, topk, float(scale), _DT[dtype])
+def make_shape(B, Hq, Hkv, n, d, topk, dtype=torch.bfloat16, scale=0.0, gate="softmax") -> SasShape:
+    return SasShape(B, Hq, Hkv, n, d, topk, float(scale), _DT[dtype], _gate(gate))
+
+
+def make_decode_shape(B, Hq, Hkv, cap, d, topk, dtype=torch.bfloat16, scale=0.0,
+                      gate="softmax") -> SasDecodeShape:
+    return SasDecodeShape(B, Hq, Hkv, cap, d, topk, float(scale), _DT[dtype], _gate(gate))
 
 
 def make_decode_paged_shape(B, Hq, Hkv, max_blocks, num_pages, d, topk, dtype=torch.bfloat16,
-                            scale=0.0) -> SasDecodePagedShape:
-    return SasDecodePagedShape(B, Hq, Hkv, max_blocks, num_pages, d, topk, float(scale), _DT[dtype])
+                            scale=0.0, gate="softmax") -> SasDecodePagedShape:
+    return SasDecodePagedShape(B, Hq, Hkv, max_blocks, num_pages, d, topk, float(scale), _DT[dtype],
+                               _gate(gate))
 
 
-def shape_of(q: torch.Tensor, k: torch.Tensor, topk: int, scale: float = 0.0) -> SasShape:
+def shape_of(q: torch.Tensor, k: torch.Tensor, topk: int, scale: float = 0.0,
+             gate="softmax") -> SasShape:
     B, Hq, n, d = q.shape
-    return make_shape(B, Hq, k.shape[1], n, d, topk, q.dtype, scale)
+    return make_shape(B, Hq, k.shape[1], n, d, topk, q.dtype, scale, gate)
 
 
 def _dt(shape):

@@ -61,6 +61,10 @@ SAS_DEV int mask_rank(uint64_t m) {
 SAS_DEV int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 
 constexpr float kLog2e = 1.4426950408889634f;
+// Smallest log-gate the external gate uses: its kernels keep the log-gate as
+// an exponent offset of the tile's weights and divide their sum by g again,
+// so g is held at e^-60 or more to keep the weights clear of underflow.
+constexpr float kMinExtLogGate = -60.f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 }  // namespace sas

@@ -17,9 +17,10 @@ int decode_nsplit(int B, int Hkv, int topk) {
 hipError_t launch_decode(int dtype, const void* q, const void* kc, const void* vc,
                          const int32_t* seq_lens, const float* s, int32_t* idx_out,
                          float* part_acc, float* part_ml, void* o, int B, int Hq, int Hkv,
-                         int cap, int d, int topk, int nsplit, float tau, hipStream_t st) {
+                         int cap, int d, int topk, int nsplit, float tau, int gate,
+                         hipStream_t st) {
   return launch_decode_any<false>(dtype, q, kc, vc, nullptr, 0, seq_lens, s, idx_out, part_acc,
-                                  part_ml, o, B, Hq, Hkv, cap, d, topk, nsplit, tau, st);
+                                  part_ml, o, B, Hq, Hkv, cap, d, topk, nsplit, tau, gate, st);
 }
 
 }  // namespace sas

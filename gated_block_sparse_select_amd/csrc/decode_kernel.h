@@ -107,7 +107,8 @@ __global__ void __launch_bounds__(256) decode_kernel(
     const typename E::T* __restrict__ vc, const int32_t* __restrict__ page_table, int num_pages,
     const int32_t* __restrict__ seq_lens, const float* __restrict__ s,
     int32_t* __restrict__ idx_out, typename E::T* __restrict__ o, float* __restrict__ part_acc,
-    float* __restrict__ part_ml, int Hq, int Hkv, int cap, int topk, int nsplit, float tau2) {
+    float* __restrict__ part_ml, int Hq, int Hkv, int cap, int topk, int nsplit, float tau2,
+    int gate) {
   static_assert(SW == 1 || SW == 4, "select by one wave or by the workgroup's four");
   constexpr int EPC = Vec16<E>::N;        // elements per 16-byte chunk
   constexpr int CPR = D / EPC;            // chunks per key row
@@ -148,16 +149,20 @@ __global__ void __launch_bounds__(256) decode_kernel(
   __shared__ float sgate[SAS_MAX_BLOCKS];
   __shared__ int scnt;
   int32_t* orow = (idx_out != nullptr && split == 0) ? idx_out + size_t(bk) * topk : nullptr;
+  // the external gate keeps its log-gate as the tile's exponent offset
+  // (clamped at -60, so no weight underflows) and divides the tile's weight
+  // sum by g again: o = sum g P v / sum P
+  const bool ext = gate == SAS_GATE_EXTERNAL;
   auto emit = [&](int pos, int m, float g) __attribute__((always_inline)) {
     sblk[pos] = where(m);
-    sgate[pos] = g * kLog2e;
+    sgate[pos] = (ext ? fmaxf(g, kMinExtLogGate) : g) * kLog2e;
     if (orow) orow[pos] = m;
   };
   const float* srow = s + size_t(bk) * nkb;
   if constexpr (SW == 1) {
     if (wave == 0) {
       float lse;
-      const int keff = select_row<CPL>(srow, icur, topk, lane, lse, emit);
+      const int keff = select_row<CPL>(srow, icur, topk, gate, lane, lse, emit);
       if (orow)
         for (int p = keff + lane; p < topk; p += 64) orow[p] = -1;
       if (lane == 0) scnt = keff;
@@ -165,7 +170,7 @@ __global__ void __launch_bounds__(256) decode_kernel(
   } else {
     __shared__ float sel_red[6 * SW];
     float lse;
-    const int keff = select_row_wg<CPL, SW>(srow, icur, topk, wave, lane, lse,
+    const int keff = select_row_wg<CPL, SW>(srow, icur, topk, gate, wave, lane, lse,
                                             (__attribute__((address_space(3))) float*)sel_red, emit);
     if (orow)
       for (int p = keff + t; p < topk; p += 256) orow[p] = -1;
@@ -211,6 +216,7 @@ __global__ void __launch_bounds__(256) decode_kernel(
   constexpr bool kBF16 = std::is_same<E, ElemBF16>::value;
   auto compute = [&]<int B>(int tile) __attribute__((always_inline)) {
     const float bias2 = tile < c_sel ? sgate[tile] : 0.f;
+    const float wsum_scale = ext ? fast_exp2(-bias2) : 1.f;   // 1/g for the external gate
     const int nvalid = tile < c_sel ? SAS_BLK : L - icur * SAS_BLK;
     float sc[KPT][GMAX];
 #pragma unroll
@@ -252,6 +258,7 @@ __global__ void __launch_bounds__(256) decode_kernel(
 #pragma unroll
         for (int e = 0; e < EPC; ++e) acc[g][e] *= corr;
       }
+      float ts = 0.f;   // this tile's weight sum
       if constexpr (kBF16) {
         typedef __attribute__((ext_vector_type(2))) __bf16 bf2;
         const bf2 ones = __builtin_bit_cast(bf2, 0x3F803F80u);
@@ -260,7 +267,7 @@ __global__ void __launch_bounds__(256) decode_kernel(
           // the weights actually used (bf16) also form the normaliser
           const bf2 pp = {(__bf16)fast_exp2(sc[2 * x][g] - mrun[g]),
                           (__bf16)fast_exp2(sc[2 * x + 1][g] - mrun[g])};
-          lrun[g] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lrun[g], false);
+          ts = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ts, false);
 #pragma unroll
           for (int w = 0; w < 4; ++w)
 #pragma unroll
@@ -272,13 +279,14 @@ __global__ void __launch_bounds__(256) decode_kernel(
 #pragma unroll
         for (int u = 0; u < KPT; ++u) {
           const float p = fast_exp2(sc[u][g] - mrun[g]);
-          lrun[g] += p;
+          ts += p;
           float vx[EPC];
           Vec16<E>::unpack(vb[B][u], vx);
 #pragma unroll
           for (int e = 0; e < EPC; ++e) acc[g][e] = __builtin_fmaf(p, vx[e], acc[g][e]);
         }
       }
+      lrun[g] = __builtin_fmaf(ts, wsum_scale, lrun[g]);
     }
   };
   [&]<int... X>(std::integer_sequence<int, X...>) __attribute__((always_inline)) {
@@ -378,36 +386,36 @@ template <class E, int D, int GMAX, int CPL, int SW, bool PAGED>
 static void dec_go(const void* q, const void* kc, const void* vc, const int32_t* pt, int np,
                    const int32_t* sl, const float* s, int32_t* idx_out, void* o, float* pa,
                    float* pm, int B, int Hq, int Hkv, int cap, int topk, int ns, float tau2,
-                   hipStream_t st) {
+                   int gate, hipStream_t st) {
   using T = typename E::T;
   hipLaunchKernelGGL((decode_kernel<E, D, GMAX, CPL, SW, PAGED>), dim3(B * Hkv * ns), dim3(256), 0, st,
                      (const T*)q, (const T*)kc, (const T*)vc, pt, np, sl, s, idx_out, (T*)o, pa, pm,
-                     Hq, Hkv, cap, topk, ns, tau2);
+                     Hq, Hkv, cap, topk, ns, tau2, gate);
 }
 
 template <class E, int D, int CPL, int SW, bool PAGED>
 static void dec_g(int G, const void* q, const void* kc, const void* vc, const int32_t* pt, int np,
                   const int32_t* sl, const float* s, int32_t* idx_out, void* o, float* pa,
                   float* pm, int B, int Hq, int Hkv, int cap, int topk, int ns, float tau2,
-                  hipStream_t st) {
-  if (G <= 4) dec_go<E, D, 4, CPL, SW, PAGED>(q, kc, vc, pt, np, sl, s, idx_out, o, pa, pm, B, Hq, Hkv, cap, topk, ns, tau2, st);
-  else if (G <= 8) dec_go<E, D, 8, CPL, SW, PAGED>(q, kc, vc, pt, np, sl, s, idx_out, o, pa, pm, B, Hq, Hkv, cap, topk, ns, tau2, st);
-  else dec_go<E, D, 16, CPL, SW, PAGED>(q, kc, vc, pt, np, sl, s, idx_out, o, pa, pm, B, Hq, Hkv, cap, topk, ns, tau2, st);
+                  int gate, hipStream_t st) {
+  if (G <= 4) dec_go<E, D, 4, CPL, SW, PAGED>(q, kc, vc, pt, np, sl, s, idx_out, o, pa, pm, B, Hq, Hkv, cap, topk, ns, tau2, gate, st);
+  else if (G <= 8) dec_go<E, D, 8, CPL, SW, PAGED>(q, kc, vc, pt, np, sl, s, idx_out, o, pa, pm, B, Hq, Hkv, cap, topk, ns, tau2, gate, st);
+  else dec_go<E, D, 16, CPL, SW, PAGED>(q, kc, vc, pt, np, sl, s, idx_out, o, pa, pm, B, Hq, Hkv, cap, topk, ns, tau2, gate, st);
 }
 
 template <class E, int D, bool PAGED>
 static void dec_c(int G, const void* q, const void* kc, const void* vc, const int32_t* pt, int np,
                   const int32_t* sl, const float* s, int32_t* idx_out, void* o, float* pa,
                   float* pm, int B, int Hq, int Hkv, int cap, int topk, int ns, float tau2,
-                  hipStream_t st) {
+                  int gate, hipStream_t st) {
   // history rows hold up to cap/64 - 1 candidate blocks
   const int nkb = cap / SAS_BLK;
   if (nkb <= 8 * 64)
-    dec_g<E, D, 8, 1, PAGED>(G, q, kc, vc, pt, np, sl, s, idx_out, o, pa, pm, B, Hq, Hkv, cap, topk, ns, tau2, st);
+    dec_g<E, D, 8, 1, PAGED>(G, q, kc, vc, pt, np, sl, s, idx_out, o, pa, pm, B, Hq, Hkv, cap, topk, ns, tau2, gate, st);
   else if (!PAGED || nkb <= 32 * 64)
-    dec_g<E, D, 32, 1, PAGED>(G, q, kc, vc, pt, np, sl, s, idx_out, o, pa, pm, B, Hq, Hkv, cap, topk, ns, tau2, st);
+    dec_g<E, D, 32, 1, PAGED>(G, q, kc, vc, pt, np, sl, s, idx_out, o, pa, pm, B, Hq, Hkv, cap, topk, ns, tau2, gate, st);
   else if constexpr (PAGED)
-    dec_g<E, D, 32, 4, PAGED>(G, q, kc, vc, pt, np, sl, s, idx_out, o, pa, pm, B, Hq, Hkv, cap, topk, ns, tau2, st);
+    dec_g<E, D, 32, 4, PAGED>(G, q, kc, vc, pt, np, sl, s, idx_out, o, pa, pm, B, Hq, Hkv, cap, topk, ns, tau2, gate, st);
 }
 
 // The decode step (and, when rows are split, the combine kernel) for either
@@ -417,17 +425,17 @@ hipError_t launch_decode_any(int dtype, const void* q, const void* kc, const voi
                              const int32_t* page_table, int num_pages, const int32_t* seq_lens,
                              const float* s, int32_t* idx_out, float* part_acc, float* part_ml,
                              void* o, int B, int Hq, int Hkv, int cap, int d, int topk, int nsplit,
-                             float tau, hipStream_t st) {
+                             float tau, int gate, hipStream_t st) {
   const int G = Hq / Hkv;
   const float tau2 = tau * kLog2e;
   {
     ProfScope ps(PAGED ? "sas_decode_paged_kernel" : "sas_decode_kernel", st);
     if (dtype == 1) {
-      if (d == 128) dec_c<ElemBF16, 128, PAGED>(G, q, kc, vc, page_table, num_pages, seq_lens, s, idx_out, o, part_acc, part_ml, B, Hq, Hkv, cap, topk, nsplit, tau2, st);
-      else dec_c<ElemBF16, 64, PAGED>(G, q, kc, vc, page_table, num_pages, seq_lens, s, idx_out, o, part_acc, part_ml, B, Hq, Hkv, cap, topk, nsplit, tau2, st);
+      if (d == 128) dec_c<ElemBF16, 128, PAGED>(G, q, kc, vc, page_table, num_pages, seq_lens, s, idx_out, o, part_acc, part_ml, B, Hq, Hkv, cap, topk, nsplit, tau2, gate, st);
+      else dec_c<ElemBF16, 64, PAGED>(G, q, kc, vc, page_table, num_pages, seq_lens, s, idx_out, o, part_acc, part_ml, B, Hq, Hkv, cap, topk, nsplit, tau2, gate, st);
     } else {
-      if (d == 128) dec_c<ElemF32, 128, PAGED>(G, q, kc, vc, page_table, num_pages, seq_lens, s, idx_out, o, part_acc, part_ml, B, Hq, Hkv, cap, topk, nsplit, tau2, st);
-      else dec_c<ElemF32, 64, PAGED>(G, q, kc, vc, page_table, num_pages, seq_lens, s, idx_out, o, part_acc, part_ml, B, Hq, Hkv, cap, topk, nsplit, tau2, st);
+      if (d == 128) dec_c<ElemF32, 128, PAGED>(G, q, kc, vc, page_table, num_pages, seq_lens, s, idx_out, o, part_acc, part_ml, B, Hq, Hkv, cap, topk, nsplit, tau2, gate, st);
+      else dec_c<ElemF32, 64, PAGED>(G, q, kc, vc, page_table, num_pages, seq_lens, s, idx_out, o, part_acc, part_ml, B, Hq, Hkv, cap, topk, nsplit, tau2, gate, st);
     }
   }
   hipError_t e = hipGetLastError();

@@ -27,7 +27,7 @@ hipError_t launch_mask_documents(const int32_t* doc_first, float* s, int B, int 
                                  hipStream_t st);
 hipError_t launch_select(const float* s, int32_t* idx, int32_t* cnt, float* log_gate,
                          float* s_lse, int rows, int nqb, int nkb, int topk,
-                         const int32_t* seq_lens, int hkv, int cap, hipStream_t st);
+                         const int32_t* seq_lens, int hkv, int cap, int gate, hipStream_t st);
 
 // ---- pooling (pool.hip); ws holds qbar and kbar (float32 [B*Hkv*nb*d] each)
 hipError_t launch_pool(int dtype, const void* q, const void* k, float* s, float* ws, int B,
@@ -43,26 +43,28 @@ hipError_t launch_revidx(const int32_t* idx, const int32_t* cnt, int32_t* rev_of
 hipError_t launch_fwd_simt(int dtype, const void* q, const void* k, const void* v,
                            const int32_t* idx, const int32_t* cnt, const float* lg, void* o,
                            float* lse, int B, int Hq, int Hkv, int n, int d, int topk,
-                           float tau, hipStream_t st);
+                           float tau, int gate, hipStream_t st);
 hipError_t launch_bwd_simt(int dtype, const void* q, const void* k, const void* v,
                            const void* o, const void* dO, const float* lse, const int32_t* idx,
                            const int32_t* cnt, const float* lg, const float* s,
                            const float* s_lse, void* dq, void* dk, void* dv, float* ds,
                            float* Dws, const int32_t* rev_off, const int32_t* rev_list, int B,
-                           int Hq, int Hkv, int n, int d, int topk, float tau, hipStream_t st);
+                           int Hq, int Hkv, int n, int d, int topk, float tau, int gate,
+                           hipStream_t st);
 
 // ---- decode (decode.hip)
 int decode_nsplit(int B, int Hkv, int topk);
 hipError_t launch_decode(int dtype, const void* q, const void* kc, const void* vc,
                          const int32_t* seq_lens, const float* s, int32_t* idx_out,
                          float* part_acc, float* part_ml, void* o, int B, int Hq, int Hkv,
-                         int cap, int d, int topk, int nsplit, float tau, hipStream_t st);
+                         int cap, int d, int topk, int nsplit, float tau, int gate,
+                         hipStream_t st);
 
 // ---- paged decode (decode_paged.hip)
 hipError_t launch_decode_paged(int dtype, const void* q, const void* k_pages, const void* v_pages,
                                const int32_t* page_table, int num_pages, const int32_t* seq_lens,
                                const float* s, int32_t* idx_out, float* part_acc, float* part_ml,
                                void* o, int B, int Hq, int Hkv, int max_blocks, int d, int topk,
-                               int nsplit, float tau, hipStream_t st);
+                               int nsplit, float tau, int gate, hipStream_t st);
 
 }  // namespace sas

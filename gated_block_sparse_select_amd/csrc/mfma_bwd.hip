@@ -23,6 +23,13 @@
 //    registers - no atomics, so the result is deterministic.
 // The split recomputes S and dP in both passes (7 tile products instead of 5)
 // in exchange for no atomics and no per-pair partial buffers.
+//
+// EXT, the external gate (g scales block m's values after an unbiased
+// softmax): with P_b = g P, the weight the forward's PV product used,
+//   dV = sum_h P_b^T dO_h,  dZ = P (g dP - D) = P_b (dP - D/g),
+//   dlg[i, m] = sum over block m of P g dP = sum of P_b dP,
+// so the kernels keep the log-gate as the tile's exponent offset and only
+// replace D by D/g (and, in the dq kernel, sum P_b dP for the gate).
 #include <type_traits>
 #include <utility>
 
@@ -33,7 +40,7 @@
 namespace sas {
 
 // ------------------------------------------------------------------ dq kernel
-template <int D, int GC>
+template <int D, int GC, bool EXT>
 __global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ o,
@@ -133,17 +140,20 @@ __global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
   auto tile = [&]<int ST, bool CUR>(int t) __attribute__((always_inline)) {
     lds_cchar* Kt = stage_buf<TK, ST, TB>();
     lds_cchar* Vt = stage_buf<TV, ST, TB>();
-    const float zoff = (CUR ? 0.f : grow[t] * kLog2e) - lse2;
+    const float bias2 = CUR ? 0.f : (EXT ? fmaxf(grow[t], kMinExtLogGate) : grow[t]) * kLog2e;
+    const float zoff = bias2 - lse2;
+    const float Dg = EXT ? Drow * fast_exp2(-bias2) : 0.f;   // EXT: D / g
     float zs = 0.f;
     bf16x8 dZp[4];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {   // one 32-key half at a time
       f32x16 S, P2;
-      // dP starts at -D (this lane's row), so the products give dP - D
+      // dP starts at -D (this lane's row), so the products give dP - D;
+      // EXT keeps dP itself (its gate gradient needs it)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         S[j] = 0.f;
-        P2[j] = -Drow;
+        P2[j] = EXT ? 0.f : -Drow;
       }
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
@@ -158,10 +168,16 @@ __global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
           const int j = 8 * jc + e;
           float p = fast_exp2(__builtin_fmaf(S[j], tau2, zoff));
           if (CUR && kt * 32 + 8 * (j >> 2) + 4 * hh + (j & 3) > rt * 32 + lr) p = 0.f;
-          x[e] = p * P2[j];
+          if constexpr (EXT) {
+            x[e] = p * (P2[j] - Dg);
+            if (!CUR) zs = __builtin_fmaf(p, P2[j], zs);
+          } else {
+            x[e] = p * P2[j];
+          }
         }
         dZp[kt * 2 + jc] = pack_bf16x8(x);
-        zs = sum_bf16x8(dZp[kt * 2 + jc], zs);   // the block-gate gradient of the dZ used
+        // the block-gate gradient of the dZ used
+        if constexpr (!EXT) zs = sum_bf16x8(dZp[kt * 2 + jc], zs);
       }
     }
 #pragma unroll
@@ -224,7 +240,7 @@ __global__ void __launch_bounds__(256) bwd_ds_kernel(const float* __restrict__ d
                                                      const float* __restrict__ s,
                                                      const float* __restrict__ s_lse,
                                                      float* __restrict__ ds, int nqb, int topk,
-                                                     int nch) {
+                                                     int nch, int gate) {
   __shared__ float dl[2048];      // topk <= 2048
   __shared__ int slot_of[2048];   // blocks per sequence <= 2048
   __shared__ float tot_s;
@@ -252,7 +268,10 @@ __global__ void __launch_bounds__(256) bwd_ds_kernel(const float* __restrict__ d
     float val = 0.f;
     if (m < hist) {
       const int sm = slot_of[m];
-      val = (sm >= 0 ? dl[sm] : 0.f) - expf(s[row * nqb + m] - sl_) * tot;
+      if (gate == SAS_GATE_SIGMOID)   // d log sigmoid(s) / ds = sigmoid(-s), no coupling
+        val = sm >= 0 ? dl[sm] / (1.f + expf(s[row * nqb + m])) : 0.f;
+      else
+        val = (sm >= 0 ? dl[sm] : 0.f) - expf(s[row * nqb + m] - sl_) * tot;
     }
     ds[row * nqb + m] = val;
   }
@@ -275,7 +294,7 @@ __global__ void __launch_bounds__(256) bwd_ds_kernel(const float* __restrict__ d
 // list entries (q-block and base-2 log-gate) are staged in LDS first, so the
 // loop issues no scalar memory loads (those return out of order and would
 // force every LDS wait to drain all outstanding LDS reads).
-template <int D>
+template <int D, bool EXT>
 __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
@@ -337,7 +356,8 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
   for (int e = tid; e < e1 - e0; e += 256) {
     const int32_t ent = lst[e0 + e];
     const int iq = ent & 0xFFFF, slot = (ent >> 16) & 0xFFFF;
-    const float b2 = slot == 0xFFFF ? 0.f : lg[(size_t(bk) * nkb + iq) * topk + slot] * kLog2e;
+    const float l = slot == 0xFFFF ? 0.f : lg[(size_t(bk) * nkb + iq) * topk + slot];
+    const float b2 = (EXT ? fmaxf(l, kMinExtLogGate) : l) * kLog2e;
     meta[e] = make_int2(iq, __float_as_int(b2));
   }
   __syncthreads();
@@ -423,8 +443,9 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
     lds_cchar* Qt = stage_buf<TQ, ST, TB>();
     lds_cchar* Ot = stage_buf<TO, ST, TB>();
     lds_cchar* St = stage_buf<TS, ST, 1024>();
-    // phase 1: S = Q K^T - lse/tau, dP = dO V^T - D
+    // phase 1: S = Q K^T - lse/tau, dP = dO V^T - D (EXT: - D/g)
     f32x16 S, P2;
+    const float ig = EXT ? fast_exp2(-bias2) : 1.f;
 #pragma unroll
     for (int jg = 0; jg < 4; ++jg) {
       const f32x4 l4 = *reinterpret_cast<lds_f32x4*>(St + so + jg * 32);
@@ -432,7 +453,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         S[4 * jg + r] = l4[r];
-        P2[4 * jg + r] = d4[r];
+        P2[4 * jg + r] = EXT ? d4[r] * ig : d4[r];
       }
     }
     bf16x8 qa[NC], oa[NC];
@@ -576,11 +597,17 @@ static void dq_launch(int nblocks, const void* q, const void* k, const void* v, 
                       const void* dO, const float* lse, const int32_t* idx, const int32_t* cnt,
                       const float* lg, void* dq, float* stats, float* dlgp, int Hq, int Hkv, int n,
                       int topk, float tau, float tau2, int BH, int h_off, int hchunks, int nch,
-                      int chunk0, hipStream_t st) {
-  hipLaunchKernelGGL((bwd_dq_kernel<D, GC>), dim3(nblocks), dim3(128 * GC), 0, st, (const uint16_t*)q,
-                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o,
-                     (const uint16_t*)dO, lse, idx, cnt, lg, (uint16_t*)dq, stats, dlgp, Hq, Hkv,
-                     n, topk, tau, tau2, BH, h_off, hchunks, nch, chunk0);
+                      int chunk0, bool ext, hipStream_t st) {
+#define SAS_DQ_KARGS (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o, \
+    (const uint16_t*)dO, lse, idx, cnt, lg, (uint16_t*)dq, stats, dlgp, Hq, Hkv, n, topk, tau,   \
+    tau2, BH, h_off, hchunks, nch, chunk0
+  if (ext)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, GC, true>), dim3(nblocks), dim3(128 * GC), 0, st,
+                       SAS_DQ_KARGS);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<D, GC, false>), dim3(nblocks), dim3(128 * GC), 0, st,
+                       SAS_DQ_KARGS);
+#undef SAS_DQ_KARGS
 }
 
 template <int D>
@@ -588,9 +615,9 @@ static void dq_dispatch(int gc, int nblocks, const void* q, const void* k, const
                         const void* o, const void* dO, const float* lse, const int32_t* idx,
                         const int32_t* cnt, const float* lg, void* dq, float* stats, float* dlgp,
                         int Hq, int Hkv, int n, int topk, float tau, float tau2, int BH, int h_off,
-                        int hchunks, int nch, int chunk0, hipStream_t st) {
+                        int hchunks, int nch, int chunk0, bool ext, hipStream_t st) {
 #define SAS_DQ_ARGS nblocks, q, k, v, o, dO, lse, idx, cnt, lg, dq, stats, dlgp, Hq, Hkv, n, \
-                    topk, tau, tau2, BH, h_off, hchunks, nch, chunk0, st
+                    topk, tau, tau2, BH, h_off, hchunks, nch, chunk0, ext, st
   switch (gc) {
     case 1: dq_launch<D, 1>(SAS_DQ_ARGS); break;
     case 2: dq_launch<D, 2>(SAS_DQ_ARGS); break;
@@ -616,8 +643,9 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
                            const float* s_lse, void* dq, void* dk, void* dv, float* ds,
                            float* stats, const int32_t* rev_off, const int32_t* rev_list,
                            float* dlgp, int B, int Hq, int Hkv, int n, int d, int topk, float tau,
-                           hipStream_t st) {
+                           int gate, hipStream_t st) {
   const int G = Hq / Hkv;
+  const bool ext = gate == SAS_GATE_EXTERNAL;
   const int nqb = n / SAS_BLK;
   const int BH = B * Hkv;
   const float tau2 = tau * kLog2e;
@@ -627,8 +655,8 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
     ProfScope ps("sas_bwd_dq_kernel", st);
     int chunk0 = 0;
     for (const HeadChunks& hc : head_chunks(G)) {
-      if (d == 128) dq_dispatch<128>(hc.gc, BH * nqb * hc.count, q, k, v, o, dO, lse, idx, cnt, lg, dq, stats, dlgp, Hq, Hkv, n, K, tau, tau2, BH, hc.h_off, hc.count, nch, chunk0, st);
-      else dq_dispatch<64>(hc.gc, BH * nqb * hc.count, q, k, v, o, dO, lse, idx, cnt, lg, dq, stats, dlgp, Hq, Hkv, n, K, tau, tau2, BH, hc.h_off, hc.count, nch, chunk0, st);
+      if (d == 128) dq_dispatch<128>(hc.gc, BH * nqb * hc.count, q, k, v, o, dO, lse, idx, cnt, lg, dq, stats, dlgp, Hq, Hkv, n, K, tau, tau2, BH, hc.h_off, hc.count, nch, chunk0, ext, st);
+      else dq_dispatch<64>(hc.gc, BH * nqb * hc.count, q, k, v, o, dO, lse, idx, cnt, lg, dq, stats, dlgp, Hq, Hkv, n, K, tau, tau2, BH, hc.h_off, hc.count, nch, chunk0, ext, st);
       chunk0 += hc.count;
     }
   }
@@ -637,23 +665,24 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
   {
     ProfScope ps("sas_bwd_ds_kernel", st);
     hipLaunchKernelGGL(bwd_ds_kernel, dim3(BH * nqb), dim3(256), 0, st, dlgp, idx, cnt, s, s_lse,
-                       ds, nqb, K, nch);
+                       ds, nqb, K, nch, gate);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
     ProfScope ps("sas_bwd_dkdv_kernel", st);
-    if (d == 128) {
-      hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3(BH * nqb), dim3(256), 0, st, (const uint16_t*)q,
-                         (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO, stats, lg,
-                         rev_off, rev_list, (uint16_t*)dk, (uint16_t*)dv, Hq, Hkv, n, topk, tau,
-                         tau2);
-    } else {
-      hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3(BH * nqb), dim3(256), 0, st, (const uint16_t*)q,
-                         (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO, stats, lg,
-                         rev_off, rev_list, (uint16_t*)dk, (uint16_t*)dv, Hq, Hkv, n, topk, tau,
-                         tau2);
-    }
+#define SAS_KV_KARGS (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, \
+    (const uint16_t*)dO, stats, lg, rev_off, rev_list, (uint16_t*)dk, (uint16_t*)dv, Hq, Hkv, n, \
+    topk, tau, tau2
+    if (d == 128 && ext)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<128, true>), dim3(BH * nqb), dim3(256), 0, st, SAS_KV_KARGS);
+    else if (d == 128)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<128, false>), dim3(BH * nqb), dim3(256), 0, st, SAS_KV_KARGS);
+    else if (ext)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<64, true>), dim3(BH * nqb), dim3(256), 0, st, SAS_KV_KARGS);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<64, false>), dim3(BH * nqb), dim3(256), 0, st, SAS_KV_KARGS);
+#undef SAS_KV_KARGS
   }
   return hipGetLastError();
 }

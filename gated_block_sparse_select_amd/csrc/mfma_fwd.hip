@@ -15,15 +15,22 @@
 // K/V tiles are double-buffered in LDS; the next tile's global loads are in
 // flight while the current one is computed.  Softmax runs in the exp2 domain.
 // Workgroups are issued largest q-block first (most tiles first).
+//
+// EXT (the external gate, g scales the values after an unbiased softmax):
+// the kernel is the same with the log-gate kept as the tile's exponent
+// offset, so the weights P g reach the PV product unchanged, and the tile's
+// weight sum is multiplied by 1/g before it joins the normaliser, which then
+// sums the unbiased weights: O / l = sum g P v / sum P.
 #include <type_traits>
 #include <utility>
 
 #include "launch.h"
 #include "mfma_common.h"
+#include "sas.h"
 
 namespace sas {
 
-template <int D, int GC>
+template <int D, int GC, bool EXT>
 __global__ void __launch_bounds__(128 * GC) fwd_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ idx,
@@ -109,7 +116,7 @@ __global__ void __launch_bounds__(128 * GC) fwd_mfma_kernel(
   auto tile = [&]<int ST, bool CUR>(int t) __attribute__((always_inline)) {
     lds_cchar* Kt = stage_buf<TK, ST, TB>();
     lds_cchar* Vt = stage_buf<TV, ST, TB>();
-    const float bias2 = CUR ? 0.f : grow[t] * kLog2e;
+    const float bias2 = CUR ? 0.f : (EXT ? fmaxf(grow[t], kMinExtLogGate) : grow[t]) * kLog2e;
 
     f32x16 S[2];
 #pragma unroll
@@ -155,6 +162,7 @@ __global__ void __launch_bounds__(128 * GC) fwd_mfma_kernel(
     }
     const float c0 = bias2 - mrow;
     bf16x8 P[4];
+    float ts = 0.f;   // EXT: this tile's weight sum
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -163,8 +171,11 @@ __global__ void __launch_bounds__(128 * GC) fwd_mfma_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) p[e] = fast_exp2(__builtin_fmaf(S[kt][8 * jc + e], tau2, c0));
         P[kt * 2 + jc] = pack_bf16x8(p);
-        lrow = sum_bf16x8(P[kt * 2 + jc], lrow);   // normalise by the weights actually used
+        // normalise by the weights actually used
+        if constexpr (EXT) ts = sum_bf16x8(P[kt * 2 + jc], ts);
+        else lrow = sum_bf16x8(P[kt * 2 + jc], lrow);
       }
+    if constexpr (EXT) lrow = __builtin_fmaf(ts, fast_exp2(-bias2), lrow);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -224,36 +235,43 @@ template <int D, int GC>
 static void fwd_launch(int nblocks, const void* q, const void* k, const void* v,
                        const int32_t* idx, const int32_t* cnt, const float* lg, void* o, float* lse,
                        int Hq, int Hkv, int n, int topk, float tau2, int BH, int h_off,
-                       int hchunks, hipStream_t st) {
-  hipLaunchKernelGGL((fwd_mfma_kernel<D, GC>), dim3(nblocks), dim3(128 * GC), 0, st,
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, cnt, lg,
-                     (uint16_t*)o, lse, Hq, Hkv, n, topk, tau2, BH, h_off, hchunks);
+                       int hchunks, bool ext, hipStream_t st) {
+  if (ext)
+    hipLaunchKernelGGL((fwd_mfma_kernel<D, GC, true>), dim3(nblocks), dim3(128 * GC), 0, st,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, cnt, lg,
+                       (uint16_t*)o, lse, Hq, Hkv, n, topk, tau2, BH, h_off, hchunks);
+  else
+    hipLaunchKernelGGL((fwd_mfma_kernel<D, GC, false>), dim3(nblocks), dim3(128 * GC), 0, st,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, cnt, lg,
+                       (uint16_t*)o, lse, Hq, Hkv, n, topk, tau2, BH, h_off, hchunks);
 }
 
 template <int D>
 static void fwd_dispatch(int gc, int nblocks, const void* q, const void* k, const void* v,
                          const int32_t* idx, const int32_t* cnt, const float* lg, void* o,
                          float* lse, int Hq, int Hkv, int n, int topk, float tau2, int BH,
-                         int h_off, int hchunks, hipStream_t st) {
+                         int h_off, int hchunks, bool ext, hipStream_t st) {
   switch (gc) {
-    case 1: fwd_launch<D, 1>(nblocks, q, k, v, idx, cnt, lg, o, lse, Hq, Hkv, n, topk, tau2, BH, h_off, hchunks, st); break;
-    case 2: fwd_launch<D, 2>(nblocks, q, k, v, idx, cnt, lg, o, lse, Hq, Hkv, n, topk, tau2, BH, h_off, hchunks, st); break;
-    default: fwd_launch<D, 4>(nblocks, q, k, v, idx, cnt, lg, o, lse, Hq, Hkv, n, topk, tau2, BH, h_off, hchunks, st); break;
+    case 1: fwd_launch<D, 1>(nblocks, q, k, v, idx, cnt, lg, o, lse, Hq, Hkv, n, topk, tau2, BH, h_off, hchunks, ext, st); break;
+    case 2: fwd_launch<D, 2>(nblocks, q, k, v, idx, cnt, lg, o, lse, Hq, Hkv, n, topk, tau2, BH, h_off, hchunks, ext, st); break;
+    default: fwd_launch<D, 4>(nblocks, q, k, v, idx, cnt, lg, o, lse, Hq, Hkv, n, topk, tau2, BH, h_off, hchunks, ext, st); break;
   }
 }
 
 hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, const int32_t* idx,
                            const int32_t* cnt, const float* lg, void* o, float* lse, int B,
-                           int Hq, int Hkv, int n, int d, int topk, float tau, hipStream_t st) {
+                           int Hq, int Hkv, int n, int d, int topk, float tau, int gate,
+                           hipStream_t st) {
   ProfScope ps("sas_fwd_mfma_kernel", st);
+  const bool ext = gate == SAS_GATE_EXTERNAL;
   const int G = Hq / Hkv;
   const int nqb = n / SAS_BLK;
   const int BH = B * Hkv;
   const float tau2 = tau * kLog2e;
   // heads in chunks of 4, then 2, then 1 (each launch covers hchunks chunks)
   for (const HeadChunks& hc : head_chunks(G)) {
-    if (d == 128) fwd_dispatch<128>(hc.gc, BH * nqb * hc.count, q, k, v, idx, cnt, lg, o, lse, Hq, Hkv, n, topk, tau2, BH, hc.h_off, hc.count, st);
-    else fwd_dispatch<64>(hc.gc, BH * nqb * hc.count, q, k, v, idx, cnt, lg, o, lse, Hq, Hkv, n, topk, tau2, BH, hc.h_off, hc.count, st);
+    if (d == 128) fwd_dispatch<128>(hc.gc, BH * nqb * hc.count, q, k, v, idx, cnt, lg, o, lse, Hq, Hkv, n, topk, tau2, BH, hc.h_off, hc.count, ext, st);
+    else fwd_dispatch<64>(hc.gc, BH * nqb * hc.count, q, k, v, idx, cnt, lg, o, lse, Hq, Hkv, n, topk, tau2, BH, hc.h_off, hc.count, ext, st);
   }
   return hipGetLastError();
 }

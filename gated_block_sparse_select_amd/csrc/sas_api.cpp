@@ -16,14 +16,15 @@ namespace sas {
 // bf16 tensor-core kernels (mfma_fwd.hip / mfma_bwd.hip)
 hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, const int32_t* idx,
                            const int32_t* cnt, const float* lg, void* o, float* lse, int B,
-                           int Hq, int Hkv, int n, int d, int topk, float tau, hipStream_t st);
+                           int Hq, int Hkv, int n, int d, int topk, float tau, int gate,
+                           hipStream_t st);
 hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const void* o,
                            const void* dO, const float* lse, const int32_t* idx,
                            const int32_t* cnt, const float* lg, const float* s,
                            const float* s_lse, void* dq, void* dk, void* dv, float* ds,
                            float* Dws, const int32_t* rev_off, const int32_t* rev_list,
                            float* dlgp, int B, int Hq, int Hkv, int n, int d, int topk, float tau,
-                           hipStream_t st);
+                           int gate, hipStream_t st);
 size_t bwd_mfma_extra_ws(int B, int Hq, int Hkv, int n, int topk);
 bool mfma_supported(int d, int G);
 }  // namespace sas
@@ -33,8 +34,9 @@ namespace {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-bool shape_ok_common(int B, int Hq, int Hkv, int len, int d, int topk, float scale) {
+bool shape_ok_common(int B, int Hq, int Hkv, int len, int d, int topk, float scale, int gate) {
   if (B < 1 || Hq < 1 || Hkv < 1) return false;
+  if (gate < SAS_GATE_SOFTMAX || gate > SAS_GATE_EXTERNAL) return false;
   if (Hq % Hkv != 0) return false;
   const int G = Hq / Hkv;
   if (G > 16) return false;
@@ -51,14 +53,16 @@ bool shape_ok_common(int B, int Hq, int Hkv, int len, int d, int topk, float sca
 sas_status check_shape(const sas_shape* s) {
   if (!s) return SAS_ERR_ARG;
   if (s->dtype != SAS_F32 && s->dtype != SAS_BF16) return SAS_ERR_DTYPE;
-  if (!shape_ok_common(s->B, s->Hq, s->Hkv, s->n, s->d, s->topk, s->scale)) return SAS_ERR_ARG;
+  if (!shape_ok_common(s->B, s->Hq, s->Hkv, s->n, s->d, s->topk, s->scale, s->gate))
+    return SAS_ERR_ARG;
   return SAS_OK;
 }
 
 sas_status check_dshape(const sas_decode_shape* s) {
   if (!s) return SAS_ERR_ARG;
   if (s->dtype != SAS_F32 && s->dtype != SAS_BF16) return SAS_ERR_DTYPE;
-  if (!shape_ok_common(s->B, s->Hq, s->Hkv, s->cap, s->d, s->topk, s->scale)) return SAS_ERR_ARG;
+  if (!shape_ok_common(s->B, s->Hq, s->Hkv, s->cap, s->d, s->topk, s->scale, s->gate))
+    return SAS_ERR_ARG;
   return SAS_OK;
 }
 
@@ -68,7 +72,8 @@ sas_status check_pshape(const sas_decode_paged_shape* s) {
   if (s->max_blocks < 1 || s->max_blocks > SAS_MAX_DECODE_BLOCKS || s->num_pages < 1)
     return SAS_ERR_ARG;
   // the remaining limits are those of a decode shape whose cap is one block
-  if (!shape_ok_common(s->B, s->Hq, s->Hkv, SAS_BLOCK, s->d, s->topk, s->scale)) return SAS_ERR_ARG;
+  if (!shape_ok_common(s->B, s->Hq, s->Hkv, SAS_BLOCK, s->d, s->topk, s->scale, s->gate))
+    return SAS_ERR_ARG;
   if (int64_t(s->B) * s->Hkv * s->max_blocks > (int64_t(1) << 30)) return SAS_ERR_ARG;
   return SAS_OK;
 }
@@ -84,6 +89,7 @@ sas_decode_shape as_decode_shape(const sas_decode_paged_shape* s) {
   d.topk = s->topk;
   d.scale = s->scale;
   d.dtype = s->dtype;
+  d.gate = s->gate;
   return d;
 }
 
@@ -185,7 +191,7 @@ void prof_after(const char* name, hipStream_t st) {
 
 extern "C" {
 
-int32_t sas_abi_version(void) { return 1; }
+int32_t sas_abi_version(void) { return 2; }
 
 const char* sas_status_string(sas_status st) {
   switch (st) {
@@ -224,7 +230,7 @@ sas_status sas_select(const sas_shape* s, const float* sc, int32_t* idx, int32_t
   const int nb = s->n / SAS_BLOCK;
   clear_stale_error();
   return from_hip(sas::launch_select(sc, idx, cnt, log_gate, s_lse, s->B * s->Hkv * nb, nb, nb,
-                                     s->topk, nullptr, s->Hkv, s->n, stream));
+                                     s->topk, nullptr, s->Hkv, s->n, s->gate, stream));
 }
 
 sas_status sas_mask_documents(const sas_shape* s, const int32_t* doc_first, float* sc,
@@ -248,9 +254,9 @@ sas_status sas_fwd(const sas_shape* s, const void* q, const void* k, const void*
   clear_stale_error();
   if (s->dtype == SAS_BF16 && sas::mfma_supported(s->d, G))
     return from_hip(sas::launch_fwd_mfma(q, k, v, idx, cnt, log_gate, o, lse, s->B, s->Hq, s->Hkv,
-                                         s->n, s->d, s->topk, tau, stream));
+                                         s->n, s->d, s->topk, tau, s->gate, stream));
   return from_hip(sas::launch_fwd_simt(s->dtype, q, k, v, idx, cnt, log_gate, o, lse, s->B, s->Hq,
-                                       s->Hkv, s->n, s->d, s->topk, tau, stream));
+                                       s->Hkv, s->n, s->d, s->topk, tau, s->gate, stream));
 }
 
 size_t sas_bwd_workspace_bytes(const sas_shape* s) {
@@ -283,10 +289,10 @@ sas_status sas_bwd(const sas_shape* s, const void* q, const void* k, const void*
     return from_hip(sas::launch_bwd_mfma(
         q, k, v, o, dO, lse, idx, cnt, log_gate, sc, s_lse, dq, dk, dv, ds, Dws, rev_off, rev_list,
         reinterpret_cast<float*>(base + w.dlg_off), s->B, s->Hq, s->Hkv, s->n, s->d, s->topk, tau,
-        stream));
+        s->gate, stream));
   return from_hip(sas::launch_bwd_simt(s->dtype, q, k, v, o, dO, lse, idx, cnt, log_gate, sc, s_lse,
                                        dq, dk, dv, ds, Dws, rev_off, rev_list, s->B, s->Hq, s->Hkv,
-                                       s->n, s->d, s->topk, tau, stream));
+                                       s->n, s->d, s->topk, tau, s->gate, stream));
 }
 
 size_t sas_decode_workspace_bytes(const sas_decode_shape* s) {
@@ -308,7 +314,7 @@ sas_status sas_decode(const sas_decode_shape* s, const void* q, const void* k_ca
   clear_stale_error();
   return from_hip(sas::launch_decode(s->dtype, q, k_cache, v_cache, seq_lens, sc, idx_out, acc, ml,
                                      o, s->B, s->Hq, s->Hkv, s->cap, s->d, s->topk, w.nsplit,
-                                     tau_of(s->scale, s->d), stream));
+                                     tau_of(s->scale, s->d), s->gate, stream));
 }
 
 size_t sas_decode_paged_workspace_bytes(const sas_decode_paged_shape* s) {
@@ -334,7 +340,7 @@ sas_status sas_decode_paged(const sas_decode_paged_shape* s, const void* q, cons
   return from_hip(sas::launch_decode_paged(s->dtype, q, k_pages, v_pages, page_table, s->num_pages,
                                            seq_lens, sc, idx_out, acc, ml, o, s->B, s->Hq, s->Hkv,
                                            s->max_blocks, s->d, s->topk, w.nsplit,
-                                           tau_of(s->scale, s->d), stream));
+                                           tau_of(s->scale, s->d), s->gate, stream));
 }
 
 const char* sas_last_hip_error(void) { return hipGetErrorName(g_last_hip); }

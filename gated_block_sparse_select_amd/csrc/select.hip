@@ -14,7 +14,7 @@ __global__ void __launch_bounds__(64) select_kernel(const float* __restrict__ s,
                                                     float* __restrict__ slse, int rows,
                                                     int nqb, int nkb, int topk,
                                                     const int32_t* __restrict__ seq_lens,
-                                                    int hkv, int cap) {
+                                                    int hkv, int cap, int gate) {
   const int lane = threadIdx.x;
   const int row = blockIdx.x;
   int i;
@@ -28,7 +28,7 @@ __global__ void __launch_bounds__(64) select_kernel(const float* __restrict__ s,
   int32_t* irow = idx + size_t(row) * topk;
   float* grow = lg + size_t(row) * topk;
   float lse;
-  const int keff = select_row<CPL>(s + size_t(row) * nkb, i, topk, lane, lse,
+  const int keff = select_row<CPL>(s + size_t(row) * nkb, i, topk, gate, lane, lse,
                                    [&](int pos, int m, float g) {
                                      irow[pos] = m;
                                      grow[pos] = g;
@@ -45,22 +45,23 @@ __global__ void __launch_bounds__(64) select_kernel(const float* __restrict__ s,
 
 template <int CPL>
 static void go(const float* s, int32_t* idx, int32_t* cnt, float* lg, float* slse, int rows,
-               int nqb, int nkb, int topk, const int32_t* sl, int hkv, int cap, hipStream_t st) {
+               int nqb, int nkb, int topk, const int32_t* sl, int hkv, int cap, int gate,
+               hipStream_t st) {
   hipLaunchKernelGGL(select_kernel<CPL>, dim3(rows), dim3(64), 0, st, s, idx, cnt, lg, slse, rows,
-                     nqb, nkb, topk, sl, hkv, cap);
+                     nqb, nkb, topk, sl, hkv, cap, gate);
 }
 
 hipError_t launch_select(const float* s, int32_t* idx, int32_t* cnt, float* lg, float* slse,
                          int rows, int nqb, int nkb, int topk, const int32_t* seq_lens, int hkv,
-                         int cap, hipStream_t st) {
+                         int cap, int gate, hipStream_t st) {
   ProfScope ps("sas_select_kernel", st);
   switch (select_cpl(nkb)) {
-    case 1: go<1>(s, idx, cnt, lg, slse, rows, nqb, nkb, topk, seq_lens, hkv, cap, st); break;
-    case 2: go<2>(s, idx, cnt, lg, slse, rows, nqb, nkb, topk, seq_lens, hkv, cap, st); break;
-    case 4: go<4>(s, idx, cnt, lg, slse, rows, nqb, nkb, topk, seq_lens, hkv, cap, st); break;
-    case 8: go<8>(s, idx, cnt, lg, slse, rows, nqb, nkb, topk, seq_lens, hkv, cap, st); break;
-    case 16: go<16>(s, idx, cnt, lg, slse, rows, nqb, nkb, topk, seq_lens, hkv, cap, st); break;
-    default: go<32>(s, idx, cnt, lg, slse, rows, nqb, nkb, topk, seq_lens, hkv, cap, st); break;
+    case 1: go<1>(s, idx, cnt, lg, slse, rows, nqb, nkb, topk, seq_lens, hkv, cap, gate, st); break;
+    case 2: go<2>(s, idx, cnt, lg, slse, rows, nqb, nkb, topk, seq_lens, hkv, cap, gate, st); break;
+    case 4: go<4>(s, idx, cnt, lg, slse, rows, nqb, nkb, topk, seq_lens, hkv, cap, gate, st); break;
+    case 8: go<8>(s, idx, cnt, lg, slse, rows, nqb, nkb, topk, seq_lens, hkv, cap, gate, st); break;
+    case 16: go<16>(s, idx, cnt, lg, slse, rows, nqb, nkb, topk, seq_lens, hkv, cap, gate, st); break;
+    default: go<32>(s, idx, cnt, lg, slse, rows, nqb, nkb, topk, seq_lens, hkv, cap, gate, st); break;
   }
   return hipGetLastError();
 }

@@ -17,6 +17,7 @@
 #pragma once
 
 #include "common.h"
+#include "sas.h"
 
 namespace sas {
 
@@ -25,13 +26,22 @@ SAS_DEV uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Log-gate of a kept block with score x in a row with candidate LSE lse, for
+// each gate kind (sas.h): x - lse (softmax; also the external gate's log g),
+// log sigmoid(x) (sigmoid), 0 (hard).
+SAS_DEV float log_gate_of(int gate, float x, float lse) {
+  if (gate == SAS_GATE_SIGMOID) return fminf(x, 0.f) - log1pf(expf(-fabsf(x)));
+  if (gate == SAS_GATE_HARD) return 0.f;
+  return x - lse;
+}
+
 // order_key(-inf): below the key of every finite score, which is at least
 // order_key(-FLT_MAX) = kNoKey + 1.  A key <= kNoKey is not a candidate.
 constexpr uint32_t kNoKey = 0x007FFFFFu;
 
 // Selects min(topk, candidates) of the blocks m < i of srow.  emit(pos, m,
 // log_gate) is called by the lane holding the pos-th kept block (pos
-// ascending with m).  Returns the number kept (wave-uniform); lse receives
+// ascending with m), with the log-gate of the gate kind.  Returns the number kept (wave-uniform); lse receives
 // the LSE over the candidates, -inf if there is none.
 //
 // Non-candidates (m >= i or a score of -inf) carry key kNoKey, below every
@@ -39,8 +49,8 @@ constexpr uint32_t kNoKey = 0x007FFFFFu;
 // than topk candidates exist, and then every key > kNoKey is kept.  The number kept is the
 // running output position, so no separate candidate count is needed.
 template <int CPL, class Emit>
-SAS_DEV int select_row(const float* __restrict__ srow, int i, int topk, int lane, float& lse,
-                       Emit&& emit) {
+SAS_DEV int select_row(const float* __restrict__ srow, int i, int topk, int gate, int lane,
+                       float& lse, Emit&& emit) {
   float val[CPL];
   uint32_t key[CPL];
   float mx = -INFINITY;
@@ -89,7 +99,7 @@ SAS_DEV int select_row(const float* __restrict__ srow, int i, int topk, int lane
     const bool take = key[j] > T || (eq && eq_seen + mask_rank(eqm) < need_eq);
     eq_seen += __popcll(eqm);
     const uint64_t tm = __ballot(take);
-    if (take) emit(base + mask_rank(tm), m, val[j] - lse);
+    if (take) emit(base + mask_rank(tm), m, log_gate_of(gate, val[j], lse));
     base += __popcll(tm);
   }
   return base;
@@ -107,8 +117,9 @@ SAS_DEV int select_row(const float* __restrict__ srow, int i, int topk, int lane
 // the per-wave counts of the waves before.  Every thread of the workgroup must
 // call it (it contains __syncthreads).
 template <int CPL, int NW, class Emit>
-SAS_DEV int select_row_wg(const float* __restrict__ srow, int i, int topk, int wave, int lane,
-                          float& lse, __attribute__((address_space(3))) float* red, Emit&& emit) {
+SAS_DEV int select_row_wg(const float* __restrict__ srow, int i, int topk, int gate, int wave,
+                          int lane, float& lse, __attribute__((address_space(3))) float* red,
+                          Emit&& emit) {
   __attribute__((address_space(3))) int* ired =
       reinterpret_cast<__attribute__((address_space(3))) int*>(red);
   const int m0 = wave * 64 * CPL;
@@ -195,7 +206,7 @@ SAS_DEV int select_row_wg(const float* __restrict__ srow, int i, int topk, int w
     const bool take = key[j] > T || (eq && eq_seen + mask_rank(eqm) < need_eq);
     eq_seen += __popcll(eqm);
     const uint64_t tm = __ballot(take);
-    if (take) emit(base + mask_rank(tm), m, val[j] - lse);
+    if (take) emit(base + mask_rank(tm), m, log_gate_of(gate, val[j], lse));
     base += __popcll(tm);
   }
   return n_gt + need_eq;

@@ -8,9 +8,11 @@
 //   gate gradient of a kept block = sum of its logit gradients (§2.6)
 //
 // One thread per (query head, query row); K/V tiles of the kept blocks are
-// staged through LDS as float32.
+// staged through LDS as float32.  The external gate (sas.h) is computed as
+// written: unbiased logits, values of kept block m scaled by g = exp(log g).
 #include "common.h"
 #include "launch.h"
+#include "sas.h"
 
 namespace sas {
 
@@ -21,7 +23,8 @@ __global__ void __launch_bounds__(1024) fwd_simt_kernel(
     const typename E::T* __restrict__ q, const typename E::T* __restrict__ k,
     const typename E::T* __restrict__ v, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ cnt, const float* __restrict__ lg, typename E::T* __restrict__ o,
-    float* __restrict__ lse, int Hq, int Hkv, int n, int topk, float tau) {
+    float* __restrict__ lse, int Hq, int Hkv, int n, int topk, float tau, int gate) {
+  const bool ext = gate == SAS_GATE_EXTERNAL;
   const int nqb = n / SAS_BLK;
   const int i = blockIdx.x % nqb;
   const int bk = blockIdx.x / nqb;
@@ -45,7 +48,9 @@ __global__ void __launch_bounds__(1024) fwd_simt_kernel(
   const size_t kvbase = (size_t(b) * Hkv + kv) * n;
   for (int t = 0; t <= c_sel; ++t) {
     const int blk = (t < c_sel) ? idx[(bk * size_t(nqb) + i) * topk + t] : i;
-    const float bias = (t < c_sel) ? lg[(bk * size_t(nqb) + i) * topk + t] : 0.f;
+    const float lgt = (t < c_sel) ? lg[(bk * size_t(nqb) + i) * topk + t] : 0.f;
+    const float bias = ext ? 0.f : lgt;       // logit bias
+    const float w = ext ? expf(lgt) : 1.f;    // value weight
     __syncthreads();
     for (int e = threadIdx.x; e < SAS_BLK * D; e += blockDim.x) {
       const int rr = e / D, cc = e % D;
@@ -68,8 +73,9 @@ __global__ void __launch_bounds__(1024) fwd_simt_kernel(
       }
       const float p = expf(z - mrun);
       lrun += p;
+      const float pw = p * w;
 #pragma unroll
-      for (int c = 0; c < D; ++c) acc[c] += p * Vs[j][c];
+      for (int c = 0; c < D; ++c) acc[c] += pw * Vs[j][c];
     }
   }
   const float inv = 1.f / lrun;
@@ -100,7 +106,8 @@ __global__ void __launch_bounds__(1024) bwd_dq_simt_kernel(
     const float* __restrict__ lse, const float* __restrict__ Dv, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ cnt, const float* __restrict__ lg, const float* __restrict__ s,
     const float* __restrict__ s_lse, typename E::T* __restrict__ dq, float* __restrict__ ds,
-    int Hq, int Hkv, int n, int topk, float tau) {
+    int Hq, int Hkv, int n, int topk, float tau, int gate) {
+  const bool ext = gate == SAS_GATE_EXTERNAL;
   const int nqb = n / SAS_BLK;
   const int i = blockIdx.x % nqb;
   const int bk = blockIdx.x / nqb;
@@ -130,7 +137,9 @@ __global__ void __launch_bounds__(1024) bwd_dq_simt_kernel(
   const int nwaves = blockDim.x / 64;
   for (int t = 0; t <= c_sel; ++t) {
     const int blk = (t < c_sel) ? idx[rowsel * topk + t] : i;
-    const float bias = (t < c_sel) ? lg[rowsel * topk + t] : 0.f;
+    const float lgt = (t < c_sel) ? lg[rowsel * topk + t] : 0.f;
+    const float bias = ext ? 0.f : lgt;
+    const float w = ext ? expf(lgt) : 1.f;
     __syncthreads();
     for (int e = threadIdx.x; e < SAS_BLK * D; e += blockDim.x) {
       const int rr = e / D, cc = e % D;
@@ -149,8 +158,9 @@ __global__ void __launch_bounds__(1024) bwd_dq_simt_kernel(
         dp += dor[c] * Vs[j][c];
       }
       const float p = expf(z - L);
+      dp *= w;
       const float dz = p * (dp - Drow);
-      tsum += dz;
+      tsum += ext ? p * dp : dz;   // gate gradient: d/dlog g
 #pragma unroll
       for (int c = 0; c < D; ++c) acc[c] += dz * Ks[j][c];
     }
@@ -183,7 +193,10 @@ __global__ void __launch_bounds__(1024) bwd_dq_simt_kernel(
     float val = 0.f;
     if (m < hist) {
       const int sl_m = slot_of[m];
-      val = (sl_m >= 0 ? dlg_s[sl_m] : 0.f) - expf(srow[m] - sl) * tot;
+      if (gate == SAS_GATE_SIGMOID)   // d log sigmoid(s) / ds = sigmoid(-s), no coupling
+        val = sl_m >= 0 ? dlg_s[sl_m] / (1.f + expf(srow[m])) : 0.f;
+      else
+        val = (sl_m >= 0 ? dlg_s[sl_m] : 0.f) - expf(srow[m] - sl) * tot;
     }
     dsrow[m] = val;
   }
@@ -197,7 +210,8 @@ __global__ void __launch_bounds__(64) bwd_dkdv_simt_kernel(
     const float* __restrict__ lse, const float* __restrict__ Dv, const float* __restrict__ lg,
     const int32_t* __restrict__ rev_off, const int32_t* __restrict__ rev_list,
     typename E::T* __restrict__ dk, typename E::T* __restrict__ dv, int Hq, int Hkv, int n,
-    int topk, float tau) {
+    int topk, float tau, int gate) {
+  const bool ext = gate == SAS_GATE_EXTERNAL;
   const int nb = n / SAS_BLK;
   const int m = blockIdx.x % nb;
   const int bk = blockIdx.x / nb;
@@ -225,7 +239,9 @@ __global__ void __launch_bounds__(64) bwd_dkdv_simt_kernel(
     const int i = ent & 0xFFFF;
     const int slot = (ent >> 16) & 0xFFFF;
     const bool own = slot == 0xFFFF;
-    const float bias = own ? 0.f : lg[(bk * size_t(nb) + i) * topk + slot];
+    const float lgt = own ? 0.f : lg[(bk * size_t(nb) + i) * topk + slot];
+    const float bias = ext ? 0.f : lgt;
+    const float w = ext ? expf(lgt) : 1.f;
     for (int g = 0; g < G; ++g) {
       const size_t row0 = (size_t(b) * Hq + kv * G + g) * n + size_t(i) * SAS_BLK;
       __syncthreads();
@@ -245,10 +261,11 @@ __global__ void __launch_bounds__(64) bwd_dkdv_simt_kernel(
           dp += Os[t][c] * vr[c];
         }
         const float p = expf(z - Ls[t]);
-        const float dz = p * (dp - Ds[t]);
+        const float dz = p * (w * dp - Ds[t]);
+        const float pw = p * w;
 #pragma unroll
         for (int c = 0; c < D; ++c) {
-          av[c] += p * Os[t][c];
+          av[c] += pw * Os[t][c];
           ak[c] += dz * Qs[t][c];
         }
       }
@@ -264,26 +281,26 @@ __global__ void __launch_bounds__(64) bwd_dkdv_simt_kernel(
 template <class E, int D>
 static hipError_t fwd_go(const void* q, const void* k, const void* v, const int32_t* idx,
                          const int32_t* cnt, const float* lg, void* o, float* lse, int B, int Hq,
-                         int Hkv, int n, int topk, float tau, hipStream_t st) {
+                         int Hkv, int n, int topk, float tau, int gate, hipStream_t st) {
   using T = typename E::T;
   const int nqb = n / SAS_BLK;
   ProfScope ps("sas_fwd_simt_kernel", st);
   hipLaunchKernelGGL((fwd_simt_kernel<E, D>), dim3(B * Hkv * nqb), dim3((Hq / Hkv) * SAS_BLK), 0,
                      st, (const T*)q, (const T*)k, (const T*)v, idx, cnt, lg, (T*)o, lse, Hq, Hkv,
-                     n, topk, tau);
+                     n, topk, tau, gate);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_simt(int dtype, const void* q, const void* k, const void* v,
                            const int32_t* idx, const int32_t* cnt, const float* lg, void* o,
                            float* lse, int B, int Hq, int Hkv, int n, int d, int topk, float tau,
-                           hipStream_t st) {
+                           int gate, hipStream_t st) {
   if (dtype == 0) {
-    if (d == 64) return fwd_go<ElemF32, 64>(q, k, v, idx, cnt, lg, o, lse, B, Hq, Hkv, n, topk, tau, st);
-    return fwd_go<ElemF32, 128>(q, k, v, idx, cnt, lg, o, lse, B, Hq, Hkv, n, topk, tau, st);
+    if (d == 64) return fwd_go<ElemF32, 64>(q, k, v, idx, cnt, lg, o, lse, B, Hq, Hkv, n, topk, tau, gate, st);
+    return fwd_go<ElemF32, 128>(q, k, v, idx, cnt, lg, o, lse, B, Hq, Hkv, n, topk, tau, gate, st);
   }
-  if (d == 64) return fwd_go<ElemBF16, 64>(q, k, v, idx, cnt, lg, o, lse, B, Hq, Hkv, n, topk, tau, st);
-  return fwd_go<ElemBF16, 128>(q, k, v, idx, cnt, lg, o, lse, B, Hq, Hkv, n, topk, tau, st);
+  if (d == 64) return fwd_go<ElemBF16, 64>(q, k, v, idx, cnt, lg, o, lse, B, Hq, Hkv, n, topk, tau, gate, st);
+  return fwd_go<ElemBF16, 128>(q, k, v, idx, cnt, lg, o, lse, B, Hq, Hkv, n, topk, tau, gate, st);
 }
 
 template <class E, int D>
@@ -292,7 +309,7 @@ static hipError_t bwd_go(const void* q, const void* k, const void* v, const void
                          const float* lg, const float* s, const float* s_lse, void* dq, void* dk,
                          void* dv, float* ds, float* Dws, const int32_t* rev_off,
                          const int32_t* rev_list, int B, int Hq, int Hkv, int n, int topk,
-                         float tau, hipStream_t st) {
+                         float tau, int gate, hipStream_t st) {
   using T = typename E::T;
   const int nb = n / SAS_BLK;
   const size_t rows = size_t(B) * Hq * n;
@@ -307,7 +324,7 @@ static hipError_t bwd_go(const void* q, const void* k, const void* v, const void
     ProfScope ps("sas_bwd_dq_simt_kernel", st);
     hipLaunchKernelGGL((bwd_dq_simt_kernel<E, D>), dim3(B * Hkv * nb), dim3((Hq / Hkv) * SAS_BLK),
                        0, st, (const T*)q, (const T*)k, (const T*)v, (const T*)dO, lse, Dws, idx,
-                       cnt, lg, s, s_lse, (T*)dq, ds, Hq, Hkv, n, topk, tau);
+                       cnt, lg, s, s_lse, (T*)dq, ds, Hq, Hkv, n, topk, tau, gate);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -315,7 +332,7 @@ static hipError_t bwd_go(const void* q, const void* k, const void* v, const void
     ProfScope ps("sas_bwd_dkdv_simt_kernel", st);
     hipLaunchKernelGGL((bwd_dkdv_simt_kernel<E, D>), dim3(B * Hkv * nb), dim3(SAS_BLK), 0, st,
                        (const T*)q, (const T*)k, (const T*)v, (const T*)dO, lse, Dws, lg, rev_off,
-                       rev_list, (T*)dk, (T*)dv, Hq, Hkv, n, topk, tau);
+                       rev_list, (T*)dk, (T*)dv, Hq, Hkv, n, topk, tau, gate);
   }
   return hipGetLastError();
 }
@@ -325,9 +342,9 @@ hipError_t launch_bwd_simt(int dtype, const void* q, const void* k, const void* 
                            const int32_t* cnt, const float* lg, const float* s,
                            const float* s_lse, void* dq, void* dk, void* dv, float* ds, float* Dws,
                            const int32_t* rev_off, const int32_t* rev_list, int B, int Hq,
-                           int Hkv, int n, int d, int topk, float tau, hipStream_t st) {
+                           int Hkv, int n, int d, int topk, float tau, int gate, hipStream_t st) {
 #define SAS_BWD_ARGS q, k, v, o, dO, lse, idx, cnt, lg, s, s_lse, dq, dk, dv, ds, Dws, rev_off, \
-                     rev_list, B, Hq, Hkv, n, topk, tau, st
+                     rev_list, B, Hq, Hkv, n, topk, tau, gate, st
   if (dtype == 0) {
     if (d == 64) return bwd_go<ElemF32, 64>(SAS_BWD_ARGS);
     return bwd_go<ElemF32, 128>(SAS_BWD_ARGS);

@@ -62,17 +62,45 @@ typedef int32_t sas_status;
 #define SAS_BF16 1
 
 #define SAS_BLOCK 64           /* tokens per block [Review §2.1] */
+
+/* Gate kinds (the `gate` field of every shape).  The selection is the same
+ * Top-K for all of them; they differ in the gate a kept block m of row i gets
+ * and in where it acts.  LSE runs over the row's candidates.
+ *   SAS_GATE_SOFTMAX   the method [Review §2.4]: log g_m = s_m - LSE(s), added
+ *                      to the logits of block m inside the softmax.
+ *   SAS_GATE_SIGMOID   normalisation ablation [Review §2.4, ablation table of
+ *                      §4]: log g_m = log sigmoid(s_m), inside the softmax;
+ *                      ds[i,m] = [m kept] dlg[i,m] sigmoid(-s[i,m]).
+ *   SAS_GATE_HARD      hard-gate ablation [Review §2.5]: g_m = 1 on kept blocks
+ *                      (log_gate = 0), trained with a straight-through
+ *                      estimator: ds is that of SAS_GATE_SOFTMAX for the bias
+ *                      gradients dlg of this forward.
+ *   SAS_GATE_EXTERNAL  placement ablation [Review §2.3]: g_m = exp(s_m - LSE(s))
+ *                      scales the values of block m after an unbiased softmax
+ *                      over the kept and current keys:
+ *                        o = sum_j P_j g_block(j) v_j,  P = softmax(tau q K_S^T)
+ *                      (g = 1 for the current block; lse is that softmax's);
+ *                      dlg[i,m] = sum over block m's keys of P * dP with
+ *                      dP = g (dO . v), and ds as for SAS_GATE_SOFTMAX.  Gates
+ *                      below e^-60 act as e^-60 (a relative change in o below
+ *                      1e-26). */
+#define SAS_GATE_SOFTMAX 0
+#define SAS_GATE_SIGMOID 1
+#define SAS_GATE_HARD 2
+#define SAS_GATE_EXTERNAL 3
 #define SAS_MAX_BLOCKS 2048    /* most blocks per sequence (n or cap <= 131072) */
 
 /* Training-layer shape.  q [B,Hq,n,d]; k, v [B,Hkv,n,d].
  * Requires B,Hq,Hkv >= 1, Hq % Hkv == 0, 1 <= Hq/Hkv <= 16, n % 64 == 0,
  * 64 <= n <= 64*SAS_MAX_BLOCKS, d in {64,128}, 0 <= topk <= SAS_MAX_BLOCKS (a row
  * with fewer history blocks keeps all of them), scale >= 0 and finite, dtype
- * SAS_F32 or SAS_BF16. */
+ * SAS_F32 or SAS_BF16, gate one of the SAS_GATE_* kinds.  sas_select, sas_fwd,
+ * sas_bwd and the decode calls must see the same gate. */
 typedef struct {
   int32_t B, Hq, Hkv, n, d, topk;
   float scale;
   int32_t dtype;
+  int32_t gate;
 } sas_shape;
 
 /* Decode shape.  q [B,Hq,d]; k_cache, v_cache [B,Hkv,cap,d]; same limits with
@@ -81,6 +109,7 @@ typedef struct {
   int32_t B, Hq, Hkv, cap, d, topk;
   float scale;
   int32_t dtype;
+  int32_t gate;
 } sas_decode_shape;
 
 #define SAS_MAX_DECODE_BLOCKS 8192  /* most blocks per sequence in paged decode (context <= 524288) */
@@ -95,6 +124,7 @@ typedef struct {
   int32_t B, Hq, Hkv, max_blocks, num_pages, d, topk;
   float scale;
   int32_t dtype;
+  int32_t gate;
 } sas_decode_paged_shape;
 
 /* Version of this ABI (bumped on any incompatible change). */
@@ -124,6 +154,7 @@ sas_status sas_pool_scores(const sas_shape* shape, const void* q, const void* k,
  *                     lower index (-0.0 == +0.0), listed in ascending order, then
  *                     padded with -1 up to topk
  *   log_gate[b,kv,i,j] = s[b,kv,i,idx[j]] - s_lse (j < cnt), -inf in the padding
+ *                     (for the gate kinds: log sigmoid(s), 0 for SAS_GATE_HARD)
  * s: device float32 [B,Hkv,n/64,n/64]; entries m >= i are never read.
  * idx: int32 [B,Hkv,n/64,topk]; cnt: int32 [B,Hkv,n/64];
  * log_gate: float32 [B,Hkv,n/64,topk]; s_lse: float32 [B,Hkv,n/64] (all written).

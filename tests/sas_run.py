@@ -28,7 +28,8 @@ def tdtype(w_dtype: str):
     return torch.float32 if w_dtype == "f32" else torch.bfloat16
 
 
-def run_layer(api, q, k, v, do, s, topk, dtype, scale=0.0, pool=False, bwd=True, doc_first=None):
+def run_layer(api, q, k, v, do, s, topk, dtype, scale=0.0, pool=False, bwd=True, doc_first=None,
+              gate="softmax"):
     """Run (pool) -> (mask documents) -> select -> fwd (-> bwd) on device
     tensors; returns a dict of device tensors.  q,k,v,do are device tensors; s
     is a device float32 tensor (masked in place when doc_first, a device int32
@@ -36,7 +37,7 @@ def run_layer(api, q, k, v, do, s, topk, dtype, scale=0.0, pool=False, bwd=True,
     B, Hq, n, d = q.shape
     Hkv = k.shape[1]
     nb = n // BLOCK
-    sh = api.make_shape(B, Hq, Hkv, n, d, topk, dtype, scale)
+    sh = api.make_shape(B, Hq, Hkv, n, d, topk, dtype, scale, gate)
     out = {}
     if pool:
         s = torch.empty((B, Hkv, nb, nb), dtype=torch.float32, device="cuda")

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_status_strings():
     L = _lib.lib()
-    assert L.sas_abi_version() == 1
+    assert L.sas_abi_version() == _lib.ABI_VERSION == 2
     for st in range(6):
         assert _lib.status_string(st).startswith("SAS")
     assert "unknown" in _lib.status_string(99)
@@ -63,7 +63,7 @@ def _sel(sh, s=FAKE, idx=FAKE, cnt=FAKE, lg=FAKE, lse=FAKE):
     (1, 4, 2, 0, 128, 2, 0.0, 1, 1),        # empty sequence
 ])
 def test_shape_validation(B, Hq, Hkv, n, d, K, scale, dt, expect):
-    sh = _lib.SasShape(B, Hq, Hkv, n, d, K, scale, dt)
+    sh = _lib.SasShape(B, Hq, Hkv, n, d, K, scale, dt, 0)
     assert _sel(sh) == expect
     L = _lib.lib()
     assert L.sas_fwd(ctypes.byref(sh), *([FAKE] * 8), None) == expect
@@ -119,7 +119,7 @@ def test_workspace_checks():
 ])
 def test_paged_decode_shape_validation(B, Hq, Hkv, maxb, pages, d, K, dt, expect):
     L = _lib.lib()
-    sh = _lib.SasDecodePagedShape(B, Hq, Hkv, maxb, pages, d, K, 0.0, dt)
+    sh = _lib.SasDecodePagedShape(B, Hq, Hkv, maxb, pages, d, K, 0.0, dt, 0)
     need = L.sas_decode_paged_workspace_bytes(ctypes.byref(sh))
     assert (need > 0) == (expect == 0)
     if expect:   # every pointer non-NULL and the workspace large: only the shape decides
@@ -155,3 +155,21 @@ def test_doc_first_from_cu_seqlens():
     for bad in ([[64, 128]], [[0, 100]], [[0, 256, 128]], [[0, 576]]):
         with pytest.raises(ValueError):
             api.doc_first_from_cu_seqlens(bad, 512)
+
+
+@pytest.mark.parametrize("gate,expect", [(0, 0), (1, 0), (2, 0), (3, 0), (4, 1), (-1, 1)])
+def test_gate_kind_validation(gate, expect):
+    """Every entry point accepts the four gate kinds and rejects others."""
+    L = _lib.lib()
+    sh = _lib.SasShape(1, 4, 2, 512, 128, 2, 0.0, 1, gate)
+    assert (L.sas_bwd_workspace_bytes(ctypes.byref(sh)) > 0) == (expect == 0)
+    if expect:
+        assert _sel(sh) == expect
+        assert L.sas_fwd(ctypes.byref(sh), *([FAKE] * 8), None) == expect
+        dsh = _lib.SasDecodeShape(4, 8, 2, 1024, 128, 2, 0.0, 1, gate)
+        assert L.sas_decode_workspace_bytes(ctypes.byref(dsh)) == 0
+        psh = _lib.SasDecodePagedShape(4, 8, 2, 64, 100, 128, 2, 0.0, 1, gate)
+        assert L.sas_decode_paged_workspace_bytes(ctypes.byref(psh)) == 0
+    assert api.make_shape(1, 4, 2, 512, 128, 2, gate="external").gate == 3
+    with pytest.raises(KeyError):
+        api.make_shape(1, 4, 2, 512, 128, 2, gate="tanh")

@@ -39,8 +39,8 @@ def api():
     return m
 
 
-def _check_select(res, s_host, topk):
-    idx, cnt, lg, lse = oracle.select(s_host, topk)
+def _check_select(res, s_host, topk, gate="softmax"):
+    idx, cnt, lg, lse = oracle.select(s_host, topk, gate)
     assert np.array_equal(host(res["cnt"]), cnt)
     assert np.array_equal(host(res["idx"]), idx)
     g_lg, g_lse = host(res["log_gate"]), host(res["s_lse"])
@@ -190,6 +190,69 @@ def test_layer_parity_full(api, name):
         assert np.all(ds_g[np.isneginf(s)] == 0.0)
 
 
+# ---------------------------------------------------------------- gate variants
+GATE_CASES = {
+    "bf16_gqa4_d128": si.custom_workload(120, 2, 8, 2, 1024, 128, 4, "bf16"),
+    "bf16_gqa5_d64_kall": si.custom_workload(121, 1, 5, 1, 512, 64, 8, "bf16", s_std=2.0),
+    "fp32_gqa2_d64": si.custom_workload(122, 1, 4, 2, 384, 64, 2, "f32"),
+}
+
+
+@pytest.mark.parametrize("gate", ["sigmoid", "hard", "external"])
+@pytest.mark.parametrize("name", list(GATE_CASES))
+def test_gate_variant_layer_parity(api, gate, name):
+    """The ablation gates through the whole layer against the oracle."""
+    w = GATE_CASES[name]
+    q, k, v, do = si.make_qkv(w)
+    s = si.make_scores(w)
+    dt = tdtype(w.dtype)
+    res = run_layer(api, dev(q, dt), dev(k, dt), dev(v, dt), dev(do, dt),
+                    torch.from_numpy(s).cuda(), w.topk, dt, gate=gate)
+    _check_select(res, s, w.topk, gate)
+    ref = oracle.sas_forward_backward(q, k, v, do, s, w.topk, gate=gate)
+    tol = TOL[w.dtype]
+    assert_o(host(res["o"]), ref["o"], w.dtype)
+    assert np.max(np.abs(host(res["lse"]) - ref["lse"])) <= tol["lse"]
+    for nm in ("dq", "dk", "dv", "ds"):
+        e = rel_l2(host(res[nm]), ref[nm])
+        assert e <= tol["grad"], (nm, e)
+
+
+@pytest.mark.parametrize("gate", ["sigmoid", "external"])
+def test_gate_variant_full_size_sampled(api, gate):
+    """The 8K Qwen3-4B layer with an ablation gate, sampled blocks."""
+    w = si.WORKLOADS[2]
+    q, k, v, do = si.make_qkv(w)
+    s = si.make_scores(w)
+    dt = tdtype(w.dtype)
+    res = run_layer(api, dev(q, dt), dev(k, dt), dev(v, dt), dev(do, dt),
+                    torch.from_numpy(s).cuda(), w.topk, dt, gate=gate)
+    idx, cnt, lg, s_lse = _check_select(res, s, w.topk, gate)
+    G = w.Hq // w.Hkv
+    tol = TOL[w.dtype]
+    o_g, dq_g, ds_g = host(res["o"]), host(res["dq"]), host(res["ds"])
+    for (b, kv, i) in _sample_blocks(w, np.random.default_rng(31)):
+        r = slice(i * BLOCK, (i + 1) * BLOCK)
+        hs = slice(kv * G, (kv + 1) * G)
+        ob, _ = oracle.fwd_gather_block(q, k, v, idx, cnt, lg, b, kv, i, gate=gate)
+        assert_o(o_g[b, hs, r], ob, w.dtype, ("o", b, kv, i))
+        dqb, _, _, _, dlg = oracle.bwd_gather_block(q, k, v, do, idx, cnt, lg, b, kv, i, gate=gate)
+        assert rel_l2(dq_g[b, hs, r], dqb) <= tol["grad"], ("dq", b, kv, i)
+        if i > 0:
+            dlg_full = np.zeros((1, 1, w.nqb, w.topk))
+            dlg_full[0, 0, i] = dlg
+            dsr = oracle.gate_jacobian(s[b:b + 1, kv:kv + 1], s_lse[b:b + 1, kv:kv + 1],
+                                       idx[b:b + 1, kv:kv + 1], cnt[b:b + 1, kv:kv + 1],
+                                       dlg_full, gate)[0, 0, i]
+            assert rel_l2(ds_g[b, kv, i], dsr) <= tol["grad"], ("ds", b, kv, i)
+    dk_g, dv_g = host(res["dk"]), host(res["dv"])
+    for (b, kv, m) in [(0, 0, 0), (0, w.Hkv - 1, w.nqb // 2), (0, 1, w.nqb - 1)]:
+        dkm, dvm = oracle.bwd_kv_block(q, k, v, do, idx, cnt, lg, b, kv, m, gate=gate)
+        r = slice(m * BLOCK, (m + 1) * BLOCK)
+        assert rel_l2(dk_g[b, kv, r], dkm) <= tol["grad"], ("dk", b, kv, m)
+        assert rel_l2(dv_g[b, kv, r], dvm) <= tol["grad"], ("dv", b, kv, m)
+
+
 # ---------------------------------------------------------------- full-size sampled checks
 def _sample_blocks(w, rng, n_blocks=5):
     picks = {(0, 0, 0), (0, w.Hkv - 1, w.nqb - 1), (0, w.Hkv // 2, min(w.topk, w.nqb - 1))}
@@ -250,9 +313,9 @@ def test_layer_parity_full_size_sampled(api, cfg):
 
 
 # ---------------------------------------------------------------- decode
-def _decode_run(api, w, q, kc, vc, lens, s):
+def _decode_run(api, w, q, kc, vc, lens, s, gate="softmax"):
     dt = tdtype(w.dtype)
-    sh = api.make_decode_shape(w.B, w.Hq, w.Hkv, w.cap, w.d, w.topk, dt)
+    sh = api.make_decode_shape(w.B, w.Hq, w.Hkv, w.cap, w.d, w.topk, dt, gate=gate)
     o = torch.empty_like(q)
     idx = torch.empty((w.B, w.Hkv, w.topk), dtype=torch.int32, device="cuda")
     ws = api.alloc_workspace(api.sas_decode_workspace_bytes(sh))
@@ -326,12 +389,12 @@ class _PagedRows:
         return _Rows()
 
 
-def _decode_paged_run(api, dtype, q, kp, vp, table, lens, s, K):
+def _decode_paged_run(api, dtype, q, kp, vp, table, lens, s, K, gate="softmax"):
     B, Hq, d = q.shape
     num_pages, Hkv = kp.shape[:2]
     max_blocks = table.shape[1]
     dt = tdtype(dtype)
-    shp = api.make_decode_paged_shape(B, Hq, Hkv, max_blocks, num_pages, d, K, dt)
+    shp = api.make_decode_paged_shape(B, Hq, Hkv, max_blocks, num_pages, d, K, dt, gate=gate)
     qd = dev(q, dt)
     o = torch.empty_like(qd)
     idx = torch.full((B, Hkv, K), -7, dtype=torch.int32, device="cuda")
@@ -421,6 +484,35 @@ def test_decode_paged_masked_long_context(api):
     ref_o, ref_idx = oracle.decode(q, _PagedRows(kp, table), _PagedRows(vp, table), lens, s, K)
     assert np.array_equal(idx, ref_idx)
     assert np.all(idx[3] == -1)
+    assert_o(o, ref_o, "bf16")
+
+
+@pytest.mark.parametrize("gate", ["sigmoid", "hard", "external"])
+@pytest.mark.parametrize("dtype,nsplit_b", [("bf16", 3), ("f32", 3), ("bf16", 256)])
+def test_decode_gate_variants(api, gate, dtype, nsplit_b):
+    """Decode with the ablation gates; 3 sequences (6 rows) split their tiles
+    over several workgroups, 256 sequences (512 rows) use one per row."""
+    w = si.DecodeWorkload(280, nsplit_b, 8, 2, 512, 128, 5, dtype, hist_blocks=7)
+    q, kc, vc, lens, s = si.make_decode_small(w)
+    dt = tdtype(dtype)
+    o, idx = _decode_run(api, w, dev(q, dt), dev(kc, dt), dev(vc, dt), lens, s, gate)
+    ref_o, ref_idx = oracle.decode(q, kc, vc, lens, s, w.topk, gate=gate)
+    assert np.array_equal(host(idx), ref_idx)
+    assert_o(host(o), ref_o, dtype)
+
+
+@pytest.mark.parametrize("gate", ["sigmoid", "external"])
+def test_decode_paged_gate_variants_long_context(api, gate):
+    B, Hq, Hkv, d, K = 2, 4, 2, 64, 32
+    max_blocks, num_pages = 8192, 4096
+    lens = [BLOCK * max_blocks, 200000]
+    q, kp, vp, table, lens, s = si.make_decode_paged(490, B, Hq, Hkv, max_blocks, num_pages, d,
+                                                     "bf16", seq_lens=lens)
+    s = s * 3.0   # a wide spread of gates
+    o, idx = _decode_paged_run(api, "bf16", q, kp, vp, table, lens, s, K, gate)
+    ref_o, ref_idx = oracle.decode(q, _PagedRows(kp, table), _PagedRows(vp, table), lens, s, K,
+                                   gate=gate)
+    assert np.array_equal(idx, ref_idx)
     assert_o(o, ref_o, "bf16")
 
 
