@@ -136,6 +136,8 @@ KERNEL_SOURCES = {
     "sas_bwd_dq_kernel": ["mfma_bwd.hip", "mfma_common.h", "common.h", "launch.h"],
     "sas_fwd_mfma_kernel": ["mfma_fwd.hip", "mfma_common.h", "common.h", "launch.h"],
     "sas_decode_kernel": ["decode.hip", "decode_kernel.h", "select_row.h", "common.h", "launch.h"],
+    "sas_decode_paged_kernel": ["decode_paged.hip", "decode_kernel.h", "select_row.h", "common.h",
+                                "launch.h"],
     "sas_pool_means_kernel": ["pool.hip", "common.h", "launch.h"],
     "sas_select_kernel": ["select.hip", "select_row.h", "common.h", "launch.h"],
 }

@@ -312,6 +312,37 @@ def test_layer_parity_full_size_sampled(api, cfg):
         assert rel_l2(dv_g[b, kv, r], dvm) <= tol["grad"], ("dv", b, kv, m)
 
 
+def test_layer_parity_max_length(api):
+    """The longest sequence the ABI accepts (n = 131072, 2048 blocks): selection
+    on every row, sampled q-blocks and key blocks against the oracle."""
+    w = si.custom_workload(130, 1, 4, 1, 64 * 2048, 64, 16, "bf16")
+    q, k, v, do = si.make_qkv(w)
+    s = si.make_scores(w)
+    dt = tdtype(w.dtype)
+    res = run_layer(api, dev(q, dt), dev(k, dt), dev(v, dt), dev(do, dt),
+                    torch.from_numpy(s).cuda(), w.topk, dt)
+    idx, cnt, lg, s_lse = _check_select(res, s, w.topk)
+    tol = TOL[w.dtype]
+    o_g, dq_g, ds_g = host(res["o"]), host(res["dq"]), host(res["ds"])
+    for i in (0, 1, 777, 2047):
+        r = slice(i * BLOCK, (i + 1) * BLOCK)
+        ob, _ = oracle.fwd_gather_block(q, k, v, idx, cnt, lg, 0, 0, i)
+        assert_o(o_g[0, :, r], ob, w.dtype, ("o", i))
+        dqb, _, _, _, dlg = oracle.bwd_gather_block(q, k, v, do, idx, cnt, lg, 0, 0, i)
+        assert rel_l2(dq_g[0, :, r], dqb) <= tol["grad"], ("dq", i)
+        if i > 0:
+            dlg_full = np.zeros((1, 1, w.nqb, w.topk))
+            dlg_full[0, 0, i] = dlg
+            dsr = oracle.gate_jacobian(s, s_lse, idx, cnt, dlg_full)[0, 0, i]
+            assert rel_l2(ds_g[0, 0, i], dsr) <= tol["grad"], ("ds", i)
+    dk_g, dv_g = host(res["dk"]), host(res["dv"])
+    for m in (1500, 2047):
+        dkm, dvm = oracle.bwd_kv_block(q, k, v, do, idx, cnt, lg, 0, 0, m)
+        r = slice(m * BLOCK, (m + 1) * BLOCK)
+        assert rel_l2(dk_g[0, 0, r], dkm) <= tol["grad"], ("dk", m)
+        assert rel_l2(dv_g[0, 0, r], dvm) <= tol["grad"], ("dv", m)
+
+
 # ---------------------------------------------------------------- decode
 def _decode_run(api, w, q, kc, vc, lens, s, gate="softmax"):
     dt = tdtype(w.dtype)
@@ -337,6 +368,19 @@ def test_decode_parity_small(api, dtype, G, d, cap, K):
     ref_o, ref_idx = oracle.decode(q, kc, vc, lens, s, K)
     assert np.array_equal(host(idx), ref_idx)
     assert_o(host(o), ref_o, dtype)
+
+
+def test_decode_parity_max_cache(api):
+    """A contiguous cache of the longest size the ABI accepts (131072 tokens,
+    rows of up to 2047 history blocks selected by one wave)."""
+    w = si.DecodeWorkload(290, 3, 8, 2, 64 * 2048, 64, 24, "bf16", hist_blocks=2047)
+    q, kc, vc, lens, s = si.make_decode_small(w)
+    lens = np.array([64 * 2048, 64 * 1500 + 7, 1], dtype=np.int32)
+    dt = tdtype(w.dtype)
+    o, idx = _decode_run(api, w, dev(q, dt), dev(kc, dt), dev(vc, dt), lens, s)
+    ref_o, ref_idx = oracle.decode(q, kc, vc, lens, s, w.topk)
+    assert np.array_equal(host(idx), ref_idx)
+    assert_o(host(o), ref_o, "bf16")
 
 
 def test_decode_parity_full_size(api):
