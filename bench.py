@@ -39,6 +39,7 @@ def parse():
     p.add_argument("--workload", type=int, default=3, choices=[2, 3, 4])
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-full-range", action="store_true", help="skip the full-range (K = n/64) line")
+    p.add_argument("--no-gates", action="store_true", help="skip the ablation-gate lines")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     p.add_argument("--decode-steps", type=int, default=50)
     p.add_argument("--copy-calibration", action="store_true",
@@ -53,7 +54,7 @@ def pair_count(cnt_np, G):
     return G * (int(c.sum()) * 64 * 64 + c.size * (64 * 65 // 2))
 
 
-def run_training(args, api, si, torch, np, w=None, steps=None, warmup=None):
+def run_training(args, api, si, torch, np, w=None, steps=None, warmup=None, gate="softmax"):
     w = si.WORKLOADS[args.workload] if w is None else w
     steps = args.steps if steps is None else steps
     warmup = args.warmup if warmup is None else warmup
@@ -63,7 +64,7 @@ def run_training(args, api, si, torch, np, w=None, steps=None, warmup=None):
     qd, kd, vd, dod = dev(q), dev(k), dev(v), dev(do)
     host = dict(q=q, k=k, v=v, do=do)
     del q, k, v, do
-    sh = api.make_shape(w.B, w.Hq, w.Hkv, w.n, w.d, w.topk, dt)
+    sh = api.make_shape(w.B, w.Hq, w.Hkv, w.n, w.d, w.topk, dt, gate=gate)
     nb = w.nqb
     pool = w.s_kind == "pool"
     s = torch.empty((w.B, w.Hkv, nb, nb), dtype=torch.float32, device="cuda")
@@ -110,6 +111,24 @@ def run_training(args, api, si, torch, np, w=None, steps=None, warmup=None):
     per_kernel = {name: dict(avg_ms=tot / max(nl, 1), launches=nl) for name, (tot, nl) in kern.items()}
     return dict(w=w, ms_step=ms_step, wall=wall, pairs=pairs, flop_fwd=flop_fwd, flop_bwd=flop_bwd,
                 per_kernel=per_kernel, host=host, s=s, sel=sel, steps=steps)
+
+
+def run_gate_variants(args, api, si, torch, np):
+    """The same 32K step with each ablation gate (same selection, same
+    effective work): ms per step and per-kernel times."""
+    out = {}
+    for gate in ("sigmoid", "hard", "external"):
+        res = run_training(args, api, si, torch, np, steps=max(1, args.steps // 4), warmup=1,
+                           gate=gate)
+        total = res["flop_fwd"] + res["flop_bwd"]
+        out[gate] = {"ms_per_step": round(res["ms_step"], 3),
+                     "TFLOPs": round(total / (res["ms_step"] * 1e-3) / 1e12, 1),
+                     "per_kernel_ms": {k: round(v["avg_ms"], 3) for k, v in res["per_kernel"].items()
+                                       if k in ("sas_fwd_mfma_kernel", "sas_bwd_dq_kernel",
+                                                "sas_bwd_dkdv_kernel")}}
+        res.clear()
+        torch.cuda.empty_cache()
+    return out
 
 
 def run_full_range(args, api, si, torch, np):
@@ -384,6 +403,8 @@ def main():
     if not args.no_full_range:
         line["full_range"] = run_full_range(args, api, si, torch, np)
         torch.cuda.empty_cache()
+    if not args.no_gates:
+        line["gate_variants"] = run_gate_variants(args, api, si, torch, np)
     if not args.no_decode:
         torch.cuda.empty_cache()
         line["decode"] = run_decode(args, api, si, torch, np)

@@ -218,6 +218,26 @@ def test_gate_variant_layer_parity(api, gate, name):
         assert e <= tol["grad"], (nm, e)
 
 
+@pytest.mark.parametrize("gate", ["sigmoid", "hard", "external"])
+def test_gate_variant_packed_documents(api, gate):
+    """Ablation gates on a packed batch: rows near a document's start keep
+    fewer blocks (or none), and no gradient crosses documents."""
+    w = si.custom_workload(123, 2, 8, 2, 1536, 128, 4, "bf16", packed=True)
+    q, k, v, do = si.make_qkv(w)
+    sd, df, s = _scores(w)
+    dt = tdtype(w.dtype)
+    res = run_layer(api, dev(q, dt), dev(k, dt), dev(v, dt), dev(do, dt), sd, w.topk, dt,
+                    doc_first=df, gate=gate)
+    _check_select(res, s, w.topk, gate)
+    ref = oracle.sas_forward_backward(q, k, v, do, s, w.topk, gate=gate)
+    tol = TOL[w.dtype]
+    assert_o(host(res["o"]), ref["o"], w.dtype)
+    for nm in ("dq", "dk", "dv", "ds"):
+        e = rel_l2(host(res[nm]), ref[nm])
+        assert e <= tol["grad"], (nm, e)
+    assert np.all(host(res["ds"])[np.isneginf(s)] == 0.0)
+
+
 @pytest.mark.parametrize("gate", ["sigmoid", "external"])
 def test_gate_variant_full_size_sampled(api, gate):
     """The 8K Qwen3-4B layer with an ablation gate, sampled blocks."""
