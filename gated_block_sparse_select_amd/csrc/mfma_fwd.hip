@@ -37,7 +37,9 @@ __global__ void __launch_bounds__(128 * GC) fwd_mfma_kernel(
     const int32_t* __restrict__ cnt, const float* __restrict__ lg, uint16_t* __restrict__ o,
     float* __restrict__ lse, int Hq, int Hkv, int n, int topk, float tau2, int BH, int h_off,
     int hchunks) {
-  constexpr int NS = kFwdStages;
+  // A one-head workgroup has only two waves: with two stages (64 KB of LDS at
+  // d = 128 instead of 96 KB) two of them fit on a CU, so all four SIMDs work.
+  constexpr int NS = GC == 1 ? 2 : kFwdStages;
   constexpr int ROWB = D * 2;
   constexpr int TB = 64 * ROWB;           // bytes of one 64 x D tile
   constexpr int JT = TB / 1024;           // 1 KB DMA slices per tile
@@ -85,7 +87,9 @@ __global__ void __launch_bounds__(128 * GC) fwd_mfma_kernel(
     dma_slices<JW>(src, k_side ? stage_buf<TK, BUF, TB>() : stage_buf<TV, BUF, TB>(), slice0, pat);
   };
   issue.template operator()<0>(0);
-  if (1 < ntiles) issue.template operator()<1>(1);
+  if constexpr (NS > 2) {
+    if (1 < ntiles) issue.template operator()<1>(1);
+  }
 
   uint32_t ko[D / 16], vo[D / 32][2];
   {
