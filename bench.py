@@ -113,6 +113,35 @@ def run_training(args, api, si, torch, np, w=None, steps=None, warmup=None, gate
                 per_kernel=per_kernel, host=host, s=s, sel=sel, steps=steps)
 
 
+def hbm_kernels(res):
+    """HBM rate of the memory-bound kernels of the step: algorithmic bytes
+    (each input byte read once, each output byte written once) over the
+    kernel's average time.
+      pooling:   q and k read (bf16), the block means written and read back
+                 (float32), the score matrix written (float32);
+      selection: the scores of the history (m < i) read, idx and log_gate
+                 (K per row), cnt and s_lse written."""
+    w = res["w"]
+    pk = res["per_kernel"]
+    nb = w.nqb
+    rows = w.B * w.Hkv * nb
+    means = 2 * rows * w.d * 4
+    out = {}
+    if "sas_pool_means_kernel" in pk and "sas_pool_dot_kernel" in pk:
+        qk = (w.B * w.Hq + w.B * w.Hkv) * w.n * w.d * 2
+        byt = qk + means + means + rows * nb * 4
+        ms = pk["sas_pool_means_kernel"]["avg_ms"] + pk["sas_pool_dot_kernel"]["avg_ms"]
+        out["pool"] = dict(bytes=byt, ms=round(ms, 4), GBs=round(byt / (ms * 1e-3) / 1e9, 1),
+                           frac=round(byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+    if "sas_select_kernel" in pk:
+        hist = w.B * w.Hkv * (nb * (nb - 1) // 2) * 4
+        byt = hist + rows * w.topk * 8 + rows * 8
+        ms = pk["sas_select_kernel"]["avg_ms"]
+        out["select"] = dict(bytes=byt, ms=round(ms, 4), GBs=round(byt / (ms * 1e-3) / 1e9, 1),
+                             frac=round(byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+    return out
+
+
 def run_gate_variants(args, api, si, torch, np):
     """The same 32K step with each ablation gate (same selection, same
     effective work): ms per step and per-kernel times."""
@@ -395,6 +424,7 @@ def main():
         "roofline": roofline_for(res),
         "effective_flop": {"fwd": res["flop_fwd"], "bwd": res["flop_bwd"], "pairs": res["pairs"]},
         "per_kernel_ms": {k: round(v["avg_ms"], 4) for k, v in res["per_kernel"].items()},
+        "hbm_kernels": hbm_kernels(res),
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(res, np)
