@@ -51,7 +51,11 @@ def _gate(gate) -> int:
     """Gate kind: one of "softmax", "sigmoid", "hard", "external", or its
     SAS_GATE_* code (other integers are passed through for the library to
     reject)."""
-    return GATES[gate] if isinstance(gate, str) else int(gate)
+    if isinstance(gate, str):
+        if gate not in GATES:
+            raise ValueError(f"unknown gate {gate!r}; one of {sorted(GATES)}")
+        return GATES[gate]
+    return int(gate)
 
 
 def make_shape(B, Hq, Hkv, n, d, topk, dtype=torch.bfloat16, scale=0.0, gate="softmax") -> SasShape:

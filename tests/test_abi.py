@@ -171,5 +171,5 @@ def test_gate_kind_validation(gate, expect):
         psh = _lib.SasDecodePagedShape(4, 8, 2, 64, 100, 128, 2, 0.0, 1, gate)
         assert L.sas_decode_paged_workspace_bytes(ctypes.byref(psh)) == 0
     assert api.make_shape(1, 4, 2, 512, 128, 2, gate="external").gate == 3
-    with pytest.raises(KeyError):
+    with pytest.raises(ValueError):
         api.make_shape(1, 4, 2, 512, 128, 2, gate="tanh")
