@@ -8,7 +8,9 @@
 //               block m of dZ  (the block gate gradient of the SAS review
 //               page, paper.oopus.info, §2.6),
 //   ds[i, m] = [m kept] dlg[i, m] - pi_i[m] sum_{kept m'} dlg[i, m'],
-//               pi_i = softmax(s[i, 0..i-1])  (chain rule through §2.4).
+//               pi_i = softmax of s[i, :] over the row's candidates (m < i,
+//               finite score)  (chain rule through §2.4); with the sigmoid
+//               gate, ds[i, m] = [m kept] dlg[i, m] sigmoid(-s[i, m]).
 //
 // Three kernels:
 //  * dq kernel, q-block outer (same workgroup shape and tile pipeline as the
