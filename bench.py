@@ -40,6 +40,7 @@ def parse():
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-full-range", action="store_true", help="skip the full-range (K = n/64) line")
     p.add_argument("--no-gates", action="store_true", help="skip the ablation-gate lines")
+    p.add_argument("--no-packed", action="store_true", help="skip the packed-documents line")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     p.add_argument("--decode-steps", type=int, default=50)
     p.add_argument("--copy-calibration", action="store_true",
@@ -76,10 +77,14 @@ def run_training(args, api, si, torch, np, w=None, steps=None, warmup=None, gate
     dq, dk, dv, ds = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd), torch.empty_like(s)
     ws_pool = api.alloc_workspace(api.sas_pool_workspace_bytes(sh))
     ws_bwd = api.alloc_workspace(api.sas_bwd_workspace_bytes(sh))
+    df = si.make_doc_first(w)
+    doc_first = torch.from_numpy(df).cuda() if df is not None else None
 
     def step():
         if pool:
             api.sas_pool_scores(sh, qd, kd, s, ws_pool)
+        if doc_first is not None:   # packed documents: mask the other documents' blocks
+            api.sas_mask_documents(sh, doc_first, s)
         api.sas_select(sh, s, sel["idx"], sel["cnt"], sel["log_gate"], sel["s_lse"])
         api.sas_fwd(sh, qd, kd, vd, sel["idx"], sel["cnt"], sel["log_gate"], o, lse)
         api.sas_bwd(sh, qd, kd, vd, o, dod, lse, sel["idx"], sel["cnt"], sel["log_gate"], s,
@@ -157,6 +162,23 @@ def run_gate_variants(args, api, si, torch, np):
                                                 "sas_bwd_dkdv_kernel")}}
         res.clear()
         torch.cuda.empty_cache()
+    return out
+
+
+def run_packed(args, api, si, torch, np):
+    """The 32K layer holding packed documents of mixed lengths (workload 7):
+    document mask + select + fwd + bwd.  Rows near a document's start keep
+    fewer blocks, and the effective work counts only the pairs kept."""
+    w = si.WORKLOADS[7]
+    res = run_training(args, api, si, torch, np, w=w, steps=max(1, args.steps // 4), warmup=1)
+    total = res["flop_fwd"] + res["flop_bwd"]
+    tf = total / (res["ms_step"] * 1e-3) / 1e12
+    docs = [len(si.packed_doc_blocks(w.cfg, b, w.nqb)) for b in range(w.B)]
+    out = {"workload": w.name, "documents": docs, "steps": res["steps"],
+           "ms_per_step": round(res["ms_step"], 3), "TFLOPs": round(tf, 1),
+           "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4), "pairs": res["pairs"],
+           "per_kernel_ms": {k: round(v["avg_ms"], 3) for k, v in res["per_kernel"].items()}}
+    res.clear()
     return out
 
 
@@ -435,6 +457,9 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_gates:
         line["gate_variants"] = run_gate_variants(args, api, si, torch, np)
+    if not args.no_packed:
+        line["packed"] = run_packed(args, api, si, torch, np)
+        torch.cuda.empty_cache()
     if not args.no_decode:
         torch.cuda.empty_cache()
         line["decode"] = run_decode(args, api, si, torch, np)
