@@ -273,6 +273,39 @@ def test_gate_variant_full_size_sampled(api, gate):
         assert rel_l2(dv_g[b, kv, r], dvm) <= tol["grad"], ("dv", b, kv, m)
 
 
+# ---------------------------------------------------------------- head-chunk mixes
+# Groups of G heads run as workgroups of 4, 2 and 1 heads: G = 2, 3, 6, 7 use
+# the two-head and one-head workgroups in every combination; K beyond the
+# history, the longest history a row can have, and each gate kind appear.
+CHUNK_CASES = [
+    # seed, B, Hq, Hkv, n, d, K, gate
+    (160, 1, 4, 2, 640, 128, 3, "softmax"),     # G = 2: one two-head chunk
+    (161, 2, 3, 1, 512, 64, 5, "external"),     # G = 3: 2 + 1
+    (162, 1, 12, 2, 448, 128, 2, "sigmoid"),    # G = 6: 4 + 2
+    (163, 1, 7, 1, 576, 128, 20, "hard"),       # G = 7: 4 + 2 + 1, K > every history
+    (164, 1, 14, 2, 320, 64, 1, "softmax"),     # G = 7 with d = 64
+]
+
+
+@pytest.mark.parametrize("case", CHUNK_CASES, ids=lambda c: f"G{c[2] // c[3]}_d{c[5]}_K{c[6]}_{c[7]}")
+def test_head_chunk_mixes(api, case):
+    seed, B, Hq, Hkv, n, d, K, gate = case
+    w = si.custom_workload(seed, B, Hq, Hkv, n, d, K, "bf16")
+    q, k, v, do = si.make_qkv(w)
+    s = si.make_scores(w)
+    dt = tdtype(w.dtype)
+    res = run_layer(api, dev(q, dt), dev(k, dt), dev(v, dt), dev(do, dt),
+                    torch.from_numpy(s).cuda(), w.topk, dt, gate=gate)
+    _check_select(res, s, w.topk, gate)
+    ref = oracle.sas_forward_backward(q, k, v, do, s, w.topk, gate=gate)
+    tol = TOL[w.dtype]
+    assert_o(host(res["o"]), ref["o"], w.dtype)
+    assert np.max(np.abs(host(res["lse"]) - ref["lse"])) <= tol["lse"]
+    for nm in ("dq", "dk", "dv", "ds"):
+        e = rel_l2(host(res[nm]), ref[nm])
+        assert e <= tol["grad"], (nm, e)
+
+
 # ---------------------------------------------------------------- full-size sampled checks
 def _sample_blocks(w, rng, n_blocks=5):
     picks = {(0, 0, 0), (0, w.Hkv - 1, w.nqb - 1), (0, w.Hkv // 2, min(w.topk, w.nqb - 1))}
