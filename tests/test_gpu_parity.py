@@ -411,7 +411,7 @@ def _decode_run(api, w, q, kc, vc, lens, s, gate="softmax"):
 
 @pytest.mark.parametrize("dtype,G,d,cap,K", [("bf16", 4, 128, 1024, 5), ("bf16", 5, 64, 512, 3),
                                              ("f32", 2, 64, 768, 2), ("bf16", 1, 128, 256, 0),
-                                             ("bf16", 12, 128, 512, 4)])
+                                             ("bf16", 12, 128, 512, 4), ("f32", 4, 128, 640, 3)])
 def test_decode_parity_small(api, dtype, G, d, cap, K):
     w = si.DecodeWorkload(200 + G, 5, 2 * G, 2, cap, d, K, dtype, hist_blocks=cap // BLOCK - 1)
     q, kc, vc, lens, s = si.make_decode_small(w)
@@ -507,7 +507,8 @@ def _decode_paged_run(api, dtype, q, kp, vp, table, lens, s, K, gate="softmax"):
     ("bf16", 4, 128, 40, 400, 5),    # a page of its own for every block
     ("bf16", 2, 64, 24, 30, 3),      # blocks share pages
     ("f32", 2, 64, 16, 64, 2),
-    ("bf16", 5, 128, 20, 100, 0)])
+    ("bf16", 5, 128, 20, 100, 0),
+    ("bf16", 4, 64, 1500, 2000, 16)])   # rows of 513..2048 blocks: one wave, 32 candidates per lane
 def test_decode_paged_parity_small(api, dtype, G, d, max_blocks, num_pages, K):
     B, Hkv = 4, 2
     q, kp, vp, table, lens, s = si.make_decode_paged(400 + max_blocks, B, G * Hkv, Hkv, max_blocks,
