@@ -77,6 +77,23 @@ def test_select_bitexact(api, case):
     _check_select(sel, s, K)
 
 
+@pytest.mark.parametrize("nb,K", [(100, 3), (1000, 40), (1999, 7)])
+def test_select_row_lengths(api, nb, K):
+    """Rows of every register layout of the selection (2, 16 and 32
+    candidates per lane), with ties, -0.0 and -inf scores mixed in."""
+    g = np.random.default_rng(nb)
+    B, Hkv = 1, 2
+    s = np.round(g.standard_normal((B, Hkv, nb, nb)) * 3).astype(np.float32)
+    s[s == 0] = np.float32(-0.0)
+    s[g.random(s.shape) < 0.05] = -np.inf
+    sh = api.make_shape(B, 2 * Hkv, Hkv, nb * BLOCK, 64, K, torch.bfloat16)
+    sel = api.alloc_select(sh)
+    api.sas_select(sh, torch.from_numpy(s).cuda(), sel["idx"], sel["cnt"], sel["log_gate"],
+                   sel["s_lse"])
+    torch.cuda.synchronize()
+    _check_select(sel, s, K)
+
+
 @pytest.mark.parametrize("cfg", [1, 2, 4])
 def test_select_full_size(api, cfg):
     w = si.WORKLOADS[cfg]
