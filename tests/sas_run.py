@@ -5,6 +5,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
+from parity_bars import rel_l2  # noqa: F401  (re-exported for the tests)
+
 BLOCK = 64
 
 
@@ -15,13 +17,6 @@ def dev(x: np.ndarray, dtype) -> torch.Tensor:
 
 def host(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy() if t.dtype != torch.int32 else t.cpu().numpy()
-
-
-def rel_l2(x, ref) -> float:
-    x = np.asarray(x, dtype=np.float64)
-    ref = np.asarray(ref, dtype=np.float64)
-    den = np.linalg.norm(ref)
-    return float(np.linalg.norm(x - ref) / (den if den > 0 else 1.0))
 
 
 def tdtype(w_dtype: str):

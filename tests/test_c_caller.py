@@ -13,6 +13,7 @@ sys.path.insert(0, os.path.join(HERE, "c_caller"))
 import build as c_build  # noqa: E402
 
 import oracle  # noqa: E402
+from parity_bars import assert_o, assert_rel  # noqa: E402
 import sas_inputs as si  # noqa: E402
 
 
@@ -59,12 +60,9 @@ def test_c_caller_layer_parity(tmp_path, gate):
     cnt = np.fromfile(tmp_path / "cnt.bin", dtype=np.int32).reshape(w.B, w.Hkv, nb)
     assert np.array_equal(idx, ref["idx"]) and np.array_equal(cnt, ref["cnt"])
     o = _from_bf16(tmp_path / "o.bin", q.shape)
-    err = np.abs(o - ref["o"])
-    assert np.all(err <= 1e-2 + 2.0 ** -8 * np.abs(ref["o"]))
+    assert_o(o, ref["o"], "bf16")
     for name, shape in (("dq", q.shape), ("dk", k.shape), ("dv", v.shape)):
         x = _from_bf16(tmp_path / f"{name}.bin", shape)
-        e = np.linalg.norm(x - ref[name]) / np.linalg.norm(ref[name])
-        assert e <= 2e-2, (name, e)
+        assert_rel(x, ref[name], 2e-2, name)
     ds = np.fromfile(tmp_path / "ds.bin", dtype=np.float32).reshape(s.shape)
-    e = np.linalg.norm(ds - ref["ds"]) / np.linalg.norm(ref["ds"])
-    assert e <= 2e-2, ("ds", e)
+    assert_rel(ds, ref["ds"], 2e-2, "ds")
