@@ -17,12 +17,14 @@ SAS_GATE_SOFTMAX, SAS_GATE_SIGMOID, SAS_GATE_HARD, SAS_GATE_EXTERNAL = range(4)
 GATES = {"softmax": SAS_GATE_SOFTMAX, "sigmoid": SAS_GATE_SIGMOID, "hard": SAS_GATE_HARD,
          "external": SAS_GATE_EXTERNAL}
 ABI_VERSION = 2
+NOALLOC_SCRATCH_BYTES = 16 << 20   # SAS_NOALLOC_SCRATCH_BYTES
 BLOCK = 64
 
 EXPORTED = [
     "sas_abi_version", "sas_status_string", "sas_pool_workspace_bytes", "sas_pool_scores",
     "sas_select", "sas_mask_documents", "sas_fwd", "sas_bwd_workspace_bytes", "sas_bwd",
-    "sas_decode_workspace_bytes", "sas_decode", "sas_decode_paged_workspace_bytes",
+    "sas_decode_workspace_bytes", "sas_decode", "sas_decode_noalloc",
+    "sas_decode_paged_workspace_bytes",
     "sas_decode_paged", "sas_prof_enable", "sas_prof_collect",
     "sas_last_hip_error",
 ]
@@ -94,6 +96,8 @@ def lib() -> ctypes.CDLL:
         L.sas_decode_workspace_bytes.argtypes = [dp]
         L.sas_decode.restype = i32
         L.sas_decode.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, st]
+        L.sas_decode_noalloc.restype = i32
+        L.sas_decode_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, st]
         pp = ctypes.POINTER(SasDecodePagedShape)
         L.sas_decode_paged_workspace_bytes.restype = sz
         L.sas_decode_paged_workspace_bytes.argtypes = [pp]

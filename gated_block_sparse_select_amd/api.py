@@ -12,7 +12,7 @@ import ctypes
 
 import torch
 
-from ._lib import (BLOCK, GATES, SAS_BF16, SAS_F32, SasDecodePagedShape, SasDecodeShape, SasError, SasShape, lib,
+from ._lib import (BLOCK, GATES, NOALLOC_SCRATCH_BYTES, SAS_BF16, SAS_F32, SasDecodePagedShape, SasDecodeShape, SasError, SasShape, lib,
                    status_string)
 
 _DT = {torch.float32: SAS_F32, torch.bfloat16: SAS_BF16}
@@ -206,6 +206,23 @@ def sas_decode(shape: SasDecodeShape, q, k_cache, v_cache, seq_lens, s, o, idx_o
                          _stream(stream)), "sas_decode")
 
 
+def sas_decode_noalloc(shape: SasDecodeShape, q, k_cache, v_cache, seq_lens, s, o, idx_out,
+                       stream=None):
+    """sas_decode with its scratch in the library's own per-GPU array (no
+    workspace argument, nothing allocated)."""
+    dt = _dt(shape)
+    _check(q, "q", dt, shape.B * shape.Hq * shape.d)
+    _check(k_cache, "k_cache", dt, shape.B * shape.Hkv * shape.cap * shape.d)
+    _check(v_cache, "v_cache", dt, shape.B * shape.Hkv * shape.cap * shape.d)
+    _check(seq_lens, "seq_lens", torch.int32, shape.B)
+    _check(s, "s", torch.float32, shape.B * shape.Hkv * (shape.cap // BLOCK))
+    _check(o, "o", dt, shape.B * shape.Hq * shape.d)
+    _check(idx_out, "idx_out", torch.int32, shape.B * shape.Hkv * shape.topk)
+    _ok(lib().sas_decode_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                 _ptr(seq_lens), _ptr(s), _ptr(o), _ptr(idx_out),
+                                 _stream(stream)), "sas_decode_noalloc")
+
+
 def sas_decode_paged_workspace_bytes(shape: SasDecodePagedShape) -> int:
     return int(lib().sas_decode_paged_workspace_bytes(ctypes.byref(shape)))
 
@@ -260,7 +277,7 @@ __all__ = [
     "sas_pool_workspace_bytes", "sas_pool_scores", "sas_select", "sas_mask_documents",
     "doc_first_from_cu_seqlens", "sas_fwd",
     "sas_bwd_workspace_bytes", "sas_bwd", "sas_decode_workspace_bytes", "sas_decode",
-    "sas_decode_paged_workspace_bytes", "sas_decode_paged", "sas_prof_enable", "sas_prof_collect",
+    "sas_decode_noalloc", "sas_decode_paged_workspace_bytes", "sas_decode_paged", "sas_prof_enable", "sas_prof_collect",
     "alloc_select", "alloc_workspace", "status_string", "SasError", "SasShape", "SasDecodeShape",
-    "SasDecodePagedShape",
+    "SasDecodePagedShape", "NOALLOC_SCRATCH_BYTES",
 ]

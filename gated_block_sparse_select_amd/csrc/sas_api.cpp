@@ -141,6 +141,44 @@ DecWs dec_layout(const sas_decode_shape* s) {
   return w;
 }
 
+}  // namespace
+
+// ----------------------------------------------------------- no-allocation scratch
+// The decode scratch of sas_decode_noalloc: one copy per GPU in the library's
+// code object.  In host code `scratch` names a host-side stand-in, not device
+// memory; host code uses only the per-device address from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[SAS_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device that runs `stream`, resolved once
+// per device with that device current.
+sas_status scratch_of(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return from_hip(e);
+  if (dev < 0 || dev >= kMaxDevices) return SAS_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return from_hip(e);
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return from_hip(e);
+    void* p = nullptr;
+    const hipError_t es = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && (e = hipSetDevice(cur)) != hipSuccess) return from_hip(e);
+    if (es != hipSuccess) return from_hip(es);
+    if (!p) return from_hip(hipErrorInvalidSymbol);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SAS_OK;
+}
+
 // ----------------------------------------------------------- profiling state
 struct ProfRec {
   const char* name;
@@ -309,6 +347,25 @@ sas_status sas_decode(const sas_decode_shape* s, const void* q, const void* k_ca
   const DecWs w = dec_layout(s);
   if (!ws || ws_bytes < w.total) return SAS_ERR_WORKSPACE;
   char* base = static_cast<char*>(ws);
+  float* acc = reinterpret_cast<float*>(base + w.acc_off);
+  float* ml = reinterpret_cast<float*>(base + w.ml_off);
+  clear_stale_error();
+  return from_hip(sas::launch_decode(s->dtype, q, k_cache, v_cache, seq_lens, sc, idx_out, acc, ml,
+                                     o, s->B, s->Hq, s->Hkv, s->cap, s->d, s->topk, w.nsplit,
+                                     tau_of(s->scale, s->d), s->gate, stream));
+}
+
+sas_status sas_decode_noalloc(const sas_decode_shape* s, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* seq_lens, const float* sc,
+                              void* o, int32_t* idx_out, hipStream_t stream) {
+  sas_status st = check_dshape(s);
+  if (st != SAS_OK) return st;
+  if (!q || !k_cache || !v_cache || !seq_lens || !sc || !o) return SAS_ERR_ARG;
+  const DecWs w = dec_layout(s);
+  if (w.total > size_t(SAS_NOALLOC_SCRATCH_BYTES)) return SAS_ERR_WORKSPACE;
+  void* base_v = nullptr;
+  if ((st = scratch_of(stream, &base_v)) != SAS_OK) return st;
+  char* base = static_cast<char*>(base_v);
   float* acc = reinterpret_cast<float*>(base + w.acc_off);
   float* ml = reinterpret_cast<float*>(base + w.ml_off);
   clear_stale_error();

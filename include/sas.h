@@ -229,6 +229,27 @@ sas_status sas_decode(const sas_decode_shape* shape, const void* q, const void* 
                       const void* v_cache, const int32_t* seq_lens, const float* s, void* o,
                       int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------- decode without allocation
+ * For callers that cannot allocate device memory or hand in a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, results and status codes as sas_decode, without
+ * ws / ws_bytes: the scratch lives in a library-owned device array of
+ * SAS_NOALLOC_SCRATCH_BYTES bytes, one per GPU, which the GPU holds from the
+ * library's load until the process ends.  Returns SAS_ERR_WORKSPACE (nothing
+ * enqueued) when sas_decode_workspace_bytes(shape) exceeds that size.  Calls
+ * no hipMalloc, hipFree or allocating routine.
+ *   - Every call on a GPU shares that GPU's array, which keeps the last call's
+ *     contents (nothing in it needs to start at zero).  Calls that overlap in
+ *     time on one GPU (other streams, other threads) race on it: the caller
+ *     must serialise them, e.g. by issuing them on one stream.
+ *   - The first call on each GPU resolves the array's device address
+ *     (hipGetSymbolAddress, with the stream's device current); make that first
+ *     call outside graph capture. */
+#define SAS_NOALLOC_SCRATCH_BYTES (16u << 20)
+sas_status sas_decode_noalloc(const sas_decode_shape* shape, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* seq_lens, const float* s,
+                              void* o, int32_t* idx_out, hipStream_t stream);
+
 /* ---------------------------------------------------------------- paged decode
  * sas_decode over a paged KV pool, the serving-side cache of [Review §2.6]:
  * the same selection and attention with cap = 64*max_blocks, where the K/V

@@ -105,6 +105,10 @@ def test_workspace_checks():
     bad = api.make_decode_shape(64, 32, 8, 1000, 128, 32)
     assert api.sas_decode_workspace_bytes(bad) == 0
     assert L.sas_decode(ctypes.byref(bad), *([FAKE] * 7), FAKE, 1 << 30, None) == 1
+    # the allocation-free decode checks its arguments before touching a device
+    assert L.sas_decode_noalloc(ctypes.byref(bad), *([FAKE] * 7), None) == 1
+    assert L.sas_decode_noalloc(ctypes.byref(dsh), *([None] * 7), None) == 1
+    assert L.sas_decode_noalloc(None, *([FAKE] * 7), None) == 1
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,maxb,pages,d,K,dt,expect", [
