@@ -42,6 +42,7 @@ def parse():
     p.add_argument("--no-gates", action="store_true", help="skip the ablation-gate lines")
     p.add_argument("--no-packed", action="store_true", help="skip the packed-documents line")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    p.add_argument("--no-configs", action="store_true", help="skip the Qwen3-4B / 14B layer lines")
     p.add_argument("--decode-steps", type=int, default=50)
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run one 1 GiB device copy (reference for HBM byte counters)")
@@ -53,6 +54,34 @@ def pair_count(cnt_np, G):
     import numpy as np
     c = cnt_np.astype(np.int64)
     return G * (int(c.sum()) * 64 * 64 + c.size * (64 * 65 // 2))
+
+
+def timed(torch, step, steps):
+    """ms per step of `steps` calls between two synchronisations (no
+    per-launch events in the library), and the host wall time."""
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps, time.perf_counter() - t0
+
+
+def kernel_pass(api, torch, step, steps):
+    """A second pass of the same calls with the library's per-launch HIP
+    events (recorded on the launch stream): {kernel: avg ms, launches} and
+    that pass's ms per step."""
+    torch.cuda.synchronize()
+    api.sas_prof_collect()          # drop anything recorded before
+    api.sas_prof_enable(True)
+    ms, _ = timed(torch, step, steps)
+    api.sas_prof_enable(False)
+    kern = api.sas_prof_collect()
+    per = {name: dict(avg_ms=tot / max(nl, 1), launches=nl) for name, (tot, nl) in kern.items()}
+    return per, ms
 
 
 def run_training(args, api, si, torch, np, w=None, steps=None, warmup=None, gate="softmax"):
@@ -92,30 +121,16 @@ def run_training(args, api, si, torch, np, w=None, steps=None, warmup=None, gate
 
     for _ in range(warmup):
         step()
-    torch.cuda.synchronize()
-    api.sas_prof_collect()          # drop anything recorded before
-    api.sas_prof_enable(True)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(steps):
-        step()
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    api.sas_prof_enable(False)
-    kern = api.sas_prof_collect()
-    ms_step = ev0.elapsed_time(ev1) / steps
+    ms_step, wall = timed(torch, step, steps)
+    per_kernel, ms_prof = kernel_pass(api, torch, step, steps)
 
     cnt = sel["cnt"].cpu().numpy()
     G = w.Hq // w.Hkv
     pairs = pair_count(cnt, G)
     flop_fwd = 4 * w.d * pairs
     flop_bwd = 10 * w.d * pairs
-    per_kernel = {name: dict(avg_ms=tot / max(nl, 1), launches=nl) for name, (tot, nl) in kern.items()}
-    return dict(w=w, ms_step=ms_step, wall=wall, pairs=pairs, flop_fwd=flop_fwd, flop_bwd=flop_bwd,
-                per_kernel=per_kernel, host=host, s=s, sel=sel, steps=steps)
+    return dict(w=w, ms_step=ms_step, ms_prof=ms_prof, wall=wall, pairs=pairs, flop_fwd=flop_fwd,
+                flop_bwd=flop_bwd, per_kernel=per_kernel, host=host, s=s, sel=sel, steps=steps)
 
 
 def hbm_kernels(res):
@@ -179,6 +194,30 @@ def run_packed(args, api, si, torch, np):
            "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4), "pairs": res["pairs"],
            "per_kernel_ms": {k: round(v["avg_ms"], 3) for k, v in res["per_kernel"].items()}}
     res.clear()
+    return out
+
+
+def run_configs(args, api, si, torch, np):
+    """The other training-layer workloads of the survey (Qwen3-4B at 8K with
+    K = 16, Qwen3-14B at 32K with K = 64 and Gumbel scores): select + fwd +
+    bwd, ms per step, effective TFLOP/s and per-kernel times."""
+    out = {}
+    for cfg in (2, 4):
+        if cfg == args.workload:
+            continue
+        w = si.WORKLOADS[cfg]
+        res = run_training(args, api, si, torch, np, w=w, steps=max(2, args.steps // 2), warmup=2)
+        total = res["flop_fwd"] + res["flop_bwd"]
+        tf = total / (res["ms_step"] * 1e-3) / 1e12
+        out[w.name] = {"B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.d, "n": w.n,
+                       "topk": w.topk, "scores": w.s_kind, "steps": res["steps"],
+                       "ms_per_step": round(res["ms_step"], 4), "TFLOPs": round(tf, 1),
+                       "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+                       "effective_flop": total, "roofline": roofline_for(res),
+                       "per_kernel_ms": {k: round(v["avg_ms"], 4)
+                                         for k, v in res["per_kernel"].items()}}
+        res.clear()
+        torch.cuda.empty_cache()
     return out
 
 
@@ -254,9 +293,23 @@ def roofline_for(res):
                 traffic=None, kernel=name)
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(res, np, budget_s=15.0):
-    """The oracle (numpy, float64 gather mode) on a bounded sample of the same
-    workload: whole q-blocks, forward + backward, until ~budget_s of CPU time."""
+    """The oracle as it stands (numpy, float64 gather mode: it is the
+    correctness reference, so it computes in float64 throughout) on a bounded
+    sample of the same workload: whole q-blocks, forward + backward, until
+    ~budget_s of CPU time."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -284,6 +337,7 @@ def cpu_baseline(res, np, budget_s=15.0):
     el = time.perf_counter() - t0
     flops = 14 * w.d * pairs
     return dict(value=round(flops / el / 1e12, 6), unit="TFLOP/s", cores=int(threads), kind="oracle",
+                cpu_model=cpu_model(), dtype="f64",
                 sample=f"{done} of {w.nqb * w.Hkv * w.B} (batch, kv-head, q-block) units of the "
                        f"{w.name} workload, kv-head 0, forward+backward in float64 gather mode, "
                        f"{el:.1f} s")
@@ -446,12 +500,15 @@ def main():
         "roofline": roofline_for(res),
         "effective_flop": {"fwd": res["flop_fwd"], "bwd": res["flop_bwd"], "pairs": res["pairs"]},
         "per_kernel_ms": {k: round(v["avg_ms"], 4) for k, v in res["per_kernel"].items()},
+        "per_kernel_pass_ms_per_step": round(res["ms_prof"], 4),
         "hbm_kernels": hbm_kernels(res),
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(res, np)
     res.clear()
     torch.cuda.empty_cache()
+    if not args.no_configs:
+        line["configs"] = run_configs(args, api, si, torch, np)
     if not args.no_full_range:
         line["full_range"] = run_full_range(args, api, si, torch, np)
         torch.cuda.empty_cache()

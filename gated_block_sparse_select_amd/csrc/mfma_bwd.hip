@@ -423,15 +423,16 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
   typedef const __attribute__((address_space(3))) f32x4 lds_f32x4;
 
   // P and dZ = P o (dP - D) of row chunk jc as bf16 operands (register
-  // j = 8*jc + e holds row rh*32 + 8*(j/4) + 4*hh + j%4 of this lane's key)
-  auto elementwise = [&]<bool OWN, int JC>(const f32x16& S, const f32x16& P2, float bias2,
-                                           bf16x8& Pp, bf16x8& Zp) __attribute__((always_inline)) {
+  // j = 8*jc + e holds row rh*32 + 8*(j/4) + 4*hh + j%4 of this lane's key);
+  // own-block steps mask the keys above each query row.
+  auto elementwise = [&]<int JC>(const f32x16& S, const f32x16& P2, float bias2, bool own,
+                                 bf16x8& Pp, bf16x8& Zp) __attribute__((always_inline)) {
     float pv[8], zv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int j = 8 * JC + e;
       float p = fast_exp2(__builtin_fmaf(S[j], tau2, bias2));
-      if (OWN && kh * 32 + lr > rh * 32 + 8 * (j >> 2) + 4 * hh + (j & 3)) p = 0.f;
+      if (own && kh * 32 + lr > rh * 32 + 8 * (j >> 2) + 4 * hh + (j & 3)) p = 0.f;
       pv[e] = p;
       zv[e] = p * P2[j];
     }
@@ -439,14 +440,15 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
     Zp = pack_bf16x8(zv);
   };
 
-  auto step = [&]<int ST, bool OWN>(float bias2) __attribute__((always_inline)) {
-    constexpr int NC = D / 16;
-    constexpr int NT = D / 32;
+  constexpr int NC = D / 16;
+  constexpr int NT = D / 32;
+  // S = Q K^T - lse/tau and dP = dO V^T - D (EXT: - D/g) of the step in
+  // stage ST: the statistics seed the accumulators, then the products over
+  // the d chunks (row chunks read two ahead).
+  auto sdp = [&]<int ST>(float bias2, f32x16& S, f32x16& P2) __attribute__((always_inline)) {
     lds_cchar* Qt = stage_buf<TQ, ST, TB>();
     lds_cchar* Ot = stage_buf<TO, ST, TB>();
     lds_cchar* St = stage_buf<TS, ST, 1024>();
-    // phase 1: S = Q K^T - lse/tau, dP = dO V^T - D (EXT: - D/g)
-    f32x16 S, P2;
     const float ig = EXT ? fast_exp2(-bias2) : 1.f;
 #pragma unroll
     for (int jg = 0; jg < 4; ++jg) {
@@ -460,94 +462,119 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
     }
     bf16x8 qa[NC], oa[NC];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < NC; ++c) {
       qa[c] = ld16(Qt, qo[c]);
       oa[c] = ld16(Ot, qo[c]);
     }
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      if (c + 2 < NC) {
-        qa[c + 2] = ld16(Qt, qo[c + 2]);
-        oa[c + 2] = ld16(Ot, qo[c + 2]);
-      }
       S = mfma32(qa[c], kop[c], S);
       P2 = mfma32(oa[c], vop[c], P2);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // phase 2: transposed operands of rows 0..15, P and dZ of rows 0..15
-    bf16x8 tO0[NT], tQ0[NT], tO1[NT], tQ1[NT];
-#pragma unroll
-    for (int dt = 0; dt < NT; ++dt) {
-      tO0[dt] = ldtr_pair(Ot, to[dt][0], to[dt][1]);
-      tQ0[dt] = ldtr_pair(Qt, to[dt][0], to[dt][1]);
-    }
-    bf16x8 Pp0, Zp0, Pp1, Zp1;
-    elementwise.template operator()<OWN, 0>(S, P2, bias2, Pp0, Zp0);
-    __builtin_amdgcn_sched_barrier(0);
-    // phase 3: dV/dK of rows 0..15 with P, dZ and operands of rows 16..31
-#pragma unroll
-    for (int dt = 0; dt < NT; ++dt) {
-      tO1[dt] = ldtr_pair(Ot + 16 * ROWB, to[dt][0], to[dt][1]);
-      tQ1[dt] = ldtr_pair(Qt + 16 * ROWB, to[dt][0], to[dt][1]);
-    }
-#pragma unroll
-    for (int dt = 0; dt < NT; ++dt) {
-      dV[dt] = mfma32(Pp0, tO0[dt], dV[dt]);
-      dK[dt] = mfma32(Zp0, tQ0[dt], dK[dt]);
-    }
-    elementwise.template operator()<OWN, 1>(S, P2, bias2, Pp1, Zp1);
-#pragma unroll
-    for (int i = 0; i < 2 * NT; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one matrix product
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six vector ops
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // phase 4: dV/dK of rows 16..31
-#pragma unroll
-    for (int dt = 0; dt < NT; ++dt) {
-      dV[dt] = mfma32(Pp1, tO1[dt], dV[dt]);
-      dK[dt] = mfma32(Zp1, tQ1[dt], dK[dt]);
     }
   };
+  // transposed Q / dO operands (rows 0..15 and 16..31 of the wave) of the
+  // step in stage ST
+  auto tr_ops = [&]<int ST>(bf16x8 (&tO)[2][NT], bf16x8 (&tQ)[2][NT]) __attribute__((always_inline)) {
+    lds_cchar* Qt = stage_buf<TQ, ST, TB>();
+    lds_cchar* Ot = stage_buf<TO, ST, TB>();
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int dt = 0; dt < NT; ++dt) {
+        tO[h][dt] = ldtr_pair(Ot + h * 16 * ROWB, to[dt][0], to[dt][1]);
+        tQ[h][dt] = ldtr_pair(Qt + h * 16 * ROWB, to[dt][0], to[dt][1]);
+      }
+  };
+  // dV += P^T dO, dK += dZ^T Q over the wave's 32 rows
+  auto dvdk = [&](const bf16x8 (&Pp)[2], const bf16x8 (&Zp)[2], const bf16x8 (&tO)[2][NT],
+                  const bf16x8 (&tQ)[2][NT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int dt = 0; dt < NT; ++dt) {
+        dV[dt] = mfma32(Pp[h], tO[h][dt], dV[dt]);
+        dK[dt] = mfma32(Zp[h], tQ[h][dt], dK[dt]);
+      }
+  };
 
-  // step s in stage ST: wait for its DMA (and for the stage it refills to be
-  // free), refill the stage NS-1 ahead, compute.  Steps 0..G-1 are the own
-  // block (no gate, causal mask; rows 0..31 see none of the keys 32..63, so
-  // that wave sits them out).
-  int ce = 0, chd = 0;   // list entry / head of the step being computed
-  auto run = [&]<int ST, bool STEADY>(int s) __attribute__((always_inline)) {
-    if (STEADY) vm_wait_barrier<(NS - 2) * PER>();
-    else wait_ahead(min(NS - 2, nsteps - 1 - s));
-    if (STEADY || s + NS - 1 < nsteps) issue.template operator()<(ST + NS - 1) % NS>();
-    const float bias2 = __int_as_float(meta[ce].y);
+  // Software pipeline over the steps: iteration s forms P and dZ of step s
+  // (vector work on the S / dP accumulated in iteration s - 1) while the
+  // matrix cores compute S and dP of step s + 1, then runs the dV/dK
+  // products of step s.  The vector work of one step thus overlaps the
+  // products of the next instead of waiting for its own.
+  //
+  // Ring: step s lives in stage s % NS.  Iteration s reads stage s (the
+  // transposed operands) and stage s + 1 (statistics and rows); after its
+  // barrier, stage s - 1 is free and is refilled with step s + NS - 1.
+  f32x16 S, P2;
+  float bias = 0.f;
+  int ce = 0, chd = 0;   // list entry / head of step s + 1 (the next one to start)
+  auto advance = [&]() __attribute__((always_inline)) {
     if (++chd == G) {
       chd = 0;
       ++ce;
     }
-    if (!STEADY && s < G) {
-      if (!(kh == 1 && rh == 0)) step.template operator()<ST, true>(0.f);
+  };
+  // prologue (steps 0 .. NS-2 were issued above): S and dP of step 0, an
+  // own-block step (no gate)
+  wait_ahead(min(NS - 2, nsteps - 1));
+  sdp.template operator()<0>(0.f, S, P2);
+  advance();
+
+  // iteration s in stage ST; CHECKED: the ring's end may fall inside
+  auto iter = [&]<int ST, bool CHECKED>(int s) __attribute__((always_inline)) {
+    constexpr int ST1 = (ST + 1) % NS;
+    const bool own = CHECKED && s < G;
+    bf16x8 tO[2][NT], tQ[2][NT], Pp[2], Zp[2];
+    if (!CHECKED || s + 1 < nsteps) {
+      // step s + 1 landed (at most one later step still in flight); every
+      // wave is done with stage s - 1
+      if (CHECKED) wait_ahead(min(NS - 3, nsteps - 2 - s));
+      else vm_wait_barrier<(NS - 3) * PER>();
+      if (!CHECKED || s + NS - 1 < nsteps) issue.template operator()<(ST + NS - 1) % NS>();
+      // base-2 log-gate of step s + 1 (0 for the own block, list entry 0)
+      const float bias_n = __int_as_float(meta[ce].y);
+      const float bias_s = bias;
+      f32x16 Sn, P2n;
+      tr_ops.template operator()<ST>(tO, tQ);
+      sdp.template operator()<ST1>(bias_n, Sn, P2n);
+      elementwise.template operator()<0>(S, P2, bias_s, own, Pp[0], Zp[0]);
+      elementwise.template operator()<1>(S, P2, bias_s, own, Pp[1], Zp[1]);
+      // issue order: the matrix products of step s + 1 with the vector work
+      // of step s between them
+#pragma unroll
+      for (int i = 0; i < 2 * NC; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+      dvdk(Pp, Zp, tO, tQ);
+      S = Sn;
+      P2 = P2n;
+      bias = bias_n;
+      advance();
     } else {
-      step.template operator()<ST, false>(bias2);
+      // last step: nothing further to start
+      tr_ops.template operator()<ST>(tO, tQ);
+      elementwise.template operator()<0>(S, P2, bias, own, Pp[0], Zp[0]);
+      elementwise.template operator()<1>(S, P2, bias, own, Pp[1], Zp[1]);
+      dvdk(Pp, Zp, tO, tQ);
     }
   };
   int s = 0;
-  // own-block steps and the ring tail use the checked form
 #pragma nounroll
   for (; s < G; s += NS)
-    [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
-      ((s + S < nsteps ? run.template operator()<S, false>(s + S) : void()), ...);
+    [&]<int... S_>(std::integer_sequence<int, S_...>) __attribute__((always_inline)) {
+      ((s + S_ < nsteps ? iter.template operator()<S_, true>(s + S_) : void()), ...);
     }(std::make_integer_sequence<int, NS>{});
 #pragma nounroll
-  for (; s + 2 * NS - 2 < nsteps; s += NS)
-    [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
-      (run.template operator()<S, true>(s + S), ...);
+  for (; s + 2 * NS - 1 < nsteps; s += NS)
+    [&]<int... S_>(std::integer_sequence<int, S_...>) __attribute__((always_inline)) {
+      (iter.template operator()<S_, false>(s + S_), ...);
     }(std::make_integer_sequence<int, NS>{});
 #pragma nounroll
   for (; s < nsteps; s += NS)
-    [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
-      ((s + S < nsteps ? run.template operator()<S, false>(s + S) : void()), ...);
+    [&]<int... S_>(std::integer_sequence<int, S_...>) __attribute__((always_inline)) {
+      ((s + S_ < nsteps ? iter.template operator()<S_, true>(s + S_) : void()), ...);
     }(std::make_integer_sequence<int, NS>{});
   __syncthreads();
 
