@@ -38,8 +38,17 @@ notes):
 * the LSE runs over all history blocks, selected or not; with fewer than K
   history blocks all of them are selected (still gated).
 * a score of -inf marks a history block that is not a candidate: no part of
-  the LSE, never kept, ds = 0; a packed batch of block-aligned documents puts
-  -inf on every block of an earlier document (``mask_documents``).
+  the LSE, never kept, ds = 0; a packed batch puts -inf on every block of an
+  earlier document (``mask_documents``).
+* packed documents of any length: each document is cut into blocks of 64
+  tokens from its own first token, its last block holding the remaining 1..64
+  tokens; blocks are numbered in token order across the documents.  The
+  block geometry ``geom`` [B, NB, 2] gives each block's first token and
+  length (a length of 0 marks a padding block at the end of a batch entry,
+  which holds no token); without it block i is tokens [64 i, 64 i + 64).  A
+  token's current block is the block holding it; causal masking inside it
+  runs on token positions.  Tokens outside every block attend to nothing
+  (their outputs are 0).
 * ties in s go to the lower block index; -0.0 and +0.0 are equal.
 * idx lists the selected blocks in ascending order, padded with -1; padded
   log_gate entries are -inf; s_lse of a row with no history is -inf.
@@ -78,8 +87,63 @@ def _f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
+# ============================================================== block geometry
+def blocks_of_documents(doc_lens):
+    """Blocks of packed documents of the given token lengths: each document is
+    cut into 64-token blocks from its own first token (the last one partial).
+    Returns (geom [NB, 2] int64: first token and length of each block,
+    doc_first [NB] int64: the first block of each block's document)."""
+    geom, first = [], []
+    tok = 0
+    for L in doc_lens:
+        L = int(L)
+        b0 = len(geom)
+        for a in range(0, L, BLOCK):
+            geom.append((tok + a, min(BLOCK, L - a)))
+            first.append(b0)
+        tok += L
+    return np.asarray(geom, dtype=np.int64).reshape(-1, 2), np.asarray(first, dtype=np.int64)
+
+
+def packed_geometry(doc_lens_per_batch):
+    """Batch version of ``blocks_of_documents``: geom [B, NB, 2], doc_first
+    [B, NB] with NB the largest block count; shorter entries are padded with
+    zero-length blocks (first token = end of the entry's documents), each its
+    own document."""
+    parts = [blocks_of_documents(dl) for dl in doc_lens_per_batch]
+    NB = max(len(g) for g, _ in parts)
+    B = len(parts)
+    geom = np.zeros((B, NB, 2), dtype=np.int64)
+    first = np.zeros((B, NB), dtype=np.int64)
+    for b, (g, f) in enumerate(parts):
+        end = int(sum(int(x) for x in doc_lens_per_batch[b]))
+        geom[b, :len(g)] = g
+        geom[b, len(g):] = (end, 0)
+        first[b, :len(f)] = f
+        first[b, len(f):] = np.arange(len(f), NB)
+    return geom, first
+
+
+def _rows(geom_b, i: int):
+    """Token rows of block i (geometry row geom_b, or the uniform grid)."""
+    if geom_b is None:
+        return np.arange(i * BLOCK, (i + 1) * BLOCK)
+    a, L = int(geom_b[i][0]), int(geom_b[i][1])
+    return np.arange(a, a + L)
+
+
+def _rsl(geom_b, i: int):
+    """The rows of block i as a slice (blocks are contiguous token ranges)."""
+    r = _rows(geom_b, i)
+    return slice(int(r[0]), int(r[-1]) + 1) if len(r) else slice(0, 0)
+
+
+def _nblocks(n: int, geom):
+    return n // BLOCK if geom is None else np.shape(geom)[1]
+
+
 # ============================================================== pooling
-def pool_scores(q, k, Hkv: int):
+def pool_scores(q, k, Hkv: int, geom=None):
     """Mean-pooled block scores (the stand-in selector of the 32K workload).
 
     s[b, kv, i, m] = qbar[b, kv, i] . kbar[b, kv, m] / sqrt(d), where qbar is
@@ -93,9 +157,22 @@ def pool_scores(q, k, Hkv: int):
     q, k = _f64(q), _f64(k)
     B, Hq, n, d = q.shape
     G = Hq // Hkv
-    nb = n // BLOCK
-    qbar = q.reshape(B, Hkv, G, nb, BLOCK, d).mean(axis=(2, 4))
-    kbar = k.reshape(B, Hkv, nb, BLOCK, d).mean(axis=3)
+    if geom is None:
+        nb = n // BLOCK
+        qbar = q.reshape(B, Hkv, G, nb, BLOCK, d).mean(axis=(2, 4))
+        kbar = k.reshape(B, Hkv, nb, BLOCK, d).mean(axis=3)
+        return np.einsum("bkid,bkmd->bkim", qbar, kbar) / math.sqrt(d)
+    # packed geometry: means over each block's own tokens (0 for an empty block)
+    nb = np.shape(geom)[1]
+    qbar = np.zeros((B, Hkv, nb, d))
+    kbar = np.zeros((B, Hkv, nb, d))
+    for b in range(B):
+        for i in range(nb):
+            r = _rows(geom[b], i)
+            if len(r) == 0:
+                continue
+            qbar[b, :, i] = q[b][:, r].reshape(Hkv, G * len(r), d).mean(axis=1)
+            kbar[b, :, i] = k[b][:, r].mean(axis=1)
     return np.einsum("bkid,bkmd->bkim", qbar, kbar) / math.sqrt(d)
 
 
@@ -187,31 +264,39 @@ def select(s, topk: int, gate: str = "softmax"):
 
 
 # ============================================================== forward
-def bias_matrix(n: int, idx_row, cnt_row, lg_row):
+def bias_matrix(n: int, idx_row, cnt_row, lg_row, geom_b=None):
     """Dense n x n additive bias of one (batch, kv-head) [Review §2.3, §2.6].
 
     A[t, j] = 0 if j is in t's own block and j <= t (current block, g_0 = 1);
     A[t, j] = log_gate of block(j) if block(j) is selected by block(t);
-    A[t, j] = -inf otherwise (skipped).
+    A[t, j] = -inf otherwise (skipped).  Blocks follow ``geom_b`` when given.
     """
-    nb = n // BLOCK
+    nb = n // BLOCK if geom_b is None else len(geom_b)
     A = np.full((n, n), NEG_INF)
     for i in range(nb):
-        r = slice(i * BLOCK, (i + 1) * BLOCK)
+        r = _rows(geom_b, i)
+        if len(r) == 0:
+            continue
         for slot in range(int(cnt_row[i])):
             m = int(idx_row[i, slot])
-            A[r, m * BLOCK:(m + 1) * BLOCK] = lg_row[i, slot]
-        tri = np.tril(np.ones((BLOCK, BLOCK), dtype=bool))
-        blk = A[r, r]
+            A[np.ix_(r, _rows(geom_b, m))] = lg_row[i, slot]
+        tri = np.tril(np.ones((len(r), len(r)), dtype=bool))
+        blk = A[np.ix_(r, r)]
         blk[tri] = 0.0
-        A[r, r] = blk
+        A[np.ix_(r, r)] = blk
     return A
 
 
 def _softmax_rows(Z):
-    L = Z.max(axis=-1, keepdims=True)
-    L = L + np.log(np.sum(np.exp(Z - L), axis=-1, keepdims=True))
-    return np.exp(Z - L), L[..., 0]
+    """Row softmax and row logsumexp; a row with no finite logit (a token
+    outside every block) gets weights 0 and logsumexp -inf."""
+    M = Z.max(axis=-1, keepdims=True)
+    empty = ~np.isfinite(M)
+    M = np.where(empty, 0.0, M)
+    with np.errstate(divide="ignore"):
+        L = M + np.log(np.sum(np.exp(Z - M), axis=-1, keepdims=True))
+    P = np.where(empty, 0.0, np.exp(Z - np.where(empty, 0.0, L)))
+    return P, np.where(empty, NEG_INF, L)[..., 0]
 
 
 def _placed(A, gate: str):
@@ -224,7 +309,7 @@ def _placed(A, gate: str):
     return A, np.ones_like(A)
 
 
-def fwd_dense(q, k, v, idx, cnt, log_gate, scale=None, gate: str = "softmax"):
+def fwd_dense(q, k, v, idx, cnt, log_gate, scale=None, gate: str = "softmax", geom=None):
     """Dense definition: for each query head h (kv-head h // G),
     Z = tau Q_h K^T + A, L = rowwise logsumexp(Z), O_h = exp(Z - L) V.
     For the external gate, Z keeps only A's mask and O_h = (exp(Z - L) o W) V
@@ -245,7 +330,8 @@ def fwd_dense(q, k, v, idx, cnt, log_gate, scale=None, gate: str = "softmax"):
     lse = np.zeros((B, Hq, n))
     for b in range(B):
         for kv in range(Hkv):
-            A, W = _placed(bias_matrix(n, idx[b, kv], cnt[b, kv], log_gate[b, kv]), gate)
+            A, W = _placed(bias_matrix(n, idx[b, kv], cnt[b, kv], log_gate[b, kv],
+                                       None if geom is None else geom[b]), gate)
             for g in range(G):
                 h = kv * G + g
                 P, L = _softmax_rows(tau * q[b, h] @ k[b, kv].T + A)
@@ -254,28 +340,31 @@ def fwd_dense(q, k, v, idx, cnt, log_gate, scale=None, gate: str = "softmax"):
     return o, lse
 
 
-def _gather_cols(i: int, idx_row, cnt_row, lg_row):
+def _gather_cols(i: int, idx_row, cnt_row, lg_row, geom_b=None):
     """Key columns of q-block i (selected blocks in slot order, then the
     current block) with their per-column log-gate (0 for the current block)
     and block slot (-1 = current)."""
     cols, bias, slot = [], [], []
     for sl in range(int(cnt_row[i])):
         m = int(idx_row[i, sl])
-        cols.append(np.arange(m * BLOCK, (m + 1) * BLOCK))
-        bias.append(np.full(BLOCK, float(lg_row[i, sl])))
-        slot.append(np.full(BLOCK, sl))
-    cols.append(np.arange(i * BLOCK, (i + 1) * BLOCK))
-    bias.append(np.zeros(BLOCK))
-    slot.append(np.full(BLOCK, -1))
+        c = _rows(geom_b, m)
+        cols.append(c)
+        bias.append(np.full(len(c), float(lg_row[i, sl])))
+        slot.append(np.full(len(c), sl))
+    c = _rows(geom_b, i)
+    cols.append(c)
+    bias.append(np.zeros(len(c)))
+    slot.append(np.full(len(c), -1))
     return np.concatenate(cols), np.concatenate(bias), np.concatenate(slot)
 
 
 def _block_logits(qi, kc, bias, slot, tau):
-    """Z for the 64 rows of one q-block over its gathered columns, with the
+    """Z for the rows of one q-block over its gathered columns, with the
     causal mask (j <= t) on the current block's columns."""
     Z = tau * qi @ kc.T + bias[None, :]
     cur = slot == -1
-    tri = np.tril(np.ones((BLOCK, BLOCK), dtype=bool))
+    nr = qi.shape[0]
+    tri = np.tril(np.ones((nr, nr), dtype=bool))
     Zc = Z[:, cur]
     Zc[~tri] = NEG_INF
     Z[:, cur] = Zc
@@ -290,21 +379,23 @@ def _placed_cols(lgc, gate: str):
 
 
 def fwd_gather_block(q, k, v, idx, cnt, log_gate, b: int, kv: int, i: int, scale=None,
-                     gate: str = "softmax"):
+                     gate: str = "softmax", geom=None):
     """Gather-mode forward of one (batch, kv-group, q-block): the formula of
     ``fwd_dense`` evaluated only on columns whose bias is finite, which is
-    exact because exp(-inf) = 0.  Returns (o [G,64,d], lse [G,64])."""
+    exact because exp(-inf) = 0.  Returns (o [G,rows,d], lse [G,rows]) for the
+    block's rows (64 of them without a geometry)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     Hq, d = q.shape[1], q.shape[3]
     Hkv = k.shape[1]
     G = Hq // Hkv
     tau = (1.0 / math.sqrt(d)) if not scale else float(scale)
-    cols, lgc, slot = _gather_cols(i, idx[b, kv], cnt[b, kv], log_gate[b, kv])
+    gb = None if geom is None else geom[b]
+    cols, lgc, slot = _gather_cols(i, idx[b, kv], cnt[b, kv], log_gate[b, kv], gb)
     bias, w = _placed_cols(lgc, gate)
     kc, vc = k[b, kv, cols], v[b, kv, cols] * w[:, None]
-    r = slice(i * BLOCK, (i + 1) * BLOCK)
-    o = np.zeros((G, BLOCK, d))
-    lse = np.zeros((G, BLOCK))
+    r = _rows(gb, i)
+    o = np.zeros((G, len(r), d))
+    lse = np.zeros((G, len(r)))
     for g in range(G):
         P, L = _softmax_rows(_block_logits(q[b, kv * G + g, r], kc, bias, slot, tau))
         o[g] = P @ vc
@@ -312,18 +403,20 @@ def fwd_gather_block(q, k, v, idx, cnt, log_gate, b: int, kv: int, i: int, scale
     return o, lse
 
 
-def fwd_gather(q, k, v, idx, cnt, log_gate, scale=None, blocks=None, gate: str = "softmax"):
-    """Gather-mode forward over all q-blocks (or the (b, kv, i) list given)."""
+def fwd_gather(q, k, v, idx, cnt, log_gate, scale=None, blocks=None, gate: str = "softmax",
+               geom=None):
+    """Gather-mode forward over all q-blocks (or the (b, kv, i) list given).
+    Tokens outside every block keep o = 0 and lse = -inf."""
     B, Hq, n, d = np.shape(q)
     Hkv = np.shape(k)[1]
     G = Hq // Hkv
     o = np.zeros((B, Hq, n, d))
-    lse = np.zeros((B, Hq, n))
+    lse = np.full((B, Hq, n), NEG_INF)
     todo = blocks if blocks is not None else [
-        (b, kv, i) for b in range(B) for kv in range(Hkv) for i in range(n // BLOCK)]
+        (b, kv, i) for b in range(B) for kv in range(Hkv) for i in range(_nblocks(n, geom))]
     for (b, kv, i) in todo:
-        ob, lb = fwd_gather_block(q, k, v, idx, cnt, log_gate, b, kv, i, scale, gate)
-        r = slice(i * BLOCK, (i + 1) * BLOCK)
+        ob, lb = fwd_gather_block(q, k, v, idx, cnt, log_gate, b, kv, i, scale, gate, geom)
+        r = _rsl(None if geom is None else geom[b], i)
         o[b, kv * G:(kv + 1) * G, r] = ob
         lse[b, kv * G:(kv + 1) * G, r] = lb
     return o, lse
@@ -371,7 +464,7 @@ def gate_jacobian(s, s_lse, idx, cnt, dlg, gate: str = "softmax"):
     return ds
 
 
-def bwd_dense(q, k, v, do, idx, cnt, log_gate, scale=None, gate: str = "softmax"):
+def bwd_dense(q, k, v, do, idx, cnt, log_gate, scale=None, gate: str = "softmax", geom=None):
     """Analytic backward of the dense definition (no autograd).
 
     With P = softmax(Z), O = P V and upstream dO:
@@ -392,10 +485,12 @@ def bwd_dense(q, k, v, do, idx, cnt, log_gate, scale=None, gate: str = "softmax"
     K = idx.shape[-1]
     tau = (1.0 / math.sqrt(d)) if not scale else float(scale)
     dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
-    dlg = np.zeros((B, Hkv, n // BLOCK, K))
+    nb = _nblocks(n, geom)
+    dlg = np.zeros((B, Hkv, nb, K))
     for b in range(B):
+        gb = None if geom is None else geom[b]
         for kv in range(Hkv):
-            A, W = _placed(bias_matrix(n, idx[b, kv], cnt[b, kv], log_gate[b, kv]), gate)
+            A, W = _placed(bias_matrix(n, idx[b, kv], cnt[b, kv], log_gate[b, kv], gb), gate)
             for g in range(G):
                 h = kv * G + g
                 P, _ = _softmax_rows(tau * q[b, h] @ k[b, kv].T + A)
@@ -407,19 +502,19 @@ def bwd_dense(q, k, v, do, idx, cnt, log_gate, scale=None, gate: str = "softmax"
                 dk[b, kv] += tau * dZ.T @ q[b, h]
                 dv[b, kv] += (P * W).T @ do[b, h]
                 G_ = P * dP if gate == "external" else dZ
-                for i in range(n // BLOCK):
-                    r = slice(i * BLOCK, (i + 1) * BLOCK)
+                for i in range(nb):
+                    r = _rows(gb, i)
                     for sl in range(int(cnt[b, kv, i])):
                         m = int(idx[b, kv, i, sl])
-                        dlg[b, kv, i, sl] += G_[r, m * BLOCK:(m + 1) * BLOCK].sum()
+                        dlg[b, kv, i, sl] += G_[np.ix_(r, _rows(gb, m))].sum()
     return dq, dk, dv, dlg
 
 
 def bwd_gather_block(q, k, v, do, idx, cnt, log_gate, b: int, kv: int, i: int, scale=None,
-                     gate: str = "softmax"):
+                     gate: str = "softmax", geom=None):
     """Backward contributions of one (batch, kv-group, q-block) in gather mode.
 
-    Returns (dq [G,64,d], cols, dk_cols [len(cols),d], dv_cols, dlg_row [K]):
+    Returns (dq [G,rows,d], cols, dk_cols [len(cols),d], dv_cols, dlg_row [K]):
     dq of the block's rows is complete; dk_cols/dv_cols are this q-block's
     additive contributions to the gathered key rows ``cols``.
     """
@@ -429,11 +524,12 @@ def bwd_gather_block(q, k, v, do, idx, cnt, log_gate, b: int, kv: int, i: int, s
     G = Hq // Hkv
     K = idx.shape[-1]
     tau = (1.0 / math.sqrt(d)) if not scale else float(scale)
-    cols, lgc, slot = _gather_cols(i, idx[b, kv], cnt[b, kv], log_gate[b, kv])
+    gb = None if geom is None else geom[b]
+    cols, lgc, slot = _gather_cols(i, idx[b, kv], cnt[b, kv], log_gate[b, kv], gb)
     bias, w = _placed_cols(lgc, gate)
     kc, vc = k[b, kv, cols], v[b, kv, cols] * w[:, None]
-    r = slice(i * BLOCK, (i + 1) * BLOCK)
-    dq = np.zeros((G, BLOCK, d))
+    r = _rows(gb, i)
+    dq = np.zeros((G, len(r), d))
     dkc = np.zeros((len(cols), d))
     dvc = np.zeros((len(cols), d))
     dlg = np.zeros(K)
@@ -453,7 +549,8 @@ def bwd_gather_block(q, k, v, do, idx, cnt, log_gate, b: int, kv: int, i: int, s
     return dq, cols, dkc, dvc, dlg
 
 
-def bwd_gather(q, k, v, do, idx, cnt, log_gate, scale=None, blocks=None, gate: str = "softmax"):
+def bwd_gather(q, k, v, do, idx, cnt, log_gate, scale=None, blocks=None, gate: str = "softmax",
+               geom=None):
     """Gather-mode backward over all q-blocks (or the listed (b, kv, i)).
 
     With ``blocks`` given, dq is exact on those q-blocks' rows only and dk/dv
@@ -465,13 +562,14 @@ def bwd_gather(q, k, v, do, idx, cnt, log_gate, scale=None, blocks=None, gate: s
     dq = np.zeros((B, Hq, n, d))
     dk = np.zeros((B, Hkv, n, d))
     dv = np.zeros((B, Hkv, n, d))
-    dlg = np.zeros((B, Hkv, n // BLOCK, K))
+    nb = _nblocks(n, geom)
+    dlg = np.zeros((B, Hkv, nb, K))
     todo = blocks if blocks is not None else [
-        (b, kv, i) for b in range(B) for kv in range(Hkv) for i in range(n // BLOCK)]
+        (b, kv, i) for b in range(B) for kv in range(Hkv) for i in range(nb)]
     for (b, kv, i) in todo:
         dqb, cols, dkc, dvc, dl = bwd_gather_block(q, k, v, do, idx, cnt, log_gate, b, kv, i, scale,
-                                                   gate)
-        dq[b, kv * G:(kv + 1) * G, i * BLOCK:(i + 1) * BLOCK] = dqb
+                                                   gate, geom)
+        dq[b, kv * G:(kv + 1) * G, _rsl(None if geom is None else geom[b], i)] = dqb
         np.add.at(dk[b, kv], cols, dkc)
         np.add.at(dv[b, kv], cols, dvc)
         dlg[b, kv, i] = dl
@@ -488,18 +586,18 @@ def reverse_lists(idx, cnt, b: int, kv: int, m: int):
 
 
 def bwd_kv_block(q, k, v, do, idx, cnt, log_gate, b: int, kv: int, m: int, scale=None,
-                 gate: str = "softmax"):
-    """dk, dv [64, d] of key block m of (b, kv), summed over every q-block
+                 gate: str = "softmax", geom=None):
+    """dk, dv [rows, d] of key block m of (b, kv), summed over every q-block
     that reads it (sampled full-size checks)."""
     d = np.shape(q)[3]
-    dk = np.zeros((BLOCK, d))
-    dv = np.zeros((BLOCK, d))
-    rows = np.arange(m * BLOCK, (m + 1) * BLOCK)
+    rows = _rows(None if geom is None else geom[b], m)
+    dk = np.zeros((len(rows), d))
+    dv = np.zeros((len(rows), d))
     for i in reverse_lists(idx, cnt, b, kv, m):
         _, cols, dkc, dvc, _ = bwd_gather_block(q, k, v, do, idx, cnt, log_gate, b, kv, i, scale,
-                                                gate)
+                                                gate, geom)
         sel = np.isin(cols, rows)
-        pos = cols[sel] - m * BLOCK
+        pos = cols[sel] - (int(rows[0]) if len(rows) else 0)
         np.add.at(dk, pos, dkc[sel])
         np.add.at(dv, pos, dvc[sel])
     return dk, dv
@@ -507,16 +605,17 @@ def bwd_kv_block(q, k, v, do, idx, cnt, log_gate, b: int, kv: int, m: int, scale
 
 # ============================================================== full pipeline
 def sas_forward_backward(q, k, v, do, s, topk: int, scale=None, mode: str = "gather",
-                         gate: str = "softmax"):
-    """select -> forward -> backward -> ds, everything float64.
+                         gate: str = "softmax", geom=None):
+    """select -> forward -> backward -> ds, everything float64 (blocks of the
+    geometry ``geom`` when given).
     Returns a dict with idx, cnt, log_gate, s_lse, o, lse, dq, dk, dv, dlg, ds."""
     idx, cnt, lg, s_lse = select(s, topk, gate)
     if mode == "dense":
-        o, lse = fwd_dense(q, k, v, idx, cnt, lg, scale, gate)
-        dq, dk, dv, dlg = bwd_dense(q, k, v, do, idx, cnt, lg, scale, gate)
+        o, lse = fwd_dense(q, k, v, idx, cnt, lg, scale, gate, geom)
+        dq, dk, dv, dlg = bwd_dense(q, k, v, do, idx, cnt, lg, scale, gate, geom)
     else:
-        o, lse = fwd_gather(q, k, v, idx, cnt, lg, scale, gate=gate)
-        dq, dk, dv, dlg = bwd_gather(q, k, v, do, idx, cnt, lg, scale, gate=gate)
+        o, lse = fwd_gather(q, k, v, idx, cnt, lg, scale, gate=gate, geom=geom)
+        dq, dk, dv, dlg = bwd_gather(q, k, v, do, idx, cnt, lg, scale, gate=gate, geom=geom)
     ds = gate_jacobian(s, s_lse, idx, cnt, dlg, gate)
     return dict(idx=idx, cnt=cnt, log_gate=lg, s_lse=s_lse, o=o, lse=lse,
                 dq=dq, dk=dk, dv=dv, dlg=dlg, ds=ds)
@@ -570,8 +669,13 @@ def decode(q, k_cache, v_cache, seq_lens, s, topk: int, scale=None, rows=None,
 
 
 # ============================================================== work counts
-def selected_pairs(cnt):
+def selected_pairs(cnt, geom=None):
     """Valid (query, key) pairs per query head, summed over (b, kv, i):
-    64*64 per selected block plus 64*65/2 for the causal current block."""
+    64*64 per selected block plus 64*65/2 for the causal current block (with
+    a geometry: rows x kept-block length, plus L(L+1)/2 for a current block of
+    L tokens; kept blocks are whole blocks of 64)."""
     cnt = np.asarray(cnt, dtype=np.int64)
-    return int(cnt.sum()) * BLOCK * BLOCK + cnt.size * (BLOCK * (BLOCK + 1) // 2)
+    if geom is None:
+        return int(cnt.sum()) * BLOCK * BLOCK + cnt.size * (BLOCK * (BLOCK + 1) // 2)
+    L = np.asarray(geom)[..., 1].astype(np.int64)[:, None, :]      # [B, 1, NB]
+    return int(np.sum(cnt * L * BLOCK + L * (L + 1) // 2))
