@@ -49,11 +49,17 @@ def parse():
     return p.parse_args()
 
 
-def pair_count(cnt_np, G):
-    """Valid (query, key) pairs summed over query heads."""
+def pair_count(cnt_np, G, lens=None):
+    """Valid (query, key) pairs summed over query heads: 64 rows x 64 keys per
+    kept block and the causal 64*65/2 of the current block; with a block table
+    (lens [B, nb] tokens per block) L rows x 64 keys per kept block and
+    L(L+1)/2 for a current block of L tokens."""
     import numpy as np
     c = cnt_np.astype(np.int64)
-    return G * (int(c.sum()) * 64 * 64 + c.size * (64 * 65 // 2))
+    if lens is None:
+        return G * (int(c.sum()) * 64 * 64 + c.size * (64 * 65 // 2))
+    L = np.asarray(lens, dtype=np.int64)[:, None, :]
+    return G * int(np.sum(c * L * 64 + L * (L + 1) // 2))
 
 
 def timed(torch, step, steps):
@@ -94,8 +100,13 @@ def run_training(args, api, si, torch, np, w=None, steps=None, warmup=None, gate
     qd, kd, vd, dod = dev(q), dev(k), dev(v), dev(do)
     host = dict(q=q, k=k, v=v, do=do)
     del q, k, v, do
-    sh = api.make_shape(w.B, w.Hq, w.Hkv, w.n, w.d, w.topk, dt, gate=gate)
-    nb = w.nqb
+    blocks = lens = None
+    if w.varlen:   # packed documents of any length: the block table
+        blocks_h, df_h = api.blocks_from_cu_seqlens(
+            [si.cu_seqlens_of(si.doc_token_lens(w, b)) for b in range(w.B)])
+        blocks, lens = blocks_h.cuda(), blocks_h[..., 1].numpy()
+    sh = api.make_shape(w.B, w.Hq, w.Hkv, w.n, w.d, w.topk, dt, gate=gate, blocks=blocks)
+    nb = api.nblocks(sh)
     pool = w.s_kind == "pool"
     s = torch.empty((w.B, w.Hkv, nb, nb), dtype=torch.float32, device="cuda")
     if not pool:
@@ -108,6 +119,8 @@ def run_training(args, api, si, torch, np, w=None, steps=None, warmup=None, gate
     ws_bwd = api.alloc_workspace(api.sas_bwd_workspace_bytes(sh))
     df = si.make_doc_first(w)
     doc_first = torch.from_numpy(df).cuda() if df is not None else None
+    if w.varlen:
+        doc_first = df_h.cuda()
 
     def step():
         if pool:
@@ -126,7 +139,7 @@ def run_training(args, api, si, torch, np, w=None, steps=None, warmup=None, gate
 
     cnt = sel["cnt"].cpu().numpy()
     G = w.Hq // w.Hkv
-    pairs = pair_count(cnt, G)
+    pairs = pair_count(cnt, G, lens)
     flop_fwd = 4 * w.d * pairs
     flop_bwd = 10 * w.d * pairs
     return dict(w=w, ms_step=ms_step, ms_prof=ms_prof, wall=wall, pairs=pairs, flop_fwd=flop_fwd,
@@ -181,15 +194,19 @@ def run_gate_variants(args, api, si, torch, np):
 
 
 def run_packed(args, api, si, torch, np):
-    """The 32K layer holding packed documents of mixed lengths (workload 7):
-    document mask + select + fwd + bwd.  Rows near a document's start keep
-    fewer blocks, and the effective work counts only the pairs kept."""
+    """The 32K layer holding packed documents of any token length (workload 7):
+    each document cut into 64-token blocks from its own first token through the
+    block table; document mask + select + fwd + bwd.  Rows near a document's
+    start keep fewer blocks, and the effective work counts only the pairs
+    kept."""
     w = si.WORKLOADS[7]
     res = run_training(args, api, si, torch, np, w=w, steps=max(1, args.steps // 4), warmup=1)
     total = res["flop_fwd"] + res["flop_bwd"]
     tf = total / (res["ms_step"] * 1e-3) / 1e12
-    docs = [len(si.packed_doc_blocks(w.cfg, b, w.nqb)) for b in range(w.B)]
-    out = {"workload": w.name, "documents": docs, "steps": res["steps"],
+    lens = [si.doc_token_lens(w, b) for b in range(w.B)]
+    docs = [len(x) for x in lens]
+    out = {"workload": w.name, "documents": docs, "document_tokens": lens,
+           "blocks": w.nqb, "steps": res["steps"],
            "ms_per_step": round(res["ms_step"], 3), "TFLOPs": round(tf, 1),
            "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4), "pairs": res["pairs"],
            "per_kernel_ms": {k: round(v["avg_ms"], 3) for k, v in res["per_kernel"].items()}}

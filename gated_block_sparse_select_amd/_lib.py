@@ -16,13 +16,13 @@ SAS_F32, SAS_BF16 = 0, 1
 SAS_GATE_SOFTMAX, SAS_GATE_SIGMOID, SAS_GATE_HARD, SAS_GATE_EXTERNAL = range(4)
 GATES = {"softmax": SAS_GATE_SOFTMAX, "sigmoid": SAS_GATE_SIGMOID, "hard": SAS_GATE_HARD,
          "external": SAS_GATE_EXTERNAL}
-ABI_VERSION = 2
+ABI_VERSION = 3
 NOALLOC_SCRATCH_BYTES = 16 << 20   # SAS_NOALLOC_SCRATCH_BYTES
 BLOCK = 64
 
 EXPORTED = [
     "sas_abi_version", "sas_status_string", "sas_pool_workspace_bytes", "sas_pool_scores",
-    "sas_select", "sas_mask_documents", "sas_fwd", "sas_bwd_workspace_bytes", "sas_bwd",
+    "sas_select", "sas_mask_documents", "sas_blocks_from_cu_seqlens", "sas_fwd", "sas_bwd_workspace_bytes", "sas_bwd",
     "sas_decode_workspace_bytes", "sas_decode", "sas_decode_noalloc",
     "sas_decode_paged_workspace_bytes",
     "sas_decode_paged", "sas_prof_enable", "sas_prof_collect",
@@ -33,7 +33,8 @@ EXPORTED = [
 class SasShape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
                 ("n", ctypes.c_int32), ("d", ctypes.c_int32), ("topk", ctypes.c_int32),
-                ("scale", ctypes.c_float), ("dtype", ctypes.c_int32), ("gate", ctypes.c_int32)]
+                ("scale", ctypes.c_float), ("dtype", ctypes.c_int32), ("gate", ctypes.c_int32),
+                ("nb", ctypes.c_int32), ("blocks", ctypes.c_void_p)]
 
 
 class SasDecodeShape(ctypes.Structure):
@@ -86,6 +87,9 @@ def lib() -> ctypes.CDLL:
         L.sas_select.argtypes = [sp, vp, vp, vp, vp, vp, st]
         L.sas_mask_documents.restype = i32
         L.sas_mask_documents.argtypes = [sp, vp, vp, st]
+        ip = ctypes.POINTER(ctypes.c_int32)
+        L.sas_blocks_from_cu_seqlens.restype = i32
+        L.sas_blocks_from_cu_seqlens.argtypes = [ip, i32, ip, ip, i32]
         L.sas_fwd.restype = i32
         L.sas_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, st]
         L.sas_bwd_workspace_bytes.restype = sz

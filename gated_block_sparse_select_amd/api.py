@@ -58,8 +58,25 @@ def _gate(gate) -> int:
     return int(gate)
 
 
-def make_shape(B, Hq, Hkv, n, d, topk, dtype=torch.bfloat16, scale=0.0, gate="softmax") -> SasShape:
-    return SasShape(B, Hq, Hkv, n, d, topk, float(scale), _DT[dtype], _gate(gate))
+def make_shape(B, Hq, Hkv, n, d, topk, dtype=torch.bfloat16, scale=0.0, gate="softmax",
+               blocks=None) -> SasShape:
+    """Training shape.  blocks: None (blocks of 64 tokens, n % 64 == 0) or a
+    device int32 tensor [B, nb, 2] of (first token, length) per block, as
+    ``blocks_from_cu_seqlens`` builds for packed documents of any length."""
+    if blocks is None:
+        return SasShape(B, Hq, Hkv, n, d, topk, float(scale), _DT[dtype], _gate(gate), 0, None)
+    _check(blocks, "blocks", torch.int32)
+    if blocks.dim() != 3 or blocks.shape[0] != B or blocks.shape[2] != 2:
+        raise ValueError("blocks must be [B, nb, 2]")
+    sh = SasShape(B, Hq, Hkv, n, d, topk, float(scale), _DT[dtype], _gate(gate),
+                  int(blocks.shape[1]), blocks.data_ptr())
+    sh._blocks_ref = blocks      # keep the table alive as long as the shape
+    return sh
+
+
+def nblocks(shape: SasShape) -> int:
+    """Blocks per batch entry: the table's nb, or n/64 without a table."""
+    return int(shape.nb) if shape.blocks else shape.n // BLOCK
 
 
 def make_decode_shape(B, Hq, Hkv, cap, d, topk, dtype=torch.bfloat16, scale=0.0,
@@ -90,7 +107,7 @@ def sas_pool_workspace_bytes(shape: SasShape) -> int:
 
 def sas_pool_scores(shape: SasShape, q, k, s, ws, stream=None):
     dt = _dt(shape)
-    nb = shape.n // BLOCK
+    nb = nblocks(shape)
     _check(q, "q", dt, shape.B * shape.Hq * shape.n * shape.d)
     _check(k, "k", dt, shape.B * shape.Hkv * shape.n * shape.d)
     _check(s, "s", torch.float32, shape.B * shape.Hkv * nb * nb)
@@ -100,7 +117,7 @@ def sas_pool_scores(shape: SasShape, q, k, s, ws, stream=None):
 
 
 def sas_select(shape: SasShape, s, idx, cnt, log_gate, s_lse, stream=None):
-    nb = shape.n // BLOCK
+    nb = nblocks(shape)
     rows = shape.B * shape.Hkv * nb
     _check(s, "s", torch.float32, rows * nb)
     _check(idx, "idx", torch.int32, rows * shape.topk)
@@ -112,17 +129,49 @@ def sas_select(shape: SasShape, s, idx, cnt, log_gate, s_lse, stream=None):
 
 
 def sas_mask_documents(shape: SasShape, doc_first, s, stream=None):
-    nb = shape.n // BLOCK
+    nb = nblocks(shape)
     _check(doc_first, "doc_first", torch.int32, shape.B * nb)
     _check(s, "s", torch.float32, shape.B * shape.Hkv * nb * nb)
     _ok(lib().sas_mask_documents(ctypes.byref(shape), _ptr(doc_first), _ptr(s), _stream(stream)),
         "sas_mask_documents")
 
 
+def blocks_from_cu_seqlens(cu_seqlens):
+    """Block table and doc_first of packed documents of any length (host int32
+    tensors [B, nb, 2] and [B, nb]) from per-entry document offsets:
+    cu_seqlens[b] is a nondecreasing list starting at 0; document j of entry b
+    holds tokens [cu[j], cu[j+1]).  Each document is cut into 64-token blocks
+    from its own first token (the library's sas_blocks_from_cu_seqlens);
+    entries with fewer blocks are padded with empty blocks."""
+    per = []
+    for b, offs in enumerate(cu_seqlens):
+        cu = (ctypes.c_int32 * len(offs))(*[int(x) for x in offs])
+        cap = sum(max(0, (int(y) - int(x) + BLOCK - 1) // BLOCK) for x, y in zip(offs, offs[1:]))
+        blk = (ctypes.c_int32 * max(2 * cap, 2))()
+        first = (ctypes.c_int32 * max(cap, 1))()
+        nb = lib().sas_blocks_from_cu_seqlens(cu, len(offs) - 1, blk, first, cap)
+        if nb < 0 or len(offs) < 1:
+            raise ValueError(f"cu_seqlens[{b}] must start at 0 and be nondecreasing")
+        per.append((list(blk)[:2 * nb], list(first)[:nb], int(offs[-1])))
+    NB = max(1, max(len(f) for _, f, _ in per))
+    blocks = torch.empty((len(per), NB, 2), dtype=torch.int32)
+    doc_first = torch.empty((len(per), NB), dtype=torch.int32)
+    for b, (blk, first, end) in enumerate(per):
+        nb = len(first)
+        blocks[b, :nb] = torch.tensor(blk, dtype=torch.int32).view(nb, 2)
+        blocks[b, nb:, 0] = end
+        blocks[b, nb:, 1] = 0
+        doc_first[b, :nb] = torch.tensor(first, dtype=torch.int32)
+        doc_first[b, nb:] = torch.arange(nb, NB, dtype=torch.int32)
+    return blocks, doc_first
+
+
 def doc_first_from_cu_seqlens(cu_seqlens, n: int):
     """doc_first [len(cu_seqlens), n/64] int32 (host) from per-entry document
-    token offsets: cu_seqlens[b] is a nondecreasing list starting at 0 whose
-    entries are multiples of 64 and at most n (the last document runs to n)."""
+    token offsets when every document starts on a multiple of 64 (the layout
+    without a block table): cu_seqlens[b] is a nondecreasing list starting at 0
+    whose entries are multiples of 64 and at most n (the last document runs to
+    n).  For documents of any length use ``blocks_from_cu_seqlens``."""
     if n % BLOCK:
         raise ValueError("n must be a multiple of 64")
     nb = n // BLOCK
@@ -144,7 +193,7 @@ def doc_first_from_cu_seqlens(cu_seqlens, n: int):
 
 def sas_fwd(shape: SasShape, q, k, v, idx, cnt, log_gate, o, lse, stream=None):
     dt = _dt(shape)
-    nb = shape.n // BLOCK
+    nb = nblocks(shape)
     rows = shape.B * shape.Hkv * nb
     _check(q, "q", dt, shape.B * shape.Hq * shape.n * shape.d)
     _check(k, "k", dt, shape.B * shape.Hkv * shape.n * shape.d)
@@ -165,7 +214,7 @@ def sas_bwd_workspace_bytes(shape: SasShape) -> int:
 def sas_bwd(shape: SasShape, q, k, v, o, dO, lse, idx, cnt, log_gate, s, s_lse, dq, dk, dv, ds,
             ws, stream=None):
     dt = _dt(shape)
-    nb = shape.n // BLOCK
+    nb = nblocks(shape)
     rows = shape.B * shape.Hkv * nb
     nq = shape.B * shape.Hq * shape.n * shape.d
     nk = shape.B * shape.Hkv * shape.n * shape.d
@@ -260,7 +309,7 @@ def sas_prof_collect(max_entries: int = 64):
 
 # ------------------------------------------------------------------ allocation helpers
 def alloc_select(shape: SasShape, device="cuda"):
-    nb = shape.n // BLOCK
+    nb = nblocks(shape)
     lead = (shape.B, shape.Hkv, nb)
     return dict(idx=torch.empty(lead + (shape.topk,), dtype=torch.int32, device=device),
                 cnt=torch.empty(lead, dtype=torch.int32, device=device),
@@ -275,7 +324,7 @@ def alloc_workspace(nbytes: int, device="cuda"):
 __all__ = [
     "make_shape", "make_decode_shape", "make_decode_paged_shape", "shape_of",
     "sas_pool_workspace_bytes", "sas_pool_scores", "sas_select", "sas_mask_documents",
-    "doc_first_from_cu_seqlens", "sas_fwd",
+    "doc_first_from_cu_seqlens", "blocks_from_cu_seqlens", "nblocks", "sas_fwd",
     "sas_bwd_workspace_bytes", "sas_bwd", "sas_decode_workspace_bytes", "sas_decode",
     "sas_decode_noalloc", "sas_decode_paged_workspace_bytes", "sas_decode_paged", "sas_prof_enable", "sas_prof_collect",
     "alloc_select", "alloc_workspace", "status_string", "SasError", "SasShape", "SasDecodeShape",

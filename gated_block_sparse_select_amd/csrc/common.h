@@ -36,6 +36,26 @@ struct ElemBF16 {
 // (softmax weights below 2^-126 flush to zero, which is harmless).
 SAS_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ------------------------------------------------------------- block geometry
+// Block i of batch entry b holds the token rows [w + lo, w + hi) inside the
+// 64-row window [w, w + 64) that the kernels load.  Without a table
+// (geo == nullptr) block i is rows [64 i, 64 i + 64).  With a table (first
+// token, length per block, packed documents) the window starts at the
+// block's first token, or at n - 64 for a short last block near the end of
+// the tensors; entries are clamped so that the window stays inside [0, n)
+// whatever the table holds (n >= 64).
+struct BlockGeo {
+  int w, lo, hi;
+};
+SAS_DEV BlockGeo block_geo(const int32_t* __restrict__ geo, int b, int nb, int n, int i) {
+  if (geo == nullptr) return BlockGeo{i * SAS_BLK, 0, SAS_BLK};
+  const int2 e = reinterpret_cast<const int2*>(geo)[size_t(b) * nb + i];
+  const int len = min(max(e.y, 0), SAS_BLK);
+  const int st = min(max(e.x, 0), n - len);
+  const int w = min(st, n - SAS_BLK);
+  return BlockGeo{w, st - w, st - w + len};
+}
+
 // ------------------------------------------------------------- wave64 reductions
 SAS_DEV float wave_max(float v) {
 #pragma unroll

@@ -29,9 +29,12 @@ hipError_t launch_select(const float* s, int32_t* idx, int32_t* cnt, float* log_
                          float* s_lse, int rows, int nqb, int nkb, int topk,
                          const int32_t* seq_lens, int hkv, int cap, int gate, hipStream_t st);
 
+// Block tables: geo is nullptr (block i = rows [64 i, 64 i + 64), nb = n/64)
+// or a device int32 [B, nb, 2] table of (first token, length), see block_geo.
+
 // ---- pooling (pool.hip); ws holds qbar and kbar (float32 [B*Hkv*nb*d] each)
 hipError_t launch_pool(int dtype, const void* q, const void* k, float* s, float* ws, int B,
-                       int Hq, int Hkv, int n, int d, hipStream_t st);
+                       int Hq, int Hkv, int n, int d, const int32_t* geo, int nb, hipStream_t st);
 
 // ---- reverse (per key block) lists (revidx.hip)
 // rev_off [B*Hkv][nkb+1] (offsets into that pair's rev_list segment of
@@ -43,14 +46,14 @@ hipError_t launch_revidx(const int32_t* idx, const int32_t* cnt, int32_t* rev_of
 hipError_t launch_fwd_simt(int dtype, const void* q, const void* k, const void* v,
                            const int32_t* idx, const int32_t* cnt, const float* lg, void* o,
                            float* lse, int B, int Hq, int Hkv, int n, int d, int topk,
-                           float tau, int gate, hipStream_t st);
+                           float tau, int gate, const int32_t* geo, int nb, hipStream_t st);
 hipError_t launch_bwd_simt(int dtype, const void* q, const void* k, const void* v,
                            const void* o, const void* dO, const float* lse, const int32_t* idx,
                            const int32_t* cnt, const float* lg, const float* s,
                            const float* s_lse, void* dq, void* dk, void* dv, float* ds,
                            float* Dws, const int32_t* rev_off, const int32_t* rev_list, int B,
                            int Hq, int Hkv, int n, int d, int topk, float tau, int gate,
-                           hipStream_t st);
+                           const int32_t* geo, int nb, hipStream_t st);
 
 // ---- decode (decode.hip)
 int decode_nsplit(int B, int Hkv, int topk);

@@ -26,6 +26,12 @@
 // The split recomputes S and dP in both passes (7 tile products instead of 5)
 // in exchange for no atomics and no per-pair partial buffers.
 //
+// Block tables (packed documents of any length, block_geo): a block is a
+// 64-row window whose rows [lo, hi) are its own tokens.  The dq kernel
+// zeroes dZ on the other rows of a q-block's window and gives them the
+// statistics (-inf, 0), so the key-outer kernel's weights there are 0; only
+// a block's own rows (dq) and keys (dk, dv) are stored.
+//
 // EXT, the external gate (g scales block m's values after an unbiased
 // softmax): with P_b = g P, the weight the forward's PV product used,
 //   dV = sum_h P_b^T dO_h,  dZ = P (g dP - D) = P_b (dP - D/g),
@@ -50,7 +56,7 @@ __global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
     const float* __restrict__ lg, uint16_t* __restrict__ dq, float* __restrict__ stats,
     float* __restrict__ dlgp, int Hq, int Hkv, int n, int topk, float tau, float tau2, int BH,
-    int h_off, int hchunks, int nch, int chunk0) {
+    int h_off, int hchunks, int nch, int chunk0, const int32_t* __restrict__ geo, int nqb) {
   constexpr int NS = kDqStages;
   constexpr int ROWB = D * 2;
   constexpr int TB = 64 * ROWB;
@@ -60,7 +66,6 @@ __global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
   constexpr int TK = 200, TV = 201;       // LDS buffer tags: K tiles, V tiles
   __shared__ float part[2][8];            // per-wave dZ sums of the last two tiles
 
-  const int nqb = n / SAS_BLK;
   const int G = Hq / Hkv;
   int bid = blockIdx.x;
   const int hc = bid % hchunks;
@@ -68,11 +73,14 @@ __global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
   const int bk = bid % BH;
   const int i = nqb - 1 - bid / BH;
   const int b = bk / Hkv, kv = bk % Hkv;
+  const BlockGeo gi = block_geo(geo, b, nqb, n, i);
+  if (gi.hi == gi.lo) return;   // a padding block holds no token (uniform exit)
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 31, hh = lane >> 5;
   const int h = kv * G + h_off + hc * GC + (wave >> 1);
   const int rt = wave & 1;
+  const bool row_ok = rt * 32 + lr >= gi.lo && rt * 32 + lr < gi.hi;
   const int chunk = chunk0 + hc;
   const size_t rowsel = size_t(bk) * nqb + i;
   const int c_sel = cnt[rowsel];
@@ -80,7 +88,7 @@ __global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
   const int32_t* irow = idx + rowsel * topk;
   const float* grow = lg + rowsel * topk;
 
-  const size_t qrow = (size_t(b) * Hq + h) * n + size_t(i) * SAS_BLK + rt * 32 + lr;
+  const size_t qrow = (size_t(b) * Hq + h) * n + size_t(gi.w) + rt * 32 + lr;
   bf16x8 qop[D / 16], dop[D / 16];
   float dpart = 0.f;
 #pragma unroll
@@ -92,13 +100,17 @@ __global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) dpart += float(dop[c][e]) * float(oo[e]);
   }
-  const float Drow = dpart + __shfl_xor(dpart, 32);
-  const float lse2 = lse[qrow] * kLog2e;
+  // rows of the window outside the block: o and lse there belong to other
+  // blocks (or to no block), so their D and lse are replaced by 0
+  const float Drow = row_ok ? dpart + __shfl_xor(dpart, 32) : 0.f;
+  const float lse_r = row_ok ? lse[qrow] : 0.f;
+  const float lse2 = lse_r * kLog2e;
   if (hh == 0) {
     // per-row statistics of this (head, q-block) for the key-block-outer pass:
-    // [-lse / tau for the 64 rows | -D for the 64 rows]
+    // [-lse / tau for the 64 rows | -D for the 64 rows]; (-inf, 0) outside the
+    // block, so the weights there are 0
     float* st = stats + ((size_t(b) * Hq + h) * nqb + i) * 128;
-    st[rt * 32 + lr] = -lse[qrow] / tau;
+    st[rt * 32 + lr] = row_ok ? -lse_r / tau : -INFINITY;
     st[64 + rt * 32 + lr] = -Drow;
   }
 
@@ -110,8 +122,9 @@ __global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
   uint32_t pat[4];
   dma_lane_pattern<D>(lane, slice0, pat);
   auto issue = [&]<int BUF>(int t) __attribute__((always_inline)) {
-    const int blk = t < c_sel ? irow[t] : i;
-    const uint16_t* src = (k_side ? k : v) + (kv0 + size_t(blk) * SAS_BLK) * D;
+    const int w0 = t < c_sel ? (geo ? block_geo(geo, b, nqb, n, irow[t]).w : irow[t] * SAS_BLK)
+                             : gi.w;
+    const uint16_t* src = (k_side ? k : v) + (kv0 + size_t(w0)) * D;
     dma_slices<JW>(src, k_side ? stage_buf<TK, BUF, TB>() : stage_buf<TV, BUF, TB>(), slice0, pat);
   };
   issue.template operator()<0>(0);
@@ -169,12 +182,13 @@ __global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
         for (int e = 0; e < 8; ++e) {
           const int j = 8 * jc + e;
           float p = fast_exp2(__builtin_fmaf(S[j], tau2, zoff));
-          if (CUR && kt * 32 + 8 * (j >> 2) + 4 * hh + (j & 3) > rt * 32 + lr) p = 0.f;
+          const int key = kt * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
+          if (CUR && (key > rt * 32 + lr || key < gi.lo)) p = 0.f;
           if constexpr (EXT) {
-            x[e] = p * (P2[j] - Dg);
-            if (!CUR) zs = __builtin_fmaf(p, P2[j], zs);
+            x[e] = row_ok ? p * (P2[j] - Dg) : 0.f;
+            if (!CUR && row_ok) zs = __builtin_fmaf(p, P2[j], zs);
           } else {
-            x[e] = p * P2[j];
+            x[e] = row_ok ? p * P2[j] : 0.f;
           }
         }
         dZp[kt * 2 + jc] = pack_bf16x8(x);
@@ -222,6 +236,7 @@ __global__ void __launch_bounds__(128 * GC) bwd_dq_kernel(
     ((c_sel % NS == S ? tile.template operator()<S, true>(c_sel) : void()), ...);
   }(std::make_integer_sequence<int, NS>{});
 
+  if (!row_ok) return;   // a window row of another block (no barrier follows)
   uint16_t* drow = dq + qrow * D;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
@@ -303,7 +318,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
     const float* __restrict__ stats, const float* __restrict__ lg,
     const int32_t* __restrict__ rev_off, const int32_t* __restrict__ rev_list,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int Hq, int Hkv, int n, int topk,
-    float tau, float tau2) {
+    float tau, float tau2, const int32_t* __restrict__ geo, int nkb) {
   constexpr int NS = kKvStages;
   static_assert(NS == 4, "stage arithmetic below assumes a 4-stage ring");
   constexpr int ROWB = D * 2;
@@ -314,7 +329,6 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
   constexpr int PER = JW + 1;           // plus the row statistics
   constexpr int TQ = 300, TO = 301, TS = 302;   // LDS buffer tags
 
-  const int nkb = n / SAS_BLK;
   const int G = Hq / Hkv;
   // key-block-major grid: consecutive workgroups take the same key block of
   // consecutive (batch, kv-head) pairs.  Workgroups are dealt round-robin to
@@ -326,12 +340,14 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
   const int m = blockIdx.x / BH;
   const int bk = blockIdx.x % BH;
   const int b = bk / Hkv, kv = bk % Hkv;
+  const BlockGeo gm = block_geo(geo, b, nkb, n, m);
+  if (gm.hi == gm.lo) return;   // a padding block holds no token (uniform exit)
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lr = lane & 31, hh = lane >> 5;
   const int kh = wave & 1, rh = wave >> 1;
 
-  const size_t kvrow0 = (size_t(b) * Hkv + kv) * n + size_t(m) * SAS_BLK;
+  const size_t kvrow0 = (size_t(b) * Hkv + kv) * n + size_t(gm.w);
   const size_t krow = kvrow0 + kh * 32 + lr;
   bf16x8 kop[D / 16], vop[D / 16];
 #pragma unroll
@@ -349,8 +365,9 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
       dV[dt][j] = 0.f;
     }
 
-  // list entries of this key block -> LDS: q-block and base-2 log-gate
-  // (0 for the own block, entry 0)
+  // list entries of this key block -> LDS: q-block | (first row of its
+  // window << 11) and base-2 log-gate (0 for the own block, entry 0); the
+  // window row is below 2^17 and the q-block below 2^11
   __shared__ int2 meta[SAS_MAX_BLOCKS];
   const int32_t* lst = rev_list + size_t(bk) * nkb * (topk + 1);
   const int32_t e0 = rev_off[size_t(bk) * (nkb + 1) + m];
@@ -360,7 +377,8 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
     const int iq = ent & 0xFFFF, slot = (ent >> 16) & 0xFFFF;
     const float l = slot == 0xFFFF ? 0.f : lg[(size_t(bk) * nkb + iq) * topk + slot];
     const float b2 = (EXT ? fmaxf(l, kMinExtLogGate) : l) * kLog2e;
-    meta[e] = make_int2(iq, __float_as_int(b2));
+    const int wq = geo ? block_geo(geo, b, nkb, n, iq).w : iq * SAS_BLK;
+    meta[e] = make_int2(iq | (wq << 11), __float_as_int(b2));
   }
   __syncthreads();
   const int nsteps = (e1 - e0) * G;
@@ -381,8 +399,9 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
   uint32_t pat[4];
   dma_lane_pattern<D>(lane, slice0, pat);
   auto issue = [&]<int BUF>() __attribute__((always_inline)) {
-    const int iq = __builtin_amdgcn_readfirstlane(meta[ie].x);
-    const char* tile = src_base + size_t(ih) * hstride + size_t(iq) * SAS_BLK * D * 2;
+    const int ent = __builtin_amdgcn_readfirstlane(meta[ie].x);
+    const int iq = ent & 2047;
+    const char* tile = src_base + size_t(ih) * hstride + size_t(ent >> 11) * ROWB;
     dma_slices<JW>(tile, q_side ? stage_buf<TQ, BUF, TB>() : stage_buf<TO, BUF, TB>(), slice0, pat);
     __builtin_amdgcn_global_load_lds(
         (glb_void*)(uniform_ptr(st_base + (size_t(ih) * nkb + iq) * 128) + opaque(st_lane)),
@@ -610,6 +629,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
     const float sc = pass == 0 ? 1.f : tau;
     for (int c = tid; c < 64 * CPR; c += 256) {
       const int key = c / CPR;
+      if (key < gm.lo || key >= gm.hi) continue;   // a window row of another block
       const __attribute__((address_space(3))) float* src = red[key >> 5] + (key & 31) * D + (c % CPR) * 8;
       bf16x8 r;
 #pragma unroll
@@ -626,10 +646,10 @@ static void dq_launch(int nblocks, const void* q, const void* k, const void* v, 
                       const void* dO, const float* lse, const int32_t* idx, const int32_t* cnt,
                       const float* lg, void* dq, float* stats, float* dlgp, int Hq, int Hkv, int n,
                       int topk, float tau, float tau2, int BH, int h_off, int hchunks, int nch,
-                      int chunk0, bool ext, hipStream_t st) {
+                      int chunk0, bool ext, const int32_t* geo, int nqb, hipStream_t st) {
 #define SAS_DQ_KARGS (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o, \
     (const uint16_t*)dO, lse, idx, cnt, lg, (uint16_t*)dq, stats, dlgp, Hq, Hkv, n, topk, tau,   \
-    tau2, BH, h_off, hchunks, nch, chunk0
+    tau2, BH, h_off, hchunks, nch, chunk0, geo, nqb
   if (ext)
     hipLaunchKernelGGL((bwd_dq_kernel<D, GC, true>), dim3(nblocks), dim3(128 * GC), 0, st,
                        SAS_DQ_KARGS);
@@ -644,9 +664,10 @@ static void dq_dispatch(int gc, int nblocks, const void* q, const void* k, const
                         const void* o, const void* dO, const float* lse, const int32_t* idx,
                         const int32_t* cnt, const float* lg, void* dq, float* stats, float* dlgp,
                         int Hq, int Hkv, int n, int topk, float tau, float tau2, int BH, int h_off,
-                        int hchunks, int nch, int chunk0, bool ext, hipStream_t st) {
+                        int hchunks, int nch, int chunk0, bool ext, const int32_t* geo, int nqb,
+                        hipStream_t st) {
 #define SAS_DQ_ARGS nblocks, q, k, v, o, dO, lse, idx, cnt, lg, dq, stats, dlgp, Hq, Hkv, n, \
-                    topk, tau, tau2, BH, h_off, hchunks, nch, chunk0, ext, st
+                    topk, tau, tau2, BH, h_off, hchunks, nch, chunk0, ext, geo, nqb, st
   switch (gc) {
     case 1: dq_launch<D, 1>(SAS_DQ_ARGS); break;
     case 2: dq_launch<D, 2>(SAS_DQ_ARGS); break;
@@ -661,9 +682,9 @@ static int n_head_chunks(int G) {
   return nch;
 }
 
-size_t bwd_mfma_extra_ws(int B, int Hq, int Hkv, int n, int topk) {
+size_t bwd_mfma_extra_ws(int B, int Hq, int Hkv, int nb, int topk) {
   const int nch = n_head_chunks(Hq / Hkv);
-  return sizeof(float) * size_t(B) * Hkv * (n / SAS_BLK) * nch * size_t(topk > 0 ? topk : 1);
+  return sizeof(float) * size_t(B) * Hkv * nb * nch * size_t(topk > 0 ? topk : 1);
 }
 
 hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const void* o,
@@ -672,10 +693,9 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
                            const float* s_lse, void* dq, void* dk, void* dv, float* ds,
                            float* stats, const int32_t* rev_off, const int32_t* rev_list,
                            float* dlgp, int B, int Hq, int Hkv, int n, int d, int topk, float tau,
-                           int gate, hipStream_t st) {
+                           int gate, const int32_t* geo, int nqb, hipStream_t st) {
   const int G = Hq / Hkv;
   const bool ext = gate == SAS_GATE_EXTERNAL;
-  const int nqb = n / SAS_BLK;
   const int BH = B * Hkv;
   const float tau2 = tau * kLog2e;
   const int nch = n_head_chunks(G);
@@ -684,8 +704,8 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
     ProfScope ps("sas_bwd_dq_kernel", st);
     int chunk0 = 0;
     for (const HeadChunks& hc : head_chunks(G)) {
-      if (d == 128) dq_dispatch<128>(hc.gc, BH * nqb * hc.count, q, k, v, o, dO, lse, idx, cnt, lg, dq, stats, dlgp, Hq, Hkv, n, K, tau, tau2, BH, hc.h_off, hc.count, nch, chunk0, ext, st);
-      else dq_dispatch<64>(hc.gc, BH * nqb * hc.count, q, k, v, o, dO, lse, idx, cnt, lg, dq, stats, dlgp, Hq, Hkv, n, K, tau, tau2, BH, hc.h_off, hc.count, nch, chunk0, ext, st);
+      if (d == 128) dq_dispatch<128>(hc.gc, BH * nqb * hc.count, q, k, v, o, dO, lse, idx, cnt, lg, dq, stats, dlgp, Hq, Hkv, n, K, tau, tau2, BH, hc.h_off, hc.count, nch, chunk0, ext, geo, nqb, st);
+      else dq_dispatch<64>(hc.gc, BH * nqb * hc.count, q, k, v, o, dO, lse, idx, cnt, lg, dq, stats, dlgp, Hq, Hkv, n, K, tau, tau2, BH, hc.h_off, hc.count, nch, chunk0, ext, geo, nqb, st);
       chunk0 += hc.count;
     }
   }
@@ -702,7 +722,7 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
     ProfScope ps("sas_bwd_dkdv_kernel", st);
 #define SAS_KV_KARGS (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, \
     (const uint16_t*)dO, stats, lg, rev_off, rev_list, (uint16_t*)dk, (uint16_t*)dv, Hq, Hkv, n, \
-    topk, tau, tau2
+    topk, tau, tau2, geo, nqb
     if (d == 128 && ext)
       hipLaunchKernelGGL((bwd_dkdv_kernel<128, true>), dim3(BH * nqb), dim3(256), 0, st, SAS_KV_KARGS);
     else if (d == 128)

@@ -16,6 +16,12 @@
 // flight while the current one is computed.  Softmax runs in the exp2 domain.
 // Workgroups are issued largest q-block first (most tiles first).
 //
+// Block tables (packed documents of any length): each block is a 64-row
+// window of the token axis of which rows [lo, hi) are the block's own
+// tokens (block_geo).  Kept history blocks are whole blocks; on the current
+// block, key j is visible from row t iff lo <= j <= t; rows outside [lo, hi)
+// are computed but not stored.
+//
 // EXT (the external gate, g scales the values after an unbiased softmax):
 // the kernel is the same with the log-gate kept as the tile's exponent
 // offset, so the weights P g reach the PV product unchanged, and the tile's
@@ -36,7 +42,7 @@ __global__ void __launch_bounds__(128 * GC) fwd_mfma_kernel(
     const uint16_t* __restrict__ v, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ cnt, const float* __restrict__ lg, uint16_t* __restrict__ o,
     float* __restrict__ lse, int Hq, int Hkv, int n, int topk, float tau2, int BH, int h_off,
-    int hchunks) {
+    int hchunks, const int32_t* __restrict__ geo, int nqb) {
   // A one-head workgroup has only two waves: with two stages (64 KB of LDS at
   // d = 128 instead of 96 KB) two of them fit on a CU, so all four SIMDs work.
   constexpr int NS = GC == 1 ? 2 : kFwdStages;
@@ -47,7 +53,6 @@ __global__ void __launch_bounds__(128 * GC) fwd_mfma_kernel(
   static_assert((2 * JT) % (2 * GC) == 0 && JT % JW == 0, "slices must split evenly over the waves");
   constexpr int TK = 100, TV = 101;       // LDS buffer tags: K tiles, V tiles
 
-  const int nqb = n / SAS_BLK;
   const int G = Hq / Hkv;
   int bid = blockIdx.x;
   const int hc = bid % hchunks;
@@ -55,18 +60,21 @@ __global__ void __launch_bounds__(128 * GC) fwd_mfma_kernel(
   const int bk = bid % BH;
   const int i = nqb - 1 - bid / BH;
   const int b = bk / Hkv, kv = bk % Hkv;
+  const BlockGeo gi = block_geo(geo, b, nqb, n, i);
+  if (gi.hi == gi.lo) return;   // a padding block holds no token (uniform exit)
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 31, hh = lane >> 5;
   const int h = kv * G + h_off + hc * GC + (wave >> 1);
   const int rt = wave & 1;
+  const bool row_ok = rt * 32 + lr >= gi.lo && rt * 32 + lr < gi.hi;
   const size_t rowsel = size_t(bk) * nqb + i;
   const int c_sel = cnt[rowsel];
   const int ntiles = c_sel + 1;
   const int32_t* irow = idx + rowsel * topk;
   const float* grow = lg + rowsel * topk;
 
-  const size_t qrow = (size_t(b) * Hq + h) * n + size_t(i) * SAS_BLK + rt * 32 + lr;
+  const size_t qrow = (size_t(b) * Hq + h) * n + size_t(gi.w) + rt * 32 + lr;
   bf16x8 qop[D / 16];
 #pragma unroll
   for (int c = 0; c < D / 16; ++c)
@@ -82,8 +90,9 @@ __global__ void __launch_bounds__(128 * GC) fwd_mfma_kernel(
   uint32_t pat[4];
   dma_lane_pattern<D>(lane, slice0, pat);
   auto issue = [&]<int BUF>(int t) __attribute__((always_inline)) {
-    const int blk = t < c_sel ? irow[t] : i;
-    const uint16_t* src = (k_side ? k : v) + (kv0 + size_t(blk) * SAS_BLK) * D;
+    const int w0 = t < c_sel ? (geo ? block_geo(geo, b, nqb, n, irow[t]).w : irow[t] * SAS_BLK)
+                             : gi.w;
+    const uint16_t* src = (k_side ? k : v) + (kv0 + size_t(w0)) * D;
     dma_slices<JW>(src, k_side ? stage_buf<TK, BUF, TB>() : stage_buf<TV, BUF, TB>(), slice0, pat);
   };
   issue.template operator()<0>(0);
@@ -140,12 +149,14 @@ __global__ void __launch_bounds__(128 * GC) fwd_mfma_kernel(
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    if (CUR) {  // causal mask of the current block: key j visible iff j <= row
+    if (CUR) {  // causal mask of the current block: key j visible iff lo <= j <= row
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (kt * 32 + 8 * (j >> 2) + 4 * hh + (j & 3) > rt * 32 + lr) S[kt][j] = -INFINITY;
+        for (int j = 0; j < 16; ++j) {
+          const int key = kt * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
+          if (key > rt * 32 + lr || key < gi.lo) S[kt][j] = -INFINITY;
+        }
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -219,6 +230,7 @@ __global__ void __launch_bounds__(128 * GC) fwd_mfma_kernel(
   }(std::make_integer_sequence<int, NS>{});
 
   lrow += __shfl_xor(lrow, 32);
+  if (!row_ok) return;   // a window row of another block (no barrier follows)
   const float inv = 1.f / lrow;
   uint16_t* orow = o + qrow * D;
 #pragma unroll
@@ -239,43 +251,43 @@ template <int D, int GC>
 static void fwd_launch(int nblocks, const void* q, const void* k, const void* v,
                        const int32_t* idx, const int32_t* cnt, const float* lg, void* o, float* lse,
                        int Hq, int Hkv, int n, int topk, float tau2, int BH, int h_off,
-                       int hchunks, bool ext, hipStream_t st) {
+                       int hchunks, bool ext, const int32_t* geo, int nqb, hipStream_t st) {
   if (ext)
     hipLaunchKernelGGL((fwd_mfma_kernel<D, GC, true>), dim3(nblocks), dim3(128 * GC), 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, cnt, lg,
-                       (uint16_t*)o, lse, Hq, Hkv, n, topk, tau2, BH, h_off, hchunks);
+                       (uint16_t*)o, lse, Hq, Hkv, n, topk, tau2, BH, h_off, hchunks, geo, nqb);
   else
     hipLaunchKernelGGL((fwd_mfma_kernel<D, GC, false>), dim3(nblocks), dim3(128 * GC), 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, cnt, lg,
-                       (uint16_t*)o, lse, Hq, Hkv, n, topk, tau2, BH, h_off, hchunks);
+                       (uint16_t*)o, lse, Hq, Hkv, n, topk, tau2, BH, h_off, hchunks, geo, nqb);
 }
 
 template <int D>
 static void fwd_dispatch(int gc, int nblocks, const void* q, const void* k, const void* v,
                          const int32_t* idx, const int32_t* cnt, const float* lg, void* o,
                          float* lse, int Hq, int Hkv, int n, int topk, float tau2, int BH,
-                         int h_off, int hchunks, bool ext, hipStream_t st) {
+                         int h_off, int hchunks, bool ext, const int32_t* geo, int nqb,
+                         hipStream_t st) {
   switch (gc) {
-    case 1: fwd_launch<D, 1>(nblocks, q, k, v, idx, cnt, lg, o, lse, Hq, Hkv, n, topk, tau2, BH, h_off, hchunks, ext, st); break;
-    case 2: fwd_launch<D, 2>(nblocks, q, k, v, idx, cnt, lg, o, lse, Hq, Hkv, n, topk, tau2, BH, h_off, hchunks, ext, st); break;
-    default: fwd_launch<D, 4>(nblocks, q, k, v, idx, cnt, lg, o, lse, Hq, Hkv, n, topk, tau2, BH, h_off, hchunks, ext, st); break;
+    case 1: fwd_launch<D, 1>(nblocks, q, k, v, idx, cnt, lg, o, lse, Hq, Hkv, n, topk, tau2, BH, h_off, hchunks, ext, geo, nqb, st); break;
+    case 2: fwd_launch<D, 2>(nblocks, q, k, v, idx, cnt, lg, o, lse, Hq, Hkv, n, topk, tau2, BH, h_off, hchunks, ext, geo, nqb, st); break;
+    default: fwd_launch<D, 4>(nblocks, q, k, v, idx, cnt, lg, o, lse, Hq, Hkv, n, topk, tau2, BH, h_off, hchunks, ext, geo, nqb, st); break;
   }
 }
 
 hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, const int32_t* idx,
                            const int32_t* cnt, const float* lg, void* o, float* lse, int B,
                            int Hq, int Hkv, int n, int d, int topk, float tau, int gate,
-                           hipStream_t st) {
+                           const int32_t* geo, int nqb, hipStream_t st) {
   ProfScope ps("sas_fwd_mfma_kernel", st);
   const bool ext = gate == SAS_GATE_EXTERNAL;
   const int G = Hq / Hkv;
-  const int nqb = n / SAS_BLK;
   const int BH = B * Hkv;
   const float tau2 = tau * kLog2e;
   // heads in chunks of 4, then 2, then 1 (each launch covers hchunks chunks)
   for (const HeadChunks& hc : head_chunks(G)) {
-    if (d == 128) fwd_dispatch<128>(hc.gc, BH * nqb * hc.count, q, k, v, idx, cnt, lg, o, lse, Hq, Hkv, n, topk, tau2, BH, hc.h_off, hc.count, ext, st);
-    else fwd_dispatch<64>(hc.gc, BH * nqb * hc.count, q, k, v, idx, cnt, lg, o, lse, Hq, Hkv, n, topk, tau2, BH, hc.h_off, hc.count, ext, st);
+    if (d == 128) fwd_dispatch<128>(hc.gc, BH * nqb * hc.count, q, k, v, idx, cnt, lg, o, lse, Hq, Hkv, n, topk, tau2, BH, hc.h_off, hc.count, ext, geo, nqb, st);
+    else fwd_dispatch<64>(hc.gc, BH * nqb * hc.count, q, k, v, idx, cnt, lg, o, lse, Hq, Hkv, n, topk, tau2, BH, hc.h_off, hc.count, ext, geo, nqb, st);
   }
   return hipGetLastError();
 }

@@ -3,7 +3,8 @@
 // paper.oopus.info, §2.2 selector equation).
 //
 //   pass 1 (HBM-bound, one pass over q and k): qbar[b,kv,i,:] = mean of the
-//     64 rows x G heads of q-block i; kbar[b,kv,m,:] = mean of key block m.
+//     rows (64, or the block's own rows of a block table) x G heads of
+//     q-block i; kbar[b,kv,m,:] = mean of key block m; 0 for an empty block.
 //   pass 2 (small): s[b,kv,i,m] = qbar_i . kbar_m / sqrt(d) for all (i, m).
 #include "common.h"
 #include "launch.h"
@@ -39,21 +40,23 @@ __global__ void __launch_bounds__(256) pool_means_kernel(const typename E::T* __
                                                          const typename E::T* __restrict__ k,
                                                          float* __restrict__ qbar,
                                                          float* __restrict__ kbar, int Hq,
-                                                         int Hkv, int n) {
+                                                         int Hkv, int n,
+                                                         const int32_t* __restrict__ geo, int nb) {
   constexpr int CG = D / 8;        // column groups of 8
   constexpr int RG = 256 / CG;     // row groups
-  const int nb = n / SAS_BLK;
   const int G = Hq / Hkv;
   const int blk = blockIdx.x % nb;
   const int bk = blockIdx.x / nb;  // b*Hkv + kv
   const int b = bk / Hkv, kv = bk % Hkv;
   const int cg = threadIdx.x % CG, rg = threadIdx.x / CG;
+  const BlockGeo bg = block_geo(geo, b, nb, n, blk);
+  const int r0 = bg.w + bg.lo, nr = bg.hi - bg.lo;   // the block's own rows
 
   float aq[8] = {0, 0, 0, 0, 0, 0, 0, 0}, ak[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int g = 0; g < G; ++g) {
     const typename E::T* base =
-        q + ((size_t(b) * Hq + kv * G + g) * n + size_t(blk) * SAS_BLK) * D + cg * 8;
-    for (int r = rg; r < SAS_BLK; r += RG) {
+        q + ((size_t(b) * Hq + kv * G + g) * n + size_t(r0)) * D + cg * 8;
+    for (int r = rg; r < nr; r += RG) {
       float x[8];
       load8<E>(base + size_t(r) * D, x);
 #pragma unroll
@@ -61,8 +64,8 @@ __global__ void __launch_bounds__(256) pool_means_kernel(const typename E::T* __
     }
   }
   {
-    const typename E::T* base = k + ((size_t(b) * Hkv + kv) * n + size_t(blk) * SAS_BLK) * D + cg * 8;
-    for (int r = rg; r < SAS_BLK; r += RG) {
+    const typename E::T* base = k + ((size_t(b) * Hkv + kv) * n + size_t(r0)) * D + cg * 8;
+    for (int r = rg; r < nr; r += RG) {
       float x[8];
       load8<E>(base + size_t(r) * D, x);
 #pragma unroll
@@ -81,8 +84,9 @@ __global__ void __launch_bounds__(256) pool_means_kernel(const typename E::T* __
     float acc = 0.f;
     for (int r = 0; r < RG; ++r) acc += red[which][r][c];
     const size_t o = (size_t(bk) * nb + blk) * D + c;
-    if (which == 0) qbar[o] = acc * (1.0f / float(SAS_BLK * G));
-    else kbar[o] = acc * (1.0f / float(SAS_BLK));
+    const float rows = float(nr > 0 ? nr : 1);   // an empty block keeps the zero sum
+    if (which == 0) qbar[o] = acc * (1.0f / (rows * float(G)));
+    else kbar[o] = acc * (1.0f / rows);
   }
 }
 
@@ -120,8 +124,7 @@ __global__ void __launch_bounds__(256) pool_dot_kernel(const float* __restrict__
 }
 
 hipError_t launch_pool(int dtype, const void* q, const void* k, float* s, float* ws, int B,
-                       int Hq, int Hkv, int n, int d, hipStream_t st) {
-  const int nb = n / SAS_BLK;
+                       int Hq, int Hkv, int n, int d, const int32_t* geo, int nb, hipStream_t st) {
   float* qbar = ws;
   float* kbar = ws + size_t(B) * Hkv * nb * d;
   {
@@ -130,17 +133,17 @@ hipError_t launch_pool(int dtype, const void* q, const void* k, float* s, float*
     if (dtype == 1) {
       if (d == 128)
         hipLaunchKernelGGL((pool_means_kernel<ElemBF16, 128>), grid, dim3(256), 0, st,
-                           (const uint16_t*)q, (const uint16_t*)k, qbar, kbar, Hq, Hkv, n);
+                           (const uint16_t*)q, (const uint16_t*)k, qbar, kbar, Hq, Hkv, n, geo, nb);
       else
         hipLaunchKernelGGL((pool_means_kernel<ElemBF16, 64>), grid, dim3(256), 0, st,
-                           (const uint16_t*)q, (const uint16_t*)k, qbar, kbar, Hq, Hkv, n);
+                           (const uint16_t*)q, (const uint16_t*)k, qbar, kbar, Hq, Hkv, n, geo, nb);
     } else {
       if (d == 128)
         hipLaunchKernelGGL((pool_means_kernel<ElemF32, 128>), grid, dim3(256), 0, st,
-                           (const float*)q, (const float*)k, qbar, kbar, Hq, Hkv, n);
+                           (const float*)q, (const float*)k, qbar, kbar, Hq, Hkv, n, geo, nb);
       else
         hipLaunchKernelGGL((pool_means_kernel<ElemF32, 64>), grid, dim3(256), 0, st,
-                           (const float*)q, (const float*)k, qbar, kbar, Hq, Hkv, n);
+                           (const float*)q, (const float*)k, qbar, kbar, Hq, Hkv, n, geo, nb);
     }
   }
   hipError_t e = hipGetLastError();

@@ -3,6 +3,7 @@
 // synchronises; every launch goes to the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -17,15 +18,15 @@ namespace sas {
 hipError_t launch_fwd_mfma(const void* q, const void* k, const void* v, const int32_t* idx,
                            const int32_t* cnt, const float* lg, void* o, float* lse, int B,
                            int Hq, int Hkv, int n, int d, int topk, float tau, int gate,
-                           hipStream_t st);
+                           const int32_t* geo, int nb, hipStream_t st);
 hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const void* o,
                            const void* dO, const float* lse, const int32_t* idx,
                            const int32_t* cnt, const float* lg, const float* s,
                            const float* s_lse, void* dq, void* dk, void* dv, float* ds,
                            float* Dws, const int32_t* rev_off, const int32_t* rev_list,
                            float* dlgp, int B, int Hq, int Hkv, int n, int d, int topk, float tau,
-                           int gate, hipStream_t st);
-size_t bwd_mfma_extra_ws(int B, int Hq, int Hkv, int n, int topk);
+                           int gate, const int32_t* geo, int nb, hipStream_t st);
+size_t bwd_mfma_extra_ws(int B, int Hq, int Hkv, int nb, int topk);
 bool mfma_supported(int d, int G);
 }  // namespace sas
 
@@ -50,11 +51,24 @@ bool shape_ok_common(int B, int Hq, int Hkv, int len, int d, int topk, float sca
   return true;
 }
 
+// Blocks of a training shape: n/64 without a table, else the table's nb.
+int nblocks(const sas_shape* s) { return s->blocks ? s->nb : s->n / SAS_BLOCK; }
+
 sas_status check_shape(const sas_shape* s) {
   if (!s) return SAS_ERR_ARG;
   if (s->dtype != SAS_F32 && s->dtype != SAS_BF16) return SAS_ERR_DTYPE;
-  if (!shape_ok_common(s->B, s->Hq, s->Hkv, s->n, s->d, s->topk, s->scale, s->gate))
+  if (s->blocks == nullptr) {
+    if (s->nb != 0 && s->nb != s->n / SAS_BLOCK) return SAS_ERR_ARG;
+    if (!shape_ok_common(s->B, s->Hq, s->Hkv, s->n, s->d, s->topk, s->scale, s->gate))
+      return SAS_ERR_ARG;
+    return SAS_OK;
+  }
+  // a block table: the limits of a shape with nb blocks of 64, with n free (>= 64)
+  if (s->nb < 1 || s->nb > SAS_MAX_BLOCKS || s->n < SAS_BLOCK || s->n > SAS_BLOCK * SAS_MAX_BLOCKS)
     return SAS_ERR_ARG;
+  if (!shape_ok_common(s->B, s->Hq, s->Hkv, s->nb * SAS_BLOCK, s->d, s->topk, s->scale, s->gate))
+    return SAS_ERR_ARG;
+  if (int64_t(s->B) * s->Hq * s->n > (int64_t(1) << 40)) return SAS_ERR_ARG;
   return SAS_OK;
 }
 
@@ -112,15 +126,16 @@ struct BwdWs {
   size_t D_off, off_off, list_off, dlg_off, total;
 };
 BwdWs bwd_layout(const sas_shape* s) {
-  const size_t nb = size_t(s->n) / SAS_BLOCK;
+  const size_t nb = size_t(nblocks(s));
   const size_t BH = size_t(s->B) * s->Hkv;
   BwdWs w{};
   w.D_off = 0;
-  // row statistics: SIMT path D [B,Hq,n]; MFMA path [lse*log2e | D] per 64 rows
-  w.off_off = align_up(w.D_off + 2 * sizeof(float) * size_t(s->B) * s->Hq * s->n);
+  // row statistics: SIMT path D [B,Hq,n]; MFMA path [-lse/tau | -D] per block's 64 window rows
+  const size_t rows = std::max(size_t(s->n), nb * SAS_BLOCK);
+  w.off_off = align_up(w.D_off + 2 * sizeof(float) * size_t(s->B) * s->Hq * rows);
   w.list_off = align_up(w.off_off + sizeof(int32_t) * BH * (nb + 1));
   w.dlg_off = align_up(w.list_off + sizeof(int32_t) * BH * nb * (size_t(s->topk) + 1));
-  w.total = align_up(w.dlg_off + sas::bwd_mfma_extra_ws(s->B, s->Hq, s->Hkv, s->n, s->topk));
+  w.total = align_up(w.dlg_off + sas::bwd_mfma_extra_ws(s->B, s->Hq, s->Hkv, int(nb), s->topk));
   return w;
 }
 
@@ -229,7 +244,7 @@ void prof_after(const char* name, hipStream_t st) {
 
 extern "C" {
 
-int32_t sas_abi_version(void) { return 2; }
+int32_t sas_abi_version(void) { return 3; }
 
 const char* sas_status_string(sas_status st) {
   switch (st) {
@@ -245,7 +260,7 @@ const char* sas_status_string(sas_status st) {
 
 size_t sas_pool_workspace_bytes(const sas_shape* s) {
   if (check_shape(s) != SAS_OK) return 0;
-  return align_up(2 * sizeof(float) * size_t(s->B) * s->Hkv * (s->n / SAS_BLOCK) * s->d);
+  return align_up(2 * sizeof(float) * size_t(s->B) * s->Hkv * size_t(nblocks(s)) * s->d);
 }
 
 sas_status sas_pool_scores(const sas_shape* s, const void* q, const void* k, float* out,
@@ -256,7 +271,7 @@ sas_status sas_pool_scores(const sas_shape* s, const void* q, const void* k, flo
   if (!ws || ws_bytes < sas_pool_workspace_bytes(s)) return SAS_ERR_WORKSPACE;
   clear_stale_error();
   return from_hip(sas::launch_pool(s->dtype, q, k, out, (float*)ws, s->B, s->Hq, s->Hkv, s->n,
-                                   s->d, stream));
+                                   s->d, s->blocks, nblocks(s), stream));
 }
 
 sas_status sas_select(const sas_shape* s, const float* sc, int32_t* idx, int32_t* cnt,
@@ -265,7 +280,7 @@ sas_status sas_select(const sas_shape* s, const float* sc, int32_t* idx, int32_t
   if (st != SAS_OK) return st;
   if (!sc || !cnt || !s_lse) return SAS_ERR_ARG;
   if (s->topk > 0 && (!idx || !log_gate)) return SAS_ERR_ARG;
-  const int nb = s->n / SAS_BLOCK;
+  const int nb = nblocks(s);
   clear_stale_error();
   return from_hip(sas::launch_select(sc, idx, cnt, log_gate, s_lse, s->B * s->Hkv * nb, nb, nb,
                                      s->topk, nullptr, s->Hkv, s->n, s->gate, stream));
@@ -277,7 +292,7 @@ sas_status sas_mask_documents(const sas_shape* s, const int32_t* doc_first, floa
   if (st != SAS_OK) return st;
   if (!doc_first || !sc) return SAS_ERR_ARG;
   clear_stale_error();
-  return from_hip(sas::launch_mask_documents(doc_first, sc, s->B, s->Hkv, s->n / SAS_BLOCK, stream));
+  return from_hip(sas::launch_mask_documents(doc_first, sc, s->B, s->Hkv, nblocks(s), stream));
 }
 
 sas_status sas_fwd(const sas_shape* s, const void* q, const void* k, const void* v,
@@ -292,9 +307,11 @@ sas_status sas_fwd(const sas_shape* s, const void* q, const void* k, const void*
   clear_stale_error();
   if (s->dtype == SAS_BF16 && sas::mfma_supported(s->d, G))
     return from_hip(sas::launch_fwd_mfma(q, k, v, idx, cnt, log_gate, o, lse, s->B, s->Hq, s->Hkv,
-                                         s->n, s->d, s->topk, tau, s->gate, stream));
+                                         s->n, s->d, s->topk, tau, s->gate, s->blocks,
+                                         nblocks(s), stream));
   return from_hip(sas::launch_fwd_simt(s->dtype, q, k, v, idx, cnt, log_gate, o, lse, s->B, s->Hq,
-                                       s->Hkv, s->n, s->d, s->topk, tau, s->gate, stream));
+                                       s->Hkv, s->n, s->d, s->topk, tau, s->gate, s->blocks,
+                                       nblocks(s), stream));
 }
 
 size_t sas_bwd_workspace_bytes(const sas_shape* s) {
@@ -317,7 +334,7 @@ sas_status sas_bwd(const sas_shape* s, const void* q, const void* k, const void*
   float* Dws = reinterpret_cast<float*>(base + w.D_off);
   int32_t* rev_off = reinterpret_cast<int32_t*>(base + w.off_off);
   int32_t* rev_list = reinterpret_cast<int32_t*>(base + w.list_off);
-  const int nb = s->n / SAS_BLOCK;
+  const int nb = nblocks(s);
   const float tau = tau_of(s->scale, s->d);
   clear_stale_error();
   hipError_t e = sas::launch_revidx(idx, cnt, rev_off, rev_list, s->B * s->Hkv, nb, s->topk, stream);
@@ -327,10 +344,10 @@ sas_status sas_bwd(const sas_shape* s, const void* q, const void* k, const void*
     return from_hip(sas::launch_bwd_mfma(
         q, k, v, o, dO, lse, idx, cnt, log_gate, sc, s_lse, dq, dk, dv, ds, Dws, rev_off, rev_list,
         reinterpret_cast<float*>(base + w.dlg_off), s->B, s->Hq, s->Hkv, s->n, s->d, s->topk, tau,
-        s->gate, stream));
+        s->gate, s->blocks, nb, stream));
   return from_hip(sas::launch_bwd_simt(s->dtype, q, k, v, o, dO, lse, idx, cnt, log_gate, sc, s_lse,
                                        dq, dk, dv, ds, Dws, rev_off, rev_list, s->B, s->Hq, s->Hkv,
-                                       s->n, s->d, s->topk, tau, s->gate, stream));
+                                       s->n, s->d, s->topk, tau, s->gate, s->blocks, nb, stream));
 }
 
 size_t sas_decode_workspace_bytes(const sas_decode_shape* s) {
@@ -398,6 +415,30 @@ sas_status sas_decode_paged(const sas_decode_paged_shape* s, const void* q, cons
                                            seq_lens, sc, idx_out, acc, ml, o, s->B, s->Hq, s->Hkv,
                                            s->max_blocks, s->d, s->topk, w.nsplit,
                                            tau_of(s->scale, s->d), s->gate, stream));
+}
+
+int32_t sas_blocks_from_cu_seqlens(const int32_t* cu, int32_t ndocs, int32_t* blocks,
+                                   int32_t* doc_first, int32_t max_blocks) {
+  if (!cu || ndocs < 0 || max_blocks < 0 || (max_blocks > 0 && (!blocks || !doc_first)))
+    return -1;
+  if (cu[0] != 0) return -1;
+  int64_t need = 0;
+  for (int32_t j = 0; j < ndocs; ++j) {
+    if (cu[j + 1] < cu[j]) return -1;
+    need += (int64_t(cu[j + 1]) - cu[j] + SAS_BLOCK - 1) / SAS_BLOCK;
+  }
+  if (need > max_blocks) return -1;
+  int32_t nb = 0;
+  for (int32_t j = 0; j < ndocs; ++j) {
+    const int32_t first = nb;
+    for (int32_t a = cu[j]; a < cu[j + 1]; a += SAS_BLOCK) {
+      blocks[2 * nb] = a;
+      blocks[2 * nb + 1] = std::min(SAS_BLOCK, cu[j + 1] - a);
+      doc_first[nb] = first;
+      ++nb;
+    }
+  }
+  return nb;
 }
 
 const char* sas_last_hip_error(void) { return hipGetErrorName(g_last_hip); }

@@ -10,6 +10,10 @@
 // One thread per (query head, query row); K/V tiles of the kept blocks are
 // staged through LDS as float32.  The external gate (sas.h) is computed as
 // written: unbiased logits, values of kept block m scaled by g = exp(log g).
+// Block tables (packed documents, block_geo): a block is a 64-row window
+// whose rows [lo, hi) are its own tokens; key j of the current block is
+// visible from row t iff lo <= j <= t, and only a block's own rows and keys
+// are stored.
 #include "common.h"
 #include "launch.h"
 #include "sas.h"
@@ -23,16 +27,18 @@ __global__ void __launch_bounds__(1024) fwd_simt_kernel(
     const typename E::T* __restrict__ q, const typename E::T* __restrict__ k,
     const typename E::T* __restrict__ v, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ cnt, const float* __restrict__ lg, typename E::T* __restrict__ o,
-    float* __restrict__ lse, int Hq, int Hkv, int n, int topk, float tau, int gate) {
+    float* __restrict__ lse, int Hq, int Hkv, int n, int topk, float tau, int gate,
+    const int32_t* __restrict__ geo, int nqb) {
   const bool ext = gate == SAS_GATE_EXTERNAL;
-  const int nqb = n / SAS_BLK;
   const int i = blockIdx.x % nqb;
   const int bk = blockIdx.x / nqb;
   const int b = bk / Hkv, kv = bk % Hkv;
+  const BlockGeo gi = block_geo(geo, b, nqb, n, i);
+  if (gi.hi == gi.lo) return;   // a padding block holds no token (uniform exit)
   const int G = Hq / Hkv;
   const int g = threadIdx.x / SAS_BLK, r = threadIdx.x % SAS_BLK;
   const int h = kv * G + g;
-  const size_t qrow = (size_t(b) * Hq + h) * n + size_t(i) * SAS_BLK + r;
+  const size_t qrow = (size_t(b) * Hq + h) * n + size_t(gi.w) + r;
 
   __shared__ float Ks[SAS_BLK][D + 1];
   __shared__ float Vs[SAS_BLK][D + 1];
@@ -51,16 +57,19 @@ __global__ void __launch_bounds__(1024) fwd_simt_kernel(
     const float lgt = (t < c_sel) ? lg[(bk * size_t(nqb) + i) * topk + t] : 0.f;
     const float bias = ext ? 0.f : lgt;       // logit bias
     const float w = ext ? expf(lgt) : 1.f;    // value weight
+    const int w0 = (t < c_sel) ? block_geo(geo, b, nqb, n, blk).w : gi.w;
     __syncthreads();
     for (int e = threadIdx.x; e < SAS_BLK * D; e += blockDim.x) {
       const int rr = e / D, cc = e % D;
-      const size_t gi = (kvbase + size_t(blk) * SAS_BLK + rr) * D + cc;
-      Ks[rr][cc] = E::ld(k + gi);
-      Vs[rr][cc] = E::ld(v + gi);
+      const size_t gx = (kvbase + size_t(w0) + rr) * D + cc;
+      Ks[rr][cc] = E::ld(k + gx);
+      Vs[rr][cc] = E::ld(v + gx);
     }
     __syncthreads();
-    const int jmax = (t < c_sel) ? SAS_BLK : r + 1;  // causal on the current block
-    for (int j = 0; j < jmax; ++j) {
+    // causal on the current block, over its own keys
+    const int jmin = (t < c_sel) ? 0 : gi.lo;
+    const int jmax = (t < c_sel) ? SAS_BLK : r + 1;
+    for (int j = jmin; j < jmax; ++j) {
       float z = bias;
 #pragma unroll
       for (int c = 0; c < D; ++c) z += qr[c] * Ks[j][c];
@@ -78,6 +87,7 @@ __global__ void __launch_bounds__(1024) fwd_simt_kernel(
       for (int c = 0; c < D; ++c) acc[c] += pw * Vs[j][c];
     }
   }
+  if (r < gi.lo || r >= gi.hi) return;   // a window row of another block
   const float inv = 1.f / lrun;
 #pragma unroll
   for (int c = 0; c < D; ++c) E::st(o + qrow * D + c, acc[c] * inv);
@@ -106,16 +116,18 @@ __global__ void __launch_bounds__(1024) bwd_dq_simt_kernel(
     const float* __restrict__ lse, const float* __restrict__ Dv, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ cnt, const float* __restrict__ lg, const float* __restrict__ s,
     const float* __restrict__ s_lse, typename E::T* __restrict__ dq, float* __restrict__ ds,
-    int Hq, int Hkv, int n, int topk, float tau, int gate) {
+    int Hq, int Hkv, int n, int topk, float tau, int gate, const int32_t* __restrict__ geo,
+    int nqb) {
   const bool ext = gate == SAS_GATE_EXTERNAL;
-  const int nqb = n / SAS_BLK;
   const int i = blockIdx.x % nqb;
   const int bk = blockIdx.x / nqb;
   const int b = bk / Hkv, kv = bk % Hkv;
+  const BlockGeo gi = block_geo(geo, b, nqb, n, i);
   const int G = Hq / Hkv;
   const int g = threadIdx.x / SAS_BLK, r = threadIdx.x % SAS_BLK;
   const int h = kv * G + g;
-  const size_t qrow = (size_t(b) * Hq + h) * n + size_t(i) * SAS_BLK + r;
+  const size_t qrow = (size_t(b) * Hq + h) * n + size_t(gi.w) + r;
+  const bool row_ok = r >= gi.lo && r < gi.hi;
   const size_t rowsel = bk * size_t(nqb) + i;
 
   __shared__ float Ks[SAS_BLK][D + 1];
@@ -132,25 +144,29 @@ __global__ void __launch_bounds__(1024) bwd_dq_simt_kernel(
     acc[c] = 0.f;
   }
   const float L = lse[qrow], Drow = Dv[qrow];
-  const int c_sel = cnt[rowsel];
+  // an empty padding block keeps nothing (cnt 0) and still writes its ds row
+  const int c_sel = gi.hi > gi.lo ? cnt[rowsel] : 0;
   const size_t kvbase = (size_t(b) * Hkv + kv) * n;
   const int nwaves = blockDim.x / 64;
-  for (int t = 0; t <= c_sel; ++t) {
+  for (int t = 0; t <= c_sel && gi.hi > gi.lo; ++t) {
     const int blk = (t < c_sel) ? idx[rowsel * topk + t] : i;
     const float lgt = (t < c_sel) ? lg[rowsel * topk + t] : 0.f;
     const float bias = ext ? 0.f : lgt;
     const float w = ext ? expf(lgt) : 1.f;
+    const int w0 = (t < c_sel) ? block_geo(geo, b, nqb, n, blk).w : gi.w;
     __syncthreads();
     for (int e = threadIdx.x; e < SAS_BLK * D; e += blockDim.x) {
       const int rr = e / D, cc = e % D;
-      const size_t gi = (kvbase + size_t(blk) * SAS_BLK + rr) * D + cc;
-      Ks[rr][cc] = E::ld(k + gi);
-      Vs[rr][cc] = E::ld(v + gi);
+      const size_t gx = (kvbase + size_t(w0) + rr) * D + cc;
+      Ks[rr][cc] = E::ld(k + gx);
+      Vs[rr][cc] = E::ld(v + gx);
     }
     __syncthreads();
-    const int jmax = (t < c_sel) ? SAS_BLK : r + 1;
+    // rows outside the block contribute nothing; the current block's own keys
+    const int jmin = (t < c_sel) ? 0 : gi.lo;
+    const int jmax = !row_ok ? 0 : (t < c_sel) ? SAS_BLK : r + 1;
     float tsum = 0.f;
-    for (int j = 0; j < jmax; ++j) {
+    for (int j = jmin; j < jmax; ++j) {
       float z = bias, dp = 0.f;
 #pragma unroll
       for (int c = 0; c < D; ++c) {
@@ -175,8 +191,10 @@ __global__ void __launch_bounds__(1024) bwd_dq_simt_kernel(
       }
     }
   }
+  if (row_ok) {
 #pragma unroll
-  for (int c = 0; c < D; ++c) E::st(dq + qrow * D + c, acc[c] * tau);
+    for (int c = 0; c < D; ++c) E::st(dq + qrow * D + c, acc[c] * tau);
+  }
 
   // gate Jacobian: ds[i,m] = [m kept] dlg - pi_m * sum(dlg), pi = softmax(s[i,:i])
   for (int m = threadIdx.x; m < nqb; m += blockDim.x) slot_of[m] = -1;
@@ -210,15 +228,16 @@ __global__ void __launch_bounds__(64) bwd_dkdv_simt_kernel(
     const float* __restrict__ lse, const float* __restrict__ Dv, const float* __restrict__ lg,
     const int32_t* __restrict__ rev_off, const int32_t* __restrict__ rev_list,
     typename E::T* __restrict__ dk, typename E::T* __restrict__ dv, int Hq, int Hkv, int n,
-    int topk, float tau, int gate) {
+    int topk, float tau, int gate, const int32_t* __restrict__ geo, int nb) {
   const bool ext = gate == SAS_GATE_EXTERNAL;
-  const int nb = n / SAS_BLK;
   const int m = blockIdx.x % nb;
   const int bk = blockIdx.x / nb;
   const int b = bk / Hkv, kv = bk % Hkv;
+  const BlockGeo gm = block_geo(geo, b, nb, n, m);
+  if (gm.hi == gm.lo) return;   // a padding block holds no token (uniform exit)
   const int G = Hq / Hkv;
   const int j = threadIdx.x;
-  const size_t krow = (size_t(b) * Hkv + kv) * n + size_t(m) * SAS_BLK + j;
+  const size_t krow = (size_t(b) * Hkv + kv) * n + size_t(gm.w) + j;
 
   __shared__ float Qs[SAS_BLK][D + 1];
   __shared__ float Os[SAS_BLK][D + 1];
@@ -242,8 +261,9 @@ __global__ void __launch_bounds__(64) bwd_dkdv_simt_kernel(
     const float lgt = own ? 0.f : lg[(bk * size_t(nb) + i) * topk + slot];
     const float bias = ext ? 0.f : lgt;
     const float w = ext ? expf(lgt) : 1.f;
+    const BlockGeo gq = block_geo(geo, b, nb, n, i);
     for (int g = 0; g < G; ++g) {
-      const size_t row0 = (size_t(b) * Hq + kv * G + g) * n + size_t(i) * SAS_BLK;
+      const size_t row0 = (size_t(b) * Hq + kv * G + g) * n + size_t(gq.w);
       __syncthreads();
       for (int x = threadIdx.x; x < SAS_BLK * D; x += 64) {
         const int rr = x / D, cc = x % D;
@@ -253,7 +273,8 @@ __global__ void __launch_bounds__(64) bwd_dkdv_simt_kernel(
       Ls[threadIdx.x] = lse[row0 + threadIdx.x];
       Ds[threadIdx.x] = Dv[row0 + threadIdx.x];
       __syncthreads();
-      for (int t = own ? j : 0; t < SAS_BLK; ++t) {
+      // the q-block's own rows; on the own block, rows at or after key j
+      for (int t = own ? max(j, gq.lo) : gq.lo; t < gq.hi; ++t) {
         float z = bias, dp = 0.f;
 #pragma unroll
         for (int c = 0; c < D; ++c) {
@@ -271,6 +292,7 @@ __global__ void __launch_bounds__(64) bwd_dkdv_simt_kernel(
       }
     }
   }
+  if (j < gm.lo || j >= gm.hi) return;   // a window row of another block
 #pragma unroll
   for (int c = 0; c < D; ++c) {
     E::st(dk + krow * D + c, ak[c] * tau);
@@ -281,26 +303,26 @@ __global__ void __launch_bounds__(64) bwd_dkdv_simt_kernel(
 template <class E, int D>
 static hipError_t fwd_go(const void* q, const void* k, const void* v, const int32_t* idx,
                          const int32_t* cnt, const float* lg, void* o, float* lse, int B, int Hq,
-                         int Hkv, int n, int topk, float tau, int gate, hipStream_t st) {
+                         int Hkv, int n, int topk, float tau, int gate, const int32_t* geo, int nqb,
+                         hipStream_t st) {
   using T = typename E::T;
-  const int nqb = n / SAS_BLK;
   ProfScope ps("sas_fwd_simt_kernel", st);
   hipLaunchKernelGGL((fwd_simt_kernel<E, D>), dim3(B * Hkv * nqb), dim3((Hq / Hkv) * SAS_BLK), 0,
                      st, (const T*)q, (const T*)k, (const T*)v, idx, cnt, lg, (T*)o, lse, Hq, Hkv,
-                     n, topk, tau, gate);
+                     n, topk, tau, gate, geo, nqb);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_simt(int dtype, const void* q, const void* k, const void* v,
                            const int32_t* idx, const int32_t* cnt, const float* lg, void* o,
                            float* lse, int B, int Hq, int Hkv, int n, int d, int topk, float tau,
-                           int gate, hipStream_t st) {
+                           int gate, const int32_t* geo, int nqb, hipStream_t st) {
   if (dtype == 0) {
-    if (d == 64) return fwd_go<ElemF32, 64>(q, k, v, idx, cnt, lg, o, lse, B, Hq, Hkv, n, topk, tau, gate, st);
-    return fwd_go<ElemF32, 128>(q, k, v, idx, cnt, lg, o, lse, B, Hq, Hkv, n, topk, tau, gate, st);
+    if (d == 64) return fwd_go<ElemF32, 64>(q, k, v, idx, cnt, lg, o, lse, B, Hq, Hkv, n, topk, tau, gate, geo, nqb, st);
+    return fwd_go<ElemF32, 128>(q, k, v, idx, cnt, lg, o, lse, B, Hq, Hkv, n, topk, tau, gate, geo, nqb, st);
   }
-  if (d == 64) return fwd_go<ElemBF16, 64>(q, k, v, idx, cnt, lg, o, lse, B, Hq, Hkv, n, topk, tau, gate, st);
-  return fwd_go<ElemBF16, 128>(q, k, v, idx, cnt, lg, o, lse, B, Hq, Hkv, n, topk, tau, gate, st);
+  if (d == 64) return fwd_go<ElemBF16, 64>(q, k, v, idx, cnt, lg, o, lse, B, Hq, Hkv, n, topk, tau, gate, geo, nqb, st);
+  return fwd_go<ElemBF16, 128>(q, k, v, idx, cnt, lg, o, lse, B, Hq, Hkv, n, topk, tau, gate, geo, nqb, st);
 }
 
 template <class E, int D>
@@ -309,9 +331,8 @@ static hipError_t bwd_go(const void* q, const void* k, const void* v, const void
                          const float* lg, const float* s, const float* s_lse, void* dq, void* dk,
                          void* dv, float* ds, float* Dws, const int32_t* rev_off,
                          const int32_t* rev_list, int B, int Hq, int Hkv, int n, int topk,
-                         float tau, int gate, hipStream_t st) {
+                         float tau, int gate, const int32_t* geo, int nb, hipStream_t st) {
   using T = typename E::T;
-  const int nb = n / SAS_BLK;
   const size_t rows = size_t(B) * Hq * n;
   {
     ProfScope ps("sas_bwd_rowdot_kernel", st);
@@ -324,7 +345,7 @@ static hipError_t bwd_go(const void* q, const void* k, const void* v, const void
     ProfScope ps("sas_bwd_dq_simt_kernel", st);
     hipLaunchKernelGGL((bwd_dq_simt_kernel<E, D>), dim3(B * Hkv * nb), dim3((Hq / Hkv) * SAS_BLK),
                        0, st, (const T*)q, (const T*)k, (const T*)v, (const T*)dO, lse, Dws, idx,
-                       cnt, lg, s, s_lse, (T*)dq, ds, Hq, Hkv, n, topk, tau, gate);
+                       cnt, lg, s, s_lse, (T*)dq, ds, Hq, Hkv, n, topk, tau, gate, geo, nb);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -332,7 +353,7 @@ static hipError_t bwd_go(const void* q, const void* k, const void* v, const void
     ProfScope ps("sas_bwd_dkdv_simt_kernel", st);
     hipLaunchKernelGGL((bwd_dkdv_simt_kernel<E, D>), dim3(B * Hkv * nb), dim3(SAS_BLK), 0, st,
                        (const T*)q, (const T*)k, (const T*)v, (const T*)dO, lse, Dws, lg, rev_off,
-                       rev_list, (T*)dk, (T*)dv, Hq, Hkv, n, topk, tau, gate);
+                       rev_list, (T*)dk, (T*)dv, Hq, Hkv, n, topk, tau, gate, geo, nb);
   }
   return hipGetLastError();
 }
@@ -342,9 +363,10 @@ hipError_t launch_bwd_simt(int dtype, const void* q, const void* k, const void* 
                            const int32_t* cnt, const float* lg, const float* s,
                            const float* s_lse, void* dq, void* dk, void* dv, float* ds, float* Dws,
                            const int32_t* rev_off, const int32_t* rev_list, int B, int Hq,
-                           int Hkv, int n, int d, int topk, float tau, int gate, hipStream_t st) {
+                           int Hkv, int n, int d, int topk, float tau, int gate,
+                           const int32_t* geo, int nb, hipStream_t st) {
 #define SAS_BWD_ARGS q, k, v, o, dO, lse, idx, cnt, lg, s, s_lse, dq, dk, dv, ds, Dws, rev_off, \
-                     rev_list, B, Hq, Hkv, n, topk, tau, gate, st
+                     rev_list, B, Hq, Hkv, n, topk, tau, gate, geo, nb, st
   if (dtype == 0) {
     if (d == 64) return bwd_go<ElemF32, 64>(SAS_BWD_ARGS);
     return bwd_go<ElemF32, 128>(SAS_BWD_ARGS);

@@ -91,16 +91,36 @@ typedef int32_t sas_status;
 #define SAS_MAX_BLOCKS 2048    /* most blocks per sequence (n or cap <= 131072) */
 
 /* Training-layer shape.  q [B,Hq,n,d]; k, v [B,Hkv,n,d].
- * Requires B,Hq,Hkv >= 1, Hq % Hkv == 0, 1 <= Hq/Hkv <= 16, n % 64 == 0,
- * 64 <= n <= 64*SAS_MAX_BLOCKS, d in {64,128}, 0 <= topk <= SAS_MAX_BLOCKS (a row
- * with fewer history blocks keeps all of them), scale >= 0 and finite, dtype
- * SAS_F32 or SAS_BF16, gate one of the SAS_GATE_* kinds.  sas_select, sas_fwd,
- * sas_bwd and the decode calls must see the same gate. */
+ * Requires B,Hq,Hkv >= 1, Hq % Hkv == 0, 1 <= Hq/Hkv <= 16, d in {64,128},
+ * 0 <= topk <= SAS_MAX_BLOCKS (a row with fewer history blocks keeps all of
+ * them), scale >= 0 and finite, dtype SAS_F32 or SAS_BF16, gate one of the
+ * SAS_GATE_* kinds.  sas_select, sas_fwd, sas_bwd and the decode calls must
+ * see the same gate.
+ *
+ * Blocks.  With blocks == NULL the sequence is cut into nb = n/64 blocks of
+ * 64 tokens (n % 64 == 0, 64 <= n <= 64*SAS_MAX_BLOCKS; nb may be given as 0
+ * or n/64).  Otherwise blocks is a DEVICE int32 table [B, nb, 2] giving, for
+ * block i of batch entry b, its first token and its number of tokens
+ * (1..64, or 0 for a padding block that holds none), and 1 <= nb <=
+ * SAS_MAX_BLOCKS, 64 <= n <= 64*SAS_MAX_BLOCKS.  This is the layout of packed documents of any
+ * length [Review §2.2 and §2.4 applied per document]: each document is cut
+ * into 64-token blocks from its own first token, so only its last block may
+ * be shorter; blocks are listed in token order; padding blocks come last.
+ * sas_blocks_from_cu_seqlens builds the table.  A block's tokens must lie in
+ * [0, n) and every block but a document's last must hold 64 tokens; table
+ * entries outside these rules are clamped on the device (nothing outside the
+ * tensors is read or written) and give unspecified results.  Every row of q,
+ * k, v and dO must hold finite values, also rows outside every block; the
+ * outputs o, lse, dq, dk and dv are written on the rows of the blocks only.
+ * All per-block tensors (s, idx, cnt, log_gate, s_lse, ds and the
+ * doc_first table) have nb in place of n/64. */
 typedef struct {
   int32_t B, Hq, Hkv, n, d, topk;
   float scale;
   int32_t dtype;
   int32_t gate;
+  int32_t nb;             /* number of blocks (0: n/64 when blocks == NULL) */
+  const int32_t* blocks;  /* NULL, or device int32 [B, nb, 2] (first token, length) */
 } sas_shape;
 
 /* Decode shape.  q [B,Hq,d]; k_cache, v_cache [B,Hkv,cap,d]; same limits with
@@ -127,7 +147,7 @@ typedef struct {
   int32_t gate;
 } sas_decode_paged_shape;
 
-/* Version of this ABI (bumped on any incompatible change). */
+/* Version of this ABI (bumped on any incompatible change): 3. */
 int32_t sas_abi_version(void);
 
 /* Human-readable text of a status code (static storage, never NULL). */
@@ -137,9 +157,11 @@ const char* sas_status_string(sas_status st);
  * Stand-in selector (mean pooling) of the 32K training workload; a score per
  * history block from q and K_{B_m} as in [Review §2.2, selector equation].
  *   s[b,kv,i,m] = qbar[b,kv,i] . kbar[b,kv,m] / sqrt(d)   for ALL i, m
- * qbar = mean of q over the 64 rows of q-block i and the G heads of group kv;
- * kbar = mean of k over the 64 rows of block m.  Means accumulate in float32.
- *   q, k: device, shape->dtype.  s: device float32 [B,Hkv,n/64,n/64] (written).
+ * qbar = mean of q over the tokens of q-block i (64 rows, or the block's
+ * rows of the blocks table) and the G heads of group kv; kbar = mean of k over
+ * the tokens of block m; an empty padding block has mean 0.  Means accumulate
+ * in float32.
+ *   q, k: device, shape->dtype.  s: device float32 [B,Hkv,nb,nb] (written).
  *   ws: device scratch of at least sas_pool_workspace_bytes(shape) bytes. */
 size_t sas_pool_workspace_bytes(const sas_shape* shape);
 sas_status sas_pool_scores(const sas_shape* shape, const void* q, const void* k, float* s,
@@ -155,35 +177,49 @@ sas_status sas_pool_scores(const sas_shape* shape, const void* q, const void* k,
  *                     padded with -1 up to topk
  *   log_gate[b,kv,i,j] = s[b,kv,i,idx[j]] - s_lse (j < cnt), -inf in the padding
  *                     (for the gate kinds: log sigmoid(s), 0 for SAS_GATE_HARD)
- * s: device float32 [B,Hkv,n/64,n/64]; entries m >= i are never read.
- * idx: int32 [B,Hkv,n/64,topk]; cnt: int32 [B,Hkv,n/64];
- * log_gate: float32 [B,Hkv,n/64,topk]; s_lse: float32 [B,Hkv,n/64] (all written).
+ * s: device float32 [B,Hkv,nb,nb]; entries m >= i are never read.
+ * idx: int32 [B,Hkv,nb,topk]; cnt: int32 [B,Hkv,nb];
+ * log_gate: float32 [B,Hkv,nb,topk]; s_lse: float32 [B,Hkv,nb] (all written).
  * idx and log_gate may be NULL when topk == 0. */
 sas_status sas_select(const sas_shape* shape, const float* s, int32_t* idx, int32_t* cnt,
                       float* log_gate, float* s_lse, hipStream_t stream);
 
 /* ---------------------------------------------------------------- packed batches
- * Several documents packed into one sequence, each starting on a block
- * boundary (pad a document to a multiple of 64 tokens; its padding sits after
- * its last real token, so causal masking keeps it out of every real row).  A
- * q-block attends only to blocks of its own document [Review §2.2 and §2.4,
- * applied per document]: this call sets, in place,
+ * Several documents packed into one sequence [Review §2.2 and §2.4, applied
+ * per document]: with the blocks table of the shape, each document is cut
+ * into 64-token blocks from its own first token.  A q-block attends only to
+ * blocks of its own document: this call sets, in place,
  *   s[b,kv,i,m] = -inf   for m < doc_first[b,i]
  * and leaves every other entry unchanged; sas_select, sas_fwd, sas_bwd and
  * sas_decode then treat those blocks as non-candidates (see the -inf rule
  * above), so the packed run gives each document what a run over it alone gives.
- *   doc_first: device int32 [B,n/64], the first block of the document holding
+ *   doc_first: device int32 [B,nb], the first block of the document holding
  *              block i (0 <= doc_first[b,i] <= i; other values are clamped to
  *              that range).
- *   s: device float32 [B,Hkv,n/64,n/64], modified in place. */
+ *   s: device float32 [B,Hkv,nb,nb], modified in place. */
 sas_status sas_mask_documents(const sas_shape* shape, const int32_t* doc_first, float* s,
                               hipStream_t stream);
+
+/* Host helper (no device work): the blocks table and doc_first of packed
+ * documents.  cu_seqlens: host int32 [ndocs+1], 0 = cu[0] <= cu[1] <= ...,
+ * document j holds tokens [cu[j], cu[j+1]) (empty documents are skipped).
+ * Writes up to max_blocks entries of blocks (host int32 [max_blocks, 2]) and
+ * doc_first (host int32 [max_blocks]) for one batch entry and returns the
+ * number of blocks, or -1 when cu_seqlens is not ascending from 0, or when the
+ * documents need more than max_blocks blocks (nothing written then).  Pad
+ * shorter batch entries with (cu[ndocs], 0) blocks whose doc_first is their
+ * own index. */
+int32_t sas_blocks_from_cu_seqlens(const int32_t* cu_seqlens, int32_t ndocs, int32_t* blocks,
+                                   int32_t* doc_first, int32_t max_blocks);
 
 /* ---------------------------------------------------------------- forward
  * Gated block-sparse attention forward [Review §2.3 equation, §2.6].
  * For each query head h and q-block i: keys = the cnt[b,kv,i] blocks idx[b,kv,i,:]
- * (bias log_gate) plus block i itself (bias 0, key j visible iff j <= query t).
- *   o   [B,Hq,n,d]  dtype of q (written; bf16 rounded to nearest even)
+ * (bias log_gate) plus block i itself (bias 0, key j visible iff j <= query t;
+ * positions are tokens, so in a block table the causal rule runs over the
+ * block's own tokens).
+ *   o   [B,Hq,n,d]  dtype of q (written on the blocks' rows; bf16 rounded to
+ *                   nearest even)
  *   lse [B,Hq,n]    float32 natural-log row logsumexp of the biased logits
  * idx/cnt/log_gate as produced by sas_select (idx ascending is NOT required,
  * but every entry j < cnt must be a block in [0, i); this is not checked on the
@@ -195,7 +231,7 @@ sas_status sas_fwd(const sas_shape* shape, const void* q, const void* k, const v
 /* ---------------------------------------------------------------- backward
  * Gradients of sum(dO * o) [Review §2.6 and the chain rule through §2.4]:
  *   dq [B,Hq,n,d], dk, dv [B,Hkv,n,d]  (dtype of q; written, not accumulated)
- *   ds [B,Hkv,n/64,n/64] float32: for m < i,
+ *   ds [B,Hkv,nb,nb] float32: for m < i,
  *        ds[i,m] = [m kept] dlg[i,m] - pi_i[m] * sum_{m' kept} dlg[i,m'],
  *        pi_i = softmax of s[i,:] over the row's candidates (0 elsewhere, and
  *        0 in a row without candidates), dlg[i,m] = sum of the logit gradients

@@ -52,10 +52,18 @@ class Workload:
     s_kind: str = "normal"   # "normal" | "pool" | "gumbel3"
     s_std: float = 1.0
     packed: bool = False     # each batch entry packs several documents (make_doc_first)
+    varlen: bool = False     # packed documents of any token length (doc_token_lens)
+    tail: int = 0            # varlen: tokens left after the last document
 
     @property
     def nqb(self) -> int:
-        return self.n // BLOCK
+        """Blocks per batch entry: n/64, or for documents of any length the
+        most blocks any batch entry needs (each document cut into 64-token
+        blocks from its first token)."""
+        if not self.varlen:
+            return self.n // BLOCK
+        return max(sum((L + BLOCK - 1) // BLOCK for L in doc_token_lens(self, b))
+                   for b in range(self.B))
 
     @property
     def name(self) -> str:
@@ -85,6 +93,7 @@ WORKLOAD_NAMES = {
     3: "qwen3-8b-layer-n32768-K32",
     4: "qwen3-14b-layer-n32768-K64",
     7: "qwen3-8b-layer-n32768-K32-packed",
+    10: "qwen3-8b-layer-n32768-K32-packed-aligned",
     8: "qwen3-8b-layer-n32768-full",
     9: "qwen3-4b-layer-n8192-full",
     5: "decode-qwen3-8b-B64-cache32768-K32",
@@ -96,7 +105,10 @@ WORKLOADS = {
                 s_kind="normal", s_std=math.sqrt(2.0)),
     3: Workload(3, 1, 32, 8, 32768, 128, 32, "bf16", s_kind="pool"),
     4: Workload(4, 1, 40, 8, 32768, 128, 64, "bf16", s_kind="gumbel3"),
-    7: Workload(7, 1, 32, 8, 32768, 128, 32, "bf16", s_kind="normal", packed=True),
+    # documents of any token length packed into the 32K sequence
+    7: Workload(7, 1, 32, 8, 32768, 128, 32, "bf16", s_kind="normal", varlen=True),
+    # documents of whole 64-token blocks (no block table)
+    10: Workload(10, 1, 32, 8, 32768, 128, 32, "bf16", s_kind="normal", packed=True),
     # full-range gated attention: K covers every history block
     8: Workload(8, 1, 32, 8, 32768, 128, 512, "bf16", s_kind="pool"),
     9: Workload(9, 1, 32, 8, 8192, 128, 128, "bf16", qkv_std=1 / math.sqrt(2),
@@ -199,10 +211,11 @@ def make_scores(w: Workload) -> np.ndarray | None:
 
 def custom_workload(seed: int, B: int, Hq: int, Hkv: int, n: int, d: int, topk: int,
                     dtype: str = "bf16", s_kind: str = "normal", qkv_std: float = 1.0,
-                    s_std: float = 1.0, packed: bool = False) -> Workload:
+                    s_std: float = 1.0, packed: bool = False, varlen: bool = False,
+                    tail: int = 0) -> Workload:
     """A smaller workload with the same value distributions (parity tests)."""
     return Workload(seed, B, Hq, Hkv, n, d, topk, dtype, qkv_std=qkv_std,
-                    s_kind=s_kind, s_std=s_std, packed=packed)
+                    s_kind=s_kind, s_std=s_std, packed=packed, varlen=varlen, tail=tail)
 
 
 # ---------------------------------------------------------------- packed documents
@@ -227,6 +240,30 @@ def packed_doc_blocks(cfg: int, b: int, nb: int) -> list[int]:
         ln = max(1, min(ln, left))
         out.append(ln)
         left -= ln
+    return out
+
+
+def doc_token_lens(w: Workload, b: int) -> list[int]:
+    """Document lengths in tokens of batch entry b of a varlen workload:
+    log-uniform between 1 token and the whole sequence, drawn until n - tail
+    tokens are filled (the last document is cut there), so documents of every
+    length mix and most are not multiples of 64.  Batch entries differ."""
+    g = np.random.default_rng([w.cfg, TID_DOCS, b, 1])
+    total = w.n - w.tail - (b * 37 if w.B > 1 else 0)    # entries of different lengths
+    out, left = [], total
+    while left > 0:
+        ln = int(np.exp(g.uniform(0.0, math.log(total + 1))))
+        ln = max(1, min(ln, left))
+        out.append(ln)
+        left -= ln
+    return out
+
+
+def cu_seqlens_of(lens) -> list[int]:
+    """Document offsets [0, L0, L0+L1, ...] of documents laid end to end."""
+    out = [0]
+    for L in lens:
+        out.append(out[-1] + int(L))
     return out
 
 

@@ -88,10 +88,10 @@ static int abi_checks(void) {
       ++fails;                                               \
     }                                                        \
   } while (0)
-  EXPECT(sas_abi_version() == 2);
+  EXPECT(sas_abi_version() == 3);
   EXPECT(strncmp(sas_status_string(SAS_OK), "SAS_OK", 6) == 0);
   void* fake = (void*)(uintptr_t)0x1000; /* never dereferenced: validation fails first */
-  sas_shape good = {1, 8, 2, 512, 128, 4, 0.0f, SAS_BF16, SAS_GATE_SOFTMAX};
+  sas_shape good = {1, 8, 2, 512, 128, 4, 0.0f, SAS_BF16, SAS_GATE_SOFTMAX, 0, NULL};
   EXPECT(sas_bwd_workspace_bytes(&good) > 0);
   sas_shape bad_n = good;
   bad_n.n = 500;
@@ -106,6 +106,21 @@ static int abi_checks(void) {
   EXPECT(sas_select(NULL, fake, fake, fake, fake, fake, NULL) == SAS_ERR_ARG);
   EXPECT(sas_bwd(&good, fake, fake, fake, fake, fake, fake, fake, fake, fake, fake, fake, fake,
                  fake, fake, fake, fake, 1, NULL) == SAS_ERR_WORKSPACE);
+  /* packed documents of any length: 100, 64 and 1 tokens */
+  const int32_t cu[4] = {0, 100, 164, 165};
+  int32_t blk[8], first[4];
+  EXPECT(sas_blocks_from_cu_seqlens(cu, 3, blk, first, 4) == 4);
+  EXPECT(blk[0] == 0 && blk[1] == 64 && blk[2] == 64 && blk[3] == 36 && blk[4] == 100 &&
+         blk[5] == 64 && blk[6] == 164 && blk[7] == 1);
+  EXPECT(first[0] == 0 && first[1] == 0 && first[2] == 2 && first[3] == 3);
+  EXPECT(sas_blocks_from_cu_seqlens(cu, 3, blk, first, 3) == -1);
+  sas_shape packed = good;
+  packed.n = 165;
+  packed.nb = 4;
+  packed.blocks = (const int32_t*)fake;
+  EXPECT(sas_bwd_workspace_bytes(&packed) > 0);
+  packed.nb = 0;
+  EXPECT(sas_bwd_workspace_bytes(&packed) == 0);
   sas_decode_paged_shape ps = {2, 8, 2, 8192, 100, 128, 32, 0.0f, SAS_BF16, SAS_GATE_EXTERNAL};
   EXPECT(sas_decode_paged_workspace_bytes(&ps) > 0);
   ps.max_blocks = SAS_MAX_DECODE_BLOCKS + 1;
@@ -131,6 +146,8 @@ static int layer(int argc, char** argv) {
   sh.scale = 0.0f;
   sh.dtype = SAS_BF16;
   sh.gate = atoi(argv[9]);
+  sh.nb = 0;          /* blocks of 64 tokens, no block table */
+  sh.blocks = NULL;
   if (sh.B < 1 || sh.Hq < 1 || sh.Hkv < 1 || sh.n < 64 || sh.d < 1 || sh.topk < 0) {
     fprintf(stderr, "bad shape arguments\n");
     return 2;

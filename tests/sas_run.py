@@ -24,15 +24,16 @@ def tdtype(w_dtype: str):
 
 
 def run_layer(api, q, k, v, do, s, topk, dtype, scale=0.0, pool=False, bwd=True, doc_first=None,
-              gate="softmax"):
+              gate="softmax", blocks=None):
     """Run (pool) -> (mask documents) -> select -> fwd (-> bwd) on device
     tensors; returns a dict of device tensors.  q,k,v,do are device tensors; s
     is a device float32 tensor (masked in place when doc_first, a device int32
-    [B, n/64] tensor, is given) or None when pool=True."""
+    [B, nb] tensor, is given) or None when pool=True.  blocks: None or the
+    device block table [B, nb, 2] of packed documents of any length."""
     B, Hq, n, d = q.shape
     Hkv = k.shape[1]
-    nb = n // BLOCK
-    sh = api.make_shape(B, Hq, Hkv, n, d, topk, dtype, scale, gate)
+    sh = api.make_shape(B, Hq, Hkv, n, d, topk, dtype, scale, gate, blocks=blocks)
+    nb = api.nblocks(sh)
     out = {}
     if pool:
         s = torch.empty((B, Hkv, nb, nb), dtype=torch.float32, device="cuda")

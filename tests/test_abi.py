@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_status_strings():
     L = _lib.lib()
-    assert L.sas_abi_version() == _lib.ABI_VERSION == 2
+    assert L.sas_abi_version() == _lib.ABI_VERSION == 3
     for st in range(6):
         assert _lib.status_string(st).startswith("SAS")
     assert "unknown" in _lib.status_string(99)
@@ -177,3 +177,37 @@ def test_gate_kind_validation(gate, expect):
     assert api.make_shape(1, 4, 2, 512, 128, 2, gate="external").gate == 3
     with pytest.raises(ValueError):
         api.make_shape(1, 4, 2, 512, 128, 2, gate="tanh")
+
+
+def test_blocks_from_cu_seqlens_matches_the_oracle_cut():
+    """The library's document cut (sas_blocks_from_cu_seqlens through the
+    binding) equals the oracle's, padding included; bad offsets are refused."""
+    import numpy as np
+    import oracle
+    lens = [[100, 64, 1, 130], [5], [64, 64, 63]]
+    cus = [[0] + list(np.cumsum(x)) for x in lens]
+    blocks, first = api.blocks_from_cu_seqlens(cus)
+    geom, ofirst = oracle.packed_geometry(lens)
+    assert np.array_equal(blocks.numpy(), geom) and np.array_equal(first.numpy(), ofirst)
+    with pytest.raises(ValueError):
+        api.blocks_from_cu_seqlens([[1, 5]])
+    with pytest.raises(ValueError):
+        api.blocks_from_cu_seqlens([[0, 70, 60]])
+
+
+def test_block_table_shape_validation():
+    """A block table frees n from multiples of 64; nb must fit the table rules."""
+    L = _lib.lib()
+    fake = FAKE
+    sh = api.make_shape(1, 8, 2, 512, 128, 4)
+    sh.n, sh.nb, sh.blocks = 700, 12, fake.value
+    assert api.sas_bwd_workspace_bytes(sh) > 0
+    assert api.sas_pool_workspace_bytes(sh) == 2 * 4 * 2 * 12 * 128
+    for nb, n in ((0, 700), (2049, 700), (12, 63), (12, 64 * 2048 + 1)):
+        sh.nb, sh.n = nb, n
+        assert api.sas_bwd_workspace_bytes(sh) == 0, (nb, n)
+    sh.blocks, sh.nb, sh.n = None, 3, 512     # without a table nb is 0 or n/64
+    assert api.sas_bwd_workspace_bytes(sh) == 0
+    sh.nb = 8
+    assert api.sas_bwd_workspace_bytes(sh) > 0
+    assert L.sas_select(ctypes.byref(sh), None, None, None, None, None, None) == 1

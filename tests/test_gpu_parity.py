@@ -319,7 +319,7 @@ def _sample_blocks(w, rng, n_blocks=5):
     return sorted(picks)
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4, 7, 9])
+@pytest.mark.parametrize("cfg", [2, 3, 4, 10, 9])
 def test_layer_parity_full_size_sampled(api, cfg):
     w = si.WORKLOADS[cfg]
     q, k, v, do = si.make_qkv(w)
@@ -629,3 +629,118 @@ def test_run_twice_bitwise(api):
     b = run_layer(api, *args, s, w.topk, torch.bfloat16)
     for nm in ("idx", "cnt", "log_gate", "s_lse", "o", "lse", "dq", "dk", "dv", "ds"):
         assert torch.equal(a[nm], b[nm]), nm
+
+
+# ---------------------------------------------------------------- packed documents of any length
+# Documents of any token length packed into one sequence: each is cut into
+# 64-token blocks from its own first token (the last block partial) through
+# the block table; outputs are compared on the documents' tokens only.
+VARLEN_CASES = {
+    # seed, B, Hq, Hkv, n, d, K, dtype, tail
+    "bf16_gqa4_d128": (140, 1, 8, 2, 1000, 128, 3, "bf16", 0),
+    "bf16_b2_gqa4_d64_tail": (141, 2, 8, 2, 700, 64, 2, "bf16", 23),   # padding blocks, tail rows
+    "bf16_gqa5_d128_kall": (142, 1, 5, 1, 600, 128, 20, "bf16", 0),
+    "bf16_gqa16_d128": (143, 1, 16, 1, 400, 128, 2, "bf16", 0),
+    "fp32_gqa2_d64": (144, 1, 4, 2, 500, 64, 2, "f32", 5),
+}
+
+
+def _varlen_inputs(api, w):
+    lens = [si.doc_token_lens(w, b) for b in range(w.B)]
+    geom, first = oracle.packed_geometry(lens)
+    blocks, doc_first = api.blocks_from_cu_seqlens([si.cu_seqlens_of(x) for x in lens])
+    # the library's block cut is integer work: bit-exact against the oracle's
+    assert np.array_equal(blocks.numpy(), geom) and np.array_equal(doc_first.numpy(), first)
+    return lens, geom, first, blocks.cuda(), doc_first.cuda()
+
+
+def _doc_rows(geom, b):
+    return np.concatenate([np.arange(a, a + L) for a, L in geom[b] if L > 0])
+
+
+@pytest.mark.parametrize("gate", ["softmax", "external"])
+@pytest.mark.parametrize("name", list(VARLEN_CASES))
+def test_varlen_layer_parity(api, name, gate):
+    seed, B, Hq, Hkv, n, d, K, dtype, tail = VARLEN_CASES[name]
+    w = si.custom_workload(seed, B, Hq, Hkv, n, d, K, dtype, varlen=True, tail=tail)
+    q, k, v, do = si.make_qkv(w)
+    s = si.make_scores(w)
+    lens, geom, first, blocks, doc_first = _varlen_inputs(api, w)
+    dt = tdtype(w.dtype)
+    res = run_layer(api, dev(q, dt), dev(k, dt), dev(v, dt), dev(do, dt),
+                    torch.from_numpy(s).cuda(), w.topk, dt, doc_first=doc_first, blocks=blocks,
+                    gate=gate)
+    sm = oracle.mask_documents(s, first).astype(np.float32)
+    assert np.array_equal(host(res["s"]), sm)
+    _check_select(res, sm, w.topk, gate)
+    ref = oracle.sas_forward_backward(q, k, v, do, sm, w.topk, gate=gate, geom=geom)
+    tol = TOL[w.dtype]
+    got = {nm: host(res[nm]) for nm in ("o", "lse", "dq", "dk", "dv")}
+    for b in range(w.B):
+        r = _doc_rows(geom, b)
+        assert_o(got["o"][b][:, r], ref["o"][b][:, r], w.dtype, "o")
+        assert_maxabs(got["lse"][b][:, r], ref["lse"][b][:, r], tol["lse"], "lse")
+        for nm in ("dq", "dk", "dv"):
+            assert_rel(got[nm][b][:, r], ref[nm][b][:, r], tol["grad"], nm)
+    assert_rel(host(res["ds"]), ref["ds"], tol["grad"], "ds")
+    assert np.all(host(res["ds"])[np.isneginf(sm)] == 0.0)
+
+
+def test_varlen_pool_parity(api):
+    """Mean pooling over each block's own tokens (partial last blocks, empty
+    padding blocks)."""
+    w = si.custom_workload(145, 2, 8, 2, 900, 128, 4, "bf16", varlen=True, tail=11)
+    q, k, _, _ = si.make_qkv(w, with_do=False)
+    lens, geom, first, blocks, _ = _varlen_inputs(api, w)
+    nb = geom.shape[1]
+    sh = api.make_shape(w.B, w.Hq, w.Hkv, w.n, w.d, w.topk, torch.bfloat16, blocks=blocks)
+    s = torch.empty((w.B, w.Hkv, nb, nb), dtype=torch.float32, device="cuda")
+    ws = api.alloc_workspace(api.sas_pool_workspace_bytes(sh))
+    api.sas_pool_scores(sh, dev(q, torch.bfloat16), dev(k, torch.bfloat16), s, ws)
+    torch.cuda.synchronize()
+    ref = oracle.pool_scores(q, k, w.Hkv, geom)
+    assert_rel(host(s), ref, 1e-5, "s_pool")
+
+
+def test_varlen_full_size_sampled(api):
+    """The 32K Qwen3-8B layer holding documents of any length (the packed
+    bench line's workload): selection on every row, sampled q-blocks (a
+    document's first and partial last blocks among them) and key blocks."""
+    w = si.WORKLOADS[7]
+    q, k, v, do = si.make_qkv(w)
+    s = si.make_scores(w)
+    lens, geom, first, blocks, doc_first = _varlen_inputs(api, w)
+    dt = tdtype(w.dtype)
+    res = run_layer(api, dev(q, dt), dev(k, dt), dev(v, dt), dev(do, dt),
+                    torch.from_numpy(s).cuda(), w.topk, dt, doc_first=doc_first, blocks=blocks)
+    sm = oracle.mask_documents(s, first).astype(np.float32)
+    idx, cnt, lg, s_lse = _check_select(res, sm, w.topk)
+    G = w.Hq // w.Hkv
+    tol = TOL[w.dtype]
+    nb = geom.shape[1]
+    partial = [i for i in range(nb) if 0 < geom[0, i, 1] < BLOCK]
+    starts = [i for i in range(1, nb) if first[0, i] == i]
+    picks = sorted({(0, 0, 0), (0, 1, partial[0]), (0, 2, partial[-1]), (0, 3, starts[0]),
+                    (0, 5, starts[-1] + 1), (0, w.Hkv - 1, nb - 1), (0, 4, nb // 2)})
+    o_g, dq_g, ds_g = host(res["o"]), host(res["dq"]), host(res["ds"])
+    for (b, kv, i) in picks:
+        r = slice(int(geom[b, i, 0]), int(geom[b, i, 0] + geom[b, i, 1]))
+        hs = slice(kv * G, (kv + 1) * G)
+        ob, _ = oracle.fwd_gather_block(q, k, v, idx, cnt, lg, b, kv, i, geom=geom)
+        assert_o(o_g[b, hs, r], ob, w.dtype, ("o", b, kv, i))
+        dqb, _, _, _, dlg = oracle.bwd_gather_block(q, k, v, do, idx, cnt, lg, b, kv, i, geom=geom)
+        assert_rel(dq_g[b, hs, r], dqb, tol["grad"], ("dq", b, kv, i))
+        if cnt[b, kv, i] > 0:
+            dlg_full = np.zeros((1, 1, nb, w.topk))
+            dlg_full[0, 0, i] = dlg
+            dsr = oracle.gate_jacobian(sm[b:b + 1, kv:kv + 1], s_lse[b:b + 1, kv:kv + 1],
+                                       idx[b:b + 1, kv:kv + 1], cnt[b:b + 1, kv:kv + 1],
+                                       dlg_full)[0, 0, i]
+            assert_rel(ds_g[b, kv, i], dsr, tol["grad"], ("ds", b, kv, i))
+    assert np.all(ds_g[np.isneginf(sm)] == 0.0)
+    dk_g, dv_g = host(res["dk"]), host(res["dv"])
+    for (b, kv, m) in [(0, 0, partial[0]), (0, 1, starts[-1]), (0, 6, nb // 3)]:
+        dkm, dvm = oracle.bwd_kv_block(q, k, v, do, idx, cnt, lg, b, kv, m, geom=geom)
+        r = slice(int(geom[b, m, 0]), int(geom[b, m, 0] + geom[b, m, 1]))
+        assert_rel(dk_g[b, kv, r], dkm, tol["grad"], ("dk", b, kv, m))
+        assert_rel(dv_g[b, kv, r], dvm, tol["grad"], ("dv", b, kv, m))
