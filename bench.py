@@ -414,11 +414,11 @@ def run_decode(args, api, si, torch, np):
     return out
 
 
-def run_decode_paged(args, api, si, torch, np):
-    """Long-context paged decode (select over every history block fused in):
-    us per call, and GB/s of the bytes a call must read (kept K/V rows, score
-    rows, page-table entries, q) over that time."""
-    w = si.PAGED_DECODE_WORKLOAD
+def run_decode_paged(args, api, si, torch, np, w=None):
+    """Long-context paged decode (selection of every history block, then the
+    kept tiles): us per call, and GB/s of the bytes a call must read (kept K/V
+    rows, score rows, page-table entries, q) over that time."""
+    w = si.PAGED_DECODE_WORKLOAD if w is None else w
     dt = torch.bfloat16
     qh, table, lens, sh_ = si.paged_decode_host(w)
     kp, vp = si.paged_pool_device(w, "cuda")
@@ -538,6 +538,11 @@ def main():
         torch.cuda.empty_cache()
         line["decode"] = run_decode(args, api, si, torch, np)
         line["decode_paged"] = run_decode_paged(args, api, si, torch, np)
+        line["decode_paged_sweep"] = [
+            {k: r[k] for k in ("workload", "us_per_call", "GBs", "per_kernel")}
+            for r in (line["decode_paged"] if w is si.PAGED_DECODE_WORKLOAD
+                      else run_decode_paged(args, api, si, torch, np, w)
+                      for w in si.PAGED_DECODE_SWEEP)]
     print(json.dumps(line), flush=True)
 
 

@@ -11,13 +11,17 @@
 // The step is HBM-bound (one pass over the kept K/V tiles), so it runs on the
 // vector units with perfectly coalesced 16-byte loads: a 64-token tile of one
 // kv-head is one contiguous 64*d element chunk of the cache (or of one page).
-// One kernel does the whole step for a (b, kv-group, split): wave 0 (or, for
-// rows over 2048 blocks, the whole workgroup) selects the row's blocks into
-// LDS, then the workgroup streams its share of the kept tiles plus the
-// current block with two tiles of loads in flight.  When one
-// workgroup covers a whole row (enough rows to fill the GPU) it writes o
-// directly; otherwise it writes an unnormalised partial (output, max, sum)
-// and a combine kernel merges the splits.
+// When one workgroup covers a whole row (enough rows to fill the GPU), one
+// kernel does the whole step: wave 0 (or, for rows over 2048 blocks, the
+// whole workgroup) selects the row's blocks into LDS, then the workgroup
+// streams the kept tiles plus the current block with two tiles of loads in
+// flight and writes o.  Otherwise (small batches, long contexts) a select
+// kernel selects each row once, into the workspace, and the row's tiles are
+// split over several workgroups; each writes an unnormalised partial
+// (output, max, sum), and a combine kernel merges them.  (Merging inside the
+// split kernel, by the last workgroup of a row to finish, was measured
+// slower: the device-scope fences and the row's serialised atomics cost more
+// than the extra launch.)
 #include <type_traits>
 #include <utility>
 
@@ -96,24 +100,34 @@ SAS_DEV float group_sum(float x) {
 // NB-1 tiles are in flight while one is computed.  The KG groups are merged once,
 // through LDS, at the end.
 //
-// SW = 1: wave 0 selects (rows of up to 64*CPL candidates); SW = 4: the whole
-// workgroup selects (up to 256*CPL).  PAGED: K/V come from a pool of one-block
+// SW = 1: wave 0 selects (rows of up to 64*CPL candidates); SW = 4: the four
+// waves select (up to 256*CPL; select_row_hier for topk <= 64, select_row_wg
+// otherwise).  PAGED: K/V come from a pool of one-block
 // pages [num_pages, Hkv, 64, d]; block m of sequence b lives in page
 // page_table[b, m] (clamped into [0, num_pages)); otherwise from the
 // contiguous cache [B, Hkv, cap, d].
-template <class E, int D, int GMAX, int CPL, int SW, bool PAGED>
+//
+// PRESEL (split rows): the row's selection comes from the workspace (written
+// by decode_select_kernel: kept blocks / pages and base-2 log-gates, the
+// current block after them, and the count), and split s streams the tiles s,
+// s + nsplit, ... of it, so it can fetch its first tile's block at once.
+template <class E, int D, int GMAX, int CPL, int SW, bool PAGED, bool PRESEL>
 __global__ void __launch_bounds__(256) decode_kernel(
     const typename E::T* __restrict__ q, const typename E::T* __restrict__ kc,
     const typename E::T* __restrict__ vc, const int32_t* __restrict__ page_table, int num_pages,
     const int32_t* __restrict__ seq_lens, const float* __restrict__ s,
-    int32_t* __restrict__ idx_out, typename E::T* __restrict__ o, float* __restrict__ part_acc,
-    float* __restrict__ part_ml, int Hq, int Hkv, int cap, int topk, int nsplit, float tau2,
-    int gate) {
+    int32_t* __restrict__ idx_out, typename E::T* __restrict__ o, DecodeScratch ws, int Hq,
+    int Hkv, int cap, int topk, int nsplit, float tau2, int gate) {
   static_assert(SW == 1 || SW == 4, "select by one wave or by the workgroup's four");
   constexpr int EPC = Vec16<E>::N;        // elements per 16-byte chunk
   constexpr int CPR = D / EPC;            // chunks per key row
   constexpr int KG = 256 / CPR;           // key groups per workgroup
   constexpr int KPT = SAS_BLK / KG;       // keys per thread per tile
+  // register buffers: NB-1 tiles of loads stay in flight while one is
+  // computed; fewer heads per kv-head leave registers for more buffers (the
+  // launches hold about two workgroups per CU, so registers are not what
+  // limits occupancy)
+  constexpr int NB = GMAX <= 4 ? 4 : 3;
   const int split = blockIdx.x % nsplit;
   const int bk = blockIdx.x / nsplit;
   const int b = bk / Hkv, kv = bk % Hkv;
@@ -148,39 +162,67 @@ __global__ void __launch_bounds__(256) decode_kernel(
   __shared__ int32_t sblk[SAS_MAX_BLOCKS];
   __shared__ float sgate[SAS_MAX_BLOCKS];
   __shared__ int scnt;
-  int32_t* orow = (idx_out != nullptr && split == 0) ? idx_out + size_t(bk) * topk : nullptr;
   // the external gate keeps its log-gate as the tile's exponent offset
   // (clamped at -60, so no weight underflows) and divides the tile's weight
   // sum by g again: o = sum g P v / sum P
   const bool ext = gate == SAS_GATE_EXTERNAL;
-  auto emit = [&](int pos, int m, float g) __attribute__((always_inline)) {
-    sblk[pos] = where(m);
-    sgate[pos] = (ext ? fmaxf(g, kMinExtLogGate) : g) * kLog2e;
-    if (orow) orow[pos] = m;
-  };
-  const float* srow = s + size_t(bk) * nkb;
-  if constexpr (SW == 1) {
-    if (wave == 0) {
-      float lse;
-      const int keff = select_row<CPL>(srow, icur, topk, gate, lane, lse, emit);
-      if (orow)
-        for (int p = keff + lane; p < topk; p += 64) orow[p] = -1;
-      if (lane == 0) scnt = keff;
-    }
+  const size_t e0 = size_t(bk) * (topk + 1);   // this row's workspace selection
+  // tiles p = t0 + r*ts, r < nloc, of the row's kept blocks followed by the
+  // current block (position c_sel)
+  int c_sel, t0, ts, nloc;
+  if constexpr (PRESEL) {
+    // the select kernel wrote the kept blocks (pages), their gates and the
+    // current block at position c_sel; split s takes tiles s, s + nsplit, ...
+    c_sel = ws.sel_cnt[bk];
+    t0 = split;
+    ts = nsplit;
+    nloc = split <= c_sel ? (c_sel - split) / nsplit + 1 : 0;
   } else {
+    int32_t* orow = idx_out != nullptr ? idx_out + size_t(bk) * topk : nullptr;
+    auto emit = [&](int pos, int m, int tg, float g) __attribute__((always_inline)) {
+      sblk[pos] = PAGED ? tg : m;
+      sgate[pos] = (ext ? fmaxf(g, kMinExtLogGate) : g) * kLog2e;
+      if (orow) orow[pos] = m;
+    };
+    auto tag_of = [&](int m) __attribute__((always_inline)) { return where(m); };
+    const float* srow = s + size_t(bk) * nkb;
     __shared__ float sel_red[6 * SW];
     float lse;
-    const int keff = select_row_wg<CPL, SW>(srow, icur, topk, gate, wave, lane, lse,
-                                            (__attribute__((address_space(3))) float*)sel_red, emit);
-    if (orow)
-      for (int p = keff + t; p < topk; p += 256) orow[p] = -1;
-    if (t == 0) scnt = keff;
+    if constexpr (SW == 1) {
+      if (wave == 0) {
+        const int keff = select_row<CPL>(srow, nkb, icur, topk, gate, lane, lse, tag_of, emit);
+        if (orow)
+          for (int p = keff + lane; p < topk; p += 64) orow[p] = -1;
+        if (lane == 0) scnt = keff;
+      }
+    } else if (topk <= 64) {
+      __shared__ float cval[SW * 64];
+      __shared__ int cidx[SW * 64], ctag[SW * 64];
+      const int keff = select_row_hier<CPL, SW>(
+          srow, nkb, icur, topk, gate, wave, lane, lse,
+          (__attribute__((address_space(3))) float*)sel_red,
+          (__attribute__((address_space(3))) float*)cval,
+          (__attribute__((address_space(3))) int*)cidx,
+          (__attribute__((address_space(3))) int*)ctag, tag_of, emit);
+      if (wave == 0) {
+        if (orow)
+          for (int p = keff + lane; p < topk; p += 64) orow[p] = -1;
+        if (lane == 0) scnt = keff;
+      }
+    } else {
+      const int keff = select_row_wg<CPL, SW>(srow, nkb, icur, topk, gate, wave, lane, lse,
+                                              (__attribute__((address_space(3))) float*)sel_red,
+                                              tag_of, emit);
+      if (orow)
+        for (int p = keff + t; p < topk; p += 64 * SW) orow[p] = -1;
+      if (t == 0) scnt = keff;
+    }
+    __syncthreads();
+    c_sel = scnt;
+    t0 = 0;
+    ts = 1;
+    nloc = c_sel + 1;
   }
-  __syncthreads();
-  const int c_sel = scnt;
-  const int ntiles = c_sel + 1;
-  const int per = (ntiles + nsplit - 1) / nsplit;
-  const int t0 = split * per, t1 = min(ntiles, t0 + per);
 
   float acc[GMAX][EPC];
   float mrun[GMAX], lrun[GMAX];
@@ -193,12 +235,20 @@ __global__ void __launch_bounds__(256) decode_kernel(
   }
 
   const size_t cache0 = (size_t(b) * Hkv + kv) * size_t(cap) * D;
-  const int cur = where(icur);
-  // register buffers: NB-1 tiles of loads stay in flight while one is computed
-  constexpr int NB = 3;
+  const int cur = PRESEL ? 0 : where(icur);
+  // tile p: its block (page) and base-2 log-gate; the current block (p ==
+  // c_sel) is unbiased
+  auto blk_of = [&](int p) __attribute__((always_inline)) {
+    if constexpr (PRESEL) return ws.sel_blk[e0 + p];
+    else return p < c_sel ? sblk[p] : cur;
+  };
+  auto bias_of = [&](int p) __attribute__((always_inline)) {
+    if constexpr (PRESEL) return ws.sel_gate[e0 + p];
+    else return p < c_sel ? sgate[p] : 0.f;
+  };
   uint4 kb[NB][KPT], vb[NB][KPT];
-  auto load = [&]<int B>(int tile) __attribute__((always_inline)) {
-    const int blk = tile < c_sel ? sblk[tile] : cur;
+  auto load = [&]<int B>(int r) __attribute__((always_inline)) {
+    const int blk = blk_of(t0 + r * ts);
     const size_t base = PAGED ? (size_t(blk) * Hkv + kv) * SAS_BLK * D : cache0 + size_t(blk) * SAS_BLK * D;
     const uint4* kt = reinterpret_cast<const uint4*>(kc + base);
     const uint4* vt = reinterpret_cast<const uint4*>(vc + base);
@@ -214,8 +264,9 @@ __global__ void __launch_bounds__(256) decode_kernel(
   // was used.
   constexpr float kSlack = 8.f;
   constexpr bool kBF16 = std::is_same<E, ElemBF16>::value;
-  auto compute = [&]<int B>(int tile) __attribute__((always_inline)) {
-    const float bias2 = tile < c_sel ? sgate[tile] : 0.f;
+  auto compute = [&]<int B>(int r) __attribute__((always_inline)) {
+    const int tile = t0 + r * ts;
+    const float bias2 = bias_of(tile);
     const float wsum_scale = ext ? fast_exp2(-bias2) : 1.f;   // 1/g for the external gate
     const int nvalid = tile < c_sel ? SAS_BLK : L - icur * SAS_BLK;
     float sc[KPT][GMAX];
@@ -290,17 +341,17 @@ __global__ void __launch_bounds__(256) decode_kernel(
     }
   };
   [&]<int... X>(std::integer_sequence<int, X...>) __attribute__((always_inline)) {
-    ((t0 + X < t1 ? load.template operator()<X>(t0 + X) : void()), ...);
+    ((X < nloc ? load.template operator()<X>(X) : void()), ...);
   }(std::make_integer_sequence<int, NB>{});
-  int tile = t0;
-  for (; tile + NB <= t1; tile += NB)
+  int r = 0;
+  for (; r + NB <= nloc; r += NB)
     [&]<int... X>(std::integer_sequence<int, X...>) __attribute__((always_inline)) {
-      ((compute.template operator()<X>(tile + X),
-        (tile + X + NB < t1 ? load.template operator()<X>(tile + X + NB) : void())),
+      ((compute.template operator()<X>(r + X),
+        (r + X + NB < nloc ? load.template operator()<X>(r + X + NB) : void())),
        ...);
     }(std::make_integer_sequence<int, NB>{});
   [&]<int... X>(std::integer_sequence<int, X...>) __attribute__((always_inline)) {
-    ((tile + X < t1 ? compute.template operator()<X>(tile + X) : void()), ...);
+    ((r + X < nloc ? compute.template operator()<X>(r + X) : void()), ...);
   }(std::make_integer_sequence<int, NB - 1>{});
 
   // merge the KG key groups: M = max of the group maxima, each group's sum
@@ -334,120 +385,250 @@ __global__ void __launch_bounds__(256) decode_kernel(
       }
     }
     const size_t bh = size_t(b) * Hq + kv * G + g;
-    if (nsplit == 1) {
+    if constexpr (!PRESEL) {
       E::st(o + bh * D + c, a / l);   // the current block always has a valid key
     } else {
       const size_t pb = bh * nsplit + split;
-      part_acc[pb * D + c] = a;
+      ws.part_acc[pb * D + c] = a;
       if (c == 0) {
-        part_ml[pb * 2] = M;
-        part_ml[pb * 2 + 1] = l;
+        ws.part_ml[pb * 2] = M;
+        ws.part_ml[pb * 2 + 1] = l;
       }
     }
   }
 }
 
-// grid: B*Hq workgroups of D threads.
+// The selection of split rows, once per (b, kv-group): NW waves select the
+// row (select_row for NW = 1, select_row_wg otherwise) into the workspace -
+// kept blocks (pages when PAGED), base-2 log-gates, count - and write
+// idx_out.
+template <int CPL, int NW, bool PAGED>
+__global__ void __launch_bounds__(64 * NW) decode_select_kernel(
+    const int32_t* __restrict__ page_table, int num_pages, const int32_t* __restrict__ seq_lens,
+    const float* __restrict__ s, int32_t* __restrict__ idx_out, DecodeScratch ws, int Hkv,
+    int cap, int topk, int gate) {
+  const int bk = blockIdx.x;
+  const int b = bk / Hkv;
+  const int t = threadIdx.x;
+  const int wave = t >> 6, lane = t & 63;
+  const int nkb = cap / SAS_BLK;
+  auto where = [&](int m) __attribute__((always_inline)) {
+    if constexpr (PAGED) {
+      const int p = page_table[size_t(b) * nkb + m];
+      return p < 0 ? 0 : (p >= num_pages ? num_pages - 1 : p);
+    } else {
+      return m;
+    }
+  };
+  int L = seq_lens[b];
+  L = L < 1 ? 1 : (L > cap ? cap : L);
+  const int icur = (L - 1) / SAS_BLK;
+  const int cur = where(icur);   // issued now, used at the end
+  const bool ext = gate == SAS_GATE_EXTERNAL;
+  int32_t* orow = idx_out != nullptr ? idx_out + size_t(bk) * topk : nullptr;
+  const size_t e0 = size_t(bk) * (topk + 1);
+  auto emit = [&](int pos, int m, int tg, float g) __attribute__((always_inline)) {
+    ws.sel_blk[e0 + pos] = PAGED ? tg : m;
+    ws.sel_gate[e0 + pos] = (ext ? fmaxf(g, kMinExtLogGate) : g) * kLog2e;
+    if (orow) orow[pos] = m;
+  };
+  auto tag_of = [&](int m) __attribute__((always_inline)) { return where(m); };
+  const float* srow = s + size_t(bk) * nkb;
+  float lse;
+  // the number kept, known to wave 0 (and to every wave after select_row_wg)
+  int keff;
+  if constexpr (NW == 1) {
+    keff = select_row<CPL>(srow, nkb, icur, topk, gate, lane, lse, tag_of, emit);
+  } else {
+    __shared__ float sel_red[6 * NW];
+    if (topk <= 64) {
+      __shared__ float cval[NW * 64];
+      __shared__ int cidx[NW * 64], ctag[NW * 64];
+      keff = select_row_hier<CPL, NW>(srow, nkb, icur, topk, gate, wave, lane, lse,
+                                      (__attribute__((address_space(3))) float*)sel_red,
+                                      (__attribute__((address_space(3))) float*)cval,
+                                      (__attribute__((address_space(3))) int*)cidx,
+                                      (__attribute__((address_space(3))) int*)ctag, tag_of, emit);
+    } else {
+      keff = select_row_wg<CPL, NW>(srow, nkb, icur, topk, gate, wave, lane, lse,
+                                    (__attribute__((address_space(3))) float*)sel_red, tag_of,
+                                    emit);
+    }
+  }
+  if (wave != 0) return;
+  // the current block follows the kept ones, unbiased
+  if (lane == 0) {
+    ws.sel_blk[e0 + keff] = cur;
+    ws.sel_gate[e0 + keff] = 0.f;
+    ws.sel_cnt[bk] = keff;
+  }
+  if (orow)
+    for (int p = keff + lane; p < topk; p += 64) orow[p] = -1;
+}
+
+// grid: B*Hq workgroups of 256 threads: merges the nsplit partials of one
+// (b, head): M = max of the splits' maxima, o = sum 2^(m - M) acc / sum
+// 2^(m - M) l.  Thread t takes column t % D of the splits t / D + (256/D) k;
+// the first KM of them are loaded together with the (max, sum) pairs, so a
+// call waits on one round of loads (more splits than that take further
+// rounds).  The column sums of the 256/D thread groups are added in group
+// order, so the result is deterministic.
 template <class E, int D>
-__global__ void __launch_bounds__(128) decode_combine_kernel(const float* __restrict__ part_acc,
+__global__ void __launch_bounds__(256) decode_combine_kernel(const float* __restrict__ part_acc,
                                                              const float* __restrict__ part_ml,
                                                              typename E::T* __restrict__ o,
                                                              int nsplit) {
-  // the splits' (max, sum) pairs go to LDS with parallel loads, so the merge
-  // below issues its partial-output loads back to back instead of one
-  // dependent load per split (decode_nsplit never exceeds 512)
-  __shared__ float sm[512], sl[512];
+  constexpr int NG = 256 / D, KM = 16;
+  __shared__ float sm[512], sl[512];   // decode_nsplit never exceeds 512
+  __shared__ float ra[NG][D], rl[NG][D];
   const size_t bh = blockIdx.x;
-  const int c = threadIdx.x;
-  for (int sp = c; sp < nsplit; sp += D) {
+  const int t = threadIdx.x, c = t % D, grp = t / D;
+  const float* pa = part_acc + bh * nsplit * D + c;
+  float x[KM];
+#pragma unroll
+  for (int k = 0; k < KM; ++k) {
+    const int sp = grp + NG * k;
+    x[k] = sp < nsplit ? pa[size_t(sp) * D] : 0.f;
+  }
+  for (int sp = t; sp < nsplit; sp += 256) {
     sm[sp] = part_ml[(bh * nsplit + sp) * 2];
     sl[sp] = part_ml[(bh * nsplit + sp) * 2 + 1];
   }
   __syncthreads();
   float M = -INFINITY;
   for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, sm[sp]);
-  float l = 0.f, a = 0.f;
-#pragma unroll 8
-  for (int sp = 0; sp < nsplit; ++sp) {
+  float a = 0.f, l = 0.f;
+  auto add = [&](int sp, float xv) __attribute__((always_inline)) {
     const float m = sm[sp];
-    const float x = part_acc[(bh * nsplit + sp) * D + c];
     if (m != -INFINITY) {   // a split without keys contributes nothing
       const float w = fast_exp2(m - M);
-      l += w * sl[sp];
-      a += w * x;
+      l = __builtin_fmaf(w, sl[sp], l);
+      a = __builtin_fmaf(w, xv, a);
     }
+  };
+#pragma unroll
+  for (int k = 0; k < KM; ++k)
+    if (grp + NG * k < nsplit) add(grp + NG * k, x[k]);
+  for (int sp = grp + NG * KM; sp < nsplit; sp += NG) add(sp, pa[size_t(sp) * D]);
+  ra[grp][c] = a;
+  rl[grp][c] = l;
+  __syncthreads();
+  if (grp != 0) return;
+#pragma unroll
+  for (int g = 1; g < NG; ++g) {
+    a += ra[g][c];
+    l += rl[g][c];
   }
-  E::st(o + bh * D + c, a / l);
+  E::st(o + bh * D + c, a / l);   // the current block always has a valid key
 }
-
 
 // ---- launch: dtype -> d -> select mode -> heads per group
-template <class E, int D, int GMAX, int CPL, int SW, bool PAGED>
+template <class E, int D, int GMAX, int CPL, int SW, bool PAGED, bool PRESEL>
 static void dec_go(const void* q, const void* kc, const void* vc, const int32_t* pt, int np,
-                   const int32_t* sl, const float* s, int32_t* idx_out, void* o, float* pa,
-                   float* pm, int B, int Hq, int Hkv, int cap, int topk, int ns, float tau2,
-                   int gate, hipStream_t st) {
+                   const int32_t* sl, const float* s, int32_t* idx_out, void* o,
+                   const DecodeScratch& ws, int B, int Hq, int Hkv, int cap, int topk, int ns,
+                   float tau2, int gate, hipStream_t st) {
   using T = typename E::T;
-  hipLaunchKernelGGL((decode_kernel<E, D, GMAX, CPL, SW, PAGED>), dim3(B * Hkv * ns), dim3(256), 0, st,
-                     (const T*)q, (const T*)kc, (const T*)vc, pt, np, sl, s, idx_out, (T*)o, pa, pm,
-                     Hq, Hkv, cap, topk, ns, tau2, gate);
+  hipLaunchKernelGGL((decode_kernel<E, D, GMAX, CPL, SW, PAGED, PRESEL>), dim3(B * Hkv * ns),
+                     dim3(256), 0, st, (const T*)q, (const T*)kc, (const T*)vc, pt, np, sl, s,
+                     idx_out, (T*)o, ws, Hq, Hkv, cap, topk, ns, tau2, gate);
 }
 
-template <class E, int D, int CPL, int SW, bool PAGED>
+template <class E, int D, int CPL, int SW, bool PAGED, bool PRESEL>
 static void dec_g(int G, const void* q, const void* kc, const void* vc, const int32_t* pt, int np,
-                  const int32_t* sl, const float* s, int32_t* idx_out, void* o, float* pa,
-                  float* pm, int B, int Hq, int Hkv, int cap, int topk, int ns, float tau2,
-                  int gate, hipStream_t st) {
-  if (G <= 4) dec_go<E, D, 4, CPL, SW, PAGED>(q, kc, vc, pt, np, sl, s, idx_out, o, pa, pm, B, Hq, Hkv, cap, topk, ns, tau2, gate, st);
-  else if (G <= 8) dec_go<E, D, 8, CPL, SW, PAGED>(q, kc, vc, pt, np, sl, s, idx_out, o, pa, pm, B, Hq, Hkv, cap, topk, ns, tau2, gate, st);
-  else dec_go<E, D, 16, CPL, SW, PAGED>(q, kc, vc, pt, np, sl, s, idx_out, o, pa, pm, B, Hq, Hkv, cap, topk, ns, tau2, gate, st);
+                  const int32_t* sl, const float* s, int32_t* idx_out, void* o,
+                  const DecodeScratch& ws, int B, int Hq, int Hkv, int cap, int topk, int ns,
+                  float tau2, int gate, hipStream_t st) {
+#define SAS_DEC_ARGS q, kc, vc, pt, np, sl, s, idx_out, o, ws, B, Hq, Hkv, cap, topk, ns, tau2, gate, st
+  if (G <= 4) dec_go<E, D, 4, CPL, SW, PAGED, PRESEL>(SAS_DEC_ARGS);
+  else if (G <= 8) dec_go<E, D, 8, CPL, SW, PAGED, PRESEL>(SAS_DEC_ARGS);
+  else dec_go<E, D, 16, CPL, SW, PAGED, PRESEL>(SAS_DEC_ARGS);
+#undef SAS_DEC_ARGS
 }
 
 template <class E, int D, bool PAGED>
 static void dec_c(int G, const void* q, const void* kc, const void* vc, const int32_t* pt, int np,
-                  const int32_t* sl, const float* s, int32_t* idx_out, void* o, float* pa,
-                  float* pm, int B, int Hq, int Hkv, int cap, int topk, int ns, float tau2,
-                  int gate, hipStream_t st) {
-  // history rows hold up to cap/64 - 1 candidate blocks
+                  const int32_t* sl, const float* s, int32_t* idx_out, void* o,
+                  const DecodeScratch& ws, int B, int Hq, int Hkv, int cap, int topk, int ns,
+                  float tau2, int gate, hipStream_t st) {
+#define SAS_DEC_ARGS G, q, kc, vc, pt, np, sl, s, idx_out, o, ws, B, Hq, Hkv, cap, topk, ns, tau2, gate, st
+  if (ns > 1) {   // rows selected beforehand (decode_select_kernel), tiles split
+    dec_g<E, D, 1, 1, PAGED, true>(SAS_DEC_ARGS);
+    return;
+  }
+  // history rows hold up to cap/64 - 1 candidate blocks; the workgroup's four
+  // waves select (select_row_hier for topk <= 64, select_row_wg otherwise)
   const int nkb = cap / SAS_BLK;
-  if (nkb <= 8 * 64)
-    dec_g<E, D, 8, 1, PAGED>(G, q, kc, vc, pt, np, sl, s, idx_out, o, pa, pm, B, Hq, Hkv, cap, topk, ns, tau2, gate, st);
-  else if (!PAGED || nkb <= 32 * 64)
-    dec_g<E, D, 32, 1, PAGED>(G, q, kc, vc, pt, np, sl, s, idx_out, o, pa, pm, B, Hq, Hkv, cap, topk, ns, tau2, gate, st);
+  if (nkb <= 2 * 256)
+    dec_g<E, D, 2, 4, PAGED, false>(SAS_DEC_ARGS);
+  else if (!PAGED || nkb <= 8 * 256)
+    dec_g<E, D, 8, 4, PAGED, false>(SAS_DEC_ARGS);
   else if constexpr (PAGED)
-    dec_g<E, D, 32, 4, PAGED>(G, q, kc, vc, pt, np, sl, s, idx_out, o, pa, pm, B, Hq, Hkv, cap, topk, ns, tau2, gate, st);
+    dec_g<E, D, 32, 4, PAGED, false>(SAS_DEC_ARGS);
+#undef SAS_DEC_ARGS
 }
 
-// The decode step (and, when rows are split, the combine kernel) for either
-// cache layout; kernel names for the profiling hooks differ per layout.
+template <bool PAGED>
+static void dec_select(const int32_t* pt, int np, const int32_t* sl, const float* s,
+                       int32_t* idx_out, const DecodeScratch& ws, int B, int Hkv, int cap, int topk,
+                       int gate, hipStream_t st) {
+#define SAS_SEL_ARGS pt, np, sl, s, idx_out, ws, Hkv, cap, topk, gate
+  // one wave for rows of up to 512 blocks, 16 waves (1..8 candidates per lane)
+  // beyond: a lone row is pure latency, so more waves shorten the search
+  const int nkb = cap / SAS_BLK;
+  if (nkb <= 8 * 64)
+    hipLaunchKernelGGL((decode_select_kernel<8, 1, PAGED>), dim3(B * Hkv), dim3(64), 0, st, SAS_SEL_ARGS);
+  else if (nkb <= 1024)
+    hipLaunchKernelGGL((decode_select_kernel<1, 16, PAGED>), dim3(B * Hkv), dim3(1024), 0, st, SAS_SEL_ARGS);
+  else if (nkb <= 2048)
+    hipLaunchKernelGGL((decode_select_kernel<2, 16, PAGED>), dim3(B * Hkv), dim3(1024), 0, st, SAS_SEL_ARGS);
+  else if (nkb <= 4096)
+    hipLaunchKernelGGL((decode_select_kernel<4, 16, PAGED>), dim3(B * Hkv), dim3(1024), 0, st, SAS_SEL_ARGS);
+  else
+    hipLaunchKernelGGL((decode_select_kernel<8, 16, PAGED>), dim3(B * Hkv), dim3(1024), 0, st, SAS_SEL_ARGS);
+#undef SAS_SEL_ARGS
+}
+
+// The decode step for either cache layout: one fused kernel when one
+// workgroup covers a row (nsplit == 1); otherwise the select kernel, the
+// split kernel and the combine kernel.  Kernel names for the
+// profiling hooks differ per layout.
 template <bool PAGED>
 hipError_t launch_decode_any(int dtype, const void* q, const void* kc, const void* vc,
                              const int32_t* page_table, int num_pages, const int32_t* seq_lens,
-                             const float* s, int32_t* idx_out, float* part_acc, float* part_ml,
-                             void* o, int B, int Hq, int Hkv, int cap, int d, int topk, int nsplit,
+                             const float* s, int32_t* idx_out, const DecodeScratch& ws, void* o,
+                             int B, int Hq, int Hkv, int cap, int d, int topk, int nsplit,
                              float tau, int gate, hipStream_t st) {
   const int G = Hq / Hkv;
   const float tau2 = tau * kLog2e;
-  {
-    ProfScope ps(PAGED ? "sas_decode_paged_kernel" : "sas_decode_kernel", st);
-    if (dtype == 1) {
-      if (d == 128) dec_c<ElemBF16, 128, PAGED>(G, q, kc, vc, page_table, num_pages, seq_lens, s, idx_out, o, part_acc, part_ml, B, Hq, Hkv, cap, topk, nsplit, tau2, gate, st);
-      else dec_c<ElemBF16, 64, PAGED>(G, q, kc, vc, page_table, num_pages, seq_lens, s, idx_out, o, part_acc, part_ml, B, Hq, Hkv, cap, topk, nsplit, tau2, gate, st);
-    } else {
-      if (d == 128) dec_c<ElemF32, 128, PAGED>(G, q, kc, vc, page_table, num_pages, seq_lens, s, idx_out, o, part_acc, part_ml, B, Hq, Hkv, cap, topk, nsplit, tau2, gate, st);
-      else dec_c<ElemF32, 64, PAGED>(G, q, kc, vc, page_table, num_pages, seq_lens, s, idx_out, o, part_acc, part_ml, B, Hq, Hkv, cap, topk, nsplit, tau2, gate, st);
-    }
+  if (nsplit > 1) {
+    ProfScope ps(PAGED ? "sas_decode_paged_select_kernel" : "sas_decode_select_kernel", st);
+    dec_select<PAGED>(page_table, num_pages, seq_lens, s, idx_out, ws, B, Hkv, cap, topk, gate, st);
   }
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  {
+    ProfScope ps(PAGED ? "sas_decode_paged_kernel" : "sas_decode_kernel", st);
+#define SAS_DEC_ARGS G, q, kc, vc, page_table, num_pages, seq_lens, s, idx_out, o, ws, B, Hq, Hkv, cap, topk, nsplit, tau2, gate, st
+    if (dtype == 1) {
+      if (d == 128) dec_c<ElemBF16, 128, PAGED>(SAS_DEC_ARGS);
+      else dec_c<ElemBF16, 64, PAGED>(SAS_DEC_ARGS);
+    } else {
+      if (d == 128) dec_c<ElemF32, 128, PAGED>(SAS_DEC_ARGS);
+      else dec_c<ElemF32, 64, PAGED>(SAS_DEC_ARGS);
+    }
+#undef SAS_DEC_ARGS
+  }
+  e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
   {
     ProfScope ps("sas_decode_combine_kernel", st);
     if (dtype == 1) {
-      if (d == 128) hipLaunchKernelGGL((decode_combine_kernel<ElemBF16, 128>), dim3(B * Hq), dim3(128), 0, st, part_acc, part_ml, (uint16_t*)o, nsplit);
-      else hipLaunchKernelGGL((decode_combine_kernel<ElemBF16, 64>), dim3(B * Hq), dim3(64), 0, st, part_acc, part_ml, (uint16_t*)o, nsplit);
+      if (d == 128) hipLaunchKernelGGL((decode_combine_kernel<ElemBF16, 128>), dim3(B * Hq), dim3(256), 0, st, ws.part_acc, ws.part_ml, (uint16_t*)o, nsplit);
+      else hipLaunchKernelGGL((decode_combine_kernel<ElemBF16, 64>), dim3(B * Hq), dim3(256), 0, st, ws.part_acc, ws.part_ml, (uint16_t*)o, nsplit);
     } else {
-      if (d == 128) hipLaunchKernelGGL((decode_combine_kernel<ElemF32, 128>), dim3(B * Hq), dim3(128), 0, st, part_acc, part_ml, (float*)o, nsplit);
-      else hipLaunchKernelGGL((decode_combine_kernel<ElemF32, 64>), dim3(B * Hq), dim3(64), 0, st, part_acc, part_ml, (float*)o, nsplit);
+      if (d == 128) hipLaunchKernelGGL((decode_combine_kernel<ElemF32, 128>), dim3(B * Hq), dim3(256), 0, st, ws.part_acc, ws.part_ml, (float*)o, nsplit);
+      else hipLaunchKernelGGL((decode_combine_kernel<ElemF32, 64>), dim3(B * Hq), dim3(256), 0, st, ws.part_acc, ws.part_ml, (float*)o, nsplit);
     }
   }
   return hipGetLastError();

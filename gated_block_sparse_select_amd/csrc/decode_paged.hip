@@ -10,12 +10,12 @@ namespace sas {
 
 hipError_t launch_decode_paged(int dtype, const void* q, const void* k_pages, const void* v_pages,
                                const int32_t* page_table, int num_pages, const int32_t* seq_lens,
-                               const float* s, int32_t* idx_out, float* part_acc, float* part_ml,
-                               void* o, int B, int Hq, int Hkv, int max_blocks, int d, int topk,
-                               int nsplit, float tau, int gate, hipStream_t st) {
+                               const float* s, int32_t* idx_out, const DecodeScratch& ws, void* o,
+                               int B, int Hq, int Hkv, int max_blocks, int d, int topk, int nsplit,
+                               float tau, int gate, hipStream_t st) {
   return launch_decode_any<true>(dtype, q, k_pages, v_pages, page_table, num_pages, seq_lens, s,
-                                 idx_out, part_acc, part_ml, o, B, Hq, Hkv, max_blocks * SAS_BLK,
-                                 d, topk, nsplit, tau, gate, st);
+                                 idx_out, ws, o, B, Hq, Hkv, max_blocks * SAS_BLK, d, topk, nsplit,
+                                 tau, gate, st);
 }
 
 }  // namespace sas

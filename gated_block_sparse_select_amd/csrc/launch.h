@@ -56,18 +56,29 @@ hipError_t launch_bwd_simt(int dtype, const void* q, const void* k, const void* 
                            const int32_t* geo, int nb, hipStream_t st);
 
 // ---- decode (decode.hip)
+// Workspace of a decode call whose rows are split over nsplit workgroups
+// (unused when nsplit == 1): per (b, kv) row the selection (kept blocks or
+// pages and base-2 log-gates, [B*Hkv][topk+1]; count [B*Hkv]), and per
+// (b, head, split) the unnormalised partial output [.. * d] and (max, sum)
+// [.. * 2].
+struct DecodeScratch {
+  int32_t* sel_blk;
+  float* sel_gate;
+  int32_t* sel_cnt;
+  float* part_acc;
+  float* part_ml;
+};
 int decode_nsplit(int B, int Hkv, int topk);
 hipError_t launch_decode(int dtype, const void* q, const void* kc, const void* vc,
                          const int32_t* seq_lens, const float* s, int32_t* idx_out,
-                         float* part_acc, float* part_ml, void* o, int B, int Hq, int Hkv,
-                         int cap, int d, int topk, int nsplit, float tau, int gate,
-                         hipStream_t st);
+                         const DecodeScratch& ws, void* o, int B, int Hq, int Hkv, int cap, int d,
+                         int topk, int nsplit, float tau, int gate, hipStream_t st);
 
 // ---- paged decode (decode_paged.hip)
 hipError_t launch_decode_paged(int dtype, const void* q, const void* k_pages, const void* v_pages,
                                const int32_t* page_table, int num_pages, const int32_t* seq_lens,
-                               const float* s, int32_t* idx_out, float* part_acc, float* part_ml,
-                               void* o, int B, int Hq, int Hkv, int max_blocks, int d, int topk,
-                               int nsplit, float tau, int gate, hipStream_t st);
+                               const float* s, int32_t* idx_out, const DecodeScratch& ws, void* o,
+                               int B, int Hq, int Hkv, int max_blocks, int d, int topk, int nsplit,
+                               float tau, int gate, hipStream_t st);
 
 }  // namespace sas

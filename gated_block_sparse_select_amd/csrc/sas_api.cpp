@@ -140,20 +140,35 @@ BwdWs bwd_layout(const sas_shape* s) {
 }
 
 // ----------------------------------------------------------- decode workspace
-// Partial outputs (and per-split max / sum) when a row's tiles are split over
-// several workgroups; a small minimum otherwise.
+// When a row's tiles are split over several workgroups: the row's selection
+// (kept blocks / pages, base-2 log-gates, count) and the split workgroups'
+// partial outputs with (max, sum); a small minimum otherwise.
 struct DecWs {
-  size_t acc_off, ml_off, total;
+  size_t blk_off, gate_off, cnt_off, acc_off, ml_off, total;
   int nsplit;
 };
 DecWs dec_layout(const sas_decode_shape* s) {
   DecWs w{};
   w.nsplit = sas::decode_nsplit(s->B, s->Hkv, s->topk);
-  const size_t parts = w.nsplit > 1 ? size_t(s->B) * s->Hq * w.nsplit : 0;
-  w.acc_off = 0;
+  const bool split = w.nsplit > 1;
+  const size_t rows = split ? size_t(s->B) * s->Hkv : 0;
+  const size_t ent = rows * (size_t(s->topk) + 1);
+  const size_t parts = split ? size_t(s->B) * s->Hq * w.nsplit : 0;
+  w.blk_off = 0;
+  w.gate_off = align_up(w.blk_off + sizeof(int32_t) * ent);
+  w.cnt_off = align_up(w.gate_off + sizeof(float) * ent);
+  w.acc_off = align_up(w.cnt_off + sizeof(int32_t) * rows);
   w.ml_off = align_up(w.acc_off + sizeof(float) * parts * s->d);
   w.total = align_up(w.ml_off + sizeof(float) * parts * 2 + 1);
   return w;
+}
+sas::DecodeScratch dec_scratch(const DecWs& w, void* base_v) {
+  char* base = static_cast<char*>(base_v);
+  return sas::DecodeScratch{reinterpret_cast<int32_t*>(base + w.blk_off),
+                            reinterpret_cast<float*>(base + w.gate_off),
+                            reinterpret_cast<int32_t*>(base + w.cnt_off),
+                            reinterpret_cast<float*>(base + w.acc_off),
+                            reinterpret_cast<float*>(base + w.ml_off)};
 }
 
 }  // namespace
@@ -363,13 +378,10 @@ sas_status sas_decode(const sas_decode_shape* s, const void* q, const void* k_ca
   if (!q || !k_cache || !v_cache || !seq_lens || !sc || !o) return SAS_ERR_ARG;
   const DecWs w = dec_layout(s);
   if (!ws || ws_bytes < w.total) return SAS_ERR_WORKSPACE;
-  char* base = static_cast<char*>(ws);
-  float* acc = reinterpret_cast<float*>(base + w.acc_off);
-  float* ml = reinterpret_cast<float*>(base + w.ml_off);
   clear_stale_error();
-  return from_hip(sas::launch_decode(s->dtype, q, k_cache, v_cache, seq_lens, sc, idx_out, acc, ml,
-                                     o, s->B, s->Hq, s->Hkv, s->cap, s->d, s->topk, w.nsplit,
-                                     tau_of(s->scale, s->d), s->gate, stream));
+  return from_hip(sas::launch_decode(s->dtype, q, k_cache, v_cache, seq_lens, sc, idx_out,
+                                     dec_scratch(w, ws), o, s->B, s->Hq, s->Hkv, s->cap, s->d,
+                                     s->topk, w.nsplit, tau_of(s->scale, s->d), s->gate, stream));
 }
 
 sas_status sas_decode_noalloc(const sas_decode_shape* s, const void* q, const void* k_cache,
@@ -382,13 +394,10 @@ sas_status sas_decode_noalloc(const sas_decode_shape* s, const void* q, const vo
   if (w.total > size_t(SAS_NOALLOC_SCRATCH_BYTES)) return SAS_ERR_WORKSPACE;
   void* base_v = nullptr;
   if ((st = scratch_of(stream, &base_v)) != SAS_OK) return st;
-  char* base = static_cast<char*>(base_v);
-  float* acc = reinterpret_cast<float*>(base + w.acc_off);
-  float* ml = reinterpret_cast<float*>(base + w.ml_off);
   clear_stale_error();
-  return from_hip(sas::launch_decode(s->dtype, q, k_cache, v_cache, seq_lens, sc, idx_out, acc, ml,
-                                     o, s->B, s->Hq, s->Hkv, s->cap, s->d, s->topk, w.nsplit,
-                                     tau_of(s->scale, s->d), s->gate, stream));
+  return from_hip(sas::launch_decode(s->dtype, q, k_cache, v_cache, seq_lens, sc, idx_out,
+                                     dec_scratch(w, base_v), o, s->B, s->Hq, s->Hkv, s->cap, s->d,
+                                     s->topk, w.nsplit, tau_of(s->scale, s->d), s->gate, stream));
 }
 
 size_t sas_decode_paged_workspace_bytes(const sas_decode_paged_shape* s) {
@@ -407,13 +416,10 @@ sas_status sas_decode_paged(const sas_decode_paged_shape* s, const void* q, cons
   const sas_decode_shape d = as_decode_shape(s);
   const DecWs w = dec_layout(&d);
   if (!ws || ws_bytes < w.total) return SAS_ERR_WORKSPACE;
-  char* base = static_cast<char*>(ws);
-  float* acc = reinterpret_cast<float*>(base + w.acc_off);
-  float* ml = reinterpret_cast<float*>(base + w.ml_off);
   clear_stale_error();
   return from_hip(sas::launch_decode_paged(s->dtype, q, k_pages, v_pages, page_table, s->num_pages,
-                                           seq_lens, sc, idx_out, acc, ml, o, s->B, s->Hq, s->Hkv,
-                                           s->max_blocks, s->d, s->topk, w.nsplit,
+                                           seq_lens, sc, idx_out, dec_scratch(w, ws), o, s->B,
+                                           s->Hq, s->Hkv, s->max_blocks, s->d, s->topk, w.nsplit,
                                            tau_of(s->scale, s->d), s->gate, stream));
 }
 

@@ -28,8 +28,8 @@ __global__ void __launch_bounds__(64) select_kernel(const float* __restrict__ s,
   int32_t* irow = idx + size_t(row) * topk;
   float* grow = lg + size_t(row) * topk;
   float lse;
-  const int keff = select_row<CPL>(s + size_t(row) * nkb, i, topk, gate, lane, lse,
-                                   [&](int pos, int m, float g) {
+  const int keff = select_row<CPL>(s + size_t(row) * nkb, i, i, topk, gate, lane, lse, NoTag{},
+                                   [&](int pos, int m, int, float g) {
                                      irow[pos] = m;
                                      grow[pos] = g;
                                    });

@@ -39,25 +39,112 @@ SAS_DEV float log_gate_of(int gate, float x, float lse) {
 // order_key(-FLT_MAX) = kNoKey + 1.  A key <= kNoKey is not a candidate.
 constexpr uint32_t kNoKey = 0x007FFFFFu;
 
-// Selects min(topk, candidates) of the blocks m < i of srow.  emit(pos, m,
-// log_gate) is called by the lane holding the pos-th kept block (pos
-// ascending with m), with the log-gate of the gate kind.  Returns the number kept (wave-uniform); lse receives
-// the LSE over the candidates, -inf if there is none.
+// Sum over the wave of a per-lane count c <= CPL, from the population counts
+// of its bits (one ballot per bit).
+template <int CPL>
+SAS_DEV int wave_count_small(uint32_t c) {
+  constexpr int NBITS = CPL < 2 ? 1 : CPL < 4 ? 2 : CPL < 8 ? 3 : CPL < 16 ? 4 : CPL < 32 ? 5 : 6;
+  int n = 0;
+#pragma unroll
+  for (int b = 0; b < NBITS; ++b) n += __popcll(__ballot((c >> b) & 1u)) << b;
+  return n;
+}
+
+// Threshold of a wave's keys for topk: keys > T are kept, then keys == T
+// lowest position first until need_eq are kept.  With search, T is the
+// largest th such that at least topk keys are >= th (a 32-step bitwise
+// search), or kNoKey when fewer than topk candidates exist (then every
+// candidate is kept).  Without search (the caller knows every candidate is
+// kept) T = kNoKey; topk == 0 keeps nothing (T = ~0, no key exceeds it).
 //
-// Non-candidates (m >= i or a score of -inf) carry key kNoKey, below every
-// candidate's key, so the search ends with T <= kNoKey exactly when fewer
-// than topk candidates exist, and then every key > kNoKey is kept.  The number kept is the
-// running output position, so no separate candidate count is needed.
-template <int CPL, class Emit>
-SAS_DEV int select_row(const float* __restrict__ srow, int i, int topk, int gate, int lane,
-                       float& lse, Emit&& emit) {
+// Each step counts the keys >= th | bit over the wave.  VCNT = false: one
+// ballot and scalar population count per key slot - fewest instructions, best
+// when several waves share a SIMD and hide each other's waits.  VCNT = true:
+// each lane counts its own keys in a vector register and the wave sums those
+// counts with a ballot per bit (wave_count_small) - far fewer scalar reads of
+// vector-written masks, each of which stalls a lone wave, so it is the faster
+// form for a wave that runs alone.
+template <int CPL, bool VCNT = false>
+SAS_DEV void wave_threshold(const uint32_t (&key)[CPL], int topk, bool search, uint32_t& T,
+                            int& need_eq) {
+  T = topk > 0 ? kNoKey : ~0u;
+  need_eq = 0;
+  if (!search || topk <= 0) return;
+  uint32_t th = 0u;   // largest th with at least topk keys >= th
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = th | (1u << bit);
+    int n_ge = 0;
+    if constexpr (VCNT) {
+      uint32_t cl = 0;
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) cl += key[j] >= c ? 1u : 0u;
+      n_ge = wave_count_small<CPL>(cl);
+    } else {
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) n_ge += __popcll(__ballot(key[j] >= c));
+    }
+    if (n_ge >= topk) th = c;
+  }
+  if (th > kNoKey) {
+    T = th;
+    int n_gt = 0;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) n_gt += __popcll(__ballot(key[j] > T));
+    need_eq = topk - n_gt;
+  }
+}
+
+// Keeps the keys wave_threshold chose: keep(j, pos) runs on the lane holding
+// the pos-th kept key, positions ascending in (j, lane) order.  Returns the
+// number kept (wave-uniform).
+template <int CPL, class Keep>
+SAS_DEV int wave_keep(const uint32_t (&key)[CPL], uint32_t T, int need_eq, Keep&& keep) {
+  int base = 0, eq_seen = 0;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const bool eq = key[j] == T;
+    const uint64_t eqm = __ballot(eq);
+    const bool take = key[j] > T || (eq && eq_seen + mask_rank(eqm) < need_eq);
+    eq_seen += __popcll(eqm);
+    const uint64_t tm = __ballot(take);
+    if (take) keep(j, base + mask_rank(tm));
+    base += __popcll(tm);
+  }
+  return base;
+}
+
+// No per-candidate tag: emit receives 0.
+struct NoTag {
+  SAS_DEV int operator()(int) const { return 0; }
+};
+
+// Selects min(topk, candidates) of the blocks m < i of srow.  Scores are
+// loaded for m < nk (nk >= i, a bound known at launch, so these loads need not
+// wait for i) and masked to m < i.  tag(m) is loaded alongside (for instance
+// the page of block m) and handed to emit, so that emitting waits on no
+// further memory access.  emit(pos, m, tag, log_gate) is called by the lane
+// holding the pos-th kept block (pos ascending with m), with the log-gate of
+// the gate kind.  Returns the number kept (wave-uniform); lse receives the
+// LSE over the candidates, -inf if there is none.
+//
+// Non-candidates (m >= i or a score of -inf) carry key kNoKey or below, under
+// every candidate's key, so the search ends with T <= kNoKey exactly when
+// fewer than topk candidates exist, and then every key > kNoKey is kept.  The
+// number kept is the running output position, so no separate candidate count
+// is needed.
+template <int CPL, class Tag, class Emit>
+SAS_DEV int select_row(const float* __restrict__ srow, int nk, int i, int topk, int gate, int lane,
+                       float& lse, Tag&& tag_of, Emit&& emit) {
   float val[CPL];
   uint32_t key[CPL];
+  int tag[CPL];
   float mx = -INFINITY;
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
     const int m = j * 64 + lane;
-    val[j] = m < i ? srow[m] : -INFINITY;
+    const float x = m < nk ? srow[m] : -INFINITY;
+    tag[j] = m < nk ? tag_of(m) : 0;
+    val[j] = m < i ? x : -INFINITY;
     key[j] = order_key(val[j]);
     mx = fmaxf(mx, val[j]);
   }
@@ -68,45 +155,110 @@ SAS_DEV int select_row(const float* __restrict__ srow, int i, int topk, int gate
   se = wave_sum(se);
   lse = mx > -INFINITY ? mx + logf(se) : -INFINITY;
 
-  // keep keys > T, then keys == T lowest index first until need_eq are kept;
-  // topk == 0 keeps nothing (no key exceeds ~0), topk >= i every candidate
-  uint32_t T = topk > 0 ? kNoKey : ~0u;
-  int need_eq = 0;
-  if (topk > 0 && topk < i) {
-    uint32_t th = 0u;   // largest th with at least topk keys >= th
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t c = th | (1u << bit);
-      int n_ge = 0;
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) n_ge += __popcll(__ballot(key[j] >= c));
-      if (n_ge >= topk) th = c;
-    }
-    if (th > kNoKey) {
-      T = th;
-      int n_gt = 0;
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) n_gt += __popcll(__ballot(key[j] > T));
-      need_eq = topk - n_gt;
-    }
-  }
-
-  int base = 0, eq_seen = 0;
-#pragma unroll
-  for (int j = 0; j < CPL; ++j) {
-    const int m = j * 64 + lane;
-    const bool eq = key[j] == T;
-    const uint64_t eqm = __ballot(eq);
-    const bool take = key[j] > T || (eq && eq_seen + mask_rank(eqm) < need_eq);
-    eq_seen += __popcll(eqm);
-    const uint64_t tm = __ballot(take);
-    if (take) emit(base + mask_rank(tm), m, log_gate_of(gate, val[j], lse));
-    base += __popcll(tm);
-  }
-  return base;
+  // topk >= i keeps every candidate without a search
+  uint32_t T;
+  int need_eq;
+  wave_threshold(key, topk, topk < i, T, need_eq);
+  return wave_keep(key, T, need_eq, [&](int j, int pos) __attribute__((always_inline)) {
+    emit(pos, j * 64 + lane, tag[j], log_gate_of(gate, val[j], lse));
+  });
 }
 
-// The same selection by a workgroup of NW waves, for rows of up to
-// NW*64*CPL candidates (long decode contexts).  Wave w holds the contiguous
+// The same selection by a workgroup of NW waves, for topk <= 64 and rows of up
+// to NW*64*CPL candidates (long decode contexts), with no barrier inside the
+// search.  Wave w holds the contiguous candidates [w*64*CPL, (w+1)*64*CPL),
+// m = w*64*CPL + j*64 + lane, and first keeps the top min(topk, its
+// candidates) of its own share (by score descending, then index ascending)
+// into its segment of LDS (SEG = 32 slots when topk <= 32, else 64); then wave
+// 0 selects the row's blocks from the NW segments, NW*SEG/64 slots per lane.
+// This is exact: a block among the row's top topk in that strict order is
+// among the top topk of its own share, which has fewer competitors, so every
+// kept block reaches the segments; and the segments, read in slot order, list
+// their blocks in ascending m, so ties at the threshold still go lowest index
+// first.  The LSE is over every candidate: the maximum, then the exp sum (per
+// wave, summed in wave order, so the result is deterministic), through red
+// (2*NW words).  cval, cidx and ctag hold NW*64 entries.  Every thread of the
+// workgroup must call it (it contains __syncthreads); emit(pos, m, tag,
+// log_gate) is called by wave 0's lanes only, and the return value (the
+// number kept) and lse are valid in wave 0 only.
+template <int CPL, int NW, class Tag, class Emit>
+SAS_DEV int select_row_hier(const float* __restrict__ srow, int nk, int i, int topk, int gate,
+                            int wave, int lane, float& lse,
+                            __attribute__((address_space(3))) float* red,
+                            __attribute__((address_space(3))) float* cval,
+                            __attribute__((address_space(3))) int* cidx,
+                            __attribute__((address_space(3))) int* ctag, Tag&& tag_of,
+                            Emit&& emit) {
+  static_assert(NW % 2 == 0, "segments pair up into rows of 64 slots");
+  const int m0 = wave * 64 * CPL;
+  const int seg = topk <= 32 ? 32 : 64;
+  float val[CPL];
+  uint32_t key[CPL];
+  int tag[CPL];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int m = m0 + j * 64 + lane;
+    const float x = m < nk ? srow[m] : -INFINITY;
+    tag[j] = m < nk ? tag_of(m) : 0;
+    val[j] = m < i ? x : -INFINITY;
+    key[j] = order_key(val[j]);
+    mx = fmaxf(mx, val[j]);
+  }
+  // this wave's share: positions [m0, min(i, m0 + 64*CPL)); a share of at
+  // most topk positions keeps every candidate without a search
+  const int share = min(max(i - m0, 0), 64 * CPL);
+  {
+    uint32_t T;
+    int need_eq;
+    wave_threshold<CPL, (NW <= 4)>(key, topk, topk < share, T, need_eq);
+    const int s0 = wave * seg;
+    const int kept = wave_keep(key, T, need_eq, [&](int j, int pos) __attribute__((always_inline)) {
+      cval[s0 + pos] = val[j];
+      cidx[s0 + pos] = m0 + j * 64 + lane;
+      ctag[s0 + pos] = tag[j];
+    });
+    if (lane >= kept && lane < seg) cval[s0 + lane] = -INFINITY;
+  }
+  mx = wave_max(mx);
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  float gmx = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) gmx = fmaxf(gmx, red[w]);
+  float se = 0.f;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) se += expf(val[j] - gmx);   // -inf terms add 0
+  se = wave_sum(se);
+  if (lane == 0) red[NW + wave] = se;
+  __syncthreads();
+  if (wave != 0) return 0;
+  float gse = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) gse += red[NW + w];
+  lse = gmx > -INFINITY ? gmx + logf(gse) : -INFINITY;
+
+  // wave 0 over the segments: R rows of 64 slots, slot e = r*64 + lane
+  auto pick = [&]<int R>() __attribute__((always_inline)) {
+    float v2[R];
+    uint32_t k2[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      v2[r] = cval[r * 64 + lane];
+      k2[r] = order_key(v2[r]);
+    }
+    uint32_t T;
+    int need_eq;
+    wave_threshold<R, true>(k2, topk, topk < i, T, need_eq);
+    return wave_keep(k2, T, need_eq, [&](int r, int pos) __attribute__((always_inline)) {
+      emit(pos, cidx[r * 64 + lane], ctag[r * 64 + lane], log_gate_of(gate, v2[r], lse));
+    });
+  };
+  return seg == 32 ? pick.template operator()<NW / 2>() : pick.template operator()<NW>();
+}
+
+// The same selection by a workgroup of NW waves, for any topk and rows of up
+// to NW*64*CPL candidates (long decode contexts).  Wave w holds the contiguous
 // candidates [w*64*CPL, (w+1)*64*CPL), m = w*64*CPL + j*64 + lane, so waves in
 // order, then j, then lanes visit m ascending.  The maximum, the exp sum
 // (summed in wave order, so the result is deterministic) and every count of
@@ -116,20 +268,24 @@ SAS_DEV int select_row(const float* __restrict__ srow, int i, int topk, int gate
 // wave has read it).  Ties at the threshold and output positions follow from
 // the per-wave counts of the waves before.  Every thread of the workgroup must
 // call it (it contains __syncthreads).
-template <int CPL, int NW, class Emit>
-SAS_DEV int select_row_wg(const float* __restrict__ srow, int i, int topk, int gate, int wave,
-                          int lane, float& lse, __attribute__((address_space(3))) float* red,
+template <int CPL, int NW, class Tag, class Emit>
+SAS_DEV int select_row_wg(const float* __restrict__ srow, int nk, int i, int topk, int gate,
+                          int wave, int lane, float& lse,
+                          __attribute__((address_space(3))) float* red, Tag&& tag_of,
                           Emit&& emit) {
   __attribute__((address_space(3))) int* ired =
       reinterpret_cast<__attribute__((address_space(3))) int*>(red);
   const int m0 = wave * 64 * CPL;
   float val[CPL];
   uint32_t key[CPL];
+  int tag[CPL];
   float mx = -INFINITY;
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
     const int m = m0 + j * 64 + lane;
-    val[j] = m < i ? srow[m] : -INFINITY;
+    const float x = m < nk ? srow[m] : -INFINITY;
+    tag[j] = m < nk ? tag_of(m) : 0;
+    val[j] = m < i ? x : -INFINITY;
     key[j] = order_key(val[j]);
     mx = fmaxf(mx, val[j]);
   }
@@ -206,7 +362,7 @@ SAS_DEV int select_row_wg(const float* __restrict__ srow, int i, int topk, int g
     const bool take = key[j] > T || (eq && eq_seen + mask_rank(eqm) < need_eq);
     eq_seen += __popcll(eqm);
     const uint64_t tm = __ballot(take);
-    if (take) emit(base + mask_rank(tm), m, log_gate_of(gate, val[j], lse));
+    if (take) emit(base + mask_rank(tm), m, tag[j], log_gate_of(gate, val[j], lse));
     base += __popcll(tm);
   }
   return n_gt + need_eq;

@@ -144,6 +144,12 @@ class PagedDecodeWorkload:
 # Qwen3-8B attention shape, one sequence of a 512K-token context (the batch-1,
 # 512K decode setting of the SAS review page, §4)
 PAGED_DECODE_WORKLOAD = PagedDecodeWorkload(6, 1, 32, 8, 8192, 128, 32)
+# the other decode settings of the review page's §4 speed-up results: batch 1
+# at 64K and 256K tokens, batch 8 at 64K
+PAGED_DECODE_SWEEP = [PagedDecodeWorkload(11, 1, 32, 8, 1024, 128, 32),
+                      PagedDecodeWorkload(12, 1, 32, 8, 4096, 128, 32),
+                      PAGED_DECODE_WORKLOAD,
+                      PagedDecodeWorkload(13, 8, 32, 8, 1024, 128, 32)]
 
 
 def rng(cfg: int, tid: int) -> np.random.Generator:
