@@ -71,23 +71,42 @@ struct Vec16<ElemF32> {
   }
 };
 
-// Sum over aligned groups of W lanes (W = 8, 16 or 32) with DPP lane
-// permutations: swap neighbours, swap pairs, mirror within 8, mirror within
-// 16 (then one swap across the two rows of 16 for W = 32).
+// x plus x of the lane that the DPP control CTRL selects (a permutation
+// within each row of 16 lanes, so no source lane is out of bounds; bound_ctrl
+// set lets the compiler fold the move into the add for every control)
 template <int CTRL>
 SAS_DEV float dpp_add(float x) {
   return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                           0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+                                           0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
-template <int W>
-SAS_DEV float group_sum(float x) {
+// Floor of the running maxima (exp2 domain) in place of -inf, so that
+// exp2(m - mrun) and the rescale exp2(mrun - mnew) never see -inf - -inf: a
+// weight against it is exp2(-inf) = 0 for invalid keys, and the first valid
+// key (any finite score is far above it) rescales everything before it by 0.
+constexpr float kMaxFloor = -1.0e30f;
+
+// Sums of N values over aligned groups of W lanes (W = 8, 16 or 32) with DPP
+// lane permutations: swap neighbours, swap pairs, mirror within 8, rotate by
+// 8 within 16 (then one swap across the two rows of 16 for W = 32).  Each level
+// runs over all N values before the next, so the N reduction chains
+// interleave (no dependent DPP back to back).
+template <int W, int N>
+SAS_DEV void group_sum_all(float* x) {
   static_assert(W == 8 || W == 16 || W == 32, "group width");
-  x = dpp_add<0xB1>(x);     // quad_perm [1,0,3,2]
-  x = dpp_add<0x4E>(x);     // quad_perm [2,3,0,1]
-  x = dpp_add<0x141>(x);    // row_half_mirror
-  if (W >= 16) x = dpp_add<0x140>(x);   // row_mirror
-  if (W == 32) x += __shfl_xor(x, 16);
-  return x;
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = dpp_add<0xB1>(x[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = dpp_add<0x4E>(x[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = dpp_add<0x141>(x[i]);
+  if constexpr (W >= 16) {   // rotate by 8 within the row: the other half
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = dpp_add<0x128>(x[i]);
+  }
+  if constexpr (W == 32) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += __shfl_xor(x[i], 16);
+  }
 }
 
 // grid: B*Hkv*nsplit workgroups of 256 threads.
@@ -127,7 +146,7 @@ __global__ void __launch_bounds__(256) decode_kernel(
   // computed; fewer heads per kv-head leave registers for more buffers (the
   // launches hold about two workgroups per CU, so registers are not what
   // limits occupancy)
-  constexpr int NB = GMAX <= 4 ? 4 : 3;
+  constexpr int NB = 3;
   const int split = blockIdx.x % nsplit;
   const int bk = blockIdx.x / nsplit;
   const int b = bk / Hkv, kv = bk % Hkv;
@@ -228,7 +247,7 @@ __global__ void __launch_bounds__(256) decode_kernel(
   float mrun[GMAX], lrun[GMAX];
 #pragma unroll
   for (int g = 0; g < GMAX; ++g) {
-    mrun[g] = -INFINITY;
+    mrun[g] = kMaxFloor;
     lrun[g] = 0.f;
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[g][e] = 0.f;
@@ -269,12 +288,14 @@ __global__ void __launch_bounds__(256) decode_kernel(
     const float bias2 = bias_of(tile);
     const float wsum_scale = ext ? fast_exp2(-bias2) : 1.f;   // 1/g for the external gate
     const int nvalid = tile < c_sel ? SAS_BLK : L - icur * SAS_BLK;
+    // every head slot g < GMAX is computed (those >= G have a zero query, and
+    // their results are never stored), so the loop has no per-head branch
     float sc[KPT][GMAX];
 #pragma unroll
     for (int u = 0; u < KPT; ++u)
 #pragma unroll
-      for (int g = 0; g < GMAX; ++g)
-        sc[u][g] = g < G ? group_sum<CPR>(Vec16<E>::dot(qv[g], kb[B][u], 0.f)) : 0.f;
+      for (int g = 0; g < GMAX; ++g) sc[u][g] = Vec16<E>::dot(qv[g], kb[B][u], 0.f);
+    group_sum_all<CPR, KPT * GMAX>(&sc[0][0]);
     // bf16: V of key pairs (2x, 2x+1) regrouped once per tile, shared by all
     // heads: word w of vp[x][h] holds elements 2w+h of the two keys, so
     // acc += p0 v0 + p1 v1 is one v_dot2_f32_bf16 per element.
@@ -293,14 +314,14 @@ __global__ void __launch_bounds__(256) decode_kernel(
     }
 #pragma unroll
     for (int g = 0; g < GMAX; ++g) {
-      if (g >= G) continue;
+      // a group without a valid key in the tile has mt = -inf: it adds
+      // weights exp2(-inf - mrun) = 0 and never raises mrun
       float mt = -INFINITY;
 #pragma unroll
       for (int u = 0; u < KPT; ++u) {
         sc[u][g] = kg + KG * u < nvalid ? __builtin_fmaf(sc[u][g], tau2, bias2) : -INFINITY;
         mt = fmaxf(mt, sc[u][g]);
       }
-      if (mt == -INFINITY) continue;   // no valid key of this group in the tile
       if (__any(mt > mrun[g] + kSlack)) {
         const float mnew = fmaxf(mrun[g], mt);
         const float corr = fast_exp2(mrun[g] - mnew);
@@ -371,18 +392,18 @@ __global__ void __launch_bounds__(256) decode_kernel(
   __syncthreads();
   for (int x = t; x < G * D; x += 256) {
     const int g = x / D, c = x % D;
-    float M = -INFINITY;
+    float M = kMaxFloor;
 #pragma unroll
     for (int k = 0; k < KG; ++k) M = fmaxf(M, sm[k][g]);
     float a = 0.f, l = 0.f;
-    if (M != -INFINITY) {
 #pragma unroll
-      for (int k = 0; k < KG; ++k) {
-        if (sm[k][g] == -INFINITY) continue;
-        const float w = fast_exp2(sm[k][g] - M);
-        a = __builtin_fmaf(w, sacc[k][g][c], a);
-        l = __builtin_fmaf(w, sl[k][g], l);
-      }
+    for (int k = 0; k < KG; ++k) {
+      // a group that saw no valid key (mrun still kMaxFloor, acc = l = 0)
+      // weighs 0 here unless no group saw one (a split without keys), when
+      // every term is 0 anyway
+      const float w = fast_exp2(sm[k][g] - M);
+      a = __builtin_fmaf(w, sacc[k][g][c], a);
+      l = __builtin_fmaf(w, sl[k][g], l);
     }
     const size_t bh = size_t(b) * Hq + kv * G + g;
     if constexpr (!PRESEL) {
