@@ -217,9 +217,15 @@ __global__ void __launch_bounds__(256) decode_kernel(
     } else if (topk <= 64) {
       __shared__ float cval[SW * 64];
       __shared__ int cidx[SW * 64], ctag[SW * 64];
+      __shared__ uint32_t thr[SW + 4];
+      // four waves merge in one level: no second-level segments
       const int keff = select_row_hier<CPL, SW>(
           srow, nkb, icur, topk, gate, wave, lane, lse,
           (__attribute__((address_space(3))) float*)sel_red,
+          (__attribute__((address_space(3))) float*)cval,
+          (__attribute__((address_space(3))) int*)cidx,
+          (__attribute__((address_space(3))) int*)ctag,
+          (__attribute__((address_space(3))) uint32_t*)thr,
           (__attribute__((address_space(3))) float*)cval,
           (__attribute__((address_space(3))) int*)cidx,
           (__attribute__((address_space(3))) int*)ctag, tag_of, emit);
@@ -463,13 +469,18 @@ __global__ void __launch_bounds__(64 * NW) decode_select_kernel(
   } else {
     __shared__ float sel_red[6 * NW];
     if (topk <= 64) {
-      __shared__ float cval[NW * 64];
-      __shared__ int cidx[NW * 64], ctag[NW * 64];
+      __shared__ float cval[NW * 64], mval[4 * 64];
+      __shared__ int cidx[NW * 64], ctag[NW * 64], midx[4 * 64], mtag[4 * 64];
+      __shared__ uint32_t thr[NW + 4];
       keff = select_row_hier<CPL, NW>(srow, nkb, icur, topk, gate, wave, lane, lse,
                                       (__attribute__((address_space(3))) float*)sel_red,
                                       (__attribute__((address_space(3))) float*)cval,
                                       (__attribute__((address_space(3))) int*)cidx,
-                                      (__attribute__((address_space(3))) int*)ctag, tag_of, emit);
+                                      (__attribute__((address_space(3))) int*)ctag,
+                                      (__attribute__((address_space(3))) uint32_t*)thr,
+                                      (__attribute__((address_space(3))) float*)mval,
+                                      (__attribute__((address_space(3))) int*)midx,
+                                      (__attribute__((address_space(3))) int*)mtag, tag_of, emit);
     } else {
       keff = select_row_wg<CPL, NW>(srow, nkb, icur, topk, gate, wave, lane, lse,
                                     (__attribute__((address_space(3))) float*)sel_red, tag_of,

@@ -16,6 +16,8 @@
 // keeps min(K, finite scores) blocks and a row without one gets LSE -inf.
 #pragma once
 
+#include <utility>
+
 #include "common.h"
 #include "sas.h"
 
@@ -64,14 +66,27 @@ SAS_DEV int wave_count_small(uint32_t c) {
 // counts with a ballot per bit (wave_count_small) - far fewer scalar reads of
 // vector-written masks, each of which stalls a lone wave, so it is the faster
 // form for a wave that runs alone.
+//
+// lo, hi (optional): bounds of the result known to the caller - at least
+// topk keys are >= lo (so lo <= T) and no key exceeds hi.  The search builds
+// T from its top bit down, one bit per step, and every value in [lo, hi]
+// shares the bits above the highest bit where lo and hi differ, so the
+// search starts with those bits set and tests only the bits below: the same
+// T in fewer steps.  lo = 0 (the default) is no bound.
 template <int CPL, bool VCNT = false>
 SAS_DEV void wave_threshold(const uint32_t (&key)[CPL], int topk, bool search, uint32_t& T,
-                            int& need_eq) {
+                            int& need_eq, uint32_t lo = 0u, uint32_t hi = ~0u) {
   T = topk > 0 ? kNoKey : ~0u;
   need_eq = 0;
   if (!search || topk <= 0) return;
   uint32_t th = 0u;   // largest th with at least topk keys >= th
-  for (int bit = 31; bit >= 0; --bit) {
+  int top = 31;
+  if (lo != 0u && lo <= hi) {
+    const uint32_t diff = lo ^ hi;
+    top = diff == 0u ? -1 : 31 - __builtin_clz(diff);
+    th = top < 0 ? lo : lo & ~((2u << top) - 1u);   // 2u << 31 wraps to 0: th = 0
+  }
+  for (int bit = top; bit >= 0; --bit) {
     const uint32_t c = th | (1u << bit);
     int n_ge = 0;
     if constexpr (VCNT) {
@@ -166,19 +181,25 @@ SAS_DEV int select_row(const float* __restrict__ srow, int nk, int i, int topk, 
 
 // The same selection by a workgroup of NW waves, for topk <= 64 and rows of up
 // to NW*64*CPL candidates (long decode contexts), with no barrier inside the
-// search.  Wave w holds the contiguous candidates [w*64*CPL, (w+1)*64*CPL),
+// searches.  Wave w holds the contiguous candidates [w*64*CPL, (w+1)*64*CPL),
 // m = w*64*CPL + j*64 + lane, and first keeps the top min(topk, its
 // candidates) of its own share (by score descending, then index ascending)
-// into its segment of LDS (SEG = 32 slots when topk <= 32, else 64); then wave
-// 0 selects the row's blocks from the NW segments, NW*SEG/64 slots per lane.
-// This is exact: a block among the row's top topk in that strict order is
-// among the top topk of its own share, which has fewer competitors, so every
-// kept block reaches the segments; and the segments, read in slot order, list
-// their blocks in ascending m, so ties at the threshold still go lowest index
-// first.  The LSE is over every candidate: the maximum, then the exp sum (per
-// wave, summed in wave order, so the result is deterministic), through red
-// (2*NW words).  cval, cidx and ctag hold NW*64 entries.  Every thread of the
-// workgroup must call it (it contains __syncthreads); emit(pos, m, tag,
+// into its segment of LDS (SEG = 32 slots when topk <= 32, else 64).  The
+// segments are then merged the same way: by wave 0 alone for NW = 4; for
+// NW >= 8 in two levels, four waves each keeping the top of NW/4 segments,
+// then wave 0 the top of their four.  This is exact: a block among the top
+// topk of a set in that strict order is among the top topk of any subset
+// holding it, so every kept block survives each level; and segments read in
+// slot order list their blocks in ascending m, so ties at the threshold
+// still go lowest index first.  Each merge search starts from bounds: the
+// largest threshold of the segments it merges (at least topk keys reach it)
+// and the row's largest key.
+//
+// The LSE is over every candidate: the maximum, then the exp sum (per wave,
+// summed in wave order, so the result is deterministic), through red (2*NW
+// words).  cval, cidx and ctag hold NW*64 entries, thr NW + 4 words, and
+// mval, midx, mtag 4*64 entries (the second level's inputs).  Every thread of
+// the workgroup must call it (it contains __syncthreads); emit(pos, m, tag,
 // log_gate) is called by wave 0's lanes only, and the return value (the
 // number kept) and lse are valid in wave 0 only.
 template <int CPL, int NW, class Tag, class Emit>
@@ -187,11 +208,18 @@ SAS_DEV int select_row_hier(const float* __restrict__ srow, int nk, int i, int t
                             __attribute__((address_space(3))) float* red,
                             __attribute__((address_space(3))) float* cval,
                             __attribute__((address_space(3))) int* cidx,
-                            __attribute__((address_space(3))) int* ctag, Tag&& tag_of,
+                            __attribute__((address_space(3))) int* ctag,
+                            __attribute__((address_space(3))) uint32_t* thr,
+                            __attribute__((address_space(3))) float* mval,
+                            __attribute__((address_space(3))) int* midx,
+                            __attribute__((address_space(3))) int* mtag, Tag&& tag_of,
                             Emit&& emit) {
-  static_assert(NW % 2 == 0, "segments pair up into rows of 64 slots");
+  static_assert(NW == 4 || NW == 8 || NW == 16, "four, eight or sixteen waves");
   const int m0 = wave * 64 * CPL;
   const int seg = topk <= 32 ? 32 : 64;
+  // a threshold that bounds a merge from below: only a real candidate key
+  // (a wave with fewer than topk candidates keeps them all and bounds nothing)
+  auto bound = [](uint32_t T) { return T > kNoKey && T != ~0u ? T : 0u; };
   float val[CPL];
   uint32_t key[CPL];
   int tag[CPL];
@@ -219,6 +247,7 @@ SAS_DEV int select_row_hier(const float* __restrict__ srow, int nk, int i, int t
       ctag[s0 + pos] = tag[j];
     });
     if (lane >= kept && lane < seg) cval[s0 + lane] = -INFINITY;
+    if (lane == 0) thr[wave] = bound(T);
   }
   mx = wave_max(mx);
   if (lane == 0) red[wave] = mx;
@@ -226,35 +255,74 @@ SAS_DEV int select_row_hier(const float* __restrict__ srow, int nk, int i, int t
   float gmx = -INFINITY;
 #pragma unroll
   for (int w = 0; w < NW; ++w) gmx = fmaxf(gmx, red[w]);
+  const uint32_t hi = order_key(gmx);   // no candidate's key exceeds it
   float se = 0.f;
 #pragma unroll
   for (int j = 0; j < CPL; ++j) se += expf(val[j] - gmx);   // -inf terms add 0
   se = wave_sum(se);
   if (lane == 0) red[NW + wave] = se;
+
+  // merge of the segments [s_first, s_first + nseg) held in (v, x, g) (R rows
+  // of 64 slots): the threshold of their top topk; keep(r, pos) on the lane
+  // holding each kept slot, positions ascending
+  auto merge = [&]<int R>(const __attribute__((address_space(3))) float* v, int row0, int s_first,
+                          int nseg, auto&& keep) __attribute__((always_inline)) {
+    float v2[R];
+    uint32_t k2[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      v2[r] = v[(row0 + r) * 64 + lane];
+      k2[r] = order_key(v2[r]);
+    }
+    uint32_t lo = 0u;
+    for (int s = 0; s < nseg; ++s) lo = max(lo, thr[s_first + s]);
+    uint32_t T;
+    int need_eq;
+    wave_threshold<R, true>(k2, topk, topk < i, T, need_eq, lo, hi);
+    const int kept = wave_keep(k2, T, need_eq, [&](int r, int pos) __attribute__((always_inline)) {
+      keep(row0 + r, pos, v2[r]);
+    });
+    return std::make_pair(kept, T);
+  };
+
+  if constexpr (NW >= 8) {
+    // first level: wave q < 4 merges segments [q*NW/4, (q+1)*NW/4)
+    constexpr int G1 = NW / 4;
+    if (wave < 4) {
+      auto lvl1 = [&]<int R>() __attribute__((always_inline)) {
+        const auto kt = merge.template operator()<R>(
+            cval, wave * R, wave * G1, G1, [&](int row, int pos, float vv) __attribute__((always_inline)) {
+              mval[wave * seg + pos] = vv;
+              midx[wave * seg + pos] = cidx[row * 64 + lane];
+              mtag[wave * seg + pos] = ctag[row * 64 + lane];
+            });
+        if (lane >= kt.first && lane < seg) mval[wave * seg + lane] = -INFINITY;
+        if (lane == 0) thr[NW + wave] = bound(kt.second);
+      };
+      if (seg == 32) lvl1.template operator()<G1 / 2>();
+      else lvl1.template operator()<G1>();
+    }
+  }
   __syncthreads();
   if (wave != 0) return 0;
   float gse = 0.f;
 #pragma unroll
   for (int w = 0; w < NW; ++w) gse += red[NW + w];
   lse = gmx > -INFINITY ? gmx + logf(gse) : -INFINITY;
-
-  // wave 0 over the segments: R rows of 64 slots, slot e = r*64 + lane
-  auto pick = [&]<int R>() __attribute__((always_inline)) {
-    float v2[R];
-    uint32_t k2[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      v2[r] = cval[r * 64 + lane];
-      k2[r] = order_key(v2[r]);
-    }
-    uint32_t T;
-    int need_eq;
-    wave_threshold<R, true>(k2, topk, topk < i, T, need_eq);
-    return wave_keep(k2, T, need_eq, [&](int r, int pos) __attribute__((always_inline)) {
-      emit(pos, cidx[r * 64 + lane], ctag[r * 64 + lane], log_gate_of(gate, v2[r], lse));
-    });
+  // last level: wave 0 over four segments (of the first level for NW >= 8,
+  // of phase A for NW = 4)
+  constexpr bool TWO = NW >= 8;
+  const __attribute__((address_space(3))) float* v = TWO ? mval : cval;
+  const __attribute__((address_space(3))) int* x = TWO ? midx : cidx;
+  const __attribute__((address_space(3))) int* g = TWO ? mtag : ctag;
+  auto last = [&]<int R>() __attribute__((always_inline)) {
+    return merge.template operator()<R>(
+               v, 0, TWO ? NW : 0, 4, [&](int row, int pos, float vv) __attribute__((always_inline)) {
+                 emit(pos, x[row * 64 + lane], g[row * 64 + lane], log_gate_of(gate, vv, lse));
+               })
+        .first;
   };
-  return seg == 32 ? pick.template operator()<NW / 2>() : pick.template operator()<NW>();
+  return seg == 32 ? last.template operator()<2>() : last.template operator()<4>();
 }
 
 // The same selection by a workgroup of NW waves, for any topk and rows of up
