@@ -428,6 +428,25 @@ def test_decode_parity_small(api, dtype, G, d, cap, K):
     assert_o(host(o), ref_o, dtype)
 
 
+@pytest.mark.parametrize("ties,K", [(False, 48), (True, 64)])
+def test_decode_parity_fused_wide_k(api, ties, K):
+    """512 rows (batch 64 x 8 kv-heads: one workgroup per row, whose four
+    waves select into 64-slot segments) with 32 < K <= 64; some rows hold
+    fewer history blocks than K, one only its current block; with ties,
+    equal scores straddle the waves' shares."""
+    w = si.DecodeWorkload(296 + K, 64, 8, 8, 4096, 64, K, "bf16", hist_blocks=63)
+    q, kc, vc, lens, s = si.make_decode_small(w)
+    lens[::7] = 40 * BLOCK + 5
+    lens[1] = 1
+    if ties:
+        s = np.round(s * 2).astype(np.float32)
+    dt = tdtype(w.dtype)
+    o, idx = _decode_run(api, w, dev(q, dt), dev(kc, dt), dev(vc, dt), lens, s)
+    ref_o, ref_idx = oracle.decode(q, kc, vc, lens, s, K)
+    assert np.array_equal(host(idx), ref_idx)
+    assert_o(host(o), ref_o, "bf16")
+
+
 def test_decode_parity_max_cache(api):
     """A contiguous cache of the longest size the ABI accepts (131072 tokens,
     rows of up to 2047 history blocks selected by one wave)."""
@@ -527,7 +546,8 @@ def test_decode_paged_parity_small(api, dtype, G, d, max_blocks, num_pages, K):
     assert_o(o, ref_o, dtype)
 
 
-@pytest.mark.parametrize("ties,K", [(False, 32), (True, 32), (False, 0), (True, 2048)])
+@pytest.mark.parametrize("ties,K", [(False, 32), (True, 32), (False, 0), (True, 2048), (False, 64),
+                                    (True, 40)])
 def test_decode_paged_long_context(api, ties, K):
     """Rows of up to 8191 history blocks (512K tokens), selected by the whole
     workgroup; with ties, equal scores straddle the waves' candidate ranges."""
