@@ -428,15 +428,16 @@ def test_decode_parity_small(api, dtype, G, d, cap, K):
     assert_o(host(o), ref_o, dtype)
 
 
-@pytest.mark.parametrize("ties,K", [(False, 48), (True, 64)])
-def test_decode_parity_fused_wide_k(api, ties, K):
+@pytest.mark.parametrize("ties,K,nkb", [(False, 48, 64), (True, 64, 64), (True, 100, 128)])
+def test_decode_parity_fused_wide_k(api, ties, K, nkb):
     """512 rows (batch 64 x 8 kv-heads: one workgroup per row, whose four
-    waves select into 64-slot segments) with 32 < K <= 64; some rows hold
-    fewer history blocks than K, one only its current block; with ties,
-    equal scores straddle the waves' shares."""
-    w = si.DecodeWorkload(296 + K, 64, 8, 8, 4096, 64, K, "bf16", hist_blocks=63)
+    waves select) with K > 32: into 64-slot segments for K <= 64, by the
+    workgroup search beyond; some rows hold fewer history blocks than K, one
+    only its current block; with ties, equal scores straddle the waves'
+    shares."""
+    w = si.DecodeWorkload(296 + K, 64, 8, 8, nkb * BLOCK, 64, K, "bf16", hist_blocks=nkb - 1)
     q, kc, vc, lens, s = si.make_decode_small(w)
-    lens[::7] = 40 * BLOCK + 5
+    lens[::7] = (K - 8) * BLOCK + 5
     lens[1] = 1
     if ties:
         s = np.round(s * 2).astype(np.float32)
