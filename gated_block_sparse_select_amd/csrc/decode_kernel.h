@@ -119,9 +119,8 @@ SAS_DEV void group_sum_all(float* x) {
 // NB-1 tiles are in flight while one is computed.  The KG groups are merged once,
 // through LDS, at the end.
 //
-// SW = 1: wave 0 selects (rows of up to 64*CPL candidates); SW = 4: the four
-// waves select (up to 256*CPL; select_row_hier for topk <= 64, select_row_wg
-// otherwise).  PAGED: K/V come from a pool of one-block
+// SW = 4: the four waves select rows of up to 256*CPL candidates
+// (select_row_hier for topk <= 64, select_row_wg otherwise).  PAGED: K/V come from a pool of one-block
 // pages [num_pages, Hkv, 64, d]; block m of sequence b lives in page
 // page_table[b, m] (clamped into [0, num_pages)); otherwise from the
 // contiguous cache [B, Hkv, cap, d].
@@ -137,16 +136,15 @@ __global__ void __launch_bounds__(256) decode_kernel(
     const int32_t* __restrict__ seq_lens, const float* __restrict__ s,
     int32_t* __restrict__ idx_out, typename E::T* __restrict__ o, DecodeScratch ws, int Hq,
     int Hkv, int cap, int topk, int nsplit, float tau2, int gate) {
-  static_assert(SW == 1 || SW == 4, "select by one wave or by the workgroup's four");
+  static_assert(SW == 4, "the workgroup's four waves select");
   constexpr int EPC = Vec16<E>::N;        // elements per 16-byte chunk
   constexpr int CPR = D / EPC;            // chunks per key row
   constexpr int KG = 256 / CPR;           // key groups per workgroup
   constexpr int KPT = SAS_BLK / KG;       // keys per thread per tile
   // register buffers: NB-1 tiles of loads stay in flight while one is
-  // computed; fewer heads per kv-head leave registers for more buffers (the
-  // launches hold about two workgroups per CU, so registers are not what
-  // limits occupancy)
-  constexpr int NB = 3;
+  // computed (three measured fastest; sixteen heads per kv-head keep two, as
+  // their accumulators and queries leave no room for a third)
+  constexpr int NB = GMAX >= 16 ? 2 : 3;
   const int split = blockIdx.x % nsplit;
   const int bk = blockIdx.x / nsplit;
   const int b = bk / Hkv, kv = bk % Hkv;
@@ -207,14 +205,7 @@ __global__ void __launch_bounds__(256) decode_kernel(
     const float* srow = s + size_t(bk) * nkb;
     __shared__ float sel_red[6 * SW];
     float lse;
-    if constexpr (SW == 1) {
-      if (wave == 0) {
-        const int keff = select_row<CPL>(srow, nkb, icur, topk, gate, lane, lse, tag_of, emit);
-        if (orow)
-          for (int p = keff + lane; p < topk; p += 64) orow[p] = -1;
-        if (lane == 0) scnt = keff;
-      }
-    } else if (topk <= 64) {
+    if (topk <= 64) {
       __shared__ float cval[SW * 64];
       __shared__ int cidx[SW * 64], ctag[SW * 64];
       __shared__ uint32_t thr[SW + 4];
@@ -295,13 +286,24 @@ __global__ void __launch_bounds__(256) decode_kernel(
     const float wsum_scale = ext ? fast_exp2(-bias2) : 1.f;   // 1/g for the external gate
     const int nvalid = tile < c_sel ? SAS_BLK : L - icur * SAS_BLK;
     // every head slot g < GMAX is computed (those >= G have a zero query, and
-    // their results are never stored), so the loop has no per-head branch
-    float sc[KPT][GMAX];
+    // their results are never stored), so the loop has no per-head branch.
+    // Up to four heads reduce all their sums together; wider groups reduce
+    // head by head (KPT chains at a time), which bounds the live values.
+    float sc[GMAX][KPT];
+    if constexpr (GMAX <= 4) {
 #pragma unroll
-    for (int u = 0; u < KPT; ++u)
+      for (int g = 0; g < GMAX; ++g)
 #pragma unroll
-      for (int g = 0; g < GMAX; ++g) sc[u][g] = Vec16<E>::dot(qv[g], kb[B][u], 0.f);
-    group_sum_all<CPR, KPT * GMAX>(&sc[0][0]);
+        for (int u = 0; u < KPT; ++u) sc[g][u] = Vec16<E>::dot(qv[g], kb[B][u], 0.f);
+      group_sum_all<CPR, KPT * GMAX>(&sc[0][0]);
+    } else {
+#pragma unroll
+      for (int g = 0; g < GMAX; ++g) {
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) sc[g][u] = Vec16<E>::dot(qv[g], kb[B][u], 0.f);
+        group_sum_all<CPR, KPT>(&sc[g][0]);
+      }
+    }
     // bf16: V of key pairs (2x, 2x+1) regrouped once per tile, shared by all
     // heads: word w of vp[x][h] holds elements 2w+h of the two keys, so
     // acc += p0 v0 + p1 v1 is one v_dot2_f32_bf16 per element.
@@ -325,8 +327,8 @@ __global__ void __launch_bounds__(256) decode_kernel(
       float mt = -INFINITY;
 #pragma unroll
       for (int u = 0; u < KPT; ++u) {
-        sc[u][g] = kg + KG * u < nvalid ? __builtin_fmaf(sc[u][g], tau2, bias2) : -INFINITY;
-        mt = fmaxf(mt, sc[u][g]);
+        sc[g][u] = kg + KG * u < nvalid ? __builtin_fmaf(sc[g][u], tau2, bias2) : -INFINITY;
+        mt = fmaxf(mt, sc[g][u]);
       }
       if (__any(mt > mrun[g] + kSlack)) {
         const float mnew = fmaxf(mrun[g], mt);
@@ -343,8 +345,8 @@ __global__ void __launch_bounds__(256) decode_kernel(
 #pragma unroll
         for (int x = 0; x < KPT / 2; ++x) {
           // the weights actually used (bf16) also form the normaliser
-          const bf2 pp = {(__bf16)fast_exp2(sc[2 * x][g] - mrun[g]),
-                          (__bf16)fast_exp2(sc[2 * x + 1][g] - mrun[g])};
+          const bf2 pp = {(__bf16)fast_exp2(sc[g][2 * x] - mrun[g]),
+                          (__bf16)fast_exp2(sc[g][2 * x + 1] - mrun[g])};
           ts = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ts, false);
 #pragma unroll
           for (int w = 0; w < 4; ++w)
@@ -356,7 +358,7 @@ __global__ void __launch_bounds__(256) decode_kernel(
       } else {
 #pragma unroll
         for (int u = 0; u < KPT; ++u) {
-          const float p = fast_exp2(sc[u][g] - mrun[g]);
+          const float p = fast_exp2(sc[g][u] - mrun[g]);
           ts += p;
           float vx[EPC];
           Vec16<E>::unpack(vb[B][u], vx);
@@ -585,7 +587,7 @@ static void dec_c(int G, const void* q, const void* kc, const void* vc, const in
                   float tau2, int gate, hipStream_t st) {
 #define SAS_DEC_ARGS G, q, kc, vc, pt, np, sl, s, idx_out, o, ws, B, Hq, Hkv, cap, topk, ns, tau2, gate, st
   if (ns > 1) {   // rows selected beforehand (decode_select_kernel), tiles split
-    dec_g<E, D, 1, 1, PAGED, true>(SAS_DEC_ARGS);
+    dec_g<E, D, 1, 4, PAGED, true>(SAS_DEC_ARGS);
     return;
   }
   // history rows hold up to cap/64 - 1 candidate blocks; the workgroup's four
