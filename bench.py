@@ -215,7 +215,7 @@ def run_packed(args, api, si, torch, np):
 
 
 def run_configs(args, api, si, torch, np):
-    """The other training-layer workloads of the survey (Qwen3-4B at 8K with
+    """The other training-layer workloads (Qwen3-4B at 8K with
     K = 16, Qwen3-14B at 32K with K = 64 and Gumbel scores): select + fwd +
     bwd, ms per step, effective TFLOP/s and per-kernel times."""
     out = {}
