@@ -270,8 +270,8 @@ __global__ void __launch_bounds__(256) decode_kernel(
     const uint4* vt = reinterpret_cast<const uint4*>(vc + base);
 #pragma unroll
     for (int u = 0; u < KPT; ++u) {
-      kb[B][u] = kt[u * 256 + t];
-      vb[B][u] = vt[u * 256 + t];
+      kb[B][u] = load_stream(kt + u * 256 + t);
+      vb[B][u] = load_stream(vt + u * 256 + t);
     }
   };
   // Lazy running max (exp2 domain): raised only when a tile's max exceeds it

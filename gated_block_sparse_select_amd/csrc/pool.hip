@@ -16,7 +16,7 @@ SAS_DEV void load8(const typename E::T* p, float* o);
 
 template <>
 SAS_DEV void load8<ElemBF16>(const uint16_t* p, float* o) {
-  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint4 u = load_stream(reinterpret_cast<const uint4*>(p));
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
