@@ -142,9 +142,10 @@ __global__ void __launch_bounds__(256) decode_kernel(
   constexpr int KG = 256 / CPR;           // key groups per workgroup
   constexpr int KPT = SAS_BLK / KG;       // keys per thread per tile
   // register buffers: NB-1 tiles of loads stay in flight while one is
-  // computed (three measured fastest; sixteen heads per kv-head keep two, as
-  // their accumulators and queries leave no room for a third)
-  constexpr int NB = GMAX >= 16 ? 2 : 3;
+  // computed.  With the non-temporal K/V loads two measured fastest (94.4 vs
+  // 95.8 us for three and 104 for four at batch 64), and two leave the
+  // eight-head groups without spills.
+  constexpr int NB = 2;
   const int split = blockIdx.x % nsplit;
   const int bk = blockIdx.x / nsplit;
   const int b = bk / Hkv, kv = bk % Hkv;
