@@ -318,7 +318,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
     const float* __restrict__ stats, const float* __restrict__ lg,
     const int32_t* __restrict__ rev_off, const int32_t* __restrict__ rev_list,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int Hq, int Hkv, int n, int topk,
-    float tau, float tau2, const int32_t* __restrict__ geo, int nkb) {
+    float tau, float tau2, const int32_t* __restrict__ geo, int nkb, int pph) {
   constexpr int NS = kKvStages;
   static_assert(NS == 4, "stage arithmetic below assumes a 4-stage ring");
   constexpr int ROWB = D * 2;
@@ -330,15 +330,18 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
   constexpr int TQ = 300, TO = 301, TS = 302;   // LDS buffer tags
 
   const int G = Hq / Hkv;
-  // key-block-major grid: consecutive workgroups take the same key block of
-  // consecutive (batch, kv-head) pairs.  Workgroups are dealt round-robin to
-  // the XCDs, so one XCD serves one kv-head's key blocks m, m+1, ... at a
-  // time; their reverse lists walk similar q-block ranges in ascending order,
-  // so a Q/dO tile one of them loads is often still in that XCD's L2 when the
-  // next needs it.  It also starts the longest lists (small m) first.
-  const int BH = gridDim.x / nkb;
-  const int m = blockIdx.x / BH;
-  const int bk = blockIdx.x % BH;
+  // Grid in phases of pph (batch, kv-head) pairs (pph divides B*Hkv; the
+  // host picks the largest whose Q/dO fit the last-level cache, so a phase's
+  // re-read tiles stay there); inside a phase, key-block-major: consecutive
+  // workgroups take the same key block of consecutive pairs.  Workgroups are
+  // dealt round-robin to the XCDs, so an XCD serves the key blocks m, m+1,
+  // ... of one or two pairs at a time; their reverse lists walk similar
+  // q-block ranges in ascending order, so a Q/dO tile one of them loads is
+  // often still in that XCD's L2 when the next needs it.  Each phase starts
+  // the longest lists (small m) first.
+  const int ph = blockIdx.x / (nkb * pph), pr = blockIdx.x % (nkb * pph);
+  const int m = pr / pph;
+  const int bk = ph * pph + pr % pph;
   const int b = bk / Hkv, kv = bk % Hkv;
   const BlockGeo gm = block_geo(geo, b, nkb, n, m);
   if (gm.hi == gm.lo) return;   // a padding block holds no token (uniform exit)
@@ -720,9 +723,17 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
   if (e != hipSuccess) return e;
   {
     ProfScope ps("sas_bwd_dkdv_kernel", st);
+    // pairs per phase: the largest divisor of B*Hkv whose Q and dO (G heads
+    // each, bf16) fit 256 MiB, the size of the last-level cache; a phase
+    // wider than that re-fetches its re-read tiles from HBM (measured: all
+    // eight kv-heads of the 32K layer at once, 537 MB, ran the step 5-8%
+    // slower than phases of two or four)
+    const size_t pair_bytes = size_t(G) * size_t(n) * size_t(d) * 2 * 2;
+    int pph = BH;
+    while (pph > 1 && (BH % pph != 0 || size_t(pph) * pair_bytes > (size_t(256) << 20))) --pph;
 #define SAS_KV_KARGS (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, \
     (const uint16_t*)dO, stats, lg, rev_off, rev_list, (uint16_t*)dk, (uint16_t*)dv, Hq, Hkv, n, \
-    topk, tau, tau2, geo, nqb
+    topk, tau, tau2, geo, nqb, pph
     if (d == 128 && ext)
       hipLaunchKernelGGL((bwd_dkdv_kernel<128, true>), dim3(BH * nqb), dim3(256), 0, st, SAS_KV_KARGS);
     else if (d == 128)
