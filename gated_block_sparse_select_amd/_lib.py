@@ -16,13 +16,14 @@ SAS_F32, SAS_BF16 = 0, 1
 SAS_GATE_SOFTMAX, SAS_GATE_SIGMOID, SAS_GATE_HARD, SAS_GATE_EXTERNAL = range(4)
 GATES = {"softmax": SAS_GATE_SOFTMAX, "sigmoid": SAS_GATE_SIGMOID, "hard": SAS_GATE_HARD,
          "external": SAS_GATE_EXTERNAL}
-ABI_VERSION = 3
+ABI_VERSION = 4
 NOALLOC_SCRATCH_BYTES = 16 << 20   # SAS_NOALLOC_SCRATCH_BYTES
 BLOCK = 64
 
 EXPORTED = [
     "sas_abi_version", "sas_status_string", "sas_pool_workspace_bytes", "sas_pool_scores",
-    "sas_select", "sas_mask_documents", "sas_blocks_from_cu_seqlens", "sas_fwd", "sas_bwd_workspace_bytes", "sas_bwd",
+    "sas_select", "sas_mask_documents", "sas_blocks_from_cu_seqlens", "sas_fwd", "sas_bwd_workspace_bytes",
+    "sas_bwd_min_workspace_bytes", "sas_bwd",
     "sas_decode_workspace_bytes", "sas_decode", "sas_decode_noalloc",
     "sas_decode_paged_workspace_bytes",
     "sas_decode_paged", "sas_prof_enable", "sas_prof_collect",
@@ -94,6 +95,8 @@ def lib() -> ctypes.CDLL:
         L.sas_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, st]
         L.sas_bwd_workspace_bytes.restype = sz
         L.sas_bwd_workspace_bytes.argtypes = [sp]
+        L.sas_bwd_min_workspace_bytes.restype = sz
+        L.sas_bwd_min_workspace_bytes.argtypes = [sp]
         L.sas_bwd.restype = i32
         L.sas_bwd.argtypes = [sp] + [vp] * 15 + [vp, sz, st]
         L.sas_decode_workspace_bytes.restype = sz

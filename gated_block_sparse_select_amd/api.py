@@ -211,6 +211,10 @@ def sas_bwd_workspace_bytes(shape: SasShape) -> int:
     return int(lib().sas_bwd_workspace_bytes(ctypes.byref(shape)))
 
 
+def sas_bwd_min_workspace_bytes(shape: SasShape) -> int:
+    return int(lib().sas_bwd_min_workspace_bytes(ctypes.byref(shape)))
+
+
 def sas_bwd(shape: SasShape, q, k, v, o, dO, lse, idx, cnt, log_gate, s, s_lse, dq, dk, dv, ds,
             ws, stream=None):
     dt = _dt(shape)
@@ -325,7 +329,7 @@ __all__ = [
     "make_shape", "make_decode_shape", "make_decode_paged_shape", "shape_of",
     "sas_pool_workspace_bytes", "sas_pool_scores", "sas_select", "sas_mask_documents",
     "doc_first_from_cu_seqlens", "blocks_from_cu_seqlens", "nblocks", "sas_fwd",
-    "sas_bwd_workspace_bytes", "sas_bwd", "sas_decode_workspace_bytes", "sas_decode",
+    "sas_bwd_workspace_bytes", "sas_bwd_min_workspace_bytes", "sas_bwd", "sas_decode_workspace_bytes", "sas_decode",
     "sas_decode_noalloc", "sas_decode_paged_workspace_bytes", "sas_decode_paged", "sas_prof_enable", "sas_prof_collect",
     "alloc_select", "alloc_workspace", "status_string", "SasError", "SasShape", "SasDecodeShape",
     "SasDecodePagedShape", "NOALLOC_SCRATCH_BYTES",

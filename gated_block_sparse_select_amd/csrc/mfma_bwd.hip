@@ -311,14 +311,16 @@ __global__ void __launch_bounds__(256) bwd_ds_kernel(const float* __restrict__ d
 // list entries (q-block and base-2 log-gate) are staged in LDS first, so the
 // loop issues no scalar memory loads (those return out of order and would
 // force every LDS wait to drain all outstanding LDS reads).
-template <int D, bool EXT>
+template <int D, bool EXT, bool DZ>
 __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
     const float* __restrict__ stats, const float* __restrict__ lg,
     const int32_t* __restrict__ rev_off, const int32_t* __restrict__ rev_list,
-    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int Hq, int Hkv, int n, int topk,
-    float tau, float tau2, const int32_t* __restrict__ geo, int nkb, int pph) {
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, uint16_t* __restrict__ dz, int Hq,
+    int Hkv, int n, int topk, float tau, float tau2, const int32_t* __restrict__ geo, int nkb,
+    int pph) {
+  static_assert(!(EXT && DZ), "the external gate's dq needs dP itself: no dZ store path");
   constexpr int NS = kKvStages;
   static_assert(NS == 4, "stage arithmetic below assumes a 4-stage ring");
   constexpr int ROWB = D * 2;
@@ -327,7 +329,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
   constexpr int JT = TB / 1024;
   constexpr int JW = 2 * JT / 4;        // Q + dO slices per wave per step
   constexpr int PER = JW + 1;           // plus the row statistics
-  constexpr int TQ = 300, TO = 301, TS = 302;   // LDS buffer tags
+  constexpr int TQ = 300, TO = 301, TS = 302, TL = 303;   // LDS buffer tags
 
   const int G = Hq / Hkv;
   // Grid in phases of pph (batch, kv-head) pairs (pph divides B*Hkv; the
@@ -372,6 +374,10 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
   // window << 11) and base-2 log-gate (0 for the own block, entry 0); the
   // window row is below 2^17 and the q-block below 2^11
   __shared__ int2 meta[SAS_MAX_BLOCKS];
+  // DZ: the dZ slot of each entry (its place in the q-block's kept list,
+  // topk for the own block)
+  typedef __attribute__((address_space(3))) int16_t lds_i16;
+  lds_i16* mslot = reinterpret_cast<lds_i16*>(stage_buf<TL, 0, DZ ? 2 * SAS_MAX_BLOCKS : 4>());
   const int32_t* lst = rev_list + size_t(bk) * nkb * (topk + 1);
   const int32_t e0 = rev_off[size_t(bk) * (nkb + 1) + m];
   const int32_t e1 = rev_off[size_t(bk) * (nkb + 1) + m + 1];
@@ -382,6 +388,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
     const float b2 = (EXT ? fmaxf(l, kMinExtLogGate) : l) * kLog2e;
     const int wq = geo ? block_geo(geo, b, nkb, n, iq).w : iq * SAS_BLK;
     meta[e] = make_int2(iq | (wq << 11), __float_as_int(b2));
+    if constexpr (DZ) mslot[e] = int16_t(slot == 0xFFFF ? topk : slot);
   }
   __syncthreads();
   const int nsteps = (e1 - e0) * G;
@@ -454,7 +461,10 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
     for (int e = 0; e < 8; ++e) {
       const int j = 8 * JC + e;
       float p = fast_exp2(__builtin_fmaf(S[j], tau2, bias2));
-      if (own && kh * 32 + lr > rh * 32 + 8 * (j >> 2) + 4 * hh + (j & 3)) p = 0.f;
+      // DZ: also the window's keys before the block (their dZ is stored for dq)
+      if (own && (kh * 32 + lr > rh * 32 + 8 * (j >> 2) + 4 * hh + (j & 3) ||
+                  (DZ && kh * 32 + lr < gm.lo)))
+        p = 0.f;
       pv[e] = p;
       zv[e] = p * P2[j];
     }
@@ -528,8 +538,33 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
   // Ring: step s lives in stage s % NS.  Iteration s reads stage s (the
   // transposed operands) and stage s + 1 (statistics and rows); after its
   // barrier, stage s - 1 is free and is refilled with step s + NS - 1.
-  f32x16 S, P2;
+  // DZ: the dZ tile of (q-block iq, kept slot, head) is the 8 KB at
+  //   dz + ((((b*Hkv + kv)*nqb + iq)*(topk + 1) + slot)*G + head) * 8192 B,
+  // in this kernel's register order: wave (kh, rh) stores Zp[h] as the 1 KB
+  // slice (kh*2 + rh)*2 + h, 16 B per lane in lane order (one contiguous
+  // store per slice).  Lane l's 16 B hold key kh*32 + l%32 and rows
+  // rh*32 + 16h + 4(l/32) + {0..3} (first 8 B) and + 8 + {0..3} (last 8 B).
+  auto ztile = [&](int e, int head) __attribute__((always_inline)) {
+    const int iq = __builtin_amdgcn_readfirstlane(meta[e].x) & 2047;
+    const int slot = __builtin_amdgcn_readfirstlane(int(mslot[e]));
+    return reinterpret_cast<uint16_t*>(const_cast<char*>(uniform_ptr(
+        dz + ((((size_t(bk) * nkb + iq) * (topk + 1) + slot) * G + head) << 12))));
+  };
+  const uint32_t zlane = lane_off((kh * 2 + rh) * 2048 + lane * 16);   // bytes
+  // global (not flat) stores: a flat store also counts in lgkmcnt, so every
+  // LDS wait of the loop would wait for it as well
+  auto store_dz = [&](uint16_t* zt, const bf16x8 (&Zp)[2]) __attribute__((always_inline)) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(1))) u32x4 g_u32x4;
+    typedef __attribute__((address_space(1))) char g_char;
+    g_char* g = reinterpret_cast<g_char*>(reinterpret_cast<uintptr_t>(zt));
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x4, Zp[h]),
+                                  reinterpret_cast<g_u32x4*>(g + zlane + h * 1024));
+  };  f32x16 S, P2;
   float bias = 0.f;
+  uint16_t* zt = nullptr;   // DZ: dZ tile of step s
   int ce = 0, chd = 0;   // list entry / head of step s + 1 (the next one to start)
   auto advance = [&]() __attribute__((always_inline)) {
     if (++chd == G) {
@@ -541,6 +576,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
   // own-block step (no gate)
   wait_ahead(min(NS - 2, nsteps - 1));
   sdp.template operator()<0>(0.f, S, P2);
+  if constexpr (DZ) zt = ztile(0, 0);
   advance();
 
   // iteration s in stage ST; CHECKED: the ring's end may fall inside
@@ -551,12 +587,16 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
     if (!CHECKED || s + 1 < nsteps) {
       // step s + 1 landed (at most one later step still in flight); every
       // wave is done with stage s - 1
+      // (DZ: the two dZ stores of step s - 1 follow step s + 2's DMA, and
+      // vmcnt counts loads and stores in issue order; the CHECKED waits are
+      // stricter, so they stay correct)
       if (CHECKED) wait_ahead(min(NS - 3, nsteps - 2 - s));
-      else vm_wait_barrier<(NS - 3) * PER>();
+      else vm_wait_barrier<(NS - 3) * PER + (DZ ? 2 : 0)>();
       if (!CHECKED || s + NS - 1 < nsteps) issue.template operator()<(ST + NS - 1) % NS>();
       // base-2 log-gate of step s + 1 (0 for the own block, list entry 0)
       const float bias_n = __int_as_float(meta[ce].y);
       const float bias_s = bias;
+      uint16_t* zt_n = DZ ? ztile(ce, chd) : nullptr;
       f32x16 Sn, P2n;
       tr_ops.template operator()<ST>(tO, tQ);
       sdp.template operator()<ST1>(bias_n, Sn, P2n);
@@ -569,16 +609,19 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
       }
+      if constexpr (DZ) store_dz(zt, Zp);
       dvdk(Pp, Zp, tO, tQ);
       S = Sn;
       P2 = P2n;
       bias = bias_n;
+      zt = zt_n;
       advance();
     } else {
       // last step: nothing further to start
       tr_ops.template operator()<ST>(tO, tQ);
       elementwise.template operator()<0>(S, P2, bias, own, Pp[0], Zp[0]);
       elementwise.template operator()<1>(S, P2, bias, own, Pp[1], Zp[1]);
+      if constexpr (DZ) store_dz(zt, Zp);
       dvdk(Pp, Zp, tO, tQ);
     }
   };
@@ -643,6 +686,239 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
   }
 }
 
+// ------------------------------------------------------------------ dZ path
+// When the workspace holds a dZ tile for every (head, q-block, kept or own
+// block), the key-block-outer kernel stores the dZ it forms (bf16, the values
+// its dK product uses) and dq becomes one product per tile,
+//   dQ_i = tau sum over the tiles of q-block i of dZ_tile K_tile,
+// with no recomputation of S and dP: the backward then executes the five
+// products of the analytic gradient (review page §2.6) plus the S and dP
+// recomputation of the key-outer pass, instead of two recomputations.  The
+// row statistics the key-outer pass seeds its accumulators with come from a
+// small pass over o and dO first.
+
+// grid: one workgroup (256 threads) per (batch, query head, q-block):
+// stats[(b*Hq + h)*nqb + i] = [-lse/tau for the window's 64 rows | -D for
+// them], D = rowsum(dO o O); (-inf, 0) on window rows outside the block, so
+// every weight there is 0.
+template <int D>
+__global__ void __launch_bounds__(256) bwd_stats_kernel(
+    const uint16_t* __restrict__ o, const uint16_t* __restrict__ dO,
+    const float* __restrict__ lse, float* __restrict__ stats, int Hq, int n, float tau,
+    const int32_t* __restrict__ geo, int nqb) {
+  constexpr int CPR = D / 8;       // 16-byte chunks per row
+  constexpr int RPP = 256 / CPR;   // rows per pass
+  const int bh = blockIdx.x / nqb, i = blockIdx.x % nqb;
+  const BlockGeo gi = block_geo(geo, bh / Hq, nqb, n, i);
+  const int tid = threadIdx.x, c = tid % CPR;
+  float* st = stats + size_t(blockIdx.x) * 128;
+  const size_t row0 = size_t(bh) * n + gi.w;
+  float acc[64 / RPP];
+#pragma unroll
+  for (int p = 0; p < 64 / RPP; ++p) {
+    const size_t off = (row0 + p * RPP + tid / CPR) * D + c * 8;
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(o + off);
+    const bf16x8 g = *reinterpret_cast<const bf16x8*>(dO + off);
+    float x = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x = __builtin_fmaf(float(a[e]), float(g[e]), x);
+    acc[p] = x;
+  }
+#pragma unroll
+  for (int p = 0; p < 64 / RPP; ++p) {
+#pragma unroll
+    for (int w = CPR / 2; w > 0; w >>= 1) acc[p] += __shfl_xor(acc[p], w);
+    const int r = p * RPP + tid / CPR;
+    if (c == 0) {
+      const bool ok = r >= gi.lo && r < gi.hi;
+      st[r] = ok ? -lse[row0 + r] / tau : -INFINITY;
+      st[64 + r] = ok ? -acc[p] : 0.f;
+    }
+  }
+}
+
+// grid: (batch, kv-head, q-block i, head chunk) as the dq kernel; 2*GC waves,
+// wave w = query head w/2 of the chunk and half w%2 of the d columns, all 64
+// rows of the window (two waves per SIMD, so one wave's LDS reads overlap the
+// other's products).  Per tile (kept blocks in list order, then the own
+// block) a ring stage holds the K tile (shared by the chunk's heads) and each
+// head's dZ tile; dQ^T += K^T dZ^T with both operands read transposed from
+// LDS.  The dZ tile arrives in the key-outer kernel's register order (8-byte
+// pieces of one key and four consecutive rows); each lane of a
+// DS_READ_B64_TR_B16 names the piece its 4 x 4 transpose needs, so the
+// operand comes out as 8 keys of one row.  On the way into LDS, 16-byte chunk
+// c of every 1 KB slice moves to c ^ ((c >> 5) << 3), so that the 64 pieces of
+// one read fall in distinct 8-byte bank slots two lanes at a time.  The sum
+// of each kept tile's dZ over the chunk's heads is the block-gate gradient
+// partial the ds kernel reads (review page §2.6).
+constexpr int kDqzStages = 3;
+template <int D, int GC>
+__global__ void __launch_bounds__(128 * GC) bwd_dqz_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ dz,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt, uint16_t* __restrict__ dq,
+    float* __restrict__ dlgp, int Hq, int Hkv, int n, int topk, int K, float tau, int BH,
+    int h_off, int hchunks, int nch, int chunk0, const int32_t* __restrict__ geo, int nqb) {
+  constexpr int NS = kDqzStages;
+  constexpr int ROWB = D * 2;
+  constexpr int TB = 64 * ROWB;
+  constexpr int JT = TB / 1024;
+  constexpr int JWK = JT / (2 * GC);      // K slices per wave
+  constexpr int ZB = 64 * 64 * 2;         // bytes of a dZ tile
+  constexpr int JWZ = ZB / 1024 / 2;      // dZ slices per wave (half its head's tile)
+  constexpr int PER = JWK + JWZ;          // DMA instructions per wave per tile
+  constexpr int DT = D / 64;              // 32-column d tiles per wave
+  static_assert(JT % (2 * GC) == 0, "K slices must split evenly over the waves");
+  constexpr int TK = 400, TZ = 401;       // LDS buffer tags
+  __shared__ float part[2][GC];           // per-head dZ sums of the last two tiles
+
+  const int G = Hq / Hkv;
+  int bid = blockIdx.x;
+  const int hc = bid % hchunks;
+  bid /= hchunks;
+  const int bk = bid % BH;
+  const int i = nqb - 1 - bid / BH;
+  const int b = bk / Hkv, kv = bk % Hkv;
+  const BlockGeo gi = block_geo(geo, b, nqb, n, i);
+  if (gi.hi == gi.lo) return;   // a padding block holds no token (uniform exit)
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int lr = lane & 31, hh = lane >> 5;
+  const int hw = wave >> 1, dh = wave & 1;   // head of the chunk, d half
+  const int hg = h_off + hc * GC + hw;       // head within the group
+  const int h = kv * G + hg;
+  const int chunk = chunk0 + hc;
+  const size_t rowsel = size_t(bk) * nqb + i;
+  const int c_sel = cnt[rowsel];
+  const int ntiles = c_sel + 1;
+  const int32_t* irow = idx + rowsel * K;
+  const uint16_t* zrow = dz + ((rowsel * size_t(topk + 1) * G + hg) << 12);
+  const size_t zstride = size_t(G) << 12;   // between the slots of one head
+
+  const size_t kv0 = (size_t(b) * Hkv + kv) * size_t(n);
+  const int slice0 = wave * JWK;
+  uint32_t patk[4];
+  dma_lane_pattern<D>(lane, slice0, patk);
+  const uint32_t patz = uint32_t(lane ^ ((lane >> 5) << 3)) * 16;
+  auto issue = [&]<int BUF>(int t) __attribute__((always_inline)) {
+    const int w0 = t < c_sel ? (geo ? block_geo(geo, b, nqb, n, irow[t]).w : irow[t] * SAS_BLK)
+                             : gi.w;
+    dma_slices<JWK>(k + (kv0 + size_t(w0)) * D, stage_buf<TK, BUF, TB>(), slice0, patk);
+    const char* zg = reinterpret_cast<const char*>(zrow + size_t(t < c_sel ? t : topk) * zstride) +
+                     dh * JWZ * 1024;
+    lds_char* zl = stage_buf<TZ, BUF, GC * ZB>() + hw * ZB + dh * JWZ * 1024;
+#pragma unroll
+    for (int u = 0; u < JWZ; ++u) dma16(uniform_ptr(zg + u * 1024) + opaque(patz), zl + u * 1024);
+  };
+  issue.template operator()<0>(0);
+  if (1 < ntiles) issue.template operator()<1>(1);
+
+  // Transposed dZ reads.  Lane j of a 16-lane group names the piece of key
+  // 16c + 4(grp >> 1) + (j >> 2) + 8w and rows 32hf + 16(grp & 1) + 4(j & 3)
+  // + 0..3 (grp = lane / 16), which the key-outer kernel's wave (c >> 1, hf)
+  // stored in slice half grp & 1, lane (key % 32) + 32 (j & 1), bytes
+  // 8 ((j >> 1) & 1); then lane i of the group receives row 32hf +
+  // 16(grp & 1) + i, keys 16c + 4(grp >> 1) + 8w + 0..3, as tr_operand
+  // orders them.  zo[w] is the byte offset for c = hf = 0; chunk c adds
+  // (c >> 1) * 4096 + (c & 1) * 256, row half hf adds 2048.
+  uint32_t to[DT][2], zo[2];
+  {
+    int toff[D / 32][2];
+    tr_offsets<D>(lane, toff);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int w = 0; w < 2; ++w) to[dt][w] = lane_off(toff[dh * DT + dt][w]);
+    const int grp = lane >> 4, j = lane & 15, zh = j & 1;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const int chunk = 4 * (grp >> 1) + (j >> 2) + 8 * (w ^ zh) + 32 * zh;   // swizzled
+      zo[w] = lane_off(hw * ZB + (grp & 1) * 1024 + chunk * 16 + 8 * ((j >> 1) & 1));
+    }
+  }
+
+  f32x16 dQ[2][DT];   // [row half][32 columns of this wave's d half]: C[m = d][n = row]
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) dQ[hf][dt][jj] = 0.f;
+
+  auto tile = [&]<int ST, bool CUR>(int t) __attribute__((always_inline)) {
+    lds_cchar* Kt = stage_buf<TK, ST, TB>();
+    lds_cchar* Zt = stage_buf<TZ, ST, GC * ZB>();
+    bf16x8 zb[2][4];   // dZ^T operands: 8 keys of key chunk c for one row of half hf
+    bf16x8 ka[DT][4];  // K^T operands: 8 keys of key chunk c for one d column
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        zb[hf][c] = ldtr_pair(Zt + hf * 2048 + (c >> 1) * 4096 + (c & 1) * 256, zo[0], zo[1]);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) ka[dt][c] = ldtr_pair(Kt + c * 16 * ROWB, to[dt][0], to[dt][1]);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        dQ[0][dt] = mfma32(ka[dt][c], zb[0][c], dQ[0][dt]);
+        dQ[1][dt] = mfma32(ka[dt][c], zb[1][c], dQ[1][dt]);
+      }
+    if (!CUR && dh == 0) {
+      float zs = 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) zs = sum_bf16x8(zb[hf][c], zs);
+      zs = wave_sum(zs);
+      if (lane == 0) part[t & 1][hw] = zs;
+    }
+  };
+  auto publish = [&](int t) __attribute__((always_inline)) {   // gate gradient of tile t
+    if (tid == 0) {
+      float a = 0.f;
+      for (int w = 0; w < GC; ++w) a += part[t & 1][w];
+      dlgp[(rowsel * nch + chunk) * K + t] = a;
+    }
+  };
+  auto kept = [&]<int ST>(int t) __attribute__((always_inline)) {
+    vm_wait_barrier<PER * (NS - 2)>();
+    if (t > 0) publish(t - 1);
+    if (t + NS - 1 < ntiles) issue.template operator()<(ST + NS - 1) % NS>(t + NS - 1);
+    tile.template operator()<ST, false>(t);
+  };
+  int t = 0;
+#pragma nounroll
+  for (; t + NS <= c_sel; t += NS)
+    [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
+      (kept.template operator()<S>(t + S), ...);
+    }(std::make_integer_sequence<int, NS>{});
+  [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
+    ((t + S < c_sel ? kept.template operator()<S>(t + S) : void()), ...);
+  }(std::make_integer_sequence<int, NS - 1>{});
+  vm_wait_barrier<0>();
+  if (c_sel > 0) publish(c_sel - 1);
+  [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
+    ((c_sel % NS == S ? tile.template operator()<S, true>(c_sel) : void()), ...);
+  }(std::make_integer_sequence<int, NS>{});
+
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int r = hf * 32 + lr;
+    if (r < gi.lo || r >= gi.hi) continue;   // a window row of another block
+    uint16_t* drow = dq + ((size_t(b) * Hq + h) * n + gi.w + r) * D + dh * (D / 2);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        bf16x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(dQ[hf][dt][4 * jg + e] * tau);
+        *reinterpret_cast<bf16x4*>(drow + dt * 32 + 8 * jg + 4 * hh) = v4;
+      }
+  }
+}
+
 // ------------------------------------------------------------------ host side
 template <int D, int GC>
 static void dq_launch(int nblocks, const void* q, const void* k, const void* v, const void* o,
@@ -690,20 +966,55 @@ size_t bwd_mfma_extra_ws(int B, int Hq, int Hkv, int nb, int topk) {
   return sizeof(float) * size_t(B) * Hkv * nb * nch * size_t(topk > 0 ? topk : 1);
 }
 
+template <int D>
+static void dqz_dispatch(int gc, int nblocks, const void* k, const void* dz, const int32_t* idx,
+                         const int32_t* cnt, void* dq, float* dlgp, int Hq, int Hkv, int n,
+                         int topk, int K, float tau, int BH, int h_off, int hchunks, int nch,
+                         int chunk0, const int32_t* geo, int nqb, hipStream_t st) {
+#define SAS_DQZ_KARGS (const uint16_t*)k, (const uint16_t*)dz, idx, cnt, (uint16_t*)dq, dlgp, Hq, \
+    Hkv, n, topk, K, tau, BH, h_off, hchunks, nch, chunk0, geo, nqb
+  switch (gc) {
+    case 1:
+      hipLaunchKernelGGL((bwd_dqz_kernel<D, 1>), dim3(nblocks), dim3(128), 0, st, SAS_DQZ_KARGS);
+      break;
+    case 2:
+      hipLaunchKernelGGL((bwd_dqz_kernel<D, 2>), dim3(nblocks), dim3(256), 0, st, SAS_DQZ_KARGS);
+      break;
+    default:
+      hipLaunchKernelGGL((bwd_dqz_kernel<D, 4>), dim3(nblocks), dim3(512), 0, st, SAS_DQZ_KARGS);
+      break;
+  }
+#undef SAS_DQZ_KARGS
+}
+
+size_t bwd_dz_bytes(int B, int Hq, int nb, int topk) {
+  return size_t(B) * Hq * size_t(nb) * (size_t(topk) + 1) * 64 * 64 * 2;
+}
+
 hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const void* o,
                            const void* dO, const float* lse, const int32_t* idx,
                            const int32_t* cnt, const float* lg, const float* s,
                            const float* s_lse, void* dq, void* dk, void* dv, float* ds,
                            float* stats, const int32_t* rev_off, const int32_t* rev_list,
-                           float* dlgp, int B, int Hq, int Hkv, int n, int d, int topk, float tau,
-                           int gate, const int32_t* geo, int nqb, hipStream_t st) {
+                           float* dlgp, void* dz, int B, int Hq, int Hkv, int n, int d, int topk,
+                           float tau, int gate, const int32_t* geo, int nqb, hipStream_t st) {
   const int G = Hq / Hkv;
   const bool ext = gate == SAS_GATE_EXTERNAL;
+  const bool zpath = dz != nullptr && !ext;
   const int BH = B * Hkv;
   const float tau2 = tau * kLog2e;
   const int nch = n_head_chunks(G);
   const int K = topk > 0 ? topk : 1;
-  {
+  hipError_t e = hipSuccess;
+  if (zpath) {
+    ProfScope ps("sas_bwd_stats_kernel", st);
+    if (d == 128)
+      hipLaunchKernelGGL((bwd_stats_kernel<128>), dim3(B * Hq * nqb), dim3(256), 0, st,
+                         (const uint16_t*)o, (const uint16_t*)dO, lse, stats, Hq, n, tau, geo, nqb);
+    else
+      hipLaunchKernelGGL((bwd_stats_kernel<64>), dim3(B * Hq * nqb), dim3(256), 0, st,
+                         (const uint16_t*)o, (const uint16_t*)dO, lse, stats, Hq, n, tau, geo, nqb);
+  } else {
     ProfScope ps("sas_bwd_dq_kernel", st);
     int chunk0 = 0;
     for (const HeadChunks& hc : head_chunks(G)) {
@@ -712,15 +1023,15 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
       chunk0 += hc.count;
     }
   }
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
-  {
+  if (!zpath) {
     ProfScope ps("sas_bwd_ds_kernel", st);
     hipLaunchKernelGGL(bwd_ds_kernel, dim3(BH * nqb), dim3(256), 0, st, dlgp, idx, cnt, s, s_lse,
                        ds, nqb, K, nch, gate);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
   {
     ProfScope ps("sas_bwd_dkdv_kernel", st);
     // pairs per phase: the largest divisor of B*Hkv whose Q and dO (G heads
@@ -732,17 +1043,39 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
     int pph = BH;
     while (pph > 1 && (BH % pph != 0 || size_t(pph) * pair_bytes > (size_t(256) << 20))) --pph;
 #define SAS_KV_KARGS (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, \
-    (const uint16_t*)dO, stats, lg, rev_off, rev_list, (uint16_t*)dk, (uint16_t*)dv, Hq, Hkv, n, \
-    topk, tau, tau2, geo, nqb, pph
+    (const uint16_t*)dO, stats, lg, rev_off, rev_list, (uint16_t*)dk, (uint16_t*)dv, \
+    (uint16_t*)dz, Hq, Hkv, n, topk, tau, tau2, geo, nqb, pph
     if (d == 128 && ext)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<128, true>), dim3(BH * nqb), dim3(256), 0, st, SAS_KV_KARGS);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<128, true, false>), dim3(BH * nqb), dim3(256), 0, st, SAS_KV_KARGS);
+    else if (d == 128 && zpath)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<128, false, true>), dim3(BH * nqb), dim3(256), 0, st, SAS_KV_KARGS);
     else if (d == 128)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<128, false>), dim3(BH * nqb), dim3(256), 0, st, SAS_KV_KARGS);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<128, false, false>), dim3(BH * nqb), dim3(256), 0, st, SAS_KV_KARGS);
     else if (ext)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<64, true>), dim3(BH * nqb), dim3(256), 0, st, SAS_KV_KARGS);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<64, true, false>), dim3(BH * nqb), dim3(256), 0, st, SAS_KV_KARGS);
+    else if (zpath)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<64, false, true>), dim3(BH * nqb), dim3(256), 0, st, SAS_KV_KARGS);
     else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<64, false>), dim3(BH * nqb), dim3(256), 0, st, SAS_KV_KARGS);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<64, false, false>), dim3(BH * nqb), dim3(256), 0, st, SAS_KV_KARGS);
 #undef SAS_KV_KARGS
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess || !zpath) return e;
+  {
+    ProfScope ps("sas_bwd_dqz_kernel", st);
+    int chunk0 = 0;
+    for (const HeadChunks& hc : head_chunks(G)) {
+      if (d == 128) dqz_dispatch<128>(hc.gc, BH * nqb * hc.count, k, dz, idx, cnt, dq, dlgp, Hq, Hkv, n, topk, K, tau, BH, hc.h_off, hc.count, nch, chunk0, geo, nqb, st);
+      else dqz_dispatch<64>(hc.gc, BH * nqb * hc.count, k, dz, idx, cnt, dq, dlgp, Hq, Hkv, n, topk, K, tau, BH, hc.h_off, hc.count, nch, chunk0, geo, nqb, st);
+      chunk0 += hc.count;
+    }
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  {
+    ProfScope ps("sas_bwd_ds_kernel", st);
+    hipLaunchKernelGGL(bwd_ds_kernel, dim3(BH * nqb), dim3(256), 0, st, dlgp, idx, cnt, s, s_lse,
+                       ds, nqb, K, nch, gate);
   }
   return hipGetLastError();
 }

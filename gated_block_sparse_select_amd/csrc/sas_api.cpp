@@ -24,9 +24,11 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
                            const int32_t* cnt, const float* lg, const float* s,
                            const float* s_lse, void* dq, void* dk, void* dv, float* ds,
                            float* Dws, const int32_t* rev_off, const int32_t* rev_list,
-                           float* dlgp, int B, int Hq, int Hkv, int n, int d, int topk, float tau,
-                           int gate, const int32_t* geo, int nb, hipStream_t st);
+                           float* dlgp, void* dz, int B, int Hq, int Hkv, int n, int d,
+                           int topk, float tau, int gate, const int32_t* geo, int nb,
+                           hipStream_t st);
 size_t bwd_mfma_extra_ws(int B, int Hq, int Hkv, int nb, int topk);
+size_t bwd_dz_bytes(int B, int Hq, int nb, int topk);
 bool mfma_supported(int d, int G);
 }  // namespace sas
 
@@ -122,8 +124,13 @@ sas_status from_hip(hipError_t e) {
 void clear_stale_error() { (void)hipGetLastError(); }
 
 // ----------------------------------------------------------- bwd workspace
+// The bf16 backward stores dZ (one 64 x 64 bf16 tile per head, q-block and
+// kept or own block) when the workspace has room for it and the tiles take
+// at most kDzMaxBytes; otherwise (and for the external gate, the float32
+// path and a smaller workspace) dq recomputes S and dP instead.
+constexpr size_t kDzMaxBytes = size_t(16) << 30;
 struct BwdWs {
-  size_t D_off, off_off, list_off, dlg_off, total;
+  size_t D_off, off_off, list_off, dlg_off, total, dz_off, total_dz;
 };
 BwdWs bwd_layout(const sas_shape* s) {
   const size_t nb = size_t(nblocks(s));
@@ -136,6 +143,12 @@ BwdWs bwd_layout(const sas_shape* s) {
   w.list_off = align_up(w.off_off + sizeof(int32_t) * BH * (nb + 1));
   w.dlg_off = align_up(w.list_off + sizeof(int32_t) * BH * nb * (size_t(s->topk) + 1));
   w.total = align_up(w.dlg_off + sas::bwd_mfma_extra_ws(s->B, s->Hq, s->Hkv, int(nb), s->topk));
+  w.dz_off = w.total;
+  w.total_dz = w.total;
+  const size_t dzb = sas::bwd_dz_bytes(s->B, s->Hq, int(nb), s->topk);
+  if (s->dtype == SAS_BF16 && s->gate != SAS_GATE_EXTERNAL &&
+      sas::mfma_supported(s->d, s->Hq / s->Hkv) && dzb <= kDzMaxBytes)
+    w.total_dz = align_up(w.dz_off + dzb);
   return w;
 }
 
@@ -259,7 +272,7 @@ void prof_after(const char* name, hipStream_t st) {
 
 extern "C" {
 
-int32_t sas_abi_version(void) { return 3; }
+int32_t sas_abi_version(void) { return 4; }
 
 const char* sas_status_string(sas_status st) {
   switch (st) {
@@ -331,6 +344,11 @@ sas_status sas_fwd(const sas_shape* s, const void* q, const void* k, const void*
 
 size_t sas_bwd_workspace_bytes(const sas_shape* s) {
   if (check_shape(s) != SAS_OK) return 0;
+  return bwd_layout(s).total_dz;
+}
+
+size_t sas_bwd_min_workspace_bytes(const sas_shape* s) {
+  if (check_shape(s) != SAS_OK) return 0;
   return bwd_layout(s).total;
 }
 
@@ -355,11 +373,13 @@ sas_status sas_bwd(const sas_shape* s, const void* q, const void* k, const void*
   hipError_t e = sas::launch_revidx(idx, cnt, rev_off, rev_list, s->B * s->Hkv, nb, s->topk, stream);
   if (e != hipSuccess) return from_hip(e);
   const int G = s->Hq / s->Hkv;
-  if (s->dtype == SAS_BF16 && sas::mfma_supported(s->d, G))
+  if (s->dtype == SAS_BF16 && sas::mfma_supported(s->d, G)) {
+    void* dz = w.total_dz > w.total && ws_bytes >= w.total_dz ? base + w.dz_off : nullptr;
     return from_hip(sas::launch_bwd_mfma(
         q, k, v, o, dO, lse, idx, cnt, log_gate, sc, s_lse, dq, dk, dv, ds, Dws, rev_off, rev_list,
-        reinterpret_cast<float*>(base + w.dlg_off), s->B, s->Hq, s->Hkv, s->n, s->d, s->topk, tau,
-        s->gate, s->blocks, nb, stream));
+        reinterpret_cast<float*>(base + w.dlg_off), dz, s->B, s->Hq, s->Hkv, s->n, s->d, s->topk,
+        tau, s->gate, s->blocks, nb, stream));
+  }
   return from_hip(sas::launch_bwd_simt(s->dtype, q, k, v, o, dO, lse, idx, cnt, log_gate, sc, s_lse,
                                        dq, dk, dv, ds, Dws, rev_off, rev_list, s->B, s->Hq, s->Hkv,
                                        s->n, s->d, s->topk, tau, s->gate, s->blocks, nb, stream));

@@ -147,7 +147,7 @@ typedef struct {
   int32_t gate;
 } sas_decode_paged_shape;
 
-/* Version of this ABI (bumped on any incompatible change): 3. */
+/* Version of this ABI (bumped on any incompatible change): 4. */
 int32_t sas_abi_version(void);
 
 /* Human-readable text of a status code (static storage, never NULL). */
@@ -238,9 +238,17 @@ sas_status sas_fwd(const sas_shape* shape, const void* q, const void* k, const v
  *        of the group's heads over rows of block i and keys of block m;
  *      and ds[i,m] = 0 for m >= i (every entry is written).
  * o and lse must come from sas_fwd on the same inputs; s, idx, cnt, log_gate
- * and s_lse are the sas_select inputs/outputs (idx ascending, as it writes).  ws: device scratch of at least
- * sas_bwd_workspace_bytes(shape) bytes, contents on entry irrelevant. */
+ * and s_lse are the sas_select inputs/outputs (idx ascending, as it writes).
+ * ws: device scratch, contents on entry irrelevant, of at least
+ * sas_bwd_min_workspace_bytes(shape) bytes (SAS_ERR_WORKSPACE otherwise).
+ * With sas_bwd_workspace_bytes(shape) bytes or more, a bf16 call with the
+ * softmax, sigmoid or hard gate keeps the logit gradient dZ of every kept and
+ * own tile (bf16, B*Hq*nb*(topk+1) tiles of 8 KiB) in ws and forms dq from
+ * it instead of recomputing the logits and dP: the same results to rounding,
+ * faster.  The two sizes are equal where that path does not apply (float32,
+ * the external gate, or tiles beyond 16 GiB). */
 size_t sas_bwd_workspace_bytes(const sas_shape* shape);
+size_t sas_bwd_min_workspace_bytes(const sas_shape* shape);
 sas_status sas_bwd(const sas_shape* shape, const void* q, const void* k, const void* v,
                    const void* o, const void* dO, const float* lse, const int32_t* idx,
                    const int32_t* cnt, const float* log_gate, const float* s,

@@ -88,7 +88,7 @@ static int abi_checks(void) {
       ++fails;                                               \
     }                                                        \
   } while (0)
-  EXPECT(sas_abi_version() == 3);
+  EXPECT(sas_abi_version() == 4);
   EXPECT(strncmp(sas_status_string(SAS_OK), "SAS_OK", 6) == 0);
   void* fake = (void*)(uintptr_t)0x1000; /* never dereferenced: validation fails first */
   sas_shape good = {1, 8, 2, 512, 128, 4, 0.0f, SAS_BF16, SAS_GATE_SOFTMAX, 0, NULL};

@@ -24,12 +24,14 @@ def tdtype(w_dtype: str):
 
 
 def run_layer(api, q, k, v, do, s, topk, dtype, scale=0.0, pool=False, bwd=True, doc_first=None,
-              gate="softmax", blocks=None):
+              gate="softmax", blocks=None, min_ws=False):
     """Run (pool) -> (mask documents) -> select -> fwd (-> bwd) on device
     tensors; returns a dict of device tensors.  q,k,v,do are device tensors; s
     is a device float32 tensor (masked in place when doc_first, a device int32
     [B, nb] tensor, is given) or None when pool=True.  blocks: None or the
-    device block table [B, nb, 2] of packed documents of any length."""
+    device block table [B, nb, 2] of packed documents of any length.  min_ws:
+    give the backward only sas_bwd_min_workspace_bytes, so that dq recomputes
+    the logits instead of reading the stored dZ tiles."""
     B, Hq, n, d = q.shape
     Hkv = k.shape[1]
     sh = api.make_shape(B, Hq, Hkv, n, d, topk, dtype, scale, gate, blocks=blocks)
@@ -52,7 +54,8 @@ def run_layer(api, q, k, v, do, s, topk, dtype, scale=0.0, pool=False, bwd=True,
     if bwd:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         ds = torch.empty_like(s)
-        ws = api.alloc_workspace(api.sas_bwd_workspace_bytes(sh))
+        ws = api.alloc_workspace(api.sas_bwd_min_workspace_bytes(sh) if min_ws
+                                 else api.sas_bwd_workspace_bytes(sh))
         api.sas_bwd(sh, q, k, v, o, do, lse, sel["idx"], sel["cnt"], sel["log_gate"], s,
                     sel["s_lse"], dq, dk, dv, ds, ws)
         out.update(dq=dq, dk=dk, dv=dv, ds=ds)

@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from gated_block_sparse_select_amd import _lib, api
 
@@ -35,7 +36,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_status_strings():
     L = _lib.lib()
-    assert L.sas_abi_version() == _lib.ABI_VERSION == 3
+    assert L.sas_abi_version() == _lib.ABI_VERSION == 4
     for st in range(6):
         assert _lib.status_string(st).startswith("SAS")
     assert "unknown" in _lib.status_string(99)
@@ -91,11 +92,19 @@ def test_null_pointers_rejected():
 def test_workspace_checks():
     L = _lib.lib()
     sh = api.make_shape(1, 32, 8, 32768, 128, 32)
-    need = api.sas_bwd_workspace_bytes(sh)
+    need = api.sas_bwd_min_workspace_bytes(sh)
     assert need > 4 * 32 * 32768      # holds at least the row statistics
     args = [FAKE] * 15
     assert L.sas_bwd(ctypes.byref(sh), *args, FAKE, need - 1, None) == 4
     assert L.sas_bwd(ctypes.byref(sh), *args, None, need, None) == 4
+    # the dZ-tile path adds one 64 x 64 bf16 tile per (head, q-block, kept or own block)
+    dz = 1 * 32 * 512 * 33 * 64 * 64 * 2
+    assert api.sas_bwd_workspace_bytes(sh) - need == (dz + 255) // 256 * 256
+    # no dZ tiles for the external gate, the float32 path, or tiles beyond 16 GiB
+    for other in (api.make_shape(1, 32, 8, 32768, 128, 32, gate="external"),
+                  api.make_shape(1, 32, 8, 32768, 128, 32, torch.float32),
+                  api.make_shape(1, 32, 8, 32768, 128, 512)):
+        assert api.sas_bwd_workspace_bytes(other) == api.sas_bwd_min_workspace_bytes(other) > 0
     pneed = api.sas_pool_workspace_bytes(sh)
     assert L.sas_pool_scores(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, pneed - 1, None) == 4
     dsh = api.make_decode_shape(64, 32, 8, 32768, 128, 32)

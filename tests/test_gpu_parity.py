@@ -199,6 +199,30 @@ def test_layer_parity_full(api, name):
 
 
 # ---------------------------------------------------------------- gate variants
+RECOMPUTE_CASES = ["bf16_gqa4_d128", "bf16_gqa5_d64", "bf16_k0", "bf16_kall", "bf16_gqa16_d128",
+                   "bf16_packed_gqa4_d128"]
+
+
+@pytest.mark.parametrize("name", RECOMPUTE_CASES)
+def test_layer_parity_recompute_path(api, name):
+    """The backward with only the minimum workspace: dq recomputes S and dP
+    per tile instead of reading the dZ tiles the key-outer pass stores.  Both
+    paths against the oracle, and against each other."""
+    w, _ = SMALL_CASES[name]
+    q, k, v, do = si.make_qkv(w)
+    sd, df, s = _scores(w)
+    dt = tdtype(w.dtype)
+    args = (dev(q, dt), dev(k, dt), dev(v, dt), dev(do, dt))
+    res = run_layer(api, *args, sd.clone(), w.topk, dt, doc_first=df, min_ws=True)
+    fast = run_layer(api, *args, sd.clone(), w.topk, dt, doc_first=df)
+    _check_select(res, s, w.topk)
+    ref = oracle.sas_forward_backward(q, k, v, do, s, w.topk)
+    tol = TOL[w.dtype]
+    for nm in ("dq", "dk", "dv", "ds"):
+        assert_rel(host(res[nm]), ref[nm], tol["grad"], nm)
+        assert_rel(host(res[nm]), host(fast[nm]), tol["grad"], nm + " (paths)")
+
+
 GATE_CASES = {
     "bf16_gqa4_d128": si.custom_workload(120, 2, 8, 2, 1024, 128, 4, "bf16"),
     "bf16_gqa5_d64_kall": si.custom_workload(121, 1, 5, 1, 512, 64, 8, "bf16", s_std=2.0),
@@ -679,9 +703,11 @@ def _doc_rows(geom, b):
     return np.concatenate([np.arange(a, a + L) for a, L in geom[b] if L > 0])
 
 
-@pytest.mark.parametrize("gate", ["softmax", "external"])
+@pytest.mark.parametrize("gate", ["softmax", "external", "softmax_min_ws"])
 @pytest.mark.parametrize("name", list(VARLEN_CASES))
 def test_varlen_layer_parity(api, name, gate):
+    min_ws = gate.endswith("_min_ws")
+    gate = gate.removesuffix("_min_ws")
     seed, B, Hq, Hkv, n, d, K, dtype, tail = VARLEN_CASES[name]
     w = si.custom_workload(seed, B, Hq, Hkv, n, d, K, dtype, varlen=True, tail=tail)
     q, k, v, do = si.make_qkv(w)
@@ -690,7 +716,7 @@ def test_varlen_layer_parity(api, name, gate):
     dt = tdtype(w.dtype)
     res = run_layer(api, dev(q, dt), dev(k, dt), dev(v, dt), dev(do, dt),
                     torch.from_numpy(s).cuda(), w.topk, dt, doc_first=doc_first, blocks=blocks,
-                    gate=gate)
+                    gate=gate, min_ws=min_ws)
     sm = oracle.mask_documents(s, first).astype(np.float32)
     assert np.array_equal(host(res["s"]), sm)
     _check_select(res, sm, w.topk, gate)
