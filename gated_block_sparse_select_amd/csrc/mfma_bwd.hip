@@ -551,18 +551,21 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
         dz + ((((size_t(bk) * nkb + iq) * (topk + 1) + slot) * G + head) << 12))));
   };
   const uint32_t zlane = lane_off((kh * 2 + rh) * 2048 + lane * 16);   // bytes
-  // global (not flat) stores: a flat store also counts in lgkmcnt, so every
-  // LDS wait of the loop would wait for it as well
+  // Buffer stores: the tile's base lives in a scalar descriptor (8 KB of
+  // records, so no store can leave the tile) and each lane adds one 32-bit
+  // offset; the non-temporal policy keeps the 4 KB-per-step stream, read
+  // back only by the dq kernel, from displacing the re-read Q/dO tiles.  (A
+  // flat store would also count in lgkmcnt and make every LDS wait of the
+  // loop wait for it.)
   auto store_dz = [&](uint16_t* zt, const bf16x8 (&Zp)[2]) __attribute__((always_inline)) {
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(1))) u32x4 g_u32x4;
-    typedef __attribute__((address_space(1))) char g_char;
-    g_char* g = reinterpret_cast<g_char*>(reinterpret_cast<uintptr_t>(zt));
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(zt, 0, 8192, 0x00020000);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      __builtin_nontemporal_store(__builtin_bit_cast(u32x4, Zp[h]),
-                                  reinterpret_cast<g_u32x4*>(g + zlane + h * 1024));
-  };  f32x16 S, P2;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, Zp[h]), rs, int(zlane),
+                                             h * 1024, 2 /* nt */);
+  };
+  f32x16 S, P2;
   float bias = 0.f;
   uint16_t* zt = nullptr;   // DZ: dZ tile of step s
   int ce = 0, chd = 0;   // list entry / head of step s + 1 (the next one to start)
@@ -713,12 +716,12 @@ __global__ void __launch_bounds__(256) bwd_stats_kernel(
   const int tid = threadIdx.x, c = tid % CPR;
   float* st = stats + size_t(blockIdx.x) * 128;
   const size_t row0 = size_t(bh) * n + gi.w;
-  float acc[64 / RPP];
+  float acc[64 / RPP];   // o and dO are read once here: non-temporal loads
 #pragma unroll
   for (int p = 0; p < 64 / RPP; ++p) {
     const size_t off = (row0 + p * RPP + tid / CPR) * D + c * 8;
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(o + off);
-    const bf16x8 g = *reinterpret_cast<const bf16x8*>(dO + off);
+    const bf16x8 a = __builtin_bit_cast(bf16x8, load_stream(reinterpret_cast<const uint4*>(o + off)));
+    const bf16x8 g = __builtin_bit_cast(bf16x8, load_stream(reinterpret_cast<const uint4*>(dO + off)));
     float x = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) x = __builtin_fmaf(float(a[e]), float(g[e]), x);
@@ -807,7 +810,9 @@ __global__ void __launch_bounds__(128 * GC) bwd_dqz_kernel(
                      dh * JWZ * 1024;
     lds_char* zl = stage_buf<TZ, BUF, GC * ZB>() + hw * ZB + dh * JWZ * 1024;
 #pragma unroll
-    for (int u = 0; u < JWZ; ++u) dma16(uniform_ptr(zg + u * 1024) + opaque(patz), zl + u * 1024);
+    for (int u = 0; u < JWZ; ++u)   // read once: the non-temporal policy (aux 2)
+      __builtin_amdgcn_global_load_lds((glb_void*)(uniform_ptr(zg + u * 1024) + opaque(patz)),
+                                       (lds_void*)(zl + u * 1024), 16, 0, 2);
   };
   issue.template operator()<0>(0);
   if (1 < ntiles) issue.template operator()<1>(1);
