@@ -153,7 +153,11 @@ def hbm_kernels(res):
       pooling:   q and k read (bf16), the block means written and read back
                  (float32), the score matrix written (float32);
       selection: the scores of the history (m < i) read, idx and log_gate
-                 (K per row), cnt and s_lse written."""
+                 (K per row), cnt and s_lse written;
+      statistics (backward): o and dO read (bf16), lse read, the row
+                 statistics [-lse/tau | -D] written (float32, 128 per block);
+      dq from the dZ tiles: every dZ tile (8 KB per head, q-block and kept or
+                 own block) read, K read, dq written."""
     w = res["w"]
     pk = res["per_kernel"]
     nb = w.nqb
@@ -172,6 +176,18 @@ def hbm_kernels(res):
         ms = pk["sas_select_kernel"]["avg_ms"]
         out["select"] = dict(bytes=byt, ms=round(ms, 4), GBs=round(byt / (ms * 1e-3) / 1e9, 1),
                              frac=round(byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+    qsize = w.B * w.Hq * w.n * w.d * 2
+    if "sas_bwd_stats_kernel" in pk:
+        byt = 2 * qsize + w.B * w.Hq * w.n * 4 + w.B * w.Hq * nb * 128 * 4
+        ms = pk["sas_bwd_stats_kernel"]["avg_ms"]
+        out["bwd_stats"] = dict(bytes=byt, ms=round(ms, 4), GBs=round(byt / (ms * 1e-3) / 1e9, 1),
+                                frac=round(byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+    if "sas_bwd_dqz_kernel" in pk:
+        tiles = int((res["sel"]["cnt"].long() + 1).sum().item()) * (w.Hq // w.Hkv)
+        byt = tiles * 8192 + w.B * w.Hkv * w.n * w.d * 2 + qsize
+        ms = pk["sas_bwd_dqz_kernel"]["avg_ms"]
+        out["bwd_dqz"] = dict(bytes=byt, ms=round(ms, 4), GBs=round(byt / (ms * 1e-3) / 1e9, 1),
+                              frac=round(byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
     return out
 
 
@@ -187,7 +203,7 @@ def run_gate_variants(args, api, si, torch, np):
                      "TFLOPs": round(total / (res["ms_step"] * 1e-3) / 1e12, 1),
                      "per_kernel_ms": {k: round(v["avg_ms"], 3) for k, v in res["per_kernel"].items()
                                        if k in ("sas_fwd_mfma_kernel", "sas_bwd_dq_kernel",
-                                                "sas_bwd_dkdv_kernel")}}
+                                                "sas_bwd_dqz_kernel", "sas_bwd_dkdv_kernel")}}
         res.clear()
         torch.cuda.empty_cache()
     return out
@@ -260,6 +276,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_qwen3-8b-n32768-K32_a
 KERNEL_SOURCES = {
     "sas_bwd_dkdv_kernel": ["mfma_bwd.hip", "mfma_common.h", "common.h", "launch.h"],
     "sas_bwd_dq_kernel": ["mfma_bwd.hip", "mfma_common.h", "common.h", "launch.h"],
+    "sas_bwd_dqz_kernel": ["mfma_bwd.hip", "mfma_common.h", "common.h", "launch.h"],
+    "sas_bwd_stats_kernel": ["mfma_bwd.hip", "mfma_common.h", "common.h", "launch.h"],
     "sas_fwd_mfma_kernel": ["mfma_fwd.hip", "mfma_common.h", "common.h", "launch.h"],
     "sas_decode_kernel": ["decode.hip", "decode_kernel.h", "select_row.h", "common.h", "launch.h"],
     "sas_decode_paged_kernel": ["decode_paged.hip", "decode_kernel.h", "select_row.h", "common.h",
@@ -292,10 +310,12 @@ def measured_traffic(kernel):
 
 def roofline_for(res):
     """Dominant kernel by time; its algorithmic FLOPs per launch are the
-    contractions it performs on valid pairs: forward 2 (4d per pair), dq pass 3
-    (S, dP, dQ: 6d), dk/dv pass 4 (S, dP, dV, dK: 8d)."""
+    contractions it performs on valid pairs: forward 2 (4d per pair), dq pass
+    recomputing the logits 3 (S, dP, dQ: 6d), dq from the stored dZ tiles 1
+    (dQ: 2d), dk/dv pass 4 (S, dP, dV, dK: 8d)."""
     w = res["w"]
-    per = {"sas_fwd_mfma_kernel": 4, "sas_bwd_dq_kernel": 6, "sas_bwd_dkdv_kernel": 8}
+    per = {"sas_fwd_mfma_kernel": 4, "sas_bwd_dq_kernel": 6, "sas_bwd_dqz_kernel": 2,
+           "sas_bwd_dkdv_kernel": 8}
     pk = res["per_kernel"]
     name = max(pk, key=lambda n: pk[n]["avg_ms"] * pk[n]["launches"])
     if name in per:
