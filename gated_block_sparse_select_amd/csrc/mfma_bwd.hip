@@ -311,6 +311,11 @@ __global__ void __launch_bounds__(256) bwd_ds_kernel(const float* __restrict__ d
 // list entries (q-block and base-2 log-gate) are staged in LDS first, so the
 // loop issues no scalar memory loads (those return out of order and would
 // force every LDS wait to drain all outstanding LDS reads).
+//
+// DZ (the dZ-tile path): each step's bf16 dZ operands are also stored, one
+// 8 KB tile per (q-block, kept slot or own block, head), for the dq kernel;
+// the own block's step then also masks the window's keys before the block's
+// first token, so that the stored tile is exactly the one dq needs.
 template <int D, bool EXT, bool DZ>
 __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -553,8 +558,9 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
   const uint32_t zlane = lane_off((kh * 2 + rh) * 2048 + lane * 16);   // bytes
   // Buffer stores: the tile's base lives in a scalar descriptor (8 KB of
   // records, so no store can leave the tile) and each lane adds one 32-bit
-  // offset; the non-temporal policy keeps the 4 KB-per-step stream, read
-  // back only by the dq kernel, from displacing the re-read Q/dO tiles.  (A
+  // offset; the non-temporal policy keeps the stream (8 KB per workgroup and
+  // step), read back only by the dq kernel, from displacing the re-read Q/dO
+  // tiles.  (A
   // flat store would also count in lgkmcnt and make every LDS wait of the
   // loop wait for it.)
   auto store_dz = [&](uint16_t* zt, const bf16x8 (&Zp)[2]) __attribute__((always_inline)) {
