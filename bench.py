@@ -154,8 +154,10 @@ def hbm_kernels(res):
                  (float32), the score matrix written (float32);
       selection: the scores of the history (m < i) read, idx and log_gate
                  (K per row), cnt and s_lse written;
-      statistics (backward): o and dO read (bf16), lse read, the row
-                 statistics [-lse/tau | -D] written (float32, 128 per block);
+      statistics with the reverse lists (backward, one launch): o and dO read
+                 (bf16), lse read, the row statistics [-lse/tau | -D] written
+                 (float32, 128 per block); the lists' idx/cnt reads and
+                 entries are under 1% of it and not counted;
       dq from the dZ tiles: every dZ tile (8 KB per head, q-block and kept or
                  own block) read, K read, dq written."""
     w = res["w"]
@@ -177,9 +179,9 @@ def hbm_kernels(res):
         out["select"] = dict(bytes=byt, ms=round(ms, 4), GBs=round(byt / (ms * 1e-3) / 1e9, 1),
                              frac=round(byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
     qsize = w.B * w.Hq * w.n * w.d * 2
-    if "sas_bwd_stats_kernel" in pk:
+    if "sas_revidx_stats_kernel" in pk:
         byt = 2 * qsize + w.B * w.Hq * w.n * 4 + w.B * w.Hq * nb * 128 * 4
-        ms = pk["sas_bwd_stats_kernel"]["avg_ms"]
+        ms = pk["sas_revidx_stats_kernel"]["avg_ms"]
         out["bwd_stats"] = dict(bytes=byt, ms=round(ms, 4), GBs=round(byt / (ms * 1e-3) / 1e9, 1),
                                 frac=round(byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
     if "sas_bwd_dqz_kernel" in pk:
@@ -277,7 +279,7 @@ KERNEL_SOURCES = {
     "sas_bwd_dkdv_kernel": ["mfma_bwd.hip", "mfma_common.h", "common.h", "launch.h"],
     "sas_bwd_dq_kernel": ["mfma_bwd.hip", "mfma_common.h", "common.h", "launch.h"],
     "sas_bwd_dqz_kernel": ["mfma_bwd.hip", "mfma_common.h", "common.h", "launch.h"],
-    "sas_bwd_stats_kernel": ["mfma_bwd.hip", "mfma_common.h", "common.h", "launch.h"],
+    "sas_revidx_stats_kernel": ["revidx.hip", "bwd_stats.h", "common.h", "launch.h"],
     "sas_fwd_mfma_kernel": ["mfma_fwd.hip", "mfma_common.h", "common.h", "launch.h"],
     "sas_decode_kernel": ["decode.hip", "decode_kernel.h", "select_row.h", "common.h", "launch.h"],
     "sas_decode_paged_kernel": ["decode_paged.hip", "decode_kernel.h", "select_row.h", "common.h",

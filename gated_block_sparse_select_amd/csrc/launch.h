@@ -41,6 +41,12 @@ hipError_t launch_pool(int dtype, const void* q, const void* k, float* s, float*
 // nkb*(topk+1) entries); entries pack (i | slot<<16), slot 0xFFFF = own block.
 hipError_t launch_revidx(const int32_t* idx, const int32_t* cnt, int32_t* rev_off,
                          int32_t* rev_list, int BH, int nb, int topk, hipStream_t st);
+// The same lists plus, in the same launch, the bf16 backward's row statistics
+// for its dZ-tile path (bwd_stats.h): stats [B*Hq*nb][128] float32.
+hipError_t launch_revidx_stats(const int32_t* idx, const int32_t* cnt, int32_t* rev_off,
+                               int32_t* rev_list, int BH, int nb, int topk, const void* o,
+                               const void* dO, const float* lse, float* stats, int B, int Hq, int n,
+                               int d, float tau, const int32_t* geo, hipStream_t st);
 
 // ---- SIMT (float32) forward / backward (simt.hip)
 hipError_t launch_fwd_simt(int dtype, const void* q, const void* k, const void* v,

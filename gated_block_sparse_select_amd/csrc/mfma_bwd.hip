@@ -700,51 +700,11 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(
 // block), the key-block-outer kernel stores the dZ it forms (bf16, the values
 // its dK product uses) and dq becomes one product per tile,
 //   dQ_i = tau sum over the tiles of q-block i of dZ_tile K_tile,
-// with no recomputation of S and dP: the backward then executes the five
-// products of the analytic gradient (review page §2.6) plus the S and dP
-// recomputation of the key-outer pass, instead of two recomputations.  The
-// row statistics the key-outer pass seeds its accumulators with come from a
-// small pass over o and dO first.
-
-// grid: one workgroup (256 threads) per (batch, query head, q-block):
-// stats[(b*Hq + h)*nqb + i] = [-lse/tau for the window's 64 rows | -D for
-// them], D = rowsum(dO o O); (-inf, 0) on window rows outside the block, so
-// every weight there is 0.
-template <int D>
-__global__ void __launch_bounds__(256) bwd_stats_kernel(
-    const uint16_t* __restrict__ o, const uint16_t* __restrict__ dO,
-    const float* __restrict__ lse, float* __restrict__ stats, int Hq, int n, float tau,
-    const int32_t* __restrict__ geo, int nqb) {
-  constexpr int CPR = D / 8;       // 16-byte chunks per row
-  constexpr int RPP = 256 / CPR;   // rows per pass
-  const int bh = blockIdx.x / nqb, i = blockIdx.x % nqb;
-  const BlockGeo gi = block_geo(geo, bh / Hq, nqb, n, i);
-  const int tid = threadIdx.x, c = tid % CPR;
-  float* st = stats + size_t(blockIdx.x) * 128;
-  const size_t row0 = size_t(bh) * n + gi.w;
-  float acc[64 / RPP];   // o and dO are read once here: non-temporal loads
-#pragma unroll
-  for (int p = 0; p < 64 / RPP; ++p) {
-    const size_t off = (row0 + p * RPP + tid / CPR) * D + c * 8;
-    const bf16x8 a = __builtin_bit_cast(bf16x8, load_stream(reinterpret_cast<const uint4*>(o + off)));
-    const bf16x8 g = __builtin_bit_cast(bf16x8, load_stream(reinterpret_cast<const uint4*>(dO + off)));
-    float x = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x = __builtin_fmaf(float(a[e]), float(g[e]), x);
-    acc[p] = x;
-  }
-#pragma unroll
-  for (int p = 0; p < 64 / RPP; ++p) {
-#pragma unroll
-    for (int w = CPR / 2; w > 0; w >>= 1) acc[p] += __shfl_xor(acc[p], w);
-    const int r = p * RPP + tid / CPR;
-    if (c == 0) {
-      const bool ok = r >= gi.lo && r < gi.hi;
-      st[r] = ok ? -lse[row0 + r] / tau : -INFINITY;
-      st[64 + r] = ok ? -acc[p] : 0.f;
-    }
-  }
-}
+// so dq does not form S and dP again: the backward executes five tile
+// products (S and dP recomputed once, in the key-outer pass, then dV, dK and
+// dQ; review page §2.6) instead of seven.  The row statistics the key-outer
+// pass seeds its accumulators with come from a small pass over o and dO
+// (bwd_stats.h), launched with the reverse lists (revidx.hip).
 
 // grid: (batch, kv-head, q-block i, head chunk) as the dq kernel; 2*GC waves,
 // wave w = query head w/2 of the chunk and half w%2 of the d columns, all 64
@@ -1017,15 +977,7 @@ hipError_t launch_bwd_mfma(const void* q, const void* k, const void* v, const vo
   const int nch = n_head_chunks(G);
   const int K = topk > 0 ? topk : 1;
   hipError_t e = hipSuccess;
-  if (zpath) {
-    ProfScope ps("sas_bwd_stats_kernel", st);
-    if (d == 128)
-      hipLaunchKernelGGL((bwd_stats_kernel<128>), dim3(B * Hq * nqb), dim3(256), 0, st,
-                         (const uint16_t*)o, (const uint16_t*)dO, lse, stats, Hq, n, tau, geo, nqb);
-    else
-      hipLaunchKernelGGL((bwd_stats_kernel<64>), dim3(B * Hq * nqb), dim3(256), 0, st,
-                         (const uint16_t*)o, (const uint16_t*)dO, lse, stats, Hq, n, tau, geo, nqb);
-  } else {
+  if (!zpath) {   // (the dZ-tile path's statistics come with the reverse lists)
     ProfScope ps("sas_bwd_dq_kernel", st);
     int chunk0 = 0;
     for (const HeadChunks& hc : head_chunks(G)) {

@@ -12,6 +12,7 @@
 // the chunk that selected it, and each (row, slot) pair of the chunk writes
 // its entry at the list cursor plus the number of earlier rows in the mask,
 // so every list comes out ascending and the output is deterministic.
+#include "bwd_stats.h"
 #include "common.h"
 #include "launch.h"
 
@@ -21,15 +22,13 @@ constexpr int kRevMaxNb = 2048;
 constexpr int kRevThreads = 1024;
 constexpr int kChunkRows = 64;            // q-blocks per fill chunk (one mask bit each)
 
-__global__ void __launch_bounds__(kRevThreads) revidx_kernel(const int32_t* __restrict__ idx,
-                                                            const int32_t* __restrict__ cnt,
-                                                            int32_t* __restrict__ rev_off,
-                                                            int32_t* __restrict__ rev_list,
-                                                            int nb, int topk) {
+// The lists of pair bh, by one workgroup of kRevThreads threads.
+SAS_DEV void revidx_pair(const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
+                         int32_t* __restrict__ rev_off, int32_t* __restrict__ rev_list, int nb,
+                         int topk, int bh) {
   __shared__ int32_t cursor[kRevMaxNb + 1];
   __shared__ unsigned long long rows[kRevMaxNb];
   __shared__ int32_t wtot[kRevThreads / 64];
-  const int bh = blockIdx.x;
   const int32_t* I = idx + size_t(bh) * nb * topk;
   const int32_t* C = cnt + size_t(bh) * nb;
   int32_t* off = rev_off + size_t(bh) * (nb + 1);
@@ -118,11 +117,57 @@ __global__ void __launch_bounds__(kRevThreads) revidx_kernel(const int32_t* __re
   }
 }
 
+__global__ void __launch_bounds__(kRevThreads) revidx_kernel(const int32_t* __restrict__ idx,
+                                                            const int32_t* __restrict__ cnt,
+                                                            int32_t* __restrict__ rev_off,
+                                                            int32_t* __restrict__ rev_list,
+                                                            int nb, int topk) {
+  revidx_pair(idx, cnt, rev_off, rev_list, nb, topk, blockIdx.x);
+}
+
+// The reverse lists together with the row statistics of the backward's
+// dZ-tile path: workgroups 0 .. BH-1 build the lists (one pair each; these
+// few latency-bound workgroups are dispatched first, so they run while the
+// rest stream o and dO), the others compute four statistics units each
+// (bwd_stats_unit, 256 threads per unit).
+template <int D>
+__global__ void __launch_bounds__(kRevThreads) revidx_stats_kernel(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt, int32_t* __restrict__ rev_off,
+    int32_t* __restrict__ rev_list, int nb, int topk, int BH, const uint16_t* __restrict__ o,
+    const uint16_t* __restrict__ dO, const float* __restrict__ lse, float* __restrict__ stats,
+    int Hq, int n, float tau, const int32_t* __restrict__ geo, int units) {
+  if (int(blockIdx.x) < BH) {
+    revidx_pair(idx, cnt, rev_off, rev_list, nb, topk, blockIdx.x);
+    return;
+  }
+  const int unit = (int(blockIdx.x) - BH) * (kRevThreads / 256) + int(threadIdx.x) / 256;
+  if (unit < units)   // uniform per 256-thread unit; no barrier follows
+    bwd_stats_unit<D>(o, dO, lse, stats, Hq, n, tau, geo, nb, unit, int(threadIdx.x) % 256);
+}
+
 hipError_t launch_revidx(const int32_t* idx, const int32_t* cnt, int32_t* rev_off,
                          int32_t* rev_list, int BH, int nb, int topk, hipStream_t st) {
   ProfScope ps("sas_revidx_kernel", st);
   hipLaunchKernelGGL(revidx_kernel, dim3(BH), dim3(kRevThreads), 0, st, idx, cnt, rev_off, rev_list,
                      nb, topk);
+  return hipGetLastError();
+}
+
+hipError_t launch_revidx_stats(const int32_t* idx, const int32_t* cnt, int32_t* rev_off,
+                               int32_t* rev_list, int BH, int nb, int topk, const void* o,
+                               const void* dO, const float* lse, float* stats, int B, int Hq, int n,
+                               int d, float tau, const int32_t* geo, hipStream_t st) {
+  ProfScope ps("sas_revidx_stats_kernel", st);
+  const int units = B * Hq * nb;
+  constexpr int per = kRevThreads / 256;
+  const dim3 grid(BH + (units + per - 1) / per);
+#define SAS_RS_ARGS idx, cnt, rev_off, rev_list, nb, topk, BH, (const uint16_t*)o, \
+    (const uint16_t*)dO, lse, stats, Hq, n, tau, geo, units
+  if (d == 128)
+    hipLaunchKernelGGL((revidx_stats_kernel<128>), grid, dim3(kRevThreads), 0, st, SAS_RS_ARGS);
+  else
+    hipLaunchKernelGGL((revidx_stats_kernel<64>), grid, dim3(kRevThreads), 0, st, SAS_RS_ARGS);
+#undef SAS_RS_ARGS
   return hipGetLastError();
 }
 

@@ -370,11 +370,20 @@ sas_status sas_bwd(const sas_shape* s, const void* q, const void* k, const void*
   const int nb = nblocks(s);
   const float tau = tau_of(s->scale, s->d);
   clear_stale_error();
-  hipError_t e = sas::launch_revidx(idx, cnt, rev_off, rev_list, s->B * s->Hkv, nb, s->topk, stream);
-  if (e != hipSuccess) return from_hip(e);
   const int G = s->Hq / s->Hkv;
-  if (s->dtype == SAS_BF16 && sas::mfma_supported(s->d, G)) {
-    void* dz = w.total_dz > w.total && ws_bytes >= w.total_dz ? base + w.dz_off : nullptr;
+  const bool mfma = s->dtype == SAS_BF16 && sas::mfma_supported(s->d, G);
+  // the dZ-tile path (bf16, a gate other than the external one, tiles within
+  // the cap, a workspace that holds them); its statistics pass runs in the
+  // reverse-list launch
+  void* dz = mfma && w.total_dz > w.total && ws_bytes >= w.total_dz ? base + w.dz_off : nullptr;
+  hipError_t e = dz != nullptr
+                     ? sas::launch_revidx_stats(idx, cnt, rev_off, rev_list, s->B * s->Hkv, nb,
+                                                s->topk, o, dO, lse, Dws, s->B, s->Hq, s->n, s->d,
+                                                tau, s->blocks, stream)
+                     : sas::launch_revidx(idx, cnt, rev_off, rev_list, s->B * s->Hkv, nb, s->topk,
+                                          stream);
+  if (e != hipSuccess) return from_hip(e);
+  if (mfma) {
     return from_hip(sas::launch_bwd_mfma(
         q, k, v, o, dO, lse, idx, cnt, log_gate, sc, s_lse, dq, dk, dv, ds, Dws, rev_off, rev_list,
         reinterpret_cast<float*>(base + w.dlg_off), dz, s->B, s->Hq, s->Hkv, s->n, s->d, s->topk,
