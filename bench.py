@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--no-packed", action="store_true", help="skip the packed-documents line")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     p.add_argument("--no-configs", action="store_true", help="skip the Qwen3-4B / 14B layer lines")
+    p.add_argument("--no-recompute", action="store_true",
+                   help="skip the headline step on the backward's recompute path")
     p.add_argument("--decode-steps", type=int, default=50)
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run one 1 GiB device copy (reference for HBM byte counters)")
@@ -90,7 +92,8 @@ def kernel_pass(api, torch, step, steps):
     return per, ms
 
 
-def run_training(args, api, si, torch, np, w=None, steps=None, warmup=None, gate="softmax"):
+def run_training(args, api, si, torch, np, w=None, steps=None, warmup=None, gate="softmax",
+                 min_ws=False):
     w = si.WORKLOADS[args.workload] if w is None else w
     steps = args.steps if steps is None else steps
     warmup = args.warmup if warmup is None else warmup
@@ -116,7 +119,10 @@ def run_training(args, api, si, torch, np, w=None, steps=None, warmup=None, gate
     lse = torch.empty((w.B, w.Hq, w.n), dtype=torch.float32, device="cuda")
     dq, dk, dv, ds = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd), torch.empty_like(s)
     ws_pool = api.alloc_workspace(api.sas_pool_workspace_bytes(sh))
-    ws_bwd = api.alloc_workspace(api.sas_bwd_workspace_bytes(sh))
+    # min_ws: only the smallest workspace the backward accepts, so that dq
+    # recomputes the logits instead of reading the stored dZ tiles
+    ws_bwd = api.alloc_workspace(api.sas_bwd_min_workspace_bytes(sh) if min_ws
+                                 else api.sas_bwd_workspace_bytes(sh))
     df = si.make_doc_first(w)
     doc_first = torch.from_numpy(df).cuda() if df is not None else None
     if w.varlen:
@@ -190,6 +196,21 @@ def hbm_kernels(res):
         ms = pk["sas_bwd_dqz_kernel"]["avg_ms"]
         out["bwd_dqz"] = dict(bytes=byt, ms=round(ms, 4), GBs=round(byt / (ms * 1e-3) / 1e9, 1),
                               frac=round(byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+    return out
+
+
+def run_recompute_path(args, api, si, torch, np):
+    """The headline step with the backward's minimum workspace (the recompute
+    path: dq forms S and dP again, no dZ tiles), timed like the gate lines, so
+    the two backward paths are compared on the same box."""
+    res = run_training(args, api, si, torch, np, steps=max(1, args.steps // 2), warmup=1,
+                       min_ws=True)
+    total = res["flop_fwd"] + res["flop_bwd"]
+    out = {"ms_per_step": round(res["ms_step"], 4),
+           "TFLOPs": round(total / (res["ms_step"] * 1e-3) / 1e12, 1),
+           "per_kernel_ms": {k: round(v["avg_ms"], 4) for k, v in res["per_kernel"].items()}}
+    res.clear()
+    torch.cuda.empty_cache()
     return out
 
 
@@ -546,6 +567,8 @@ def main():
         line["cpu_baseline"] = cpu_baseline(res, np)
     res.clear()
     torch.cuda.empty_cache()
+    if not args.no_recompute:
+        line["recompute_path"] = run_recompute_path(args, api, si, torch, np)
     if not args.no_configs:
         line["configs"] = run_configs(args, api, si, torch, np)
     if not args.no_full_range:
