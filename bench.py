@@ -555,7 +555,9 @@ def main():
                    "n": w.n, "block": 64, "topk": w.topk,
                    "scores": "device mean-pool" if w.s_kind == "pool" else w.s_kind,
                    "step": "pool+select+fwd+bwd(dq,dk,dv,ds)" if w.s_kind == "pool"
-                   else "select+fwd+bwd(dq,dk,dv,ds)"},
+                   else "select+fwd+bwd(dq,dk,dv,ds)",
+                   "backward": "dZ tiles" if "sas_bwd_dqz_kernel" in res["per_kernel"]
+                   else "recompute"},
         "frac_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
         "roofline": roofline_for(res),
         "effective_flop": {"fwd": res["flop_fwd"], "bwd": res["flop_bwd"], "pairs": res["pairs"]},
