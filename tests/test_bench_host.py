@@ -67,3 +67,29 @@ def test_hbm_kernel_bytes():
     hist = w.Hkv * nb * (nb - 1) // 2 * 4                    # scores m < i
     assert h["select"]["bytes"] == hist + w.Hkv * nb * (w.topk * 8 + 8)
     assert abs(h["pool"]["frac"] - h["pool"]["GBs"] / 8000.0) < 1e-3
+
+
+def test_backward_pass_bytes_and_dq_flops():
+    """The dZ-tile backward's memory-bound passes: the statistics (o and dO
+    read, lse read, 128 floats per (head, block) written) and dq from the
+    tiles (one 8 KB dZ tile per head and kept or own block, K read once, dq
+    written); its dq kernel counts one contraction (2d FLOP per pair)."""
+    import torch
+    w = si.WORKLOADS[3]
+    g = np.random.default_rng(1)
+    cnt = np.minimum(np.arange(w.nqb), w.topk)[None, None, :].repeat(w.Hkv, axis=1)
+    cnt = cnt.astype(np.int32) - (g.random(cnt.shape) < 0.1)     # some rows keep fewer
+    cnt = np.maximum(cnt, 0).astype(np.int32)
+    res = dict(w=w, sel={"cnt": torch.from_numpy(cnt)}, pairs=10**9,
+               per_kernel={"sas_revidx_stats_kernel": dict(avg_ms=0.09, launches=5),
+                           "sas_bwd_dqz_kernel": dict(avg_ms=1.0, launches=5),
+                           "sas_bwd_dkdv_kernel": dict(avg_ms=3.0, launches=5)})
+    h = bench.hbm_kernels(res)
+    qsize = w.Hq * w.n * w.d * 2
+    assert h["bwd_stats"]["bytes"] == 2 * qsize + w.Hq * w.n * 4 + w.Hq * w.nqb * 128 * 4
+    tiles = int((cnt.astype(np.int64) + 1).sum()) * (w.Hq // w.Hkv)
+    assert h["bwd_dqz"]["bytes"] == tiles * 8192 + w.Hkv * w.n * w.d * 2 + qsize
+    # the dq-from-tiles kernel, when it dominates, counts 2d per pair
+    res["per_kernel"]["sas_bwd_dqz_kernel"]["avg_ms"] = 9.0
+    r = bench.roofline_for(res)
+    assert r["kernel"] == "sas_bwd_dqz_kernel" and r["flop_per_launch"] == 2 * w.d * 10**9
