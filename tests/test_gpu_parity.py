@@ -343,19 +343,23 @@ def _sample_blocks(w, rng, n_blocks=5):
     return sorted(picks)
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4, 10, 9])
-def test_layer_parity_full_size_sampled(api, cfg):
+@pytest.mark.parametrize("cfg,min_ws", [(2, False), (3, False), (4, False), (10, False),
+                                        (9, False), (3, True)],
+                         ids=["2", "3", "4", "10", "9", "3-recompute"])
+def test_layer_parity_full_size_sampled(api, cfg, min_ws):
+    """Full-size layers on sampled blocks; min_ws runs the backward with its
+    minimum workspace (dq recomputes the logits, no dZ tiles)."""
     w = si.WORKLOADS[cfg]
     q, k, v, do = si.make_qkv(w)
     dt = tdtype(w.dtype)
     qd, kd, vd, dod = dev(q, dt), dev(k, dt), dev(v, dt), dev(do, dt)
     df = None
     if w.s_kind == "pool":
-        res = run_layer(api, qd, kd, vd, dod, None, w.topk, dt, pool=True)
+        res = run_layer(api, qd, kd, vd, dod, None, w.topk, dt, pool=True, min_ws=min_ws)
         s = host(res["s"])      # selection parity is defined on the device scores
     else:
         sd, df, s = _scores(w)
-        res = run_layer(api, qd, kd, vd, dod, sd, w.topk, dt, doc_first=df)
+        res = run_layer(api, qd, kd, vd, dod, sd, w.topk, dt, doc_first=df, min_ws=min_ws)
         assert np.array_equal(host(res["s"]), s)
     idx, cnt, lg, s_lse = _check_select(res, s, w.topk)
     rng = np.random.default_rng(cfg)
